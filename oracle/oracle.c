@@ -1,0 +1,446 @@
+/*
+ * CPU oracle for the quantized mixture-of-experts expert FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU baseline of the
+ * benchmark do.  It shares no code, header, table or helper with the HIP path.
+ *
+ * It is the plain definition of what the layer computes, written out in scalar
+ * C with no blocking, fusion or reordering.  Sources (titles of the pages):
+ *   [Q8] "Q8 0 support" (Strata pull request 255), section "GPU expert kernels":
+ *        Q8_0 expert blocks of 32 ("qk 32"), the Q8_0 x Q8_1 block dot, the
+ *        grouped gate/up/down expert path; section "Verified against an oracle":
+ *        Strata's GPU experts quantise activations to Q8_1.
+ *   [KQ] same page, the K-quant follow-up commit: the block sum uses the sum
+ *        of the QUANTISED activations, not the float sum.
+ *   [SY] "Sync upstream Strata v0.1.39 into Lanes" (pull request 24), the SYCL
+ *        port commits: Q8_1 activation bytes match only with a correctly
+ *        rounded fp32 divide; per-token top-k routing over the experts.
+ *   [E0] edge0-strata README, section "Changes from upstream Strata":
+ *        latent-MoE with dense Q8 D/U projections into a 1280/1792-wide latent
+ *        space, expert group labels, Q4_0 x Q8_1 rows.
+ * Where the pages leave a step open the reading taken is stated at that step.
+ *
+ * Precision: integer block sums are exact int32; per-block contributions
+ * d_w * d_a * isum are exact in double; rows, router logits, softmax, SwiGLU
+ * and the combine are evaluated in double and rounded to float where the layer
+ * stores a float.  Build without fast-math and with -ffp-contract=off.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_Q8_0 8
+#define ORC_Q4_0 2
+#define ORC_QK 32
+#define ORC_Q8_1_BYTES 36
+
+typedef struct {
+    int hidden, n_experts, top_k, n_ff, latent;
+    int expert_fmt;           /* ORC_Q8_0 or ORC_Q4_0 */
+    int n_groups, topk_groups;/* 0 = no group limit */
+} orc_desc;
+
+/* Optional per-step outputs, indexed by position i in the token list. */
+typedef struct {
+    double*  logits;   /* [n][E]                      */
+    int32_t* ids;      /* [n][k]                      */
+    float*   weights;  /* [n][k]                      */
+    uint8_t* xq;       /* [n][H/32][36]   Q8_1(x)     */
+    float*   z;        /* [n][L]          latent only */
+    uint8_t* zq;       /* [n][L/32][36]   latent only */
+    float*   h;        /* [n][k][F]                   */
+    uint8_t* hq;       /* [n][k][F/32][36]            */
+    float*   y;        /* [n][k][Kout]                */
+    float*   ylat;     /* [n][L]          latent only */
+    uint8_t* ylq;      /* [n][L/32][36]   latent only */
+    int32_t* isum_gu;  /* [n][k][2F][Kin/32]  gate rows then up rows */
+    int32_t* isum_dn;  /* [n][k][Kout][F/32]          */
+    int32_t* isum_d;   /* [n][L][H/32]    latent only */
+    int32_t* isum_u;   /* [n][H][L/32]    latent only */
+} orc_taps;
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Exact value of a binary16 bit pattern (subnormals included). */
+double orc_f16_decode(uint16_t h) {
+    int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/*
+ * Round a double to binary16, to nearest with ties to even, in one step.
+ * The bit patterns of finite binary16 values are monotonic in magnitude, so a
+ * magnitude a is written as n quanta of its binade (quantum 2^-24 below 2^-14,
+ * 2^(E-10) in binade [2^E, 2^(E+1))), n is rounded with rint (ties to even in
+ * the default rounding mode) and the pattern is rebuilt; a carry out of the
+ * mantissa lands in the next exponent, and past 65504 on infinity.
+ */
+uint16_t orc_f16_encode(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7E00;
+    if (a == 0.0) return sign;
+    if (a >= 65520.0) return sign | 0x7C00;
+    if (a < ldexp(1.0, -14)) {
+        double n = rint(ldexp(a, 24));          /* exact scaling */
+        return sign | (uint16_t)n;               /* n <= 1024; 1024 is 2^-14 */
+    }
+    int ex;
+    frexp(a, &ex);                               /* a = f * 2^ex, f in [0.5, 1) */
+    int E = ex - 1;                              /* a in [2^E, 2^(E+1)) */
+    double n = rint(ldexp(a, 10 - E));           /* in [1024, 2048] */
+    uint32_t bits = ((uint32_t)(E + 15) << 10) + (uint32_t)(n - 1024.0);
+    return sign | (uint16_t)bits;
+}
+
+static inline uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static inline void wr16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)(v & 0xFF); p[1] = (uint8_t)(v >> 8); }
+
+/* ------------------------------------------------------------------------ */
+/* Q8_1 activation blocks [Q8], [KQ], [SY]                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Quantise 32 floats to one Q8_1 block: bytes 0-1 binary16 d, bytes 2-3
+ * binary16 s, bytes 4-35 int8 q.
+ *   amax = max |v|, d = amax / 127 (fp32, correctly rounded divide [SY]),
+ *   q_j  = round-half-away-from-zero(v_j / d) (fp32 divide), 0 when d == 0,
+ *   s    = d * sum_j q_j (fp32 product; the quantised sum [KQ]).
+ * Readings: ties round away from zero (C roundf); q is taken from the fp32 d,
+ * only its binary16 rounding is stored; "d == 0" covers amax == 0 and an amax
+ * so small that amax / 127 underflows.
+ */
+void orc_quantize_q8_1_block(const float* v, uint8_t* out) {
+    float amax = 0.0f;
+    for (int j = 0; j < ORC_QK; ++j) {
+        float a = fabsf(v[j]);
+        if (a > amax) amax = a;
+    }
+    float d = amax / 127.0f;
+    int sum = 0;
+    for (int j = 0; j < ORC_QK; ++j) {
+        int q = 0;
+        if (d != 0.0f) q = (int)roundf(v[j] / d);
+        out[4 + j] = (uint8_t)(int8_t)q;
+        sum += q;
+    }
+    wr16(out, orc_f16_encode((double)d));
+    float s = d * (float)sum;
+    wr16(out + 2, orc_f16_encode((double)s));
+}
+
+/* n floats (n a multiple of 32) to n/32 Q8_1 blocks */
+void orc_quantize_q8_1(const float* v, int n, uint8_t* out) {
+    for (int b = 0; b < n / ORC_QK; ++b) orc_quantize_q8_1_block(v + b * ORC_QK, out + b * ORC_Q8_1_BYTES);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weight blocks and block dots                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Q8_0: binary16 d then 32 int8 q; weight value d * q [Q8]. */
+int32_t orc_isum_q8_0(const uint8_t* w, const uint8_t* a) {
+    int32_t s = 0;
+    for (int j = 0; j < ORC_QK; ++j) s += (int32_t)(int8_t)w[2 + j] * (int32_t)(int8_t)a[4 + j];
+    return s;
+}
+
+/*
+ * Q4_0: binary16 d then 16 bytes; byte j holds element j in its low nibble and
+ * element j + 16 in its high nibble; weight value d * (c - 8) [E0].
+ * Reading: the standard nibble order (the pages call the formats llama.cpp's).
+ */
+int32_t orc_isum_q4_0(const uint8_t* w, const uint8_t* a) {
+    int32_t s = 0;
+    for (int j = 0; j < 16; ++j) {
+        int lo = (w[2 + j] & 0x0F) - 8;
+        int hi = (w[2 + j] >> 4) - 8;
+        s += lo * (int32_t)(int8_t)a[4 + j];
+        s += hi * (int32_t)(int8_t)a[4 + j + 16];
+    }
+    return s;
+}
+
+static inline int fmt_bytes(int fmt) { return fmt == ORC_Q4_0 ? 18 : 34; }
+
+/* Dequantised value of element j of a weight block, for the cross-check tests. */
+double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
+    double d = orc_f16_decode(rd16(w));
+    if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
+    int c = j < 16 ? (w[2 + j] & 0x0F) : (w[2 + j - 16] >> 4);
+    return d * (double)(c - 8);
+}
+
+/*
+ * One output of a quantised matrix-vector product:
+ *   y = sum_b f16(d_w,b) * f16(d_a,b) * isum_b
+ * Each term is exact in double (22-bit scale product times a 20-bit integer);
+ * the terms are added in block order in double and the sum rounded to float.
+ */
+float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
+    int bb = fmt_bytes(fmt);
+    double acc = 0.0;
+    for (int b = 0; b < nblk; ++b) {
+        const uint8_t* w = row + (size_t)b * bb;
+        const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
+        int32_t is = fmt == ORC_Q8_0 ? orc_isum_q8_0(w, a) : orc_isum_q4_0(w, a);
+        if (isum_tap) isum_tap[b] = is;
+        acc += orc_f16_decode(rd16(w)) * orc_f16_decode(rd16(a)) * (double)is;
+    }
+    return (float)acc;
+}
+
+/* rows outputs of a [rows][nblk] block matrix times a Q8_1 vector */
+void orc_matvec(int fmt, int rows, int nblk, const uint8_t* W, const uint8_t* act, float* y,
+                int32_t* isum_tap) {
+    size_t rb = (size_t)nblk * fmt_bytes(fmt);
+    for (int r = 0; r < rows; ++r)
+        y[r] = orc_row_dot(fmt, W + r * rb, act, nblk, isum_tap ? isum_tap + (size_t)r * nblk : NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router [SY], [E0]                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For one token: logits l_e = sum_i x_i W_r[e,i] (+ b_e) in double; with group
+ * labels, the groups ranked by their largest logit and the experts outside the
+ * best topk_groups groups dropped; the top_k experts by logit (exact ties go to
+ * the lower expert or group id); weights = softmax over the chosen logits,
+ * w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max), rounded to float.
+ * Readings: group score = largest member logit; softmax after top-k equals
+ * softmax over all experts renormalised over the chosen ones.
+ */
+void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const float* br,
+                     const int32_t* groups, int32_t* ids, float* w, double* logits_out) {
+    int H = d->hidden, E = d->n_experts, k = d->top_k;
+    double* l = (double*)malloc(sizeof(double) * E);
+    char* allowed = (char*)malloc(E);
+    for (int e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int i = 0; i < H; ++i) acc += (double)x[i] * (double)Wr[(size_t)e * H + i];
+        if (br) acc += (double)br[e];
+        l[e] = acc;
+        allowed[e] = 1;
+        if (logits_out) logits_out[e] = acc;
+    }
+    if (d->n_groups > 0 && groups) {
+        int G = d->n_groups;
+        double* gs = (double*)malloc(sizeof(double) * G);
+        char* gsel = (char*)calloc(G, 1);
+        for (int g = 0; g < G; ++g) gs[g] = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if (l[e] > gs[groups[e]]) gs[groups[e]] = l[e];
+        for (int n = 0; n < d->topk_groups; ++n) {
+            int best = -1;
+            for (int g = 0; g < G; ++g)
+                if (!gsel[g] && (best < 0 || gs[g] > gs[best])) best = g;
+            gsel[best] = 1;
+        }
+        for (int e = 0; e < E; ++e) allowed[e] = gsel[groups[e]];
+        free(gs);
+        free(gsel);
+    }
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (allowed[e] && (best < 0 || l[e] > l[best])) best = e;
+        ids[j] = best;
+        allowed[best] = 0;
+    }
+    double m = l[ids[0]], s = 0.0;
+    for (int j = 0; j < k; ++j) s += exp(l[ids[j]] - m);
+    for (int j = 0; j < k; ++j) w[j] = (float)(exp(l[ids[j]] - m) / s);
+    free(l);
+    free(allowed);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert FFN and the layer [Q8], [E0]                                       */
+/* ------------------------------------------------------------------------ */
+
+static size_t expert_bytes(const orc_desc* d) {
+    int kin = d->latent ? d->latent : d->hidden;
+    int kout = kin;
+    size_t blocks = (size_t)2 * d->n_ff * (kin / ORC_QK) + (size_t)kout * (d->n_ff / ORC_QK);
+    return blocks * fmt_bytes(d->expert_fmt);
+}
+
+size_t orc_expert_bytes(const orc_desc* d) { return expert_bytes(d); }
+
+/*
+ * One expert on one quantised input aq (Kin/32 Q8_1 blocks):
+ *   g = W_gate aq, u = W_up aq (float), h = silu(g) * u = g / (1 + e^-g) * u
+ *   (double from the float g and u, rounded to float), hq = Q8_1(h) per 32,
+ *   y = W_down hq (float).  SwiGLU with the gate first is the reading taken.
+ */
+void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, float* h,
+                    uint8_t* hq, float* y, int32_t* isum_gu, int32_t* isum_dn) {
+    int fmt = d->expert_fmt, F = d->n_ff;
+    int kin = d->latent ? d->latent : d->hidden, kout = kin;
+    int nbi = kin / ORC_QK, nbf = F / ORC_QK;
+    size_t rbi = (size_t)nbi * fmt_bytes(fmt);
+    const uint8_t* gate = blob;
+    const uint8_t* up = gate + (size_t)F * rbi;
+    const uint8_t* down = up + (size_t)F * rbi;
+    for (int r = 0; r < F; ++r) {
+        float g = orc_row_dot(fmt, gate + r * rbi, aq, nbi, isum_gu ? isum_gu + (size_t)r * nbi : NULL);
+        float u = orc_row_dot(fmt, up + r * rbi, aq, nbi,
+                              isum_gu ? isum_gu + (size_t)(F + r) * nbi : NULL);
+        double gd = (double)g;
+        h[r] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+    }
+    orc_quantize_q8_1(h, F, hq);
+    orc_matvec(fmt, kout, nbf, down, hq, y, isum_dn);
+}
+
+typedef struct {
+    const orc_desc* d;
+    const float *x, *Wr, *br;
+    const int32_t* groups;
+    const uint8_t *experts, *D, *U;
+    float* out;
+    const orc_taps* taps;
+    const int32_t* list;
+    int n;
+    int next;
+    pthread_mutex_t mu;
+} job_t;
+
+#define TAP(ptr, stride) ((ptr) ? (ptr) + (size_t)i * (stride) : NULL)
+
+static void run_token(job_t* J, int i) {
+    const orc_desc* d = J->d;
+    const orc_taps* tp = J->taps;
+    int t = J->list ? J->list[i] : i;
+    int H = d->hidden, E = d->n_experts, k = d->top_k, F = d->n_ff, L = d->latent;
+    int kin = L ? L : H, kout = kin;
+    const float* x = J->x + (size_t)t * H;
+    int32_t ids[512];
+    float w[512];
+    orc_route_token(d, x, J->Wr, J->br, J->groups, ids, w,
+                    tp ? TAP(tp->logits, E) : NULL);
+    if (tp && tp->ids) memcpy(tp->ids + (size_t)i * k, ids, sizeof(int32_t) * k);
+    if (tp && tp->weights) memcpy(tp->weights + (size_t)i * k, w, sizeof(float) * k);
+
+    uint8_t* xq = (uint8_t*)malloc((size_t)(H / ORC_QK) * ORC_Q8_1_BYTES);
+    orc_quantize_q8_1(x, H, xq);
+    if (tp && tp->xq) memcpy(tp->xq + (size_t)i * (H / ORC_QK) * ORC_Q8_1_BYTES, xq, (size_t)(H / ORC_QK) * ORC_Q8_1_BYTES);
+
+    const uint8_t* ain = xq;                  /* the experts' quantised input */
+    uint8_t* zq = NULL;
+    float* z = NULL;
+    if (L) {                                   /* latent: z = D Q8_1(x), experts on Q8_1(z) */
+        z = (float*)malloc(sizeof(float) * L);
+        zq = (uint8_t*)malloc((size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        orc_matvec(ORC_Q8_0, L, H / ORC_QK, J->D, xq, z, tp ? TAP(tp->isum_d, (size_t)L * (H / ORC_QK)) : NULL);
+        orc_quantize_q8_1(z, L, zq);
+        if (tp && tp->z) memcpy(tp->z + (size_t)i * L, z, sizeof(float) * L);
+        if (tp && tp->zq) memcpy(tp->zq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, zq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        ain = zq;
+    }
+
+    size_t eb = expert_bytes(d);
+    float* h = (float*)malloc(sizeof(float) * F);
+    uint8_t* hq = (uint8_t*)malloc((size_t)(F / ORC_QK) * ORC_Q8_1_BYTES);
+    float* y = (float*)malloc(sizeof(float) * (size_t)k * kout);
+    for (int j = 0; j < k; ++j) {
+        size_t a = (size_t)i * k + j;
+        orc_expert_ffn(d, J->experts + (size_t)ids[j] * eb, ain, h, hq, y + (size_t)j * kout,
+                       tp && tp->isum_gu ? tp->isum_gu + a * 2 * F * (kin / ORC_QK) : NULL,
+                       tp && tp->isum_dn ? tp->isum_dn + a * kout * (F / ORC_QK) : NULL);
+        if (tp && tp->h) memcpy(tp->h + a * F, h, sizeof(float) * F);
+        if (tp && tp->hq) memcpy(tp->hq + a * (F / ORC_QK) * ORC_Q8_1_BYTES, hq, (size_t)(F / ORC_QK) * ORC_Q8_1_BYTES);
+        if (tp && tp->y) memcpy(tp->y + a * kout, y + (size_t)j * kout, sizeof(float) * kout);
+    }
+    /* combine: out = sum_j w_j y_j, in rank order, in double */
+    float* comb = L ? (float*)malloc(sizeof(float) * L) : J->out + (size_t)i * H;
+    for (int r = 0; r < kout; ++r) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j) acc += (double)w[j] * (double)y[(size_t)j * kout + r];
+        comb[r] = (float)acc;
+    }
+    if (L) {                                   /* out = U Q8_1(y_lat) */
+        uint8_t* ylq = (uint8_t*)malloc((size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        orc_quantize_q8_1(comb, L, ylq);
+        if (tp && tp->ylat) memcpy(tp->ylat + (size_t)i * L, comb, sizeof(float) * L);
+        if (tp && tp->ylq) memcpy(tp->ylq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, ylq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        orc_matvec(ORC_Q8_0, H, L / ORC_QK, J->U, ylq, J->out + (size_t)i * H,
+                   tp ? TAP(tp->isum_u, (size_t)H * (L / ORC_QK)) : NULL);
+        free(ylq);
+        free(comb);
+        free(z);
+        free(zq);
+    }
+    free(xq);
+    free(h);
+    free(hq);
+    free(y);
+}
+
+static void* worker(void* p) {
+    job_t* J = (job_t*)p;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int i = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (i >= J->n) break;
+        run_token(J, i);
+    }
+    return NULL;
+}
+
+/*
+ * The layer for the tokens in list[0..n) (all of 0..n-1 when list is NULL):
+ * route on x; Q8_1(x); latent: z = D Q8_1(x), experts on Q8_1(z); every chosen
+ * expert's FFN; combine in rank order; latent: out = U Q8_1(y_lat).
+ * out and every tap are indexed by position in the list.  Tokens are spread
+ * over nthreads threads; each token is computed by one thread alone.
+ * Returns 0, or -1 on a bad argument.
+ */
+int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const float* br,
+                      const int32_t* groups, const uint8_t* experts, const uint8_t* D,
+                      const uint8_t* U, const int32_t* list, int n, float* out,
+                      const orc_taps* taps, int nthreads) {
+    if (!d || !x || !Wr || !experts || !out || n < 0) return -1;
+    if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
+    if (d->latent && (!D || !U)) return -1;
+    if (d->n_groups > 0) {                     /* every group holds E / n_groups experts */
+        int G = d->n_groups;
+        if (!groups || d->n_experts % G || d->topk_groups < 1 || d->topk_groups > G ||
+            d->topk_groups * (d->n_experts / G) < d->top_k) return -1;
+        int* cnt = (int*)calloc(G, sizeof(int));
+        int bad = 0;
+        for (int e = 0; e < d->n_experts; ++e) {
+            if (groups[e] < 0 || groups[e] >= G) { bad = 1; break; }
+            cnt[groups[e]]++;
+        }
+        for (int g = 0; g < G && !bad; ++g) bad = cnt[g] != d->n_experts / G;
+        free(cnt);
+        if (bad) return -1;
+    }
+    job_t J;
+    J.d = d; J.x = x; J.Wr = Wr; J.br = br; J.groups = groups; J.experts = experts;
+    J.D = D; J.U = U; J.out = out; J.taps = taps; J.list = list; J.n = n; J.next = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads == 1) {
+        worker(&J);
+    } else {
+        pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, worker, &J);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}

@@ -1,0 +1,244 @@
+"""Seeded synthetic workloads for the quantized MoE layer.
+
+This module only draws inputs; it holds none of the layer's arithmetic.  The
+random numbers come from ``synth.c`` (counter-based splitmix64), so any tensor
+or any slice of one can be drawn on its own.  Scales are drawn in double
+precision and rounded to IEEE binary16 by numpy's ``astype(np.float16)``.
+
+Distributions (the workloads of the quantized MoE layer, Strata "Q8_0 support"
+page, section "GPU expert kernels", and the edge0-strata README, section
+"Changes from upstream Strata"):
+
+* activations ``x ~ N(0, 1)`` fp32, router ``W_r ~ N(0, 1/512)`` fp32, optional
+  per-expert router bias ``b ~ N(0, 1)``;
+* Q8_0 weight blocks: 32 int8 codes uniform in [-127, 127] and a binary16 scale
+  ``d = |N(0, 0.02)| / 127``;
+* Q4_0 weight blocks: 32 nibbles uniform in [0, 15] and ``d = |N(0, 0.02)| / 8``;
+* expert group labels ``group[e] = e // (E // n_groups)``.
+
+Canonical block layouts (little-endian): Q8_0 = binary16 d, 32 x int8 (34 B);
+Q4_0 = binary16 d, 16 bytes whose low nibble is element j and high nibble
+element j + 16 (18 B).  A canonical expert blob holds gate [F][Kin/32],
+up [F][Kin/32] and down [Kout][F/32] blocks, in that order, rows row-major.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libsynth.so")
+_lib = None
+
+Q8_0 = 8
+Q4_0 = 2
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18}
+
+
+def build_synth(force: bool = False) -> str:
+    """Compile the generator core with gcc (host code only)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(
+            os.path.join(_HERE, "synth.c")):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                               os.path.join(_HERE, "synth.c"), "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build_synth()
+        lib = ctypes.CDLL(_SO)
+        u64, dbl, vp = ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
+        lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, dbl, vp]
+        lib.synth_absnormal_f64.argtypes = [u64, u64, u64, u64, dbl, vp]
+        lib.synth_int8_sym127.argtypes = [u64, u64, u64, u64, vp]
+        lib.synth_nibble_bytes.argtypes = [u64, u64, u64, u64, vp]
+        lib.synth_interleave_blocks.argtypes = [u64, vp, vp, u64, vp]
+        for f in (lib.synth_normal_f32, lib.synth_absnormal_f64, lib.synth_int8_sym127,
+                  lib.synth_nibble_bytes, lib.synth_interleave_blocks):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+# stream ids: one per tensor
+S_X = 0x100          # + batch index
+S_WR = 2
+S_BIAS = 3
+S_EXP_Q = 0x10000    # + 4 * expert + role
+S_EXP_D = 0x20000
+S_DENSE = 0x30000    # D quants, D scales, U quants, U scales
+
+
+def normal_f32(seed: int, stream: int, n: int, scale: float = 1.0, first: int = 0,
+               out: Optional[np.ndarray] = None) -> np.ndarray:
+    if out is None:
+        out = np.empty(n, dtype=np.float32)
+    _L().synth_normal_f32(seed, stream, first, n, scale, _ptr(out))
+    return out
+
+
+def absnormal_f64(seed: int, stream: int, n: int, scale: float, first: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.float64)
+    _L().synth_absnormal_f64(seed, stream, first, n, scale, _ptr(out))
+    return out
+
+
+def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
+           out: Optional[np.ndarray] = None) -> np.ndarray:
+    """nblk canonical weight blocks of format fmt, as a uint8 array of nblk * 34 (or 18) bytes."""
+    lib = _L()
+    if fmt == Q8_0:
+        pay = 32
+        payload = np.empty(nblk * pay, dtype=np.int8)
+        lib.synth_int8_sym127(seed, q_stream, 0, nblk * pay, _ptr(payload))
+        scale = absnormal_f64(seed, d_stream, nblk, 0.02 / 127.0)
+    elif fmt == Q4_0:
+        pay = 16
+        payload = np.empty(nblk * pay, dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, q_stream, 0, nblk * pay, _ptr(payload))
+        scale = absnormal_f64(seed, d_stream, nblk, 0.02 / 8.0)
+    else:
+        raise ValueError(f"unknown block format {fmt}")
+    d16 = scale.astype(np.float16).view(np.uint16)
+    if out is None:
+        out = np.empty(nblk * (2 + pay), dtype=np.uint8)
+    assert out.nbytes == nblk * (2 + pay)
+    lib.synth_interleave_blocks(nblk, _ptr(d16), _ptr(payload), pay, _ptr(out))
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic MoE layer: shapes, formats and the seed that fills it."""
+    name: str
+    hidden: int
+    n_experts: int
+    top_k: int
+    n_ff: int
+    tokens: int
+    latent: int = 0
+    expert_fmt: int = Q8_0
+    n_groups: int = 0
+    topk_groups: int = 0
+    bias: bool = False
+    seed: int = 0
+
+    @property
+    def k_in(self) -> int:
+        return self.latent if self.latent else self.hidden
+
+    @property
+    def k_out(self) -> int:
+        return self.latent if self.latent else self.hidden
+
+    @property
+    def block_bytes(self) -> int:
+        return BLOCK_BYTES[self.expert_fmt]
+
+    def role_rows(self):
+        """(rows, blocks per row) of gate, up, down."""
+        return [(self.n_ff, self.k_in // 32), (self.n_ff, self.k_in // 32),
+                (self.k_out, self.n_ff // 32)]
+
+    @property
+    def expert_bytes(self) -> int:
+        return sum(r * b for r, b in self.role_rows()) * self.block_bytes
+
+    def with_tokens(self, t: int) -> "Workload":
+        return dataclasses.replace(self, tokens=t)
+
+    def dense_shapes(self):
+        """(rows, blocks per row) of D [L x H] and U [H x L]; empty when not latent."""
+        if not self.latent:
+            return []
+        return [(self.latent, self.hidden // 32), (self.hidden, self.latent // 32)]
+
+
+# The five layers measured and checked here.
+WORKLOADS = {
+    "tiny": Workload("tiny", hidden=512, n_experts=8, top_k=2, n_ff=256, tokens=4, seed=1000),
+    "decode": Workload("decode", hidden=4096, n_experts=128, top_k=8, n_ff=1536, tokens=1,
+                       seed=1001),
+    "latent_q8": Workload("latent_q8", hidden=4096, n_experts=256, top_k=8, n_ff=1024, tokens=1,
+                          latent=1280, n_groups=16, topk_groups=4, seed=1002),
+    "latent_q4": Workload("latent_q4", hidden=7168, n_experts=256, top_k=8, n_ff=1024, tokens=1,
+                          latent=1792, expert_fmt=Q4_0, n_groups=16, topk_groups=4, seed=1003),
+    "prefill": Workload("prefill", hidden=4096, n_experts=128, top_k=8, n_ff=1536, tokens=2048,
+                        bias=True, seed=1004),
+}
+
+
+def gen_x(w: Workload, batch: int = 0, tokens: Optional[int] = None) -> np.ndarray:
+    t = w.tokens if tokens is None else tokens
+    return normal_f32(w.seed, S_X + batch, t * w.hidden).reshape(t, w.hidden)
+
+
+def gen_router(w: Workload) -> np.ndarray:
+    return normal_f32(w.seed, S_WR, w.n_experts * w.hidden,
+                      scale=float(np.sqrt(1.0 / 512.0))).reshape(w.n_experts, w.hidden)
+
+
+def gen_bias(w: Workload) -> Optional[np.ndarray]:
+    if not w.bias:
+        return None
+    return normal_f32(w.seed, S_BIAS, w.n_experts)
+
+
+def gen_groups(w: Workload) -> Optional[np.ndarray]:
+    if not w.n_groups:
+        return None
+    per = w.n_experts // w.n_groups
+    return (np.arange(w.n_experts, dtype=np.int32) // per).astype(np.int32)
+
+
+def gen_expert(w: Workload, e: int, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Canonical blob of expert e (gate, up, down)."""
+    if out is None:
+        out = np.empty(w.expert_bytes, dtype=np.uint8)
+    off = 0
+    for role, (rows, nb) in enumerate(w.role_rows()):
+        n = rows * nb * w.block_bytes
+        blocks(w.expert_fmt, w.seed, S_EXP_Q + 4 * e + role, S_EXP_D + 4 * e + role, rows * nb,
+               out=out[off:off + n])
+        off += n
+    return out
+
+
+def gen_experts(w: Workload, out: Optional[np.ndarray] = None) -> np.ndarray:
+    if out is None:
+        out = np.empty(w.n_experts * w.expert_bytes, dtype=np.uint8)
+    eb = w.expert_bytes
+    for e in range(w.n_experts):
+        gen_expert(w, e, out=out[e * eb:(e + 1) * eb])
+    return out
+
+
+def gen_dense(w: Workload):
+    """Canonical Q8_0 D [L][H/32] and U [H][L/32]; (None, None) when not latent."""
+    if not w.latent:
+        return None, None
+    res = []
+    for i, (rows, nb) in enumerate(w.dense_shapes()):
+        res.append(blocks(Q8_0, w.seed, S_DENSE + 2 * i, S_DENSE + 2 * i + 1, rows * nb))
+    return res[0], res[1]
+
+
+def gen_layer(w: Workload, batch: int = 0):
+    """All inputs of one layer call as a dict of numpy arrays (None where absent)."""
+    D, U = gen_dense(w)
+    return dict(x=gen_x(w, batch), router_w=gen_router(w), router_b=gen_bias(w),
+                groups=gen_groups(w), experts=gen_experts(w), D=D, U=U)

@@ -1,0 +1,561 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Every check here compares the oracle with something it does not compute
+itself: IEEE 754 bit patterns, hand-derived golden blocks, exact rational
+arithmetic, brute-force integer sums, library sorts, closed forms and
+invariants of the layer.  A plausible slip in the oracle (a dropped term, a
+wrong sign or index, a swapped operand, the wrong rounding mode) fails at least
+one of them.
+"""
+import dataclasses
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- exact helpers
+def _parse(s):
+    """'127*2^-20', '2^-24', '1 + 3*2^-11', '1365 * 2^-12' -> Fraction (tiny grammar)."""
+    s = s.replace(" ", "")
+    if s in ("inf", "-inf"):
+        return s
+    total = Fraction(0)
+    s = s.replace("^-", "^m")
+    for term in s.replace("-", "+-").split("+"):
+        if not term:
+            continue
+        neg = term.startswith("-")
+        term = term.lstrip("-")
+        val = Fraction(1)
+        for f in term.split("*"):
+            if "^" in f:
+                b, e = f.split("^")
+                val *= Fraction(int(b)) ** int(e.replace("m", "-"))
+            else:
+                val *= Fraction(f)
+        total += -val if neg else val
+    return total
+
+
+def _binade(a: Fraction) -> int:
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def rn(fr: Fraction, mant_bits: int, emin: int) -> Fraction:
+    """Round a rational to the nearest value with mant_bits significand bits (ties to even),
+    gradual underflow below 2^emin.  Overflow is not modelled."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = max(_binade(a), emin)
+    q = Fraction(2) ** (e - (mant_bits - 1))
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * q
+
+
+def rn32(fr):
+    return rn(Fraction(fr), 24, -126)
+
+
+def rn16(fr):
+    return rn(Fraction(fr), 11, -14)
+
+
+def half_away(fr: Fraction) -> int:
+    a = abs(fr)
+    n = int(math.floor(a + Fraction(1, 2)))
+    return -n if fr < 0 else n
+
+
+def q8_1_exact(v32: np.ndarray):
+    """Q8_1 of a float32 block from the definition, in exact rational arithmetic."""
+    vals = [Fraction(float(x)) for x in v32]
+    amax = max(abs(x) for x in vals)
+    d = rn32(amax / 127)
+    q = [0 if d == 0 else half_away(rn32(x / d)) for x in vals]
+    s = rn32(d * sum(q))
+    return d, s, q
+
+
+# ------------------------------------------------------------------ binary16
+def test_f16_decode_ieee_patterns(orc):
+    g = json.load(open(os.path.join(GOLD, "f16_patterns.json")))
+    for c in g["cases"]:
+        bits = int(c["bits"], 16)
+        got = orc.f16_decode(bits)
+        if c["value"] == "inf":
+            assert got == math.inf
+        else:
+            assert Fraction(got) == _parse(c["value"]), c
+
+
+def test_f16_encode_ieee_rounding(orc):
+    g = json.load(open(os.path.join(GOLD, "f16_patterns.json")))
+    for c in g["cases"]:
+        if c["value"] == "inf":
+            continue
+        assert orc.f16_encode(float(_parse(c["value"]))) == int(c["bits"], 16), c
+    for c in g["rounding"]["cases"]:
+        v = _parse(c["value"]) if "^" in c["value"] else Fraction(c["value"])
+        assert orc.f16_encode(float(v)) == int(c["bits"], 16), c
+
+
+def test_f16_roundtrip_all_patterns(orc):
+    for h in range(0, 1 << 16, 7):
+        e = (h >> 10) & 31
+        if e == 31 and (h & 1023):
+            continue  # NaN
+        assert orc.f16_encode(orc.f16_decode(h)) == h
+
+
+def test_f16_encode_matches_numpy(orc):
+    """numpy's double -> binary16 conversion is a correctly rounded library routine."""
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([
+        rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000),
+        (np.arange(-300, 300) + 0.5) * 2.0 ** -24,     # subnormal ties
+        1.0 + (np.arange(0, 64) + 0.5) * 2.0 ** -10,    # normal ties
+        [65504.0, 65519.0, 65520.0, 1e6, -65520.0]])
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    for v, r in zip(vals, ref):
+        assert orc.f16_encode(float(v)) == int(r), v
+
+
+def test_f16_encode_exact_rational(orc):
+    rng = np.random.default_rng(8)
+    for v in rng.standard_normal(300) * 1e-3:
+        assert Fraction(orc.f16_decode(orc.f16_encode(float(v)))) == rn16(Fraction(float(v)))
+
+
+# ---------------------------------------------------------------- Q8_1 blocks
+def _golden_q8_1():
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    for c in g["q8_1"]:
+        if "fill" in c:
+            v = np.full(32, float(_parse(c["fill"])), dtype=np.float32)
+            q = np.full(32, c["q_all"], dtype=np.int8)
+        else:
+            v = np.zeros(c["pad_zero_to"], dtype=np.float32)
+            v[:len(c["v"])] = [float(_parse(s)) for s in c["v"]]
+            q = np.zeros(32, dtype=np.int8)
+            q[:len(c["q"])] = c["q"]
+        yield c, v, q
+
+
+def test_q8_1_golden_blocks(orc):
+    for c, v, q in _golden_q8_1():
+        blk = orc.quantize_q8_1(v)[0]
+        assert (int(blk[0]) | int(blk[1]) << 8) == int(c["d16"], 16), c["name"]
+        assert (int(blk[2]) | int(blk[3]) << 8) == int(c["s16"], 16), c["name"]
+        assert np.array_equal(blk[4:].view(np.int8), q), c["name"]
+
+
+def _check_exact(orc, v):
+    blk = orc.quantize_q8_1(v)[0]
+    d, s, q = q8_1_exact(v)
+    assert np.array_equal(blk[4:].view(np.int8).astype(int), np.array(q)), v
+    assert Fraction(orc.f16_decode(int(blk[0]) | int(blk[1]) << 8)) == rn16(d)
+    assert Fraction(orc.f16_decode(int(blk[2]) | int(blk[3]) << 8)) == rn16(s)
+
+
+def test_q8_1_exact_rational_random(orc):
+    rng = np.random.default_rng(11)
+    for scale in (1.0, 1e-3, 30.0, 2.0 ** -18):
+        for _ in range(40):
+            _check_exact(orc, (rng.standard_normal(32) * scale).astype(np.float32))
+
+
+def test_q8_1_true_divide_not_reciprocal(orc):
+    """Blocks where v * (1/d) and v / d round to different integers: the oracle must take the
+    correctly rounded divide."""
+    rng = np.random.default_rng(12)
+    found = 0
+    for _ in range(4000):
+        amax = np.float32(rng.uniform(0.5, 8.0))
+        d = rn32(Fraction(float(amax)) / 127)
+        inv = rn32(1 / d)
+        n = int(rng.integers(1, 126))
+        centre = rn32((n + Fraction(1, 2)) * d)
+        for k in range(-3, 4):
+            v = np.float32(float(centre))
+            v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(-np.inf), dtype=np.float32) \
+                if k else v
+            for _ in range(abs(k) - 1):
+                v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(-np.inf), dtype=np.float32)
+            if half_away(rn32(Fraction(float(v)) / d)) != half_away(rn32(Fraction(float(v)) * inv)):
+                blk = np.zeros(32, np.float32)
+                blk[0] = amax
+                blk[1] = v
+                _check_exact(orc, blk)
+                found += 1
+        if found >= 5:
+            break
+    assert found >= 5
+
+
+def test_q8_1_invariants(orc):
+    rng = np.random.default_rng(13)
+    v = (rng.standard_normal((64, 32)) * rng.uniform(0.01, 10, (64, 1))).astype(np.float32)
+    blk = orc.quantize_q8_1(v.reshape(-1)).reshape(64, 36)
+    for b in range(64):
+        q = blk[b, 4:].view(np.int8).astype(np.int64)
+        assert np.abs(q).max() == 127
+        assert abs(int(q[np.argmax(np.abs(v[b]))])) == 127
+        assert np.all((q == 0) | (np.sign(q) == np.sign(v[b])))
+        d = float(np.float32(np.abs(v[b]).max()) / np.float32(127))
+        assert np.all(np.abs(v[b] - d * q) <= 0.5 * d * (1 + 1e-6))
+    # power-of-two scaling leaves q unchanged and scales d exactly
+    b2 = orc.quantize_q8_1((v[:8] * np.float32(4.0)).reshape(-1)).reshape(8, 36)
+    assert np.array_equal(b2[:, 4:], blk[:8, 4:])
+    for b in range(8):
+        assert orc.f16_decode(int(b2[b, 0]) | int(b2[b, 1]) << 8) == pytest.approx(
+            4 * orc.f16_decode(int(blk[b, 0]) | int(blk[b, 1]) << 8), rel=2 ** -10)
+
+
+# ------------------------------------------------------------------ block dots
+def _rand_q8_0(rng, n):
+    b = np.zeros((n, 34), np.uint8)
+    d = (np.abs(rng.standard_normal(n)) * 0.02 / 127).astype(np.float16).view(np.uint16)
+    b[:, 0] = d & 0xFF
+    b[:, 1] = d >> 8
+    b[:, 2:] = rng.integers(-127, 128, (n, 32)).astype(np.int8).view(np.uint8)
+    return b
+
+
+def _rand_q4_0(rng, n):
+    b = np.zeros((n, 18), np.uint8)
+    d = (np.abs(rng.standard_normal(n)) * 0.02 / 8).astype(np.float16).view(np.uint16)
+    b[:, 0] = d & 0xFF
+    b[:, 1] = d >> 8
+    b[:, 2:] = rng.integers(0, 256, (n, 16)).astype(np.uint8)
+    return b
+
+
+def _rand_q8_1(orc, rng, n):
+    return orc.quantize_q8_1(rng.standard_normal(32 * n).astype(np.float32)).reshape(n, 36)
+
+
+def test_isum_q8_0_bruteforce(orc):
+    rng = np.random.default_rng(21)
+    w = _rand_q8_0(rng, 200)
+    a = _rand_q8_1(orc, rng, 200)
+    for i in range(200):
+        ref = int(np.dot(w[i, 2:].view(np.int8).astype(np.int64), a[i, 4:].view(np.int8).astype(np.int64)))
+        assert orc.isum(8, w[i], a[i]) == ref
+    # extremes: |isum| reaches 32 * 127 * 127
+    w1 = w[0].copy(); w1[2:] = np.uint8(127)
+    a1 = a[0].copy(); a1[4:] = np.uint8(127)
+    assert orc.isum(8, w1, a1) == 516128
+    a1[4:] = np.int8(-127).view(np.uint8)
+    assert orc.isum(8, w1, a1) == -516128
+
+
+def test_isum_q4_0_golden_nibble_order(orc):
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    for c in g["q4_0"]:
+        w = np.zeros(18, np.uint8)
+        d = int(c["d16"], 16)
+        w[0], w[1] = d & 0xFF, d >> 8
+        w[2:] = int(c["rest"], 16)
+        if c["bytes"]:
+            w[2] = int(c["bytes"], 16)
+        a = np.zeros(36, np.uint8)
+        a[4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+        assert orc.isum(2, w, a) == c["isum"], c["name"]
+
+
+def test_isum_q4_0_bruteforce(orc):
+    rng = np.random.default_rng(22)
+    w = _rand_q4_0(rng, 200)
+    a = _rand_q8_1(orc, rng, 200)
+    for i in range(200):
+        codes = np.concatenate([w[i, 2:] & 0x0F, w[i, 2:] >> 4]).astype(np.int64) - 8
+        ref = int(np.dot(codes, a[i, 4:].view(np.int8).astype(np.int64)))
+        assert orc.isum(2, w[i], a[i]) == ref
+
+
+@pytest.mark.parametrize("fmt", [8, 2])
+def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
+    """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
+    d_w * d_a * isum; the row sums them in block order."""
+    rng = np.random.default_rng(23 + fmt)
+    nblk = 12
+    W = (_rand_q8_0 if fmt == 8 else _rand_q4_0)(rng, 5 * nblk)
+    A = _rand_q8_1(orc, rng, nblk)
+    y, isum = orc.matvec(fmt, W.reshape(-1), 5, nblk, A.reshape(-1), with_isum=True)
+    for r in range(5):
+        acc = 0.0
+        for b in range(nblk):
+            wb = W[r * nblk + b]
+            da = orc.f16_decode(int(A[b, 0]) | int(A[b, 1]) << 8)
+            deq = [orc.dequant_weight(fmt, wb, j) * (da * int(np.int8(A[b, 4 + j]))) for j in range(32)]
+            blk = math.fsum(deq)
+            dw = orc.f16_decode(int(wb[0]) | int(wb[1]) << 8)
+            assert blk == dw * da * isum[r, b]          # exact, no tolerance
+            # the dequantised values themselves: d * q (Q8_0) or d * (c - 8) (Q4_0)
+            if fmt == 8:
+                assert orc.dequant_weight(fmt, wb, 5) == dw * int(np.int8(wb[2 + 5]))
+            else:
+                assert orc.dequant_weight(fmt, wb, 20) == dw * ((int(wb[2 + 4]) >> 4) - 8)
+            acc += blk
+        assert y[r] == np.float32(acc)
+
+
+# -------------------------------------------------------------------- router
+def _wl(**kw):
+    from quantized_moe_expert_softmax_amd.synth import Workload
+    base = dict(name="pin", hidden=64, n_experts=8, top_k=3, n_ff=64, tokens=5, seed=5)
+    base.update(kw)
+    return Workload(**base)
+
+
+def _topk_bruteforce(l, k, allowed):
+    idx = [e for e in range(len(l)) if allowed[e]]
+    order = sorted(idx, key=lambda e: (-l[e], e))   # library sort: larger logit first, ties lower id
+    return order[:k]
+
+
+def test_router_logits_topk_softmax(orc, synth):
+    w = _wl(n_experts=16, top_k=4)
+    rng = np.random.default_rng(31)
+    Wr = (rng.standard_normal((16, 64)) / np.sqrt(512)).astype(np.float32)
+    br = rng.standard_normal(16).astype(np.float32)
+    for t in range(20):
+        x = rng.standard_normal(64).astype(np.float32)
+        ids, wt, l = orc.route_token(w, x, Wr, br)
+        ref_l = Wr.astype(np.float64) @ x.astype(np.float64) + br.astype(np.float64)
+        assert np.allclose(l, ref_l, rtol=0, atol=1e-13)
+        assert list(ids) == _topk_bruteforce(l, 4, [1] * 16)
+        ex = np.exp(l[ids] - l[ids].max())
+        assert np.allclose(wt, ex / ex.sum(), rtol=1e-6, atol=0)
+        assert abs(float(np.sum(wt.astype(np.float64))) - 1.0) < 4e-7
+        assert np.all(np.diff(wt) <= 0)
+
+
+def test_router_ties_go_to_lower_index(orc):
+    w = _wl(n_experts=8, top_k=3)
+    Wr = np.zeros((8, 64), np.float32)
+    Wr[5] = 1.0
+    Wr[2] = 1.0
+    Wr[6] = 0.5
+    x = np.ones(64, np.float32)
+    ids, wt, _ = orc.route_token(w, x, Wr)
+    assert list(ids) == [2, 5, 6]
+    assert wt[0] == wt[1]
+
+
+def test_router_k1_and_k_equals_e(orc):
+    rng = np.random.default_rng(33)
+    Wr = rng.standard_normal((8, 64)).astype(np.float32)
+    x = rng.standard_normal(64).astype(np.float32)
+    ids, wt, l = orc.route_token(_wl(top_k=1), x, Wr)
+    assert ids[0] == int(np.argmax(l)) and wt[0] == 1.0
+    ids, wt, l = orc.route_token(_wl(top_k=8), x, Wr)
+    full = np.exp(l - l.max()) / np.exp(l - l.max()).sum()
+    assert sorted(ids) == list(range(8))
+    assert np.allclose(wt, full[ids], rtol=1e-6)
+
+
+def test_router_zero_input_uniform(orc):
+    w = _wl(top_k=3)
+    ids, wt, l = orc.route_token(w, np.zeros(64, np.float32), np.ones((8, 64), np.float32))
+    assert list(ids) == [0, 1, 2]
+    assert np.all(wt == np.float32(1.0 / 3.0))
+
+
+def test_router_group_limit_bruteforce(orc):
+    """Group-limited routing on tiny E by enumerating group choices."""
+    import itertools
+    rng = np.random.default_rng(34)
+    E, G, TG, k = 12, 4, 2, 3
+    w = _wl(n_experts=E, top_k=k, n_groups=G, topk_groups=TG)
+    for trial in range(30):
+        perm = rng.permutation(E)
+        groups = (perm // (E // G)).astype(np.int32)       # non-contiguous labels
+        Wr = rng.standard_normal((E, 64)).astype(np.float32)
+        x = rng.standard_normal(64).astype(np.float32)
+        ids, wt, l = orc.route_token(w, x, Wr, None, groups)
+        gmax = [max(l[e] for e in range(E) if groups[e] == g) for g in range(G)]
+        # the chosen groups are the set of TG groups with the largest maxima (ties: lower ids)
+        best = max(itertools.combinations(range(G), TG),
+                   key=lambda c: (sorted([gmax[g] for g in c], reverse=True), [-g for g in c]))
+        allowed = [groups[e] in best for e in range(E)]
+        assert list(ids) == _topk_bruteforce(l, k, allowed)
+        assert all(groups[e] in best for e in ids)
+
+
+# ---------------------------------------------------------------- expert FFN
+def _blob_from_rows(rows_blocks):
+    return np.concatenate([r.reshape(-1) for r in rows_blocks]).astype(np.uint8)
+
+
+def _q8_0_row(nblk, entries):
+    """A Q8_0 row with d = 1.0 and the given {element: q} entries."""
+    b = np.zeros((nblk, 34), np.uint8)
+    b[:, 0], b[:, 1] = 0x00, 0x3C
+    for j, q in entries.items():
+        b[j // 32, 2 + j % 32] = np.uint8(np.int8(q))
+    return b
+
+
+def test_swiglu_closed_form_gate_first(orc):
+    """g and u set to exact known values: h = g / (1 + e^-g) * u, gate first."""
+    w = _wl(hidden=32, n_ff=32, n_experts=1, top_k=1)
+    act = np.zeros((1, 36), np.uint8)
+    act[0, 1] = 0x3C                       # d = 1
+    act[0, 4] = 2                          # x_0 = 2
+    gate = [_q8_0_row(1, {0: 1 + r % 3}) for r in range(32)]      # g_r = 2 * (1 + r % 3)
+    up = [_q8_0_row(1, {0: -(r % 5)}) for r in range(32)]         # u_r = -2 * (r % 5)
+    down = [_q8_0_row(1, {r: 1}) for r in range(32)]              # y_r = hq_r * d_h
+    blob = _blob_from_rows(gate + up + down)
+    r = orc.expert_ffn(w, blob, act)
+    for i in range(32):
+        g, u = 2.0 * (1 + i % 3), -2.0 * (i % 5)
+        assert r["h"][i] == np.float32(g / (1.0 + math.exp(-g)) * u)
+    # down with an identity: y_r = f16(d_h) * q_r, the dequantised Q8_1(h)
+    d_h = orc.f16_decode(int(r["hq"][0, 0]) | int(r["hq"][0, 1]) << 8)
+    assert np.array_equal(r["y"], (d_h * r["hq"][0, 4:].view(np.int8).astype(np.float64)).astype(np.float32))
+
+
+def test_silu_zero_gate(orc):
+    w = _wl(hidden=32, n_ff=32, n_experts=1, top_k=1)
+    act = np.zeros((1, 36), np.uint8)
+    act[0, 1], act[0, 4] = 0x3C, 3
+    gate = [_q8_0_row(1, {}) for _ in range(32)]                  # g = 0 -> silu(0) = 0
+    up = [_q8_0_row(1, {0: 7}) for _ in range(32)]
+    down = [_q8_0_row(1, {0: 1}) for _ in range(32)]
+    r = orc.expert_ffn(w, _blob_from_rows(gate + up + down), act)
+    assert np.all(r["h"] == 0) and np.all(r["y"] == 0)
+
+
+def _layer_inputs(synth, w, batch=0):
+    return synth.gen_layer(w, batch)
+
+
+def test_identical_experts_independent_of_routing(orc, synth):
+    w = _wl(hidden=64, n_experts=6, top_k=3, n_ff=64, tokens=6)
+    inp = _layer_inputs(synth, w)
+    one = synth.gen_expert(w, 0)
+    experts = np.tile(one, w.n_experts)
+    out, taps = orc.layer_forward(w, inp["x"], inp["router_w"], experts=experts, taps=("xq", "ids"))
+    for t in range(w.tokens):
+        y = orc.expert_ffn(w, one, taps["xq"][t])["y"]
+        assert np.allclose(out[t], y, rtol=1e-6, atol=1e-7 * np.abs(y).max())
+    assert len({tuple(r) for r in taps["ids"]}) > 1       # routing really differed
+
+
+def test_zero_weights_and_zero_input(orc, synth):
+    w = _wl(tokens=4)
+    inp = _layer_inputs(synth, w)
+    zero = inp["experts"].copy()
+    bb = w.block_bytes
+    zb = zero.reshape(-1, bb)
+    zb[:, 2:] = 0
+    out, _ = orc.layer_forward(w, inp["x"], inp["router_w"], experts=zero)
+    assert np.all(out == 0)
+    out, taps = orc.layer_forward(w, np.zeros_like(inp["x"]), inp["router_w"],
+                                  experts=inp["experts"], taps=("ids", "weights"))
+    assert np.all(out == 0)
+    assert np.all(taps["ids"] == np.arange(w.top_k)) and np.all(taps["weights"] == np.float32(1 / 3))
+
+
+def test_token_list_matches_full_run(orc, synth):
+    w = _wl(tokens=7)
+    inp = _layer_inputs(synth, w)
+    full, _ = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"], nthreads=3)
+    part, _ = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"], tokens=[6, 2])
+    assert np.array_equal(part, full[[6, 2]])
+
+
+def _dequant_rows(orc, fmt, blocks, rows, nblk):
+    bb = 34 if fmt == 8 else 18
+    B = blocks.reshape(rows * nblk, bb)
+    d = B[:, :2].copy().view(np.float16).astype(np.float64).reshape(-1)
+    if fmt == 8:
+        q = B[:, 2:].view(np.int8).astype(np.float64)
+    else:
+        q = np.concatenate([B[:, 2:] & 0x0F, B[:, 2:] >> 4], axis=1).astype(np.float64) - 8
+    return (d[:, None] * q).reshape(rows, nblk * 32)
+
+
+@pytest.mark.parametrize("latent,fmt", [(0, 8), (0, 2), (64, 8), (64, 2)])
+def test_layer_close_to_unquantised_float_layer(orc, synth, latent, fmt):
+    """Sanity band: the quantised layer is within activation-quantisation error (about 1e-2
+    relative) of the same layer in float64 with unquantised activations.  Catches transposed
+    operands, a swapped gate/up, a missing combine weight."""
+    w = _wl(hidden=128, n_experts=8, top_k=2, n_ff=96, tokens=6, latent=latent, expert_fmt=fmt,
+            n_groups=4 if latent else 0, topk_groups=2 if latent else 0, seed=9)
+    inp = _layer_inputs(synth, w)
+    if latent:
+        # At these small widths the latent chain's values are ~1e-5, where the binary16 Q8_1
+        # scale is subnormal and keeps only a bit or two; x * 32 puts them where the full-size
+        # layers put them (y_lat ~ 1e-2).
+        inp["x"] = inp["x"] * np.float32(32.0)
+    out, taps = orc.layer_forward(w, inp["x"], inp["router_w"], groups=inp["groups"],
+                                  experts=inp["experts"], D=inp["D"], U=inp["U"],
+                                  taps=("ids", "weights"))
+    H, F, kin = w.hidden, w.n_ff, w.k_in
+    eb = w.expert_bytes
+    x = inp["x"].astype(np.float64)
+    if latent:
+        Dm = _dequant_rows(orc, 8, inp["D"], latent, H // 32)
+        Um = _dequant_rows(orc, 8, inp["U"], H, latent // 32)
+    ref = np.zeros((w.tokens, H))
+    for t in range(w.tokens):
+        a = Dm @ x[t] if latent else x[t]
+        acc = np.zeros(kin)
+        for j, e in enumerate(taps["ids"][t]):
+            blob = inp["experts"][e * eb:(e + 1) * eb]
+            bb = w.block_bytes
+            n_gu = F * (kin // 32) * bb
+            G = _dequant_rows(orc, fmt, blob[:n_gu], F, kin // 32)
+            Uu = _dequant_rows(orc, fmt, blob[n_gu:2 * n_gu], F, kin // 32)
+            Dn = _dequant_rows(orc, fmt, blob[2 * n_gu:], kin, F // 32)
+            g, u = G @ a, Uu @ a
+            acc += float(taps["weights"][t, j]) * (Dn @ (g / (1 + np.exp(-g)) * u))
+        ref[t] = Um @ acc if latent else acc
+    rel = np.sqrt(np.mean((out - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
+    assert 1e-4 < rel < 5e-2, rel
+
+
+def test_latent_selection_dense(orc, synth):
+    """D selecting the first L hidden units with d = 1, q = 1 makes z the dequantised Q8_1(x)
+    prefix exactly."""
+    w = _wl(hidden=128, n_experts=4, top_k=2, n_ff=64, tokens=3, latent=64, seed=4)
+    inp = _layer_inputs(synth, w)
+    D = np.zeros((64, 4, 34), np.uint8)
+    D[:, :, 1] = 0x3C
+    for r in range(64):
+        D[r, r // 32, 2 + r % 32] = 1
+    out, taps = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                                  D=D.reshape(-1), U=inp["U"], taps=("xq", "z"))
+    for t in range(3):
+        xq = taps["xq"][t]
+        deq = np.concatenate([orc.f16_decode(int(b[0]) | int(b[1]) << 8) * b[4:].view(np.int8).astype(np.float64)
+                              for b in xq])
+        assert np.array_equal(taps["z"][t], deq[:64].astype(np.float32))
+
+
+def test_oracle_refuses_bad_groups(orc, synth):
+    w = _wl(n_experts=8, top_k=3, n_groups=4, topk_groups=1)   # 1 group of 2 < k = 3
+    inp = _layer_inputs(synth, dataclasses.replace(w, n_groups=0, topk_groups=0))
+    with pytest.raises(ValueError):
+        orc.layer_forward(w, inp["x"], inp["router_w"], groups=np.arange(8, dtype=np.int32) // 2,
+                          experts=inp["experts"])
