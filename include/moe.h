@@ -1,0 +1,181 @@
+/*
+ * moe.h - C ABI of the quantized mixture-of-experts expert FFN for AMD MI355X
+ * (gfx950).  Implemented by libmoe.so (hand-written HIP kernels).
+ *
+ * The layer (sources are the pages' titles and sections):
+ *   - "Q8 0 support" (Strata pull request 255), section "GPU expert kernels":
+ *     Q8_0 expert weights in blocks of 32, multiplied against activations
+ *     quantised to Q8_1 blocks; the grouped gate/up/down expert kernels;
+ *     the follow-up commit: the Q8_1 block sum is the sum of the quantised
+ *     activations; unsupported format pairs are refused by name at start-up.
+ *   - "Sync upstream Strata v0.1.39 into Lanes" (pull request 24), the SYCL port
+ *     commits: per-token top-k routing over 256/512 experts, tokens grouped by
+ *     expert, activation quantisation that matches byte for byte only with a
+ *     correctly rounded fp32 divide, a split-K down kernel bit-identical to the
+ *     single-token one.
+ *   - edge0-strata README, section "Changes from upstream Strata": latent MoE,
+ *     dense Q8 D/U projections into a 1280- or 1792-wide latent space, expert
+ *     group labels, Q4_0 expert rows against Q8_1 activations.
+ *
+ * For each token t (x_t fp32, H wide):
+ *   1. router logits l_e = x_t . W_r[e] (+ b_e), accumulated in fp64;
+ *   2. with group labels: keep the experts of the topk_groups groups with the
+ *      largest member logit; top_k experts by logit (ties: lower id);
+ *      w_j = softmax over the chosen logits;
+ *   3. a = Q8_1(x_t) (latent: a = Q8_1(z_t), z_t = D . Q8_1(x_t));
+ *   4. per chosen expert e_j: g = W_gate a, u = W_up a, h = silu(g) * u,
+ *      y_j = W_down . Q8_1(h);
+ *   5. out_t = sum_j w_j y_j in rank order (latent: out_t = U . Q8_1(that sum)).
+ * Q8_1 of 32 floats: d = max|v| / 127 (fp32 divide), q = round-half-away(v / d),
+ * stored as binary16 d, binary16 s = d * sum(q), 32 int8 q.
+ *
+ * Conventions for every function below:
+ *   - Returns MOE_OK or a negative moe_status; no exception crosses the ABI.
+ *     moe_last_error() then names the refused argument (thread-local text).
+ *   - All shape, format and device checks happen in moe_layer_create / the
+ *     pack calls; moe_layer_forward re-checks only T, k and pointers.
+ *   - The caller owns every buffer.  The library allocates no device memory;
+ *     moe_layer holds host metadata only.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *     Forward calls are asynchronous on it and never synchronise the host.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,          /* bad argument: null pointer, size, T or k out of range   */
+    MOE_EUNSUPPORTED = -2,    /* valid but unsupported: format pair, dims not multiples  */
+    MOE_EDEVICE = -3,         /* no device, or the device is not gfx950                  */
+    MOE_EHIP = -4,            /* a HIP runtime call failed                                */
+    MOE_ENOMEM = -5           /* workspace or host staging too small / allocation failed  */
+} moe_status;
+
+/* Block formats.  The values mirror the pages' "case 8" of the format switch. */
+enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2 };
+
+/* Which packed tensor a pack call is about. */
+enum { MOE_PACK_EXPERTS = 0, MOE_PACK_D = 1, MOE_PACK_U = 2 };
+
+typedef struct {
+    int32_t hidden;       /* H: multiple of 256                                          */
+    int32_t n_experts;    /* E: 1..512                                                    */
+    int32_t top_k;        /* k: 1..min(E, 32)                                             */
+    int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
+    int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
+    int32_t expert_fmt;   /* MOE_FMT_Q8_0 or MOE_FMT_Q4_0                                 */
+    int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 (ignored when latent == 0)          */
+    int32_t n_groups;     /* 0 = no group limit; else divides E                           */
+    int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/
+    int32_t max_tokens;   /* largest T a forward call may pass: 1..65536                  */
+} moe_desc;
+
+typedef struct moe_layer moe_layer;
+
+/*
+ * Canonical (host, array-of-structs) layouts that the pack calls accept:
+ *   Q8_0 block = binary16 d (little-endian) + 32 int8 q              (34 bytes)
+ *   Q4_0 block = binary16 d + 16 bytes; byte j: element j in the low nibble,
+ *                element j+16 in the high nibble; value d*(c-8)       (18 bytes)
+ *   EXPERTS: for e in 0..E-1: gate [F][Kin/32], up [F][Kin/32], down [Kout][F/32]
+ *            blocks, rows row-major; Kin = Kout = latent ? L : H.
+ *   D: [L][H/32] Q8_0 blocks.  U: [H][L/32] Q8_0 blocks.
+ * The packed (device) layout has the same byte count; it splits codes from
+ * scales and orders gate/up rows in 32-row pairs.  It is private to the library.
+ */
+
+/* Validates desc and checks that `device` is a gfx950 GPU.  Shape and format
+ * errors are reported before the device is looked at.  *out receives a new
+ * host object; free it with moe_layer_destroy. */
+moe_status moe_layer_create(const moe_desc* desc, int device, moe_layer** out);
+void moe_layer_destroy(moe_layer* layer);
+
+/* Validates desc only (no device needed); the same checks as moe_layer_create. */
+moe_status moe_desc_check(const moe_desc* desc);
+
+/* Bytes of the canonical = packed form of one tensor (which = MOE_PACK_*).
+ * Needs no device.  MOE_PACK_D/U on a plain layer give MOE_EINVAL. */
+moe_status moe_pack_bytes(const moe_desc* desc, int which, size_t* bytes);
+
+/* Host-to-host layout conversion, canonical -> packed and back.  Needs no
+ * device.  Buffers hold moe_pack_bytes bytes and must not overlap. */
+moe_status moe_pack_host(const moe_desc* desc, int which, const void* canonical, void* packed);
+moe_status moe_unpack_host(const moe_desc* desc, int which, const void* packed, void* canonical);
+
+/* Converts a host canonical tensor and copies it to device memory dev_dst
+ * (moe_pack_bytes bytes), in chunks through host staging memory that the call
+ * allocates and frees.  Returns when the copy is complete. */
+moe_status moe_pack(const moe_layer* layer, int which, const void* host_canonical,
+                    void* dev_dst, void* stream);
+
+/* Device workspace a forward call with T tokens needs (T <= max_tokens).
+ * The workspace must be zero-filled before its first use; every call leaves
+ * its internal counters at zero again, so one zeroing suffices. */
+moe_status moe_workspace_bytes(const moe_layer* layer, int T, size_t* bytes);
+
+/*
+ * The layer on device memory.  x [T][H] fp32; router_w [E][H] fp32; router_b
+ * [E] fp32 or NULL; group_of_expert [E] int32 labels in [0, n_groups) with
+ * E/n_groups experts per label, or NULL when n_groups == 0; expert_packs, D, U
+ * the packed tensors (D, U NULL when latent == 0); k must equal desc.top_k;
+ * out [T][H] fp32.  T == 0 is a no-op.  Inputs must be finite (NaN/Inf:
+ * unspecified output).  Deterministic: the same inputs give bitwise the same
+ * out.  Calls sharing one workspace must not overlap in time.
+ */
+moe_status moe_layer_forward(const moe_layer* layer, const float* x, int T,
+                             const float* router_w, const float* router_b,
+                             const int32_t* group_of_expert, const void* expert_packs,
+                             const void* D, const void* U, int k, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-step outputs for checking, all device pointers, each NULL to skip.
+ * Token-major; a = t*k + j indexes assignments.  Q8_1 taps use the canonical
+ * 36-byte block (binary16 d, binary16 s, 32 int8).  Integer block sums are
+ * recorded only for tokens t < tap_tokens.
+ */
+typedef struct {
+    double*  logits;   /* [T][E]                                                   */
+    int32_t* ids;      /* [T][k]                                                   */
+    float*   weights;  /* [T][k]                                                   */
+    uint8_t* xq;       /* [T][H/32][36]  Q8_1(x)                                   */
+    float*   z;        /* [T][L]         latent only                               */
+    uint8_t* zq;       /* [T][L/32][36]  latent only                               */
+    float*   h;        /* [T*k][F]       silu(g)*u                                 */
+    uint8_t* hq;       /* [T*k][F/32][36]                                          */
+    float*   y;        /* [T*k][Kout]    each expert's down output                 */
+    float*   ylat;     /* [T][L]         latent only, the combined latent vector   */
+    uint8_t* ylq;      /* [T][L/32][36]  latent only                               */
+    int32_t* isum_gu;  /* [tap_tokens*k][2F][Kin/32]  gate rows, then up rows      */
+    int32_t* isum_dn;  /* [tap_tokens*k][Kout][F/32]                               */
+    int32_t* isum_d;   /* [tap_tokens][L][H/32]   latent only                      */
+    int32_t* isum_u;   /* [tap_tokens][H][L/32]   latent only                      */
+    int32_t  tap_tokens;
+} moe_taps;
+
+/* moe_layer_forward that also fills the non-NULL taps (slower kernels of the
+ * same code).  out is identical to moe_layer_forward's. */
+moe_status moe_layer_forward_taps(const moe_layer* layer, const float* x, int T,
+                                  const float* router_w, const float* router_b,
+                                  const int32_t* group_of_expert, const void* expert_packs,
+                                  const void* D, const void* U, int k, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const moe_taps* taps);
+
+/* Text of the last error on this thread ("" when none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

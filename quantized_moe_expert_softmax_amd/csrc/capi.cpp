@@ -1,0 +1,396 @@
+// Host side of libmoe: the C ABI declared in include/moe.h.
+//
+// Validation follows the pages' boundary conventions (Strata "Q8 0 support",
+// K-quant follow-up commit: an unsupported (gate/up format, down format, dims)
+// combination is refused by name at start-up, and an unknown type is refused
+// rather than leaving an output unwritten; Strata PR 24: launchers refuse an
+// unsupported device).  Every refusal returns a status and leaves a message
+// for moe_last_error().
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+struct moe_layer {
+    moe_desc desc;
+    Dims dims;
+    int device;
+};
+
+static thread_local std::string g_err;
+
+static moe_status fail(moe_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+static moe_status hip_fail(hipError_t e, const char* what) {
+    return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" const char* moe_last_error(void) { return g_err.c_str(); }
+extern "C" const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+static bool mult(int v, int m) { return v > 0 && v % m == 0; }
+
+extern "C" moe_status moe_desc_check(const moe_desc* d) {
+    if (!d) return fail(MOE_EINVAL, "desc is NULL");
+    if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0)
+        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is neither Q8_0 (8) nor Q4_0 (2)", d->expert_fmt);
+    if (d->latent && d->dense_fmt != MOE_FMT_Q8_0)
+        return fail(MOE_EUNSUPPORTED, "dense_fmt %d: the D/U projections support Q8_0 (8) only",
+                    d->dense_fmt);
+    if (!mult(d->hidden, 256) || d->hidden > 8192)
+        return fail(d->hidden <= 0 ? MOE_EINVAL : MOE_EUNSUPPORTED,
+                    "hidden %d must be a positive multiple of 256, at most 8192", d->hidden);
+    if (!mult(d->n_ff, 256) || d->n_ff > 8192)
+        return fail(d->n_ff <= 0 ? MOE_EINVAL : MOE_EUNSUPPORTED,
+                    "n_ff %d must be a positive multiple of 256, at most 8192", d->n_ff);
+    if (d->latent != 0 && (!mult(d->latent, 256) || d->latent > 8192))
+        return fail(d->latent < 0 ? MOE_EINVAL : MOE_EUNSUPPORTED,
+                    "latent %d must be 0 or a positive multiple of 256, at most 8192", d->latent);
+    if (d->n_experts < 1 || d->n_experts > 512)
+        return fail(MOE_EINVAL, "n_experts %d out of range 1..512", d->n_experts);
+    if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 32)
+        return fail(MOE_EINVAL, "top_k %d out of range 1..min(n_experts=%d, 32)", d->top_k,
+                    d->n_experts);
+    if (d->n_groups < 0) return fail(MOE_EINVAL, "n_groups %d is negative", d->n_groups);
+    if (d->n_groups > 0) {
+        if (d->n_groups > 64 || d->n_experts % d->n_groups)
+            return fail(MOE_EUNSUPPORTED, "n_groups %d must divide n_experts %d and be at most 64",
+                        d->n_groups, d->n_experts);
+        if (d->topk_groups < 1 || d->topk_groups > d->n_groups)
+            return fail(MOE_EINVAL, "topk_groups %d out of range 1..n_groups=%d", d->topk_groups,
+                        d->n_groups);
+        if (d->topk_groups * (d->n_experts / d->n_groups) < d->top_k)
+            return fail(MOE_EINVAL, "topk_groups %d x %d experts per group < top_k %d",
+                        d->topk_groups, d->n_experts / d->n_groups, d->top_k);
+    }
+    if (d->max_tokens < 1 || d->max_tokens > 65536)
+        return fail(MOE_EINVAL, "max_tokens %d out of range 1..65536", d->max_tokens);
+    const int kin = d->latent ? d->latent : d->hidden;
+    if (!mv_config_ok(kin, d->expert_fmt, true))
+        return fail(MOE_EUNSUPPORTED, "no gate/up kernel for %d-wide %s rows", kin,
+                    d->expert_fmt == MOE_FMT_Q4_0 ? "Q4_0" : "Q8_0");
+    if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
+        return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
+    if (d->latent && (!mv_config_ok(d->hidden, MOE_FMT_Q8_0, false) ||
+                      !mv_config_ok(d->latent, MOE_FMT_Q8_0, false)))
+        return fail(MOE_EUNSUPPORTED, "no D/U kernel for hidden %d, latent %d", d->hidden,
+                    d->latent);
+    g_err.clear();
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_layer_create(const moe_desc* desc, int device, moe_layer** out) {
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    moe_status s = moe_desc_check(desc);
+    if (s != MOE_OK) return s;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n == 0) return fail(MOE_EDEVICE, "no HIP device available");
+    if (device < 0 || device >= n)
+        return fail(MOE_EDEVICE, "device %d out of range (%d devices)", device, n);
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(MOE_EDEVICE, "device %d is %s; the kernels are built for gfx950 only", device,
+                    p.gcnArchName);
+    moe_layer* L = new moe_layer;
+    L->desc = *desc;
+    L->dims = make_dims(*desc);
+    L->device = device;
+    *out = L;
+    return MOE_OK;
+}
+
+extern "C" void moe_layer_destroy(moe_layer* layer) { delete layer; }
+
+// ---------------------------------------------------------------------------
+// packing
+
+static moe_status tensor_bytes(const moe_desc* d, int which, size_t* bytes, Dims* dims) {
+    moe_status s = moe_desc_check(d);
+    if (s != MOE_OK) return s;
+    Dims m = make_dims(*d);
+    if (dims) *dims = m;
+    switch (which) {
+        case MOE_PACK_EXPERTS: *bytes = (size_t)m.E * m.expert_bytes; return MOE_OK;
+        case MOE_PACK_D:
+        case MOE_PACK_U:
+            if (!m.L) return fail(MOE_EINVAL, "D/U requested for a layer with latent == 0");
+            *bytes = which == MOE_PACK_D ? m.D.bytes() : m.U.bytes();
+            return MOE_OK;
+        default: return fail(MOE_EINVAL, "unknown tensor %d", which);
+    }
+}
+
+extern "C" moe_status moe_pack_bytes(const moe_desc* d, int which, size_t* bytes) {
+    if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+    return tensor_bytes(d, which, bytes, nullptr);
+}
+
+// Canonical row index of packed row p of a block matrix.
+typedef int (*RowMap)(int p, int F);
+static int identity_row(int p, int) { return p; }
+static int gate_up_row(int p, int F) {
+    int fb = p / 64, r = p % 64;
+    return r < 32 ? fb * 32 + r : F + fb * 32 + (r - 32);
+}
+
+// One matrix: canonical blocks (rows in canonical order) <-> packed codes/scales.
+static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t* canon,
+                           uint8_t* packed, bool to_packed) {
+    const int bb = block_bytes(M.fmt), cb = code_bytes(M.fmt);
+    uint8_t* codes = packed + M.codes_off;
+    uint8_t* scales = packed + M.scales_off;
+    for (int p = 0; p < M.rows; ++p) {
+        const int r = map(p, F);
+        for (int b = 0; b < M.nblk; ++b) {
+            const size_t cpos = ((size_t)r * M.nblk + b) * bb;
+            const size_t ppos = ((size_t)p * M.nblk + b);
+            if (to_packed) {
+                memcpy(scales + 2 * ppos, canon + cpos, 2);
+                memcpy(codes + ppos * cb, canon + cpos + 2, cb);
+            } else {
+                uint8_t* c = const_cast<uint8_t*>(canon);
+                memcpy(c + cpos, scales + 2 * ppos, 2);
+                memcpy(c + cpos + 2, codes + ppos * cb, cb);
+            }
+        }
+    }
+}
+
+static void convert_expert(const Dims& m, const uint8_t* canon, uint8_t* packed, bool to_packed) {
+    convert_matrix(m.gu, gate_up_row, m.F, canon, packed, to_packed);
+    convert_matrix(m.dn, identity_row, m.F, canon + m.gu.bytes(), packed + m.dn_off, to_packed);
+}
+
+static moe_status convert(const moe_desc* d, int which, const void* src, void* dst, bool to_packed) {
+    size_t bytes;
+    Dims m;
+    moe_status s = tensor_bytes(d, which, &bytes, &m);
+    if (s != MOE_OK) return s;
+    if (!src || !dst) return fail(MOE_EINVAL, "NULL buffer");
+    const uint8_t* canon = (const uint8_t*)(to_packed ? src : dst);
+    uint8_t* packed = (uint8_t*)(to_packed ? dst : (void*)src);
+    if (which == MOE_PACK_EXPERTS) {
+        for (int e = 0; e < m.E; ++e)
+            convert_expert(m, canon + (size_t)e * m.expert_bytes, packed + (size_t)e * m.expert_bytes,
+                           to_packed);
+    } else {
+        convert_matrix(which == MOE_PACK_D ? m.D : m.U, identity_row, 0, canon, packed, to_packed);
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_pack_host(const moe_desc* d, int which, const void* canonical,
+                                    void* packed) {
+    return convert(d, which, canonical, packed, true);
+}
+
+extern "C" moe_status moe_unpack_host(const moe_desc* d, int which, const void* packed,
+                                      void* canonical) {
+    return convert(d, which, packed, canonical, false);
+}
+
+namespace {
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+}  // namespace
+
+extern "C" moe_status moe_pack(const moe_layer* L, int which, const void* host_canonical,
+                               void* dev_dst, void* stream) {
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    if (!host_canonical || !dev_dst) return fail(MOE_EINVAL, "NULL buffer");
+    size_t bytes;
+    Dims m;
+    moe_status s = tensor_bytes(&L->desc, which, &bytes, &m);
+    if (s != MOE_OK) return s;
+    DeviceGuard g(L->device);
+    if (!g.ok) return fail(MOE_EDEVICE, "cannot select device %d", L->device);
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* src = (const uint8_t*)host_canonical;
+    uint8_t* dst = (uint8_t*)dev_dst;
+    size_t chunk = which == MOE_PACK_EXPERTS ? m.expert_bytes : bytes;
+    std::vector<uint8_t> stage;
+    try {
+        stage.resize(chunk);
+    } catch (...) {
+        return fail(MOE_ENOMEM, "host staging of %zu bytes failed", chunk);
+    }
+    for (size_t off = 0; off < bytes; off += chunk) {
+        if (which == MOE_PACK_EXPERTS)
+            convert_expert(m, src + off, stage.data(), true);
+        else
+            convert_matrix(which == MOE_PACK_D ? m.D : m.U, identity_row, 0, src, stage.data(), true);
+        hipError_t e = hipMemcpyAsync(dst + off, stage.data(), chunk, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "copy of packed weights");
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
+    if (!L || !bytes) return fail(MOE_EINVAL, "NULL argument");
+    if (T < 0 || T > L->desc.max_tokens)
+        return fail(MOE_EINVAL, "T %d out of range 0..max_tokens=%d", T, L->desc.max_tokens);
+    *bytes = ws_layout(L->dims, std::max(T, 1)).total;
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+
+// Decode sizes run the down projection per token with the combine fused;
+// larger T runs it per expert bucket and combines afterwards.
+static const int DOWN_TOK_MAX_T = 8;
+
+static moe_status forward_impl(const moe_layer* L, const float* x, int T, const float* router_w,
+                               const float* router_b, const int32_t* groups, const void* experts,
+                               const void* Dp, const void* Up, int k, float* out, void* workspace,
+                               size_t ws_bytes, void* stream, const moe_taps* taps) {
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    const Dims& m = L->dims;
+    if (k != m.k) return fail(MOE_EINVAL, "k %d differs from the layer's top_k %d", k, m.k);
+    if (T < 0 || T > m.max_tokens)
+        return fail(MOE_EINVAL, "T %d out of range 0..max_tokens=%d", T, m.max_tokens);
+    if (T == 0) return MOE_OK;
+    if (!x || !router_w || !experts || !out || !workspace)
+        return fail(MOE_EINVAL, "NULL x, router_w, expert_packs, out or workspace");
+    if (m.L && (!Dp || !Up)) return fail(MOE_EINVAL, "latent layer needs D and U");
+    if (m.G && !groups) return fail(MOE_EINVAL, "n_groups %d needs group_of_expert", m.G);
+    const WsLayout w = ws_layout(m, T);
+    if (ws_bytes < w.total)
+        return fail(MOE_ENOMEM, "workspace of %zu bytes < %zu needed for T=%d", ws_bytes, w.total, T);
+    DeviceGuard g(L->device);
+    if (!g.ok) return fail(MOE_EDEVICE, "cannot select device %d", L->device);
+
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const uint8_t* ex = (const uint8_t*)experts;
+    const int A = T * m.k;
+    ActPtr xq{(int8_t*)(ws + w.xq_q), (uint32_t*)(ws + w.xq_ds), (int32_t*)(ws + w.xq_sq)};
+    ActPtr zq{(int8_t*)(ws + w.zq_q), (uint32_t*)(ws + w.zq_ds), (int32_t*)(ws + w.zq_sq)};
+    ActPtr hq{(int8_t*)(ws + w.hq_q), (uint32_t*)(ws + w.hq_ds), (int32_t*)(ws + w.hq_sq)};
+    ActPtr ylq{(int8_t*)(ws + w.ylq_q), (uint32_t*)(ws + w.ylq_ds), (int32_t*)(ws + w.ylq_sq)};
+    float* z = (float*)(ws + w.z);
+    float* y = (float*)(ws + w.y);
+    float* ylat = (float*)(ws + w.ylat);
+    Buckets b;
+    b.ctrl = (const uint32_t*)(ws + w.ctrl);
+    b.active = (const int32_t*)(ws + w.active);
+    b.counts = (const int32_t*)(ws + w.counts);
+    b.lists = (const int32_t*)(ws + w.lists);
+    b.tile_start = (const int32_t*)(ws + w.tile_start);
+    b.ids = (const int32_t*)(ws + w.ids);
+    b.wts = (const float*)(ws + w.wts);
+    Taps tp;
+    if (taps) {
+        tp.h = taps->h;
+        tp.isum_gu = taps->isum_gu;
+        tp.isum_dn = taps->isum_dn;
+        tp.isum_d = taps->isum_d;
+        tp.isum_u = taps->isum_u;
+        tp.tap_tokens = std::min(std::max(taps->tap_tokens, 0), T);
+        if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
+    }
+    const bool down_tok = !m.L && T <= DOWN_TOK_MAX_T;
+    if (taps && down_tok) tp.y = taps->y;
+
+    hipError_t e;
+#define CK(call, what)                                  \
+    do {                                                \
+        e = (call);                                     \
+        if (e != hipSuccess) return hip_fail(e, what);  \
+    } while (0)
+
+    CK(launch_quant_rows(x, T, m.H, xq, st), "quantise x");
+    CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, st),
+       "router");
+    CK(launch_bucket(m, w, ws, T, 32, st), "bucketing");
+    ActPtr ain = xq;
+    if (m.L) {
+        CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
+        CK(launch_quant_rows(z, T, m.L, zq, st), "quantise z");
+        ain = zq;
+    }
+    CK(launch_gate_up_mv(m, T, ex, ain, b, hq, tp, st), "gate/up");
+    if (down_tok) {
+        CK(launch_down_tok_mv(m, T, ex, hq, b, out, tp, st), "down+combine");
+    } else {
+        CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
+        if (!m.L) {
+            CK(launch_combine(y, b.wts, T, m.k, m.H, out, st), "combine");
+        } else {
+            CK(launch_combine(y, b.wts, T, m.k, m.L, ylat, st), "combine");
+            CK(launch_quant_rows(ylat, T, m.L, ylq, st), "quantise y_lat");
+            CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st),
+               "U");
+        }
+    }
+    if (taps) {
+        if (taps->ids) CK(hipMemcpyAsync(taps->ids, b.ids, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, st), "tap ids");
+        if (taps->weights) CK(hipMemcpyAsync(taps->weights, b.wts, sizeof(float) * A, hipMemcpyDeviceToDevice, st), "tap weights");
+        CK(launch_tap_q8_1(xq, T, m.H, taps->xq, st), "tap xq");
+        CK(launch_tap_q8_1(hq, A, m.F, taps->hq, st), "tap hq");
+        if (m.L) {
+            CK(launch_tap_q8_1(zq, T, m.L, taps->zq, st), "tap zq");
+            CK(launch_tap_q8_1(ylq, T, m.L, taps->ylq, st), "tap ylq");
+            if (taps->z) CK(hipMemcpyAsync(taps->z, z, sizeof(float) * T * m.L, hipMemcpyDeviceToDevice, st), "tap z");
+            if (taps->ylat) CK(hipMemcpyAsync(taps->ylat, ylat, sizeof(float) * T * m.L, hipMemcpyDeviceToDevice, st), "tap ylat");
+        }
+        if (!down_tok && taps->y)
+            CK(hipMemcpyAsync(taps->y, y, sizeof(float) * (size_t)A * m.kout, hipMemcpyDeviceToDevice, st), "tap y");
+    }
+#undef CK
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_layer_forward(const moe_layer* L, const float* x, int T,
+                                        const float* router_w, const float* router_b,
+                                        const int32_t* groups, const void* experts, const void* D,
+                                        const void* U, int k, float* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+extern "C" moe_status moe_layer_forward_taps(const moe_layer* L, const float* x, int T,
+                                             const float* router_w, const float* router_b,
+                                             const int32_t* groups, const void* experts,
+                                             const void* D, const void* U, int k, float* out,
+                                             void* workspace, size_t workspace_bytes, void* stream,
+                                             const moe_taps* taps) {
+    if (!taps) return fail(MOE_EINVAL, "taps is NULL");
+    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
+                        workspace_bytes, stream, taps);
+}

@@ -1,0 +1,55 @@
+// Kernel launchers of libmoe (host side of the HIP translation units).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// Where the expert FFN kernels find routing and buckets.
+struct Buckets {
+    const uint32_t* ctrl;     // CW_N_ACTIVE, CW_N_TILES
+    const int32_t* active;    // slot -> expert
+    const int32_t* counts;    // [E] tokens per expert
+    const int32_t* lists;     // [E][T] assignments a = t*k + j, token order
+    const int32_t* tile_start;// [E+1] first token tile of each slot
+    const int32_t* ids;       // [T][k]
+    const float* wts;         // [T][k]
+};
+
+struct Taps {                 // device pointers, NULL = off
+    float* h = nullptr;       // [A][F]
+    float* y = nullptr;       // [A][Kout]
+    int32_t* isum_gu = nullptr;
+    int32_t* isum_dn = nullptr;
+    int32_t* isum_d = nullptr;
+    int32_t* isum_u = nullptr;
+    int tap_tokens = 0;
+};
+
+hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStream_t st);
+hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
+                         const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
+                         hipStream_t st);
+hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, int tile_m,
+                         hipStream_t st);
+hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R, float* out,
+                          hipStream_t st);
+hipError_t launch_tap_q8_1(ActPtr a, long rows, int K, uint8_t* out, hipStream_t st);
+
+// True when the matrix-vector kernels have a configuration for rows of K
+// elements of format fmt (gate_up: the 64-row gate/up slab kernel).
+bool mv_config_ok(int K, int fmt, bool gate_up);
+
+// Decode-path expert and dense kernels (matrix-vector, one pass over the weights).
+hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+                             const Buckets& b, ActPtr hq, const Taps& taps, hipStream_t st);
+hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+                              const Buckets& b, float* out, const Taps& taps, hipStream_t st);
+hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+                               const Buckets& b, float* y, const Taps& taps, hipStream_t st);
+hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
+                           int32_t* isum_tap, int tap_tokens, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,147 @@
+// Internal layout and launch interface of libmoe (host and device code of the
+// library only; the public ABI is include/moe.h).
+//
+// Packed block matrix [rows][nblk] (any format): the codes of all rows first,
+// row-major (32 bytes per Q8_0 block, 16 per Q4_0 block, in element order for
+// Q8_0 and in the canonical nibble-byte order for Q4_0), then the binary16
+// scales, row-major [row][block].  Same byte count as the canonical blocks.
+//
+// Packed expert: gate/up matrix of 2F rows then the down matrix [Kout][F/32].
+// The gate/up rows come in pairs of 32-row tiles: packed row fb*64 + r holds
+// gate row fb*32 + r for r < 32 and up row fb*32 + r - 32 otherwise, so one
+// 64-row slab carries everything SwiGLU needs for 32 outputs.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int QK = 32;              // elements per block
+constexpr int Q8_1_CANON = 36;      // canonical Q8_1 block bytes
+
+inline int code_bytes(int fmt) { return fmt == MOE_FMT_Q4_0 ? 16 : 32; }
+inline int block_bytes(int fmt) { return code_bytes(fmt) + 2; }
+
+struct MatLayout {                  // one packed block matrix
+    int rows = 0, nblk = 0, fmt = MOE_FMT_Q8_0;
+    size_t codes_off = 0;           // from the matrix base
+    size_t scales_off = 0;
+    size_t row_code_bytes() const { return (size_t)nblk * code_bytes(fmt); }
+    size_t bytes() const { return (size_t)rows * nblk * block_bytes(fmt); }
+};
+
+inline MatLayout mat_layout(int rows, int nblk, int fmt) {
+    MatLayout m;
+    m.rows = rows;
+    m.nblk = nblk;
+    m.fmt = fmt;
+    m.codes_off = 0;
+    m.scales_off = (size_t)rows * nblk * code_bytes(fmt);
+    return m;
+}
+
+struct Dims {
+    int H, E, k, F, L, kin, kout, fmt, dfmt, G, TG, max_tokens;
+    MatLayout gu, dn;               // offsets within one expert
+    size_t dn_off;                  // byte offset of the down matrix in an expert
+    size_t expert_bytes;
+    MatLayout D, U;                 // latent dense projections
+};
+
+inline Dims make_dims(const moe_desc& d) {
+    Dims m;
+    m.H = d.hidden; m.E = d.n_experts; m.k = d.top_k; m.F = d.n_ff; m.L = d.latent;
+    m.kin = d.latent ? d.latent : d.hidden;
+    m.kout = m.kin;
+    m.fmt = d.expert_fmt; m.dfmt = MOE_FMT_Q8_0;
+    m.G = d.n_groups; m.TG = d.topk_groups; m.max_tokens = d.max_tokens;
+    m.gu = mat_layout(2 * m.F, m.kin / QK, m.fmt);
+    m.dn = mat_layout(m.kout, m.F / QK, m.fmt);
+    m.dn_off = m.gu.bytes();
+    m.expert_bytes = m.gu.bytes() + m.dn.bytes();
+    if (m.L) {
+        m.D = mat_layout(m.L, m.H / QK, MOE_FMT_Q8_0);
+        m.U = mat_layout(m.H, m.L / QK, MOE_FMT_Q8_0);
+    }
+    return m;
+}
+
+// Quantised activations in the workspace (Q8_1 content, split layout):
+//   q  int8   [rows][K]
+//   ds uint32 [rows][K/32]   binary16 d in the low half, binary16 s in the high half
+//   sq int32  [rows][K/32]   sum of the block's q (exact)
+struct ActPtr {
+    int8_t* q;
+    uint32_t* ds;
+    int32_t* sq;
+};
+
+constexpr int ROUTER_SPLIT_MAX = 16;
+
+// Control words at the start of the workspace.
+enum CtrlWord {
+    CW_BUCKET_ARRIVE = 0,   // arrivals of the per-expert bucketing workgroups
+    CW_N_ACTIVE = 1,        // experts with at least one token
+    CW_N_TILES = 2,         // token tiles over all active experts (grouped GEMM)
+    CW_COUNT = 64
+};
+
+struct WsLayout {
+    size_t ctrl, logit_part, ids, wts, counts, active, tile_start, lists;
+    size_t xq_q, xq_ds, xq_sq;
+    size_t z, zq_q, zq_ds, zq_sq;
+    size_t hq_q, hq_ds, hq_sq;
+    size_t y;
+    size_t ylat, ylq_q, ylq_ds, ylq_sq;
+    size_t total;
+    int T, S;                       // tokens, router K-splits
+};
+
+inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline int router_splits(const Dims& m, int T) {
+    // enough workgroups to spread the router matrix at small T
+    if (T > 32) return 1;
+    int s = 1;
+    while (s < ROUTER_SPLIT_MAX && (m.E / 4) * s * 2 <= 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
+    return s;
+}
+
+inline WsLayout ws_layout(const Dims& m, int T) {
+    WsLayout w;
+    w.T = T;
+    w.S = router_splits(m, T);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = al256(o + bytes); return r; };
+    size_t A = (size_t)T * m.k;
+    w.ctrl = take(sizeof(uint32_t) * CW_COUNT);
+    w.logit_part = take(sizeof(double) * w.S * T * m.E);
+    w.ids = take(sizeof(int32_t) * A);
+    w.wts = take(sizeof(float) * A);
+    w.counts = take(sizeof(int32_t) * m.E);
+    w.active = take(sizeof(int32_t) * m.E);
+    w.tile_start = take(sizeof(int32_t) * (m.E + 1));
+    w.lists = take(sizeof(int32_t) * (size_t)m.E * T);
+    w.xq_q = take((size_t)T * m.H);
+    w.xq_ds = take(sizeof(uint32_t) * T * (m.H / QK));
+    w.xq_sq = take(sizeof(int32_t) * T * (m.H / QK));
+    const size_t L = m.L ? m.L : QK;
+    w.z = take(sizeof(float) * (size_t)T * L);
+    w.zq_q = take((size_t)T * L);
+    w.zq_ds = take(sizeof(uint32_t) * T * (L / QK));
+    w.zq_sq = take(sizeof(int32_t) * T * (L / QK));
+    w.hq_q = take(A * m.F);
+    w.hq_ds = take(sizeof(uint32_t) * A * (m.F / QK));
+    w.hq_sq = take(sizeof(int32_t) * A * (m.F / QK));
+    w.y = take(sizeof(float) * A * m.kout);
+    w.ylat = take(sizeof(float) * (size_t)T * L);
+    w.ylq_q = take((size_t)T * L);
+    w.ylq_ds = take(sizeof(uint32_t) * T * (L / QK));
+    w.ylq_sq = take(sizeof(int32_t) * T * (L / QK));
+    w.total = o;
+    return w;
+}
+
+}  // namespace moe

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/moe.h declares, descriptors are validated with named
+refusals, the packer round-trips and places blocks where the layout says."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_moe_expert_softmax_amd import moe, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return moe.lib()
+    except (ImportError, OSError) as e:
+        pytest.fail(f"libmoe.so does not load: {e}")
+
+
+def test_exports_match_header(L):
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    declared = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", hdr))
+    assert declared == set(moe.EXPORTS), declared ^ set(moe.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert moe.moe_version().startswith("moe-gfx950")
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_descs_valid(L, name):
+    w = synth.WORKLOADS[name]
+    moe.moe_desc_check(moe.desc_of(w, max_tokens=2048))
+
+
+def _refused(desc, status, word):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_desc_check(desc)
+    assert ei.value.status == status, ei.value
+    assert word in ei.value.message, ei.value.message
+
+
+def test_desc_refusals_name_the_cause(L):
+    ok = dict(hidden=512, n_experts=8, top_k=2, n_ff=256, max_tokens=4)
+    _refused(moe.make_desc(**{**ok, "expert_fmt": 6}), moe.MOE_EUNSUPPORTED, "expert_fmt")
+    _refused(moe.make_desc(**{**ok, "hidden": 500}), moe.MOE_EUNSUPPORTED, "hidden")
+    _refused(moe.make_desc(**{**ok, "hidden": 0}), moe.MOE_EINVAL, "hidden")
+    _refused(moe.make_desc(**{**ok, "n_ff": 384}), moe.MOE_EUNSUPPORTED, "n_ff")
+    _refused(moe.make_desc(**{**ok, "top_k": 9}), moe.MOE_EINVAL, "top_k")
+    _refused(moe.make_desc(**{**ok, "top_k": 0}), moe.MOE_EINVAL, "top_k")
+    _refused(moe.make_desc(**{**ok, "n_experts": 0}), moe.MOE_EINVAL, "n_experts")
+    _refused(moe.make_desc(**{**ok, "max_tokens": 0}), moe.MOE_EINVAL, "max_tokens")
+    _refused(moe.make_desc(**{**ok, "n_groups": 3, "topk_groups": 1}), moe.MOE_EUNSUPPORTED, "n_groups")
+    _refused(moe.make_desc(**{**ok, "n_groups": 4, "topk_groups": 0}), moe.MOE_EINVAL, "topk_groups")
+    _refused(moe.make_desc(**{**ok, "n_groups": 4, "topk_groups": 5}), moe.MOE_EINVAL, "topk_groups")
+    _refused(moe.make_desc(**{**ok, "n_groups": 8, "topk_groups": 1}), moe.MOE_EINVAL, "top_k")
+    _refused(moe.make_desc(**{**ok, "latent": 256, "dense_fmt": 2}), moe.MOE_EUNSUPPORTED, "dense_fmt")
+    _refused(moe.make_desc(**{**ok, "latent": 300}), moe.MOE_EUNSUPPORTED, "latent")
+    _refused(moe.make_desc(**{**ok, "hidden": 8192 + 256}), moe.MOE_EUNSUPPORTED, "hidden")
+    assert L.moe_desc_check(None) == moe.MOE_EINVAL
+
+
+def test_create_without_gpu_is_a_device_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_create(moe.make_desc(512, 8, 2, 256, max_tokens=4), 0)
+    assert ei.value.status == moe.MOE_EDEVICE
+    # shape errors are reported before the device is looked at
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_create(moe.make_desc(500, 8, 2, 256, max_tokens=4), 0)
+    assert ei.value.status == moe.MOE_EUNSUPPORTED
+
+
+def test_pack_bytes(L):
+    w = synth.WORKLOADS["decode"]
+    d = moe.desc_of(w)
+    assert moe.moe_pack_bytes(d, moe.MOE_PACK_EXPERTS) == 128 * 20_054_016
+    with pytest.raises(moe.MoeError):
+        moe.moe_pack_bytes(d, moe.MOE_PACK_D)
+    w2 = synth.WORKLOADS["latent_q4"]
+    d2 = moe.desc_of(w2)
+    assert moe.moe_pack_bytes(d2, moe.MOE_PACK_EXPERTS) == 256 * 3_096_576
+    assert moe.moe_pack_bytes(d2, moe.MOE_PACK_D) == 1792 * 224 * 34
+    assert moe.moe_pack_bytes(d2, moe.MOE_PACK_U) == 7168 * 56 * 34
+
+
+def _small(fmt=8, latent=0):
+    return synth.Workload("pk", hidden=512, n_experts=3, top_k=2, n_ff=256, tokens=2,
+                          latent=latent, expert_fmt=fmt, seed=77)
+
+
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (8, 256), (2, 256)])
+def test_pack_roundtrip(L, fmt, latent):
+    w = _small(fmt, latent)
+    d = moe.desc_of(w)
+    ex = synth.gen_experts(w)
+    packed = np.empty_like(ex)
+    moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
+    assert not np.array_equal(packed, ex)
+    back = np.zeros_like(ex)
+    moe.moe_unpack_host(d, moe.MOE_PACK_EXPERTS, packed.ctypes.data, back.ctypes.data)
+    assert np.array_equal(back, ex)
+    if latent:
+        D, U = synth.gen_dense(w)
+        for which, t in ((moe.MOE_PACK_D, D), (moe.MOE_PACK_U, U)):
+            p = np.empty_like(t)
+            moe.moe_pack_host(d, which, t.ctypes.data, p.ctypes.data)
+            b = np.zeros_like(t)
+            moe.moe_unpack_host(d, which, p.ctypes.data, b.ctypes.data)
+            assert np.array_equal(b, t)
+
+
+@pytest.mark.parametrize("fmt", [8, 2])
+def test_pack_layout_positions(L, fmt):
+    """Spot-check the documented packed layout: codes of all rows, then binary16 scales;
+    gate/up rows interleaved in 32-row tiles."""
+    w = _small(fmt)
+    d = moe.desc_of(w)
+    ex = synth.gen_experts(w)
+    packed = np.empty_like(ex)
+    moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
+    bb = 34 if fmt == 8 else 18
+    cb = bb - 2
+    F, K = w.n_ff, w.hidden
+    nb = K // 32
+    e = 2
+    blob = ex[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    pk = packed[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    codes_gu = pk[:2 * F * nb * cb]
+    scales_gu = pk[2 * F * nb * cb:2 * F * nb * bb]
+    for (canon_row, packed_row) in [(0, 0), (31, 31), (F + 0, 32), (F + 31, 63), (32, 64),
+                                    (F + 33, 97), (F - 1, 64 * (F // 32 - 1) + 31)]:
+        for b in (0, nb - 1, 5):
+            cblk = blob[(canon_row * nb + b) * bb:(canon_row * nb + b + 1) * bb]
+            assert np.array_equal(codes_gu[(packed_row * nb + b) * cb:(packed_row * nb + b + 1) * cb], cblk[2:])
+            assert np.array_equal(scales_gu[(packed_row * nb + b) * 2:(packed_row * nb + b) * 2 + 2], cblk[:2])
+    # down matrix: rows in order
+    dn_c = blob[2 * F * nb * bb:]
+    dn_p = pk[2 * F * nb * bb:]
+    nbf = F // 32
+    rows = w.k_out
+    for r, b in [(0, 0), (rows - 1, nbf - 1), (17, 3)]:
+        cblk = dn_c[(r * nbf + b) * bb:(r * nbf + b + 1) * bb]
+        assert np.array_equal(dn_p[(r * nbf + b) * cb:(r * nbf + b + 1) * cb], cblk[2:])
+        off = rows * nbf * cb + (r * nbf + b) * 2
+        assert np.array_equal(dn_p[off:off + 2], cblk[:2])
+
+
+def test_forward_argument_checks_without_gpu(L):
+    # a NULL layer is refused before anything touches a device
+    st = L.moe_layer_forward(None, None, 1, None, None, None, None, None, None, 2, None, None, 0, None)
+    assert st == moe.MOE_EINVAL
+    ws = ctypes.c_size_t()
+    assert L.moe_workspace_bytes(None, 1, ctypes.byref(ws)) == moe.MOE_EINVAL
