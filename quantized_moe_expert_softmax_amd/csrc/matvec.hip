@@ -350,30 +350,38 @@ static bool pick(int nch, int& lpr, int& cpl) {
 
 #define MOE_LPR_CPL_SWITCH(LPR_, CPL_, CALL)                                      \
     switch (LPR_ * 16 + CPL_) {                                                    \
-        case 8 * 16 + 1: { constexpr int L = 8, C = 1; CALL; break; }             \
-        case 8 * 16 + 2: { constexpr int L = 8, C = 2; CALL; break; }             \
-        case 8 * 16 + 3: { constexpr int L = 8, C = 3; CALL; break; }             \
-        case 8 * 16 + 4: { constexpr int L = 8, C = 4; CALL; break; }             \
-        case 8 * 16 + 5: { constexpr int L = 8, C = 5; CALL; break; }             \
-        case 8 * 16 + 6: { constexpr int L = 8, C = 6; CALL; break; }             \
-        case 8 * 16 + 7: { constexpr int L = 8, C = 7; CALL; break; }             \
-        case 8 * 16 + 8: { constexpr int L = 8, C = 8; CALL; break; }             \
-        case 16 * 16 + 5: { constexpr int L = 16, C = 5; CALL; break; }           \
-        case 16 * 16 + 6: { constexpr int L = 16, C = 6; CALL; break; }           \
-        case 16 * 16 + 7: { constexpr int L = 16, C = 7; CALL; break; }           \
-        case 16 * 16 + 8: { constexpr int L = 16, C = 8; CALL; break; }           \
-        case 32 * 16 + 5: { constexpr int L = 32, C = 5; CALL; break; }           \
-        case 32 * 16 + 6: { constexpr int L = 32, C = 6; CALL; break; }           \
-        case 32 * 16 + 7: { constexpr int L = 32, C = 7; CALL; break; }           \
-        case 32 * 16 + 8: { constexpr int L = 32, C = 8; CALL; break; }           \
-        case 64 * 16 + 1: { constexpr int L = 64, C = 1; CALL; break; }           \
-        case 64 * 16 + 2: { constexpr int L = 64, C = 2; CALL; break; }           \
-        case 64 * 16 + 3: { constexpr int L = 64, C = 3; CALL; break; }           \
-        case 64 * 16 + 4: { constexpr int L = 64, C = 4; CALL; break; }           \
-        case 64 * 16 + 5: { constexpr int L = 64, C = 5; CALL; break; }           \
-        case 64 * 16 + 6: { constexpr int L = 64, C = 6; CALL; break; }           \
-        case 64 * 16 + 7: { constexpr int L = 64, C = 7; CALL; break; }           \
-        case 64 * 16 + 8: { constexpr int L = 64, C = 8; CALL; break; }           \
+        case 8 * 16 + 1: { constexpr int L = 8, C = 1; CALL; break; }          \
+        case 8 * 16 + 2: { constexpr int L = 8, C = 2; CALL; break; }          \
+        case 8 * 16 + 3: { constexpr int L = 8, C = 3; CALL; break; }          \
+        case 8 * 16 + 4: { constexpr int L = 8, C = 4; CALL; break; }          \
+        case 8 * 16 + 5: { constexpr int L = 8, C = 5; CALL; break; }          \
+        case 8 * 16 + 6: { constexpr int L = 8, C = 6; CALL; break; }          \
+        case 8 * 16 + 7: { constexpr int L = 8, C = 7; CALL; break; }          \
+        case 8 * 16 + 8: { constexpr int L = 8, C = 8; CALL; break; }          \
+        case 16 * 16 + 1: { constexpr int L = 16, C = 1; CALL; break; }        \
+        case 16 * 16 + 2: { constexpr int L = 16, C = 2; CALL; break; }        \
+        case 16 * 16 + 3: { constexpr int L = 16, C = 3; CALL; break; }        \
+        case 16 * 16 + 4: { constexpr int L = 16, C = 4; CALL; break; }        \
+        case 16 * 16 + 5: { constexpr int L = 16, C = 5; CALL; break; }        \
+        case 16 * 16 + 6: { constexpr int L = 16, C = 6; CALL; break; }        \
+        case 16 * 16 + 7: { constexpr int L = 16, C = 7; CALL; break; }        \
+        case 16 * 16 + 8: { constexpr int L = 16, C = 8; CALL; break; }        \
+        case 32 * 16 + 1: { constexpr int L = 32, C = 1; CALL; break; }        \
+        case 32 * 16 + 2: { constexpr int L = 32, C = 2; CALL; break; }        \
+        case 32 * 16 + 3: { constexpr int L = 32, C = 3; CALL; break; }        \
+        case 32 * 16 + 4: { constexpr int L = 32, C = 4; CALL; break; }        \
+        case 32 * 16 + 5: { constexpr int L = 32, C = 5; CALL; break; }        \
+        case 32 * 16 + 6: { constexpr int L = 32, C = 6; CALL; break; }        \
+        case 32 * 16 + 7: { constexpr int L = 32, C = 7; CALL; break; }        \
+        case 32 * 16 + 8: { constexpr int L = 32, C = 8; CALL; break; }        \
+        case 64 * 16 + 1: { constexpr int L = 64, C = 1; CALL; break; }        \
+        case 64 * 16 + 2: { constexpr int L = 64, C = 2; CALL; break; }        \
+        case 64 * 16 + 3: { constexpr int L = 64, C = 3; CALL; break; }        \
+        case 64 * 16 + 4: { constexpr int L = 64, C = 4; CALL; break; }        \
+        case 64 * 16 + 5: { constexpr int L = 64, C = 5; CALL; break; }        \
+        case 64 * 16 + 6: { constexpr int L = 64, C = 6; CALL; break; }        \
+        case 64 * 16 + 7: { constexpr int L = 64, C = 7; CALL; break; }        \
+        case 64 * 16 + 8: { constexpr int L = 64, C = 8; CALL; break; }        \
         default: return hipErrorInvalidConfiguration;                              \
     }
 
@@ -396,17 +404,7 @@ static bool pick_gu(int nch, int& lpr, int& cpl) {
 bool mv_config_ok(int K, int fmt, bool gate_up) {
     int l, c;
     if (gate_up ? !pick_gu(nchunks(K, fmt), l, c) : !pick(nchunks(K, fmt), l, c)) return false;
-    int key = l * 16 + c;
-    switch (key) {
-        case 8 * 16 + 1: case 8 * 16 + 2: case 8 * 16 + 3: case 8 * 16 + 4: case 8 * 16 + 5:
-        case 8 * 16 + 6: case 8 * 16 + 7: case 8 * 16 + 8: case 16 * 16 + 5: case 16 * 16 + 6:
-        case 16 * 16 + 7: case 16 * 16 + 8: case 32 * 16 + 5: case 32 * 16 + 6: case 32 * 16 + 7:
-        case 32 * 16 + 8: case 64 * 16 + 1: case 64 * 16 + 2: case 64 * 16 + 3: case 64 * 16 + 4:
-        case 64 * 16 + 5: case 64 * 16 + 6: case 64 * 16 + 7: case 64 * 16 + 8:
-            return true;
-        default:
-            return false;
-    }
+    return c >= 1 && c <= 8 && (l == 8 || l == 16 || l == 32 || l == 64);
 }
 
 template <int FMT, bool TAP>
