@@ -32,7 +32,7 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-fast-math", "-ffp-contract=fast", "-Wall", "-Wno-unused-function",
+          "-fno-fast-math", "-ffp-contract=fast-honor-pragmas", "-Wall", "-Wno-unused-function",
           "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include")]
 
 

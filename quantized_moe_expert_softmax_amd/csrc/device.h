@@ -85,7 +85,12 @@ __device__ __forceinline__ void quant_q8_1_32(float v, int l, int8_t* q32, uint3
     int s = group_sum_i<32>(q);
     q32[l] = (int8_t)q;
     if (l == 0) {
-        *ds = f2h_bits(d) | (f2h_bits(d * (float)s) << 16);
+        // s is the fp32 product, rounded to binary16 afterwards; the empty asm
+        // keeps the backend from fusing the two roundings into one
+        // multiply-to-half (v_fma_mixlo_f16).
+        float p = d * (float)s;
+        asm volatile("" : "+v"(p));
+        *ds = f2h_bits(d) | (f2h_bits(p) << 16);
         *sq = s;
     }
 }

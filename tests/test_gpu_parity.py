@@ -156,3 +156,19 @@ def test_token_permutation_permutes_output():
     op = gh.run_plain(layer, np.ascontiguousarray(inp["x"][perm]))
     assert np.array_equal(op, o[perm])       # each token is computed on its own
     layer.close()
+
+
+def test_quantizer_double_rounding_blocks():
+    """Q8_1 blocks whose s needs the fp32 rounding before the binary16 one."""
+    import oracle
+    import quant_cases
+    blocks = quant_cases.double_rounding_blocks(8)
+    w = _variant(tokens=4)
+    inp = gh.make_inputs(w)
+    x = inp["x"].reshape(-1, 32).copy()
+    x[3:3 + 8 * 7:7] = blocks
+    x = x.reshape(4, w.hidden)
+    layer = gh.gpu_layer(w, inp, 4)
+    g = gh.run_taps(layer, w, x, 0)
+    assert np.array_equal(g["xq"], oracle.quantize_q8_1(x))
+    layer.close()

@@ -13,9 +13,12 @@ import math
 import os
 from fractions import Fraction
 
+import sys
+
 import numpy as np
 import pytest
 
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -559,3 +562,12 @@ def test_oracle_refuses_bad_groups(orc, synth):
     with pytest.raises(ValueError):
         orc.layer_forward(w, inp["x"], inp["router_w"], groups=np.arange(8, dtype=np.int32) // 2,
                           experts=inp["experts"])
+
+
+def test_q8_1_s_is_rounded_twice(orc):
+    """s is rounded to fp32 and then to binary16; blocks where one rounding differs."""
+    import quant_cases
+    blocks = quant_cases.double_rounding_blocks(6)
+    assert len(blocks) == 6
+    for v in blocks:
+        _check_exact(orc, v)
