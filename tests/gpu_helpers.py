@@ -97,7 +97,15 @@ def dense_isums(fmt, blocks, rows, nblk, acts):
 
 def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batch: int = 0,
                layer=None, inp=None, check_det: bool = True):
-    """Full parity check of one workload at T tokens.  tokens: oracle sample (None = all)."""
+    """Full parity check of one workload at T tokens.  tokens: oracle sample (None = all).
+
+    Unique results are compared exactly: routing ids, Q8_1(x), every integer
+    block sum and every requantisation of a GPU intermediate.  Floating-point
+    results have more than one correct value: a GPU intermediate computed in a
+    different fp32 order can sit on the other side of a Q8_1 rounding boundary
+    (a "flip").  Tokens without a flip must match the oracle's output within
+    2e-3 of its RMS; tokens with one must match the oracle evaluated on the
+    GPU's own quantised intermediates, and flips must be rare."""
     w = dataclasses.replace(w, tokens=T)
     if inp is None:
         inp = make_inputs(w, batch)
@@ -111,7 +119,8 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
     sample = list(range(T)) if tokens is None else list(tokens)
     ref, rt = oracle.layer_forward(w, x, inp["router_w"], inp["router_b"], inp["groups"],
                                    inp["experts"], inp["D"], inp["U"], tokens=sample,
-                                   taps=("logits", "ids", "weights", "xq", "z", "h", "y", "ylat"),
+                                   taps=("logits", "ids", "weights", "xq", "z", "zq", "h", "hq",
+                                         "y", "ylat", "ylq"),
                                    nthreads=8)
     k, F = w.top_k, w.n_ff
     kin, kout = w.k_in, w.k_out
@@ -130,8 +139,6 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
         assert np.array_equal(g["ids"][t], rt["ids"][i]), (t, g["ids"][t], rt["ids"][i])
         assert np.allclose(g["weights"][t], rt["weights"][i], rtol=4e-7, atol=0), t
     report["near_ties"] = len(ties)
-    ok_rows = [i for i in range(len(sample)) if i not in ties]
-    okt = [sample[i] for i in ok_rows]
 
     # Q8_1(x): bit-exact
     assert np.array_equal(g["xq"][sample], oracle.quantize_q8_1(x[sample]))
@@ -149,11 +156,10 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
     else:
         ain = g["xq"]
 
-    # hq is Q8_1 of the GPU's own h, bit for bit
+    # every requantisation is Q8_1 of the GPU's own intermediate, bit for bit
     assert np.array_equal(g["hq"], oracle.quantize_q8_1(g["h"]))
-    A_s = [t * k + j for t in okt for j in range(k)]
-    h_ref = rt["h"][ok_rows].reshape(-1, F)
-    assert rel_max(g["h"][A_s], h_ref) < 2e-3
+    if w.latent:
+        assert np.array_equal(g["ylq"], oracle.quantize_q8_1(g["ylat"]))
 
     # integer block sums of gate/up (on the GPU's expert input) and down (on the GPU's hq)
     tt = min(tap_tokens, T)
@@ -165,25 +171,55 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
             gu = blob[:2 * F * nbi * bb]
             y_gu, is_gu = oracle.matvec(w.expert_fmt, gu, 2 * F, nbi, ain[t].reshape(-1), with_isum=True)
             assert np.array_equal(g["isum_gu"][a], is_gu), (t, j)
+            # h from the oracle's g and u on the GPU's own input: fp32 order only
+            gg, uu = y_gu[:F].astype(np.float64), y_gu[F:].astype(np.float64)
+            h_own = (gg / (1.0 + np.exp(-gg)) * uu).astype(np.float32)
+            assert rel_max(g["h"][a], h_own) < 1e-4, (t, j, rel_max(g["h"][a], h_own))
             dn = blob[2 * F * nbi * bb:]
             y_dn, is_dn = oracle.matvec(w.expert_fmt, dn, kout, nbf, g["hq"][a].reshape(-1), with_isum=True)
             assert np.array_equal(g["isum_dn"][a], is_dn), (t, j)
             assert rel_max(g["y"][a], y_dn) < 1e-5
-
-    # each expert's down output against the oracle's (different hq flips allowed)
-    y_ref = rt["y"][ok_rows].reshape(-1, kout)
-    report["y_rel"] = rel_max(g["y"][A_s], y_ref)
-    assert report["y_rel"] < 2e-3
-
     if w.latent:
-        assert np.array_equal(g["ylq"], oracle.quantize_q8_1(g["ylat"]))
         H, L = w.hidden, w.latent
         _, iss = dense_isums(8, inp["U"], H, L // 32, g["ylq"][:tt])
         assert np.array_equal(g["isum_u"][:tt], iss)
 
-    # the layer output: max |diff| / RMS(ref) <= 2e-3
-    report["out_rel"] = rel_max(g["out"][okt], ref[ok_rows])
-    assert report["out_rel"] <= 2e-3, report
+    # the layer output, token by token
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    flips, clean_err = [], 0.0
+    for i, t in enumerate(sample):
+        if i in ties:
+            continue
+        a_t = [t * k + j for j in range(k)]
+        flipped = not np.array_equal(g["hq"][a_t], rt["hq"][i])
+        if w.latent:
+            flipped |= not np.array_equal(g["zq"][t], rt["zq"][i])
+            flipped |= not np.array_equal(g["ylq"][t], rt["ylq"][i])
+        err = float(np.max(np.abs(g["out"][t].astype(np.float64) - ref[i]))) / rms
+        if not flipped:
+            assert err <= 2e-3, (t, err)
+            clean_err = max(clean_err, err)
+            continue
+        flips.append(t)
+        # the oracle on the GPU's own quantised intermediates
+        y_own = []
+        for j, a in enumerate(a_t):
+            e = int(g["ids"][t, j])
+            dn = inp["experts"][e * eb:(e + 1) * eb][2 * F * nbi * bb:]
+            y_own.append(oracle.matvec(w.expert_fmt, dn, kout, nbf, g["hq"][a].reshape(-1)))
+        y_own = np.stack(y_own).astype(np.float64)
+        comb = (g["weights"][t].astype(np.float64)[:, None] * y_own).sum(0)
+        if w.latent:
+            assert rel_max(g["ylat"][t], comb) < 1e-5, t
+            out_own = oracle.matvec(8, inp["U"], w.hidden, w.latent // 32, g["ylq"][t].reshape(-1))
+        else:
+            out_own = comb
+        assert rel_max(g["out"][t], out_own) < 1e-5, (t, rel_max(g["out"][t], out_own))
+    report["out_rel_clean"] = clean_err
+    report["flip_tokens"] = flips
+    d = g["out"][sample].astype(np.float64) - ref
+    report["out_rms_rel"] = float(np.sqrt(np.mean(d ** 2))) / rms
+    assert len(flips) <= max(1, len(sample) // 2), report
 
     if check_det:
         o1 = run_plain(layer, x)
