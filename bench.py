@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized MoE expert-FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--tokens T]
+
+A step is one whole layer call (router logits, top-k softmax, Q8_1 activation
+quantisation, grouped gate/up + SwiGLU + requantisation, grouped down, combine,
+and for latent layers the D/U projections) over one batch of synthetic tokens,
+with every input already resident in HBM.  Steps rotate over several device
+copies of the expert weights and a pool of token batches so that a step cannot
+be served from the 256 MB MALL by an earlier one.
+
+Prints one JSON line: tokens/s (value), the dominant kernel's achieved HBM
+bandwidth against the 8 TB/s peak (roofline, from HIP events recorded on the
+library's stream around that kernel), and the CPU oracle's throughput on a
+bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+Q8_1_BLOCK = 36
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--workload", default="decode",
+                   help="tiny | decode | latent_q8 | latent_q4 | prefill")
+    p.add_argument("--tokens", type=int, default=None, help="tokens per step (default: the workload's)")
+    p.add_argument("--copies", type=int, default=None, help="device copies of the expert weights")
+    p.add_argument("--pool", type=int, default=64, help="distinct token batches")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile-steps", action="store_true",
+                   help="also print per-stage milliseconds to stderr")
+    return p.parse_args()
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, T, n_active):
+    """Bytes the method must move per step, and per launch of the gate/up kernel.
+
+    gate/up: the active experts' gate and up blocks, the quantised expert input
+    (T rows of Kin/32 Q8_1 blocks) and the quantised h it writes (T*k rows of F/32
+    Q8_1 blocks).  Layer: router weights, x, every active expert's blocks, D and
+    U, and out."""
+    H, E, k, F, L = w.hidden, w.n_experts, w.top_k, w.n_ff, w.latent
+    kin, kout, bb = w.k_in, w.k_out, w.block_bytes
+    gu_w = 2 * F * (kin // 32) * bb
+    dn_w = kout * (F // 32) * bb
+    act_in = T * (kin // 32) * Q8_1_BLOCK
+    hq = T * k * (F // 32) * Q8_1_BLOCK
+    gate_up = n_active * gu_w + act_in + hq
+    dense = 0
+    if L:
+        dense = L * (H // 32) * 34 + H * (L // 32) * 34
+    layer = E * H * 4 + T * H * 4 + n_active * (gu_w + dn_w) + dense + T * H * 4
+    return gate_up, layer, n_active * (gu_w + dn_w)
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the layer is a "
+                          "single-GPU kernel path; see DESIGN.md for how it would shard",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_expert_softmax_amd import moe, synth
+
+    w0 = synth.WORKLOADS[a.workload]
+    T = a.tokens or w0.tokens
+    w = synth.Workload(**{**w0.__dict__, "tokens": T})
+    dev = torch.device("cuda", 0)
+    # keep the token pool within 512 MB of device memory
+    pool = max(2, min(a.pool, (512 << 20) // (T * w.hidden * 4)))
+    a.pool = pool
+    t_gen = time.time()
+    inp = synth.gen_layer(w)
+    xs = [synth.gen_x(w, batch=b) for b in range(a.pool)]
+    t_gen = time.time() - t_gen
+
+    desc = moe.desc_of(w, max_tokens=T)
+    layer = moe.MoeLayer(desc, inp, device=0)
+    copies = a.copies or (1 if w.expert_bytes * w.n_experts * T > (1 << 33) else 4)
+    ex = [layer.experts] + [layer.experts.clone() for _ in range(copies - 1)]
+    Ds = [layer.D] + ([layer.D.clone() for _ in range(copies - 1)] if w.latent else [None] * (copies - 1))
+    Us = [layer.U] + ([layer.U.clone() for _ in range(copies - 1)] if w.latent else [None] * (copies - 1))
+    xd = torch.from_numpy(np.stack(xs)).to(dev)
+    out = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
+    ws = layer.workspace(T)
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    P = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    base = (layer.handle,)
+
+    def args(i):
+        c = i % copies
+        return (layer.handle, xd[i % a.pool].data_ptr(), T, layer.router_w.data_ptr(),
+                P(layer.router_b), P(layer.groups), ex[c].data_ptr(), P(Ds[c]), P(Us[c]),
+                w.top_k, out.data_ptr(), ws.data_ptr(), ws.numel(), st)
+
+    # distinct experts per batch (for the byte counts), from the routing tap
+    n_active = []
+    for b in range(a.pool):
+        ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
+        taps = moe.moe_taps()
+        taps.ids = ids.data_ptr()
+        moe.moe_layer_forward_taps(*args(b), taps)
+        torch.cuda.synchronize()
+        n_active.append(len(np.unique(ids.cpu().numpy())))
+    mean_active = float(np.mean(n_active))
+    del base
+
+    # timed region: whole-layer steps
+    for i in range(a.warmup):
+        moe.moe_layer_forward(*args(i))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        moe.moe_layer_forward(*args(i))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+
+    # the same steps again with HIP events on the library's stream at stage boundaries
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_EV_COUNT)]
+           for _ in range(a.steps)]
+    for i in range(a.warmup):
+        moe.moe_layer_forward(*args(i))
+    for i in range(a.steps):
+        moe.moe_layer_forward_events(*args(i), [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+
+    def stage(i0, i1):
+        return float(np.mean([evs[s][i0].elapsed_time(evs[s][i1]) for s in range(a.steps)]))
+
+    st_ms = {"route": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_ROUTED),
+             "dense_in": stage(moe.MOE_EV_ROUTED, moe.MOE_EV_EXPERT_IN),
+             "gate_up": stage(moe.MOE_EV_EXPERT_IN, moe.MOE_EV_GATE_UP),
+             "down": stage(moe.MOE_EV_GATE_UP, moe.MOE_EV_DOWN),
+             "dense_out": stage(moe.MOE_EV_DOWN, moe.MOE_EV_END),
+             "layer_events": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_END)}
+    if a.profile_steps:
+        print(json.dumps({"stage_ms": st_ms}), file=sys.stderr)
+
+    gu_bytes, layer_bytes, expert_bytes = algorithmic_bytes(w, T, mean_active)
+    gu_gbs = gu_bytes / (st_ms["gate_up"] * 1e-3) / 1e9
+    tokens_s = T * a.steps / (t1 - t0)
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_gate_up_{a.workload}_T{T}.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("src_hash") == src_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        ncores = 1
+        chunk = min(T, 8)
+        t_c0 = time.perf_counter()
+        done = 0
+        b = 0
+        while time.perf_counter() - t_c0 < a.cpu_seconds:
+            toks = list(range((b // a.pool) * chunk % T, (b // a.pool) * chunk % T + chunk))
+            oracle.layer_forward(w, xs[b % a.pool], inp["router_w"], inp["router_b"],
+                                 inp["groups"], inp["experts"], inp["D"], inp["U"],
+                                 tokens=[t % T for t in toks], nthreads=ncores)
+            done += chunk
+            b += 1
+        el = time.perf_counter() - t_c0
+        cpu = {"value": done / el, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
+               "sample": f"{done} tokens ({b} calls of {chunk} tokens from the batches of "
+                         f"this workload), {el:.1f} s on one host thread"}
+
+    res = {
+        "metric": "MoE-layer tokens/s (decode), expert-weight GB/s as % of HBM peak",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x int8 -> int32 blocks, fp32 scales/accumulation",
+        "data": "synthetic, seeded (counter-based splitmix64)",
+        "config": {"workload": a.workload, "hidden": w.hidden, "n_experts": w.n_experts,
+                   "top_k": w.top_k, "n_ff": w.n_ff, "latent": w.latent,
+                   "expert_fmt": "Q4_0" if w.expert_fmt == synth.Q4_0 else "Q8_0",
+                   "tokens_per_step": T, "weight_copies": copies, "token_batches": a.pool,
+                   "mean_active_experts": mean_active},
+        "roofline": {"bound": "hbm", "kernel": "gate_up (grouped gate/up + SwiGLU + Q8_1)",
+                     "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": gu_bytes,
+                     "avg_launch_ms": st_ms["gate_up"]},
+        "layer_gbs": layer_bytes / (ms_step * 1e-3) / 1e9,
+        "expert_gbs": expert_bytes / ((st_ms["gate_up"] + st_ms["down"]) * 1e-3) / 1e9,
+        "stage_ms": st_ms,
+        "cpu_baseline": cpu,
+        "input_generation_s": t_gen,
+    }
+    print(json.dumps(res))
+    layer.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -169,6 +169,29 @@ moe_status moe_layer_forward_taps(const moe_layer* layer, const float* x, int T,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const moe_taps* taps);
 
+/*
+ * Stage boundaries for timing (the pages' per-stage profiler idea: milliseconds
+ * per stage of a layer).  moe_layer_forward_events records events[i] (each a
+ * hipEvent_t created by the caller, passed as void*; NULL entries are skipped)
+ * on `stream` at these points of the kernel sequence:
+ *   MOE_EV_BEGIN    before the first kernel
+ *   MOE_EV_ROUTED   after quantising x, routing and bucketing
+ *   MOE_EV_EXPERT_IN after the latent D projection (== ROUTED when latent == 0)
+ *   MOE_EV_GATE_UP  after the grouped gate/up + SwiGLU + requantisation
+ *   MOE_EV_DOWN     after the grouped down projection and the combine
+ *   MOE_EV_END      after the last kernel (latent: after U)
+ * The kernels and out are those of moe_layer_forward.
+ */
+enum { MOE_EV_BEGIN = 0, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN,
+       MOE_EV_END, MOE_EV_COUNT };
+
+moe_status moe_layer_forward_events(const moe_layer* layer, const float* x, int T,
+                                    const float* router_w, const float* router_b,
+                                    const int32_t* group_of_expert, const void* expert_packs,
+                                    const void* D, const void* U, int k, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events);
+
 /* Text of the last error on this thread ("" when none). */
 const char* moe_last_error(void);
 

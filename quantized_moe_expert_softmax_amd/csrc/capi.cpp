@@ -277,7 +277,8 @@ static const int DOWN_TOK_MAX_T = 8;
 static moe_status forward_impl(const moe_layer* L, const float* x, int T, const float* router_w,
                                const float* router_b, const int32_t* groups, const void* experts,
                                const void* Dp, const void* Up, int k, float* out, void* workspace,
-                               size_t ws_bytes, void* stream, const moe_taps* taps) {
+                               size_t ws_bytes, void* stream, const moe_taps* taps,
+                               void* const* events) {
     if (!L) return fail(MOE_EINVAL, "layer is NULL");
     const Dims& m = L->dims;
     if (k != m.k) return fail(MOE_EINVAL, "k %d differs from the layer's top_k %d", k, m.k);
@@ -332,31 +333,43 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         e = (call);                                     \
         if (e != hipSuccess) return hip_fail(e, what);  \
     } while (0)
+#define EV(i)                                                                          \
+    do {                                                                               \
+        if (events && events[i]) CK(hipEventRecord((hipEvent_t)events[i], st), "event"); \
+    } while (0)
 
+    EV(MOE_EV_BEGIN);
     CK(launch_quant_rows(x, T, m.H, xq, st), "quantise x");
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, st),
        "router");
     CK(launch_bucket(m, w, ws, T, 32, st), "bucketing");
+    EV(MOE_EV_ROUTED);
     ActPtr ain = xq;
     if (m.L) {
         CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
         CK(launch_quant_rows(z, T, m.L, zq, st), "quantise z");
         ain = zq;
     }
+    EV(MOE_EV_EXPERT_IN);
     CK(launch_gate_up_mv(m, T, ex, ain, b, hq, tp, st), "gate/up");
+    EV(MOE_EV_GATE_UP);
     if (down_tok) {
         CK(launch_down_tok_mv(m, T, ex, hq, b, out, tp, st), "down+combine");
+        EV(MOE_EV_DOWN);
     } else {
         CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
         if (!m.L) {
             CK(launch_combine(y, b.wts, T, m.k, m.H, out, st), "combine");
+            EV(MOE_EV_DOWN);
         } else {
             CK(launch_combine(y, b.wts, T, m.k, m.L, ylat, st), "combine");
+            EV(MOE_EV_DOWN);
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "quantise y_lat");
             CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st),
                "U");
         }
     }
+    EV(MOE_EV_END);
     if (taps) {
         if (taps->ids) CK(hipMemcpyAsync(taps->ids, b.ids, sizeof(int32_t) * A, hipMemcpyDeviceToDevice, st), "tap ids");
         if (taps->weights) CK(hipMemcpyAsync(taps->weights, b.wts, sizeof(float) * A, hipMemcpyDeviceToDevice, st), "tap weights");
@@ -371,6 +384,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (!down_tok && taps->y)
             CK(hipMemcpyAsync(taps->y, y, sizeof(float) * (size_t)A * m.kout, hipMemcpyDeviceToDevice, st), "tap y");
     }
+#undef EV
 #undef CK
     return MOE_OK;
 }
@@ -381,7 +395,17 @@ extern "C" moe_status moe_layer_forward(const moe_layer* L, const float* x, int 
                                         const void* U, int k, float* out, void* workspace,
                                         size_t workspace_bytes, void* stream) {
     return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
-                        workspace_bytes, stream, nullptr);
+                        workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" moe_status moe_layer_forward_events(const moe_layer* L, const float* x, int T,
+                                               const float* router_w, const float* router_b,
+                                               const int32_t* groups, const void* experts,
+                                               const void* D, const void* U, int k, float* out,
+                                               void* workspace, size_t workspace_bytes,
+                                               void* stream, void* const* events) {
+    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
+                        workspace_bytes, stream, nullptr, events);
 }
 
 extern "C" moe_status moe_layer_forward_taps(const moe_layer* L, const float* x, int T,
@@ -392,5 +416,5 @@ extern "C" moe_status moe_layer_forward_taps(const moe_layer* L, const float* x,
                                              const moe_taps* taps) {
     if (!taps) return fail(MOE_EINVAL, "taps is NULL");
     return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
-                        workspace_bytes, stream, taps);
+                        workspace_bytes, stream, taps, nullptr);
 }

@@ -23,7 +23,10 @@ MOE_PACK_EXPERTS, MOE_PACK_D, MOE_PACK_U = 0, 1, 2
 # every function include/moe.h declares
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_bytes",
            "moe_pack_host", "moe_unpack_host", "moe_pack", "moe_workspace_bytes",
-           "moe_layer_forward", "moe_layer_forward_taps", "moe_last_error", "moe_version"]
+           "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
+           "moe_last_error", "moe_version"]
+MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END = range(6)
+MOE_EV_COUNT = 6
 
 
 class MoeError(RuntimeError):
@@ -70,9 +73,10 @@ def lib():
         fwd = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         L.moe_layer_forward.argtypes = fwd
         L.moe_layer_forward_taps.argtypes = fwd + [P(moe_taps)]
+        L.moe_layer_forward_events.argtypes = fwd + [P(vp)]
         for f in ("moe_desc_check", "moe_layer_create", "moe_pack_bytes", "moe_pack_host",
                   "moe_unpack_host", "moe_pack", "moe_workspace_bytes", "moe_layer_forward",
-                  "moe_layer_forward_taps"):
+                  "moe_layer_forward_taps", "moe_layer_forward_events"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -157,6 +161,14 @@ def moe_layer_forward_taps(handle, x, T, router_w, router_b, groups, experts, D,
     _check(lib().moe_layer_forward_taps(handle, x, T, router_w, router_b, groups, experts, D, U, k,
                                         out, workspace, workspace_bytes, stream,
                                         ctypes.byref(taps)))
+
+
+def moe_layer_forward_events(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,
+                             workspace, workspace_bytes, stream, events) -> None:
+    """events: sequence of MOE_EV_COUNT hipEvent_t handles (ints) or 0."""
+    arr = (ctypes.c_void_p * MOE_EV_COUNT)(*[e or None for e in events])
+    _check(lib().moe_layer_forward_events(handle, x, T, router_w, router_b, groups, experts, D, U,
+                                          k, out, workspace, workspace_bytes, stream, arr))
 
 
 # ---------------------------------------------------------------------------

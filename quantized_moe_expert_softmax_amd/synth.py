@@ -218,12 +218,20 @@ def gen_expert(w: Workload, e: int, out: Optional[np.ndarray] = None) -> np.ndar
     return out
 
 
-def gen_experts(w: Workload, out: Optional[np.ndarray] = None) -> np.ndarray:
+def gen_experts(w: Workload, out: Optional[np.ndarray] = None, threads: int = 8) -> np.ndarray:
+    """All experts' canonical blobs, drawn on `threads` threads (each expert's
+    stream is independent, so the result does not depend on the thread count)."""
     if out is None:
         out = np.empty(w.n_experts * w.expert_bytes, dtype=np.uint8)
     eb = w.expert_bytes
-    for e in range(w.n_experts):
-        gen_expert(w, e, out=out[e * eb:(e + 1) * eb])
+    if threads <= 1:
+        for e in range(w.n_experts):
+            gen_expert(w, e, out=out[e * eb:(e + 1) * eb])
+        return out
+    import concurrent.futures as cf
+    _L()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda e: gen_expert(w, e, out=out[e * eb:(e + 1) * eb]), range(w.n_experts)))
     return out
 
 
