@@ -48,6 +48,42 @@ def parse():
     return p.parse_args()
 
 
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime this process already has mapped
+    (the one torch and libmoe share)."""
+
+    def __init__(self):
+        import ctypes
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = self.ct.c_void_p()
+        if self.lib.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e: int) -> None:
+        self.lib.hipEventDestroy(e)
+
+
 def src_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
@@ -148,16 +184,16 @@ def main():
     ms_step = (t1 - t0) * 1e3 / a.steps
 
     # the same steps again with HIP events on the library's stream at stage boundaries
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_EV_COUNT)]
-           for _ in range(a.steps)]
+    he = HipEvents()
+    evs = [[he.create() for _ in range(moe.MOE_EV_COUNT)] for _ in range(a.steps)]
     for i in range(a.warmup):
         moe.moe_layer_forward(*args(i))
     for i in range(a.steps):
-        moe.moe_layer_forward_events(*args(i), [e.cuda_event for e in evs[i]])
+        moe.moe_layer_forward_events(*args(i), evs[i])
     torch.cuda.synchronize()
 
     def stage(i0, i1):
-        return float(np.mean([evs[s][i0].elapsed_time(evs[s][i1]) for s in range(a.steps)]))
+        return float(np.mean([he.elapsed_ms(evs[s][i0], evs[s][i1]) for s in range(a.steps)]))
 
     st_ms = {"route": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_ROUTED),
              "dense_in": stage(moe.MOE_EV_ROUTED, moe.MOE_EV_EXPERT_IN),
@@ -165,6 +201,9 @@ def main():
              "down": stage(moe.MOE_EV_GATE_UP, moe.MOE_EV_DOWN),
              "dense_out": stage(moe.MOE_EV_DOWN, moe.MOE_EV_END),
              "layer_events": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_END)}
+    for row in evs:
+        for e in row:
+            he.destroy(e)
     if a.profile_steps:
         print(json.dumps({"stage_ms": st_ms}), file=sys.stderr)
 

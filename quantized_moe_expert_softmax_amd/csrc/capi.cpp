@@ -324,8 +324,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         tp.tap_tokens = std::min(std::max(taps->tap_tokens, 0), T);
         if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
     }
-    const bool down_tok = !m.L && T <= DOWN_TOK_MAX_T;
+    const bool down_tok = T <= DOWN_TOK_MAX_T;
     if (taps && down_tok) tp.y = taps->y;
+    const ActPtr none{nullptr, nullptr, nullptr};
 
     hipError_t e;
 #define CK(call, what)                                  \
@@ -339,35 +340,34 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     } while (0)
 
     EV(MOE_EV_BEGIN);
-    CK(launch_quant_rows(x, T, m.H, xq, st), "quantise x");
-    CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, st),
-       "router");
-    CK(launch_bucket(m, w, ws, T, 32, st), "bucketing");
+    bool bucketed = false;
+    CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
+                     &bucketed, st), "router");
+    if (!bucketed) CK(launch_bucket(m, w, ws, T, 32, st), "bucketing");
     EV(MOE_EV_ROUTED);
-    ActPtr ain = xq;
     if (m.L) {
-        CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
-        CK(launch_quant_rows(z, T, m.L, zq, st), "quantise z");
-        ain = zq;
+        // z = D . Q8_1(x), fp32; the gate/up kernel quantises it on the way in
+        CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
+                           tp.tap_tokens, st), "D");
     }
     EV(MOE_EV_EXPERT_IN);
-    CK(launch_gate_up_mv(m, T, ex, ain, b, hq, tp, st), "gate/up");
+    if (m.L)
+        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st), "gate/up");
+    else
+        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st), "gate/up");
     EV(MOE_EV_GATE_UP);
+    float* comb = m.L ? ylat : out;     // the combined expert outputs
     if (down_tok) {
-        CK(launch_down_tok_mv(m, T, ex, hq, b, out, tp, st), "down+combine");
-        EV(MOE_EV_DOWN);
+        CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st), "down+combine");
     } else {
         CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
-        if (!m.L) {
-            CK(launch_combine(y, b.wts, T, m.k, m.H, out, st), "combine");
-            EV(MOE_EV_DOWN);
-        } else {
-            CK(launch_combine(y, b.wts, T, m.k, m.L, ylat, st), "combine");
-            EV(MOE_EV_DOWN);
-            CK(launch_quant_rows(ylat, T, m.L, ylq, st), "quantise y_lat");
-            CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st),
-               "U");
-        }
+        CK(launch_combine(y, b.wts, T, m.k, m.kout, comb, st), "combine");
+    }
+    EV(MOE_EV_DOWN);
+    if (m.L) {
+        // out = U . Q8_1(y_lat); the U kernel quantises y_lat on the way in
+        CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, none, ylat, taps ? ylq : none, out,
+                           tp.isum_u, tp.tap_tokens, st), "U");
     }
     EV(MOE_EV_END);
     if (taps) {

@@ -63,9 +63,67 @@ __device__ __forceinline__ int group_sum_i(int v) {
     return v;
 }
 
+// Sum over aligned groups of W lanes (W = 1..64), the result in every lane of
+// the group: DPP quad permutes and row mirrors inside a 16-lane row, then the
+// gfx950 row swaps (v_permlane16_swap / v_permlane32_swap) across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum_fast(float v) {
+    if constexpr (W >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+    if constexpr (W >= 16) v += dpp_mov<0x140>(v); // row_mirror
+    if constexpr (W >= 32) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (W >= 64) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
+// fp64 value of another lane for one reduction step (STEP 0..5: xor 1, xor 2,
+// mirror within 8, mirror within 16, the other row of a pair, the other half),
+// through DPP and the gfx950 row swaps: no LDS round trip.
+template <int STEP>
+__device__ __forceinline__ double xlane_d(double v) {
+    const long long b = __double_as_longlong(v);
+    int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
+    if constexpr (STEP < 4) {
+        constexpr int CTRL = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+        lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xf, 0xf, false);
+        hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xf, 0xf, false);
+    } else if constexpr (STEP == 4) {
+        auto a = __builtin_amdgcn_permlane16_swap((unsigned)lo, (unsigned)lo, false, false);
+        auto c = __builtin_amdgcn_permlane16_swap((unsigned)hi, (unsigned)hi, false, false);
+        const bool odd_row = (threadIdx.x & 16) != 0;
+        lo = (int)(odd_row ? a[0] : a[1]);
+        hi = (int)(odd_row ? c[0] : c[1]);
+    } else {
+        auto a = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)lo, false, false);
+        auto c = __builtin_amdgcn_permlane32_swap((unsigned)hi, (unsigned)hi, false, false);
+        const bool upper = (threadIdx.x & 32) != 0;
+        lo = (int)(upper ? a[0] : a[1]);
+        hi = (int)(upper ? c[0] : c[1]);
+    }
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over the wave in a fixed order (every lane gets the same value: each
+// step adds partner values that are equal across the partner pair).
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += xlane_d<0>(v);
+    v += xlane_d<1>(v);
+    v += xlane_d<2>(v);
+    v += xlane_d<3>(v);
+    v += xlane_d<4>(v);
+    v += xlane_d<5>(v);
     return v;
 }
 

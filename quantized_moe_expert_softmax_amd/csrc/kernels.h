@@ -29,9 +29,11 @@ struct Taps {                 // device pointers, NULL = off
 };
 
 hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStream_t st);
+// Q8_1(x) and the router logits; then top-k and softmax per token, and for
+// decode sizes the bucketing too (*bucketed = true).
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         hipStream_t st);
+                         ActPtr xq, bool* bucketed, hipStream_t st);
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, int tile_m,
                          hipStream_t st);
 hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R, float* out,
@@ -39,17 +41,21 @@ hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R,
 hipError_t launch_tap_q8_1(ActPtr a, long rows, int K, uint8_t* out, hipStream_t st);
 
 // True when the matrix-vector kernels have a configuration for rows of K
-// elements of format fmt (gate_up: the 64-row gate/up slab kernel).
+// elements of format fmt.
 bool mv_config_ok(int K, int fmt, bool gate_up);
 
 // Decode-path expert and dense kernels (matrix-vector, one pass over the weights).
+// The expert input is either quantised rows (ain) or fp32 rows quantised inside
+// the kernel (ain_f32, with `keep` receiving the Q8_1 blocks when non-null).
 hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
-                             const Buckets& b, ActPtr hq, const Taps& taps, hipStream_t st);
+                             const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
+                             const Taps& taps, hipStream_t st);
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st);
 hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st);
-hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
-                           int32_t* isum_tap, int tap_tokens, hipStream_t st);
+hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
+                           const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
+                           int tap_tokens, hipStream_t st);
 
 }  // namespace moe

@@ -3,17 +3,18 @@
 //
 // Prior art (Strata PR 24, SYCL port commits): the grouped expert kernels split
 // each format into a once-per-weight part and a per-token part because a
-// verify window routes one expert for up to 6 tokens, and a handful of lanes per
-// row beat a full warp on short rows; 16-byte loads streamed faster than
+// verify window routes one expert for up to 6 tokens; a handful of lanes per
+// row beat a whole warp on short rows; 16-byte loads streamed faster than
 // 4-byte ones.  Here, for gfx950:
-//   * a lane group of LPR lanes owns one weight row; lane sl of the group loads
-//     16-byte chunks c = j*LPR + sl (j < CPL), so a wave's loads are contiguous;
-//   * the weights are loaded once into registers and reused for every token of
-//     the expert's bucket; the Q8_1 activation chunks are read per token;
+//   * the workgroup stages the Q8_1 activations of its tokens in LDS once
+//     (quantising fp32 rows on the way in when the producer left them fp32);
+//   * a group of LPR lanes owns a weight row; lane sl loads the 16-byte chunks
+//     c = j*LPR + sl (j < CPL), so each wave's loads are contiguous; one pass of
+//     rows sits in registers while the next pass is already being loaded;
 //   * each chunk is 16 int8 codes (half a Q8_0 block) or one Q4_0 block, dotted
-//     with packed int8 dot products; the row is reduced across the group.
-// The per-block integer sums are exact; the scale products and the row sums are
-// fp32.
+//     with v_dot4 against the LDS activations, scaled by d_w * d_a per block;
+//   * rows are reduced with DPP row ops and the gfx950 row swaps.
+// Integer block sums are exact; scale products and row sums are fp32.
 #include <algorithm>
 
 #include "kernels.h"
@@ -26,143 +27,280 @@ struct Fmt {
     static constexpr int CPB = FMT == MOE_FMT_Q4_0 ? 1 : 2;   // 16-byte chunks per block
 };
 
-// Integer sum of chunk c (of a weight row held in wq) against activation row
-// `arow` (K int8 codes, sums asq).  Q8_0: half a block; Q4_0: a whole block.
-template <int FMT>
-__device__ __forceinline__ int chunk_isum(const v4i& wq, const int8_t* arow, const int32_t* asq,
-                                          int c) {
-    if constexpr (FMT == MOE_FMT_Q4_0) {
-        v4i lo = ld16(arow + c * 32);
-        v4i hi = ld16(arow + c * 32 + 16);
-        return dot_q4(wq, lo, hi) - 8 * asq[c];
-    } else {
-        v4i a = ld16(arow + c * 16);
-        return dot16(wq, a);
+// Q8_1 of one value per lane of a 32-lane group (see quant_q8_1_32), returned
+// to every lane: code, (d, s) binary16 pair, code sum.
+struct Q81 {
+    int q;
+    uint32_t ds;
+    int sum;
+};
+
+__device__ __forceinline__ Q81 q8_1_lane(float v) {
+    float amax = fabsf(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    float d = amax / 127.0f;
+    int q = 0;
+    if (d != 0.0f) q = (int)__builtin_roundf(v / d);
+    int s = group_sum_i<32>(q);
+    float p = d * (float)s;            // fp32 product, then binary16 (no fused rounding)
+    asm volatile("" : "+v"(p));
+    return Q81{q, f2h_bits(d) | (f2h_bits(p) << 16), s};
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging of the activation rows a workgroup works on.
+//   s_q  int8  [n][K]
+//   s_d  float [n][K/32]   the binary16 d of each block, as float
+//   s_sq int   [n][K/32]   code sums (used by Q4_0 weights)
+// src_row[i] is the row of the source buffer that becomes LDS row i.
+__device__ __forceinline__ void stage_q(const ActPtr& a, int K, const int32_t* src_row, int n,
+                                        int8_t* s_q, float* s_d, int32_t* s_sq) {
+    const int nb = K / QK, c16 = K / 16;
+    for (int idx = threadIdx.x; idx < n * c16; idx += blockDim.x) {
+        const int i = idx / c16, c = idx - i * c16;
+        *reinterpret_cast<v4i*>(s_q + i * K + c * 16) = ld16(a.q + (size_t)src_row[i] * K + c * 16);
+    }
+    for (int idx = threadIdx.x; idx < n * nb; idx += blockDim.x) {
+        const int i = idx / nb, b = idx - i * nb;
+        const size_t g = (size_t)src_row[i] * nb + b;
+        s_d[idx] = h2f(a.ds[g]);
+        s_sq[idx] = a.sq[g];
+    }
+}
+
+// fp32 rows quantised to Q8_1 straight into LDS; one 32-lane group per block.
+// When `keep` has a q pointer the blocks are also written to it (row src_row[i]).
+__device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t* src_row, int n,
+                                          int8_t* s_q, float* s_d, int32_t* s_sq, ActPtr keep) {
+    const int nb = K / QK;
+    const int ng = blockDim.x / 32, g = threadIdx.x / 32, l = threadIdx.x & 31;
+    for (int blk = g; blk < n * nb; blk += ng) {
+        const int i = blk / nb, b = blk - i * nb;
+        const size_t row = src_row[i];
+        const Q81 r = q8_1_lane(src[row * K + b * QK + l]);
+        s_q[i * K + b * QK + l] = (int8_t)r.q;
+        if (l == 0) {
+            s_d[blk] = h2f(r.ds);
+            s_sq[blk] = r.sum;
+        }
+        if (keep.q) {
+            keep.q[row * K + b * QK + l] = (int8_t)r.q;
+            if (l == 0) {
+                keep.ds[row * nb + b] = r.ds;
+                keep.sq[row * nb + b] = r.sum;
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up + SwiGLU + Q8_1 requantisation.  Workgroup = (slot, fb): the 64-row
-// slab of gate rows fb*32.. and up rows fb*32.. of the slot's expert, for every
-// token routed to it.  Output: hq rows a = t*k + j, 32 codes of block fb.
+// The row-tile engine: for `rows` rows of a packed block matrix (codes at
+// codes + r*rowb, binary16 scales at scl + r*nb) and the n LDS activation rows,
+// emit(i, r, W[r] . act[i]) from lane 0 of each row's lane group.
+// Loads are unconditional (a chunk index past the row is clamped to the last
+// chunk and its contribution masked later), and the scale stays as raw binary16
+// bits until it is used, so no load waits on another.
+template <int FMT, int LPR, int CPL>
+__device__ __forceinline__ void load_row(const uint8_t* row, const uint16_t* rscl, int sl, int NCH,
+                                         v4i (&wq)[CPL], uint32_t (&wsc)[CPL]) {
+    using F = Fmt<FMT>;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = min(j * LPR + sl, NCH - 1);
+        wq[j] = ld16(row + (size_t)c * 16);
+        wsc[j] = rscl[c / F::CPB];
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const int8_t* arow, const int32_t* asq,
+                                              int c) {
+    if constexpr (FMT == MOE_FMT_Q4_0) {
+        const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
+        const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
+        return dot_q4(wq, lo, hi) - 8 * asq[c];
+    } else {
+        const v4i a = *reinterpret_cast<const v4i*>(arow + c * 16);
+        return dot16(wq, a);
+    }
+}
+
+// One pass: the rows of this pass (weights in wq/wsc) against the n staged rows.
+template <int FMT, int LPR, int CPL, bool TAP, class Emit, class EmitIsum>
+__device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const uint32_t (&wsc)[CPL], int r,
+                                         int sl, int NCH, int nb, int n, int K,
+                                         const int8_t* s_q, const float* s_d,
+                                         const int32_t* s_sq, Emit& emit, EmitIsum& emit_isum,
+                                         bool tap) {
+    using F = Fmt<FMT>;
+#pragma unroll 1
+    for (int i = 0; i < n; ++i) {
+        const int8_t* arow = s_q + i * K;
+        const float* ad = s_d + i * nb;
+        const int32_t* asq = s_sq + i * nb;
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const bool valid = j * LPR + sl < NCH;
+            const int c = min(j * LPR + sl, NCH - 1);
+            const int blk = c / F::CPB;
+            const int is = chunk_isum_lds<FMT>(wq[j], arow, asq, c);
+            acc = fmaf((float)is, valid ? h2f(wsc[j]) * ad[blk] : 0.0f, acc);
+            if constexpr (TAP) {
+                if (tap) {
+                    int full = is;
+                    if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
+                    if (valid && (F::CPB == 1 || (sl & 1) == 0)) emit_isum(i, r, blk, full);
+                }
+            }
+        }
+        const float v = group_sum_fast<LPR>(acc);
+        if (sl == 0) emit(i, r, v);
+    }
+}
+
+// All passes of a row tile.  Two register buffers alternate (A: even passes,
+// B: odd passes) so the next pass is always in flight while one is dotted and
+// no register copy forces a wait.  A load past the last pass re-reads the last
+// pass's rows (it is never used) so that every load is unconditional.  On
+// entry A must hold pass 0 when `a_loaded`.
+template <int FMT, int LPR, int CPL, int NW, bool TAP, int PASSES = 0, class Emit, class EmitIsum>
+__device__ __forceinline__ void row_tile(const uint8_t* codes, const uint16_t* scl, size_t rowb,
+                                         int nb, int rows, int n, int K, const int8_t* s_q,
+                                         const float* s_d, const int32_t* s_sq, Emit emit,
+                                         EmitIsum emit_isum, bool tap, v4i (&wA)[CPL],
+                                         uint32_t (&sA)[CPL], bool a_loaded) {
+    using F = Fmt<FMT>;
+    constexpr int RPW = 64 / LPR;
+    const int NCH = nb * F::CPB;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sl = lane % LPR, rg = lane / LPR;
+    const int passes = PASSES ? PASSES : rows / (NW * RPW);
+    if constexpr (PASSES == 1) {
+        // a single pass: one buffer
+        const int r = wave * RPW + rg;
+        if (!a_loaded) load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+        pass_dot<FMT, LPR, CPL, TAP>(wA, sA, r, sl, NCH, nb, n, K, s_q, s_d, s_sq, emit, emit_isum,
+                                     tap);
+        return;
+    }
+    auto row_of = [&](int p) { return (min(p, passes - 1) * NW + wave) * RPW + rg; };
+    v4i wB[CPL];
+    uint32_t sB[CPL];
+    if (!a_loaded) {
+        const int r = row_of(0);
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+    }
+    for (int p = 0; p < passes; p += 2) {
+        {
+            const int r = row_of(p + 1);
+            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wB, sB);
+        }
+        pass_dot<FMT, LPR, CPL, TAP>(wA, sA, row_of(p), sl, NCH, nb, n, K, s_q, s_d, s_sq, emit,
+                                     emit_isum, tap);
+        {
+            const int r = row_of(p + 2);
+            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+        }
+        if (p + 1 < passes)
+            pass_dot<FMT, LPR, CPL, TAP>(wB, sB, row_of(p + 1), sl, NCH, nb, n, K, s_q, s_d, s_sq,
+                                         emit, emit_isum, tap);
+    }
+}
+
+// LDS bytes of n staged rows of K elements (codes, d, sums), 16-byte aligned.
+__host__ __device__ constexpr size_t stage_bytes(int n, int K) {
+    return (size_t)n * K + 2 * (size_t)n * (K / QK) * 4;
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU + Q8_1.  Workgroup = (slot, fb): the 64-row slab of gate
+// rows fb*32.. and up rows fb*32.. of the slot's expert, for every token routed
+// to it.  Output: hq rows a = t*k + j, block fb.
 struct GUArgs {
     const uint8_t* experts;
     size_t eb, gu_scales_off;
-    int K, F, k, T;
-    ActPtr ain;
+    int K, F, k, T, tch;
+    ActPtr ain;           // quantised expert input rows [T][K], or
+    const float* ain_f32; // fp32 rows [T][K] quantised in the prologue (latent z)
+    ActPtr keep;          // where the prologue also stores Q8_1(z) (taps), q == nullptr: off
     Buckets b;
     ActPtr hq;
     Taps taps;
 };
 
-constexpr int GU_TCH = 32;  // tokens buffered in LDS before the SwiGLU epilogue
-
-template <int FMT, int LPR, int CPL>
-__device__ __forceinline__ void load_row_chunks(const uint8_t* row, const uint16_t* rscl, int sl,
-                                                int NCH, v4i (&wq)[CPL], float (&wsc)[CPL]) {
-    using F = Fmt<FMT>;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = j * LPR + sl;
-        if (c < NCH) {
-            wq[j] = ld16(row + (size_t)c * 16);
-            wsc[j] = h2f(rscl[c / F::CPB]);
-        } else {
-            wq[j] = v4i{0, 0, 0, 0};
-            wsc[j] = 0.0f;
-        }
-    }
-}
-
+// (the second launch bound is the minimum number of waves per SIMD: 3 lets
+// three 4-wave workgroups share a CU)
 template <int FMT, int LPR, int CPL, int NW, bool TAP>
-__global__ __launch_bounds__(NW * 64) void k_gate_up_mv(GUArgs A) {
-    using F = Fmt<FMT>;
-    constexpr int RPW = 64 / LPR;
-    constexpr int PASSES = 64 / (NW * RPW);
-    static_assert(PASSES >= 1 && PASSES * NW * RPW == 64, "64 rows per workgroup");
-    __shared__ float gu_s[GU_TCH][64];
-
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs A) {
+    constexpr int PASSES = 64 / (NW * (64 / LPR));
+    extern __shared__ __align__(16) char smem[];
     const int FB = A.F / QK;
     const int slot = blockIdx.x / FB, fb = blockIdx.x - slot * FB;
     if (slot >= (int)A.b.ctrl[CW_N_ACTIVE]) return;
     const int e = A.b.active[slot];
     const int cnt = A.b.counts[e];
     const int32_t* lst = A.b.lists + (size_t)e * A.T;
-    const int nb = A.K / QK;
-    const int NCH = nb * F::CPB;
-    const size_t rowb = (size_t)nb * F::QB;
+    const int K = A.K, nb = K / QK, TCH = A.tch;
+    const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
     const uint8_t* ebase = A.experts + (size_t)e * A.eb;
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
     const uint16_t* scl = reinterpret_cast<const uint16_t*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * nb;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sl = lane % LPR, rg = lane / LPR;
 
-    for (int i0 = 0; i0 < cnt; i0 += GU_TCH) {
-        const int n = min(GU_TCH, cnt - i0);
-        // one pass = one row per lane group; the next pass's row is loaded
-        // while this one is dotted with the tokens
-        v4i wq[CPL];
-        float wsc[CPL];
-        {
-            const int r = wave * RPW + rg;
-            load_row_chunks<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wq, wsc);
+    int8_t* s_q = reinterpret_cast<int8_t*>(smem);
+    float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
+    int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
+    float* s_gu = reinterpret_cast<float*>(smem + stage_bytes(TCH, K));
+    int32_t* s_a = reinterpret_cast<int32_t*>(s_gu + TCH * 64);
+    int32_t* s_t = s_a + TCH;
+
+    // the first pass of weights is requested before the activations are staged
+    v4i wA[CPL];
+    uint32_t sA[CPL];
+    {
+        constexpr int RPW = 64 / LPR;
+        const int lane = threadIdx.x & 63;
+        const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, lane % LPR,
+                                nb * Fmt<FMT>::CPB, wA, sA);
+    }
+    for (int i0 = 0; i0 < cnt; i0 += TCH) {
+        const int n = min(TCH, cnt - i0);
+        if (threadIdx.x < n) {
+            const int a = lst[i0 + threadIdx.x];
+            s_a[threadIdx.x] = a;
+            s_t[threadIdx.x] = a / A.k;
         }
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int r = (p * NW + wave) * RPW + rg;
-            v4i wn[CPL];
-            float wsn[CPL];
-            if (p + 1 < PASSES) {
-                const int rn = ((p + 1) * NW + wave) * RPW + rg;
-                load_row_chunks<FMT, LPR, CPL>(codes + rn * rowb, scl + (size_t)rn * nb, sl, NCH, wn, wsn);
+        __syncthreads();
+        if (A.ain_f32)
+            stage_f32(A.ain_f32, K, s_t, n, s_q, s_d, s_sq, fb == 0 ? A.keep : ActPtr{});
+        else
+            stage_q(A.ain, K, s_t, n, s_q, s_d, s_sq);
+        __syncthreads();
+        const bool tap = TAP && A.taps.isum_gu;
+        auto emit = [&](int i, int r, float v) { s_gu[i * 64 + r] = v; };
+        auto emit_isum = [&](int i, int r, int blk, int v) {
+            if (s_t[i] < A.taps.tap_tokens) {
+                const int row = r < 32 ? fb * 32 + r : A.F + fb * 32 + (r - 32);
+                A.taps.isum_gu[((size_t)s_a[i] * 2 * A.F + row) * nb + blk] = v;
             }
-#pragma unroll 1
-            for (int i = 0; i < n; ++i) {
-                const int a = lst[i0 + i];
-                const int t = a / A.k;
-                const int8_t* arow = A.ain.q + (size_t)t * A.K;
-                const uint32_t* ads = A.ain.ds + (size_t)t * nb;
-                const int32_t* asq = A.ain.sq + (size_t)t * nb;
-                const bool tap = TAP && A.taps.isum_gu && t < A.taps.tap_tokens;
-                float acc = 0.0f;
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    const int c = j * LPR + sl;
-                    const bool valid = c < NCH;
-                    const int blk = c / F::CPB;
-                    const int is = valid ? chunk_isum<FMT>(wq[j], arow, asq, c) : 0;
-                    acc += (float)is * (wsc[j] * (valid ? h2f(ads[blk]) : 0.0f));
-                    if constexpr (TAP) {
-                        if (tap) {
-                            int full = is;
-                            if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
-                            if (valid && (F::CPB == 1 || (sl & 1) == 0)) {
-                                const int row = r < 32 ? fb * 32 + r : A.F + fb * 32 + (r - 32);
-                                A.taps.isum_gu[((size_t)a * 2 * A.F + row) * nb + blk] = full;
-                            }
-                        }
-                    }
-                }
-                const float v = group_sum<LPR>(acc);
-                if (sl == 0) gu_s[i][r] = v;
-            }
-            if (p + 1 < PASSES) {
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    wq[j] = wn[j];
-                    wsc[j] = wsn[j];
-                }
-            }
-        }
+        };
+        row_tile<FMT, LPR, CPL, NW, TAP, PASSES>(codes, scl, rowb, nb, 64, n, K, s_q, s_d, s_sq,
+                                                 emit, emit_isum, tap, wA, sA, i0 == 0);
         __syncthreads();
         // SwiGLU and Q8_1: one 32-lane group per token, lane = output f
         for (int ii = threadIdx.x / 32; ii < n; ii += NW * 2) {
             const int f = threadIdx.x & 31;
-            const float g = gu_s[ii][f], u = gu_s[ii][32 + f];
+            const float g = s_gu[ii * 64 + f], u = s_gu[ii * 64 + 32 + f];
             const float h = g / (1.0f + expf(-g)) * u;
-            const int a = lst[i0 + ii];
-            const size_t hb = (size_t)a * FB + fb;
-            quant_q8_1_32(h, f, A.hq.q + (size_t)a * A.F + fb * 32, A.hq.ds + hb, A.hq.sq + hb);
+            const int a = s_a[ii];
+            const Q81 r = q8_1_lane(h);
+            A.hq.q[(size_t)a * A.F + fb * 32 + f] = (int8_t)r.q;
+            if (f == 0) {
+                A.hq.ds[(size_t)a * FB + fb] = r.ds;
+                A.hq.sq[(size_t)a * FB + fb] = r.sum;
+            }
             if constexpr (TAP) {
                 if (A.taps.h) A.taps.h[(size_t)a * A.F + fb * 32 + f] = h;
             }
@@ -172,16 +310,18 @@ __global__ __launch_bounds__(NW * 64) void k_gate_up_mv(GUArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows kernel: out[s][r] = W_g[r] . act[s] for the rows of a block matrix and a
-// list of activation rows.  Expert mode (b.ctrl != nullptr): group = slot, W_g =
-// the down matrix of expert active[slot], rows of act/out = the expert's
-// assignments.  Dense mode: one matrix, act/out rows 0..T-1.
+// Rows kernel: out[s][r] = W_g[r] . act[s] for a tile of rows of a block matrix.
+// Expert mode (b.ctrl != nullptr): group = slot, W_g = the down matrix of expert
+// active[slot], act/out rows = the expert's assignments (hq rows).  Dense mode:
+// one matrix, act/out rows = tokens 0..T-1 (D on Q8_1(x), U on Q8_1(y_lat)).
 struct RowsArgs {
     const uint8_t* base;
     size_t group_stride, codes_off, scales_off;
-    int rows, K, T;
+    int rows, K, T, rt, tch;
     Buckets b;                 // b.ctrl == nullptr: dense mode
-    ActPtr ain;
+    ActPtr ain;                // quantised act rows, or
+    const float* ain_f32;      // fp32 act rows quantised in the prologue
+    ActPtr keep;               // Q8_1 of the fp32 rows, stored for taps (q == nullptr: off)
     float* out;                // [act row][rows]
     int tap_div;               // token of act row s = s / tap_div
     int32_t* isum_tap;         // [act row][rows][K/32]
@@ -189,11 +329,9 @@ struct RowsArgs {
 };
 
 template <int FMT, int LPR, int CPL, int NW, bool TAP>
-__global__ __launch_bounds__(NW * 64) void k_rows_mv(RowsArgs A) {
-    using F = Fmt<FMT>;
-    constexpr int RPW = 64 / LPR;
-    constexpr int RT = NW * RPW;
-    const int NRT = A.rows / RT;
+__global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
+    extern __shared__ __align__(16) char smem[];
+    const int NRT = A.rows / A.rt;
     const int g = blockIdx.x / NRT, rt = blockIdx.x - g * NRT;
     const uint8_t* mat;
     const int32_t* lst = nullptr;
@@ -208,138 +346,147 @@ __global__ __launch_bounds__(NW * 64) void k_rows_mv(RowsArgs A) {
         mat = A.base;
         cnt = A.T;
     }
-    const int nb = A.K / QK;
-    const int NCH = nb * F::CPB;
-    const size_t rowb = (size_t)nb * F::QB;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sl = lane % LPR, rg = lane / LPR;
-    const int r = rt * RT + wave * RPW + rg;
-    const uint8_t* codes = mat + A.codes_off + (size_t)r * rowb;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.scales_off) + (size_t)r * nb;
+    const int K = A.K, nb = K / QK, TCH = A.tch;
+    const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
+    const uint8_t* codes = mat + A.codes_off + (size_t)rt * A.rt * rowb;
+    const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.scales_off) + (size_t)rt * A.rt * nb;
+    int8_t* s_q = reinterpret_cast<int8_t*>(smem);
+    float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
+    int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
+    int32_t* s_s = reinterpret_cast<int32_t*>(smem + stage_bytes(TCH, K));
 
-    v4i wq[CPL];
-    float wsc[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = j * LPR + sl;
-        if (c < NCH) {
-            wq[j] = ld16(codes + (size_t)c * 16);
-            wsc[j] = h2f(scl[c / F::CPB]);
-        } else {
-            wq[j] = v4i{0, 0, 0, 0};
-            wsc[j] = 0.0f;
-        }
-    }
-    for (int i = 0; i < cnt; ++i) {
-        const int s = lst ? lst[i] : i;
-        const int8_t* arow = A.ain.q + (size_t)s * A.K;
-        const uint32_t* ads = A.ain.ds + (size_t)s * nb;
-        const int32_t* asq = A.ain.sq + (size_t)s * nb;
-        const bool tap = TAP && A.isum_tap && s / A.tap_div < A.tap_tokens;
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int c = j * LPR + sl;
-            const bool valid = c < NCH;
-            const int blk = c / F::CPB;
-            const int is = valid ? chunk_isum<FMT>(wq[j], arow, asq, c) : 0;
-            acc += (float)is * (wsc[j] * (valid ? h2f(ads[blk]) : 0.0f));
-            if constexpr (TAP) {
-                if (tap) {
-                    int full = is;
-                    if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
-                    if (valid && (F::CPB == 1 || (sl & 1) == 0))
-                        A.isum_tap[((size_t)s * A.rows + r) * nb + blk] = full;
-                }
-            }
-        }
-        const float v = group_sum<LPR>(acc);
-        if (sl == 0) A.out[(size_t)s * A.rows + r] = v;
+    for (int i0 = 0; i0 < cnt; i0 += TCH) {
+        const int n = min(TCH, cnt - i0);
+        if (threadIdx.x < n) s_s[threadIdx.x] = lst ? lst[i0 + threadIdx.x] : i0 + threadIdx.x;
+        __syncthreads();
+        if (A.ain_f32)
+            stage_f32(A.ain_f32, K, s_s, n, s_q, s_d, s_sq, rt == 0 ? A.keep : ActPtr{});
+        else
+            stage_q(A.ain, K, s_s, n, s_q, s_d, s_sq);
+        __syncthreads();
+        const int r0 = rt * A.rt;
+        auto emit = [&](int i, int r, float v) { A.out[(size_t)s_s[i] * A.rows + r0 + r] = v; };
+        auto emit_isum = [&](int i, int r, int blk, int v) {
+            if (s_s[i] / A.tap_div < A.tap_tokens)
+                A.isum_tap[((size_t)s_s[i] * A.rows + r0 + r) * nb + blk] = v;
+        };
+        v4i wA[CPL];
+        uint32_t sA[CPL];
+        row_tile<FMT, LPR, CPL, NW, TAP>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d, s_sq, emit,
+                                         emit_isum, TAP && A.isum_tap, wA, sA, false);
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Down projection with the combine fused, one workgroup per (token, row tile):
-// out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]), rank order.
+// Down projection with the combine fused, one workgroup per (token, 16-row
+// tile); wave j computes rank j's expert rows, then the tile is combined in
+// rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).
 struct DownTokArgs {
     const uint8_t* experts;
     size_t eb, dn_off, dn_scales_off;
     int F, Kout, k;
     ActPtr hq;
     Buckets b;
-    float* out;
+    float* out;              // [T][Kout]: the layer output, or y_lat for a latent layer
     Taps taps;
 };
 
-template <int FMT, int LPR, int CPL, int NW, bool TAP>
-__global__ __launch_bounds__(NW * 64) void k_down_tok_mv(DownTokArgs A) {
+constexpr int DT_RT = 16;    // output rows per workgroup
+constexpr int DT_NW = 8;     // waves per workgroup (ranks in parallel)
+constexpr int DT_KMAX = 32;  // largest top_k
+
+template <int FMT, int LPR, int CPL, bool TAP>
+__global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     using F = Fmt<FMT>;
     constexpr int RPW = 64 / LPR;
-    constexpr int RT = NW * RPW;
-    const int NRT = A.Kout / RT;
+    constexpr int NA = F::CPB == 1 ? 2 : 1;     // 16-byte activation pieces per chunk
+    __shared__ float s_y[DT_KMAX][DT_RT];
+    const int NRT = A.Kout / DT_RT;
     const int t = blockIdx.x / NRT, rt = blockIdx.x - t * NRT;
     const int nb = A.F / QK;
     const int NCH = nb * F::CPB;
     const size_t rowb = (size_t)nb * F::QB;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sl = lane % LPR, rg = lane / LPR;
-    const int r = rt * RT + wave * RPW + rg;
-    const bool tap = TAP && t < A.taps.tap_tokens;
-    float o = 0.0f;
-    for (int j = 0; j < A.k; ++j) {
+    const bool tap = TAP && t < A.taps.tap_tokens && A.taps.isum_dn;
+    constexpr int PASSES = DT_RT / RPW;
+    for (int j = wave; j < A.k; j += DT_NW) {
         const int a = t * A.k + j;
         const int e = A.b.ids[a];
-        const float wj = A.b.wts[a];
         const uint8_t* mat = A.experts + (size_t)e * A.eb + A.dn_off;
-        const uint8_t* codes = mat + (size_t)r * rowb;
-        const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.dn_scales_off) + (size_t)r * nb;
+        const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
+        const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * nb;
+        v4i wq[CPL], wn[CPL];
+        uint32_t wsc[CPL], wsn[CPL];
+        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * nb, sl, NCH, wq, wsc);
+        // this rank's activation chunks, the same for every row
+        v4i act[CPL][NA];
+        int asq[CPL];
         const int8_t* arow = A.hq.q + (size_t)a * A.F;
-        const uint32_t* ads = A.hq.ds + (size_t)a * nb;
-        const int32_t* asq = A.hq.sq + (size_t)a * nb;
-        v4i wq[CPL];
-        float wsc[CPL];
+        uint32_t ads[CPL];
 #pragma unroll
         for (int jj = 0; jj < CPL; ++jj) {
-            const int c = jj * LPR + sl;
-            if (c < NCH) {
-                wq[jj] = ld16(codes + (size_t)c * 16);
-                wsc[jj] = h2f(scl[c / F::CPB]);
-            } else {
-                wq[jj] = v4i{0, 0, 0, 0};
-                wsc[jj] = 0.0f;
-            }
+            const int c = min(jj * LPR + sl, NCH - 1);
+#pragma unroll
+            for (int h = 0; h < NA; ++h) act[jj][h] = ld16(arow + c * 16 * NA + h * 16);
+            asq[jj] = F::CPB == 1 ? A.hq.sq[(size_t)a * nb + c] : 0;
+            ads[jj] = A.hq.ds[(size_t)a * nb + c / F::CPB];
         }
-        float acc = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < CPL; ++jj) {
-            const int c = jj * LPR + sl;
-            const bool valid = c < NCH;
-            const int blk = c / F::CPB;
-            const int is = valid ? chunk_isum<FMT>(wq[jj], arow, asq, c) : 0;
-            acc += (float)is * (wsc[jj] * (valid ? h2f(ads[blk]) : 0.0f));
-            if constexpr (TAP) {
-                if (tap && A.taps.isum_dn) {
-                    int full = is;
-                    if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
-                    if (valid && (F::CPB == 1 || (sl & 1) == 0))
-                        A.taps.isum_dn[((size_t)a * A.Kout + r) * nb + blk] = full;
+        for (int p = 0; p < PASSES; ++p) {
+            const int r = p * RPW + rg;
+            if (p + 1 < PASSES)
+                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * nb, sl,
+                                        NCH, wn, wsn);
+            float acc = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) {
+                const int c = jj * LPR + sl;
+                const bool valid = c < NCH;
+                int is;
+                if constexpr (F::CPB == 1)
+                    is = dot_q4(wq[jj], act[jj][0], act[jj][NA - 1]) - 8 * asq[jj];
+                else
+                    is = dot16(wq[jj], act[jj][0]);
+                acc = fmaf((float)is, valid ? h2f(wsc[jj]) * h2f(ads[jj]) : 0.0f, acc);
+                if constexpr (TAP) {
+                    if (tap) {
+                        int full = is;
+                        if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
+                        if (valid && (F::CPB == 1 || (sl & 1) == 0))
+                            A.taps.isum_dn[((size_t)a * A.Kout + rt * DT_RT + r) * nb + c / F::CPB] = full;
+                    }
                 }
             }
-        }
-        const float y = group_sum<LPR>(acc);
-        o = fmaf(wj, y, o);
-        if constexpr (TAP) {
-            if (sl == 0 && A.taps.y) A.taps.y[(size_t)a * A.Kout + r] = y;
+            const float y = group_sum_fast<LPR>(acc);
+            if (sl == 0) s_y[j][r] = y;
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) {
+                wq[jj] = wn[jj];
+                wsc[jj] = wsn[jj];
+            }
         }
     }
-    if (sl == 0) A.out[(size_t)t * A.Kout + r] = o;
+    __syncthreads();
+    if (threadIdx.x < DT_RT) {
+        const int r = threadIdx.x;
+        float o = 0.0f;
+        for (int j = 0; j < A.k; ++j) {
+            const int a = t * A.k + j;
+            o = fmaf(A.b.wts[a], s_y[j][r], o);
+            if constexpr (TAP) {
+                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * DT_RT + r] = s_y[j][r];
+            }
+        }
+        A.out[(size_t)t * A.Kout + rt * DT_RT + r] = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // configuration choice and dispatch
 
-// lanes per row and 16-byte chunks per lane for a row of nch chunks, with at
-// most max_regs chunks held per lane when `passes` rows share a lane group.
+// lanes per row and 16-byte chunks per lane for a row of nch chunks
 static bool pick(int nch, int& lpr, int& cpl) {
     for (int c = 8; c >= 1; --c)
         for (int l = 8; l <= 64; l *= 2)
@@ -348,58 +495,24 @@ static bool pick(int nch, int& lpr, int& cpl) {
     return false;
 }
 
-#define MOE_LPR_CPL_SWITCH(LPR_, CPL_, CALL)                                      \
-    switch (LPR_ * 16 + CPL_) {                                                    \
-        case 8 * 16 + 1: { constexpr int L = 8, C = 1; CALL; break; }          \
-        case 8 * 16 + 2: { constexpr int L = 8, C = 2; CALL; break; }          \
-        case 8 * 16 + 3: { constexpr int L = 8, C = 3; CALL; break; }          \
-        case 8 * 16 + 4: { constexpr int L = 8, C = 4; CALL; break; }          \
-        case 8 * 16 + 5: { constexpr int L = 8, C = 5; CALL; break; }          \
-        case 8 * 16 + 6: { constexpr int L = 8, C = 6; CALL; break; }          \
-        case 8 * 16 + 7: { constexpr int L = 8, C = 7; CALL; break; }          \
-        case 8 * 16 + 8: { constexpr int L = 8, C = 8; CALL; break; }          \
-        case 16 * 16 + 1: { constexpr int L = 16, C = 1; CALL; break; }        \
-        case 16 * 16 + 2: { constexpr int L = 16, C = 2; CALL; break; }        \
-        case 16 * 16 + 3: { constexpr int L = 16, C = 3; CALL; break; }        \
-        case 16 * 16 + 4: { constexpr int L = 16, C = 4; CALL; break; }        \
-        case 16 * 16 + 5: { constexpr int L = 16, C = 5; CALL; break; }        \
-        case 16 * 16 + 6: { constexpr int L = 16, C = 6; CALL; break; }        \
-        case 16 * 16 + 7: { constexpr int L = 16, C = 7; CALL; break; }        \
-        case 16 * 16 + 8: { constexpr int L = 16, C = 8; CALL; break; }        \
-        case 32 * 16 + 1: { constexpr int L = 32, C = 1; CALL; break; }        \
-        case 32 * 16 + 2: { constexpr int L = 32, C = 2; CALL; break; }        \
-        case 32 * 16 + 3: { constexpr int L = 32, C = 3; CALL; break; }        \
-        case 32 * 16 + 4: { constexpr int L = 32, C = 4; CALL; break; }        \
-        case 32 * 16 + 5: { constexpr int L = 32, C = 5; CALL; break; }        \
-        case 32 * 16 + 6: { constexpr int L = 32, C = 6; CALL; break; }        \
-        case 32 * 16 + 7: { constexpr int L = 32, C = 7; CALL; break; }        \
-        case 32 * 16 + 8: { constexpr int L = 32, C = 8; CALL; break; }        \
-        case 64 * 16 + 1: { constexpr int L = 64, C = 1; CALL; break; }        \
-        case 64 * 16 + 2: { constexpr int L = 64, C = 2; CALL; break; }        \
-        case 64 * 16 + 3: { constexpr int L = 64, C = 3; CALL; break; }        \
-        case 64 * 16 + 4: { constexpr int L = 64, C = 4; CALL; break; }        \
-        case 64 * 16 + 5: { constexpr int L = 64, C = 5; CALL; break; }        \
-        case 64 * 16 + 6: { constexpr int L = 64, C = 6; CALL; break; }        \
-        case 64 * 16 + 7: { constexpr int L = 64, C = 7; CALL; break; }        \
-        case 64 * 16 + 8: { constexpr int L = 64, C = 8; CALL; break; }        \
-        default: return hipErrorInvalidConfiguration;                              \
-    }
-
-// Chunks per row of a Kin-wide row, and the (lanes, chunks) pair the kernels use.
 static int nchunks(int K, int fmt) { return fmt == MOE_FMT_Q4_0 ? K / 32 : K / 16; }
 
-// gate/up: one pass of rows in registers plus the prefetched next pass, so at
-// most 5 chunks per lane when there is more than one pass.
-constexpr int GU_NW = 8;   // waves per gate/up workgroup
-
+// gate/up: two passes of weights live at once, so at most 5 chunks per lane
+// (4 preferred: whole 4 KB rows per wave at K = 4096)
 static bool pick_gu(int nch, int& lpr, int& cpl) {
-    for (int l = 64; l >= 8; l /= 2)
-        for (int c = 8; c >= 1; --c) {
-            int passes = 64 / (GU_NW * (64 / l));
-            if (l * c == nch && (passes == 1 || c <= 5)) { lpr = l; cpl = c; return true; }
-        }
-    return false;
+    for (int c = 4; c >= 1; --c)
+        for (int l = 64; l >= 8; l /= 2)
+            if (l * c == nch) { lpr = l; cpl = c; return true; }
+    for (int c = 5; c <= 8; ++c)             // one pass of 8-lane rows: one buffer
+        if (8 * c == nch) { lpr = 8; cpl = c; return true; }
+    for (int l = 64; l >= 16; l /= 2)
+        for (int c = 5; c <= 8; ++c)
+            if (l * c == nch) { lpr = l; cpl = c; return true; }
+    return pick(nch, lpr, cpl);
 }
+
+// staged tokens per chunk: about 32 KB of codes
+static int pick_tch(int K) { return std::max(4, std::min(16, 32768 / K)); }
 
 bool mv_config_ok(int K, int fmt, bool gate_up) {
     int l, c;
@@ -407,99 +520,155 @@ bool mv_config_ok(int K, int fmt, bool gate_up) {
     return c >= 1 && c <= 8 && (l == 8 || l == 16 || l == 32 || l == 64);
 }
 
+#define MOE_LPR_CPL_SWITCH(LPR_, CPL_, CALL)                                      \
+    switch (LPR_ * 16 + CPL_) {                                                    \
+        case 8 * 16 + 1: { constexpr int L = 8, C = 1; CALL; break; }             \
+        case 8 * 16 + 2: { constexpr int L = 8, C = 2; CALL; break; }             \
+        case 8 * 16 + 3: { constexpr int L = 8, C = 3; CALL; break; }             \
+        case 8 * 16 + 4: { constexpr int L = 8, C = 4; CALL; break; }             \
+        case 8 * 16 + 5: { constexpr int L = 8, C = 5; CALL; break; }             \
+        case 8 * 16 + 6: { constexpr int L = 8, C = 6; CALL; break; }             \
+        case 8 * 16 + 7: { constexpr int L = 8, C = 7; CALL; break; }             \
+        case 8 * 16 + 8: { constexpr int L = 8, C = 8; CALL; break; }             \
+        case 16 * 16 + 1: { constexpr int L = 16, C = 1; CALL; break; }           \
+        case 16 * 16 + 2: { constexpr int L = 16, C = 2; CALL; break; }           \
+        case 16 * 16 + 3: { constexpr int L = 16, C = 3; CALL; break; }           \
+        case 16 * 16 + 4: { constexpr int L = 16, C = 4; CALL; break; }           \
+        case 16 * 16 + 5: { constexpr int L = 16, C = 5; CALL; break; }           \
+        case 16 * 16 + 6: { constexpr int L = 16, C = 6; CALL; break; }           \
+        case 16 * 16 + 7: { constexpr int L = 16, C = 7; CALL; break; }           \
+        case 16 * 16 + 8: { constexpr int L = 16, C = 8; CALL; break; }           \
+        case 32 * 16 + 1: { constexpr int L = 32, C = 1; CALL; break; }           \
+        case 32 * 16 + 2: { constexpr int L = 32, C = 2; CALL; break; }           \
+        case 32 * 16 + 3: { constexpr int L = 32, C = 3; CALL; break; }           \
+        case 32 * 16 + 4: { constexpr int L = 32, C = 4; CALL; break; }           \
+        case 32 * 16 + 5: { constexpr int L = 32, C = 5; CALL; break; }           \
+        case 32 * 16 + 6: { constexpr int L = 32, C = 6; CALL; break; }           \
+        case 32 * 16 + 7: { constexpr int L = 32, C = 7; CALL; break; }           \
+        case 32 * 16 + 8: { constexpr int L = 32, C = 8; CALL; break; }           \
+        case 64 * 16 + 1: { constexpr int L = 64, C = 1; CALL; break; }           \
+        case 64 * 16 + 2: { constexpr int L = 64, C = 2; CALL; break; }           \
+        case 64 * 16 + 3: { constexpr int L = 64, C = 3; CALL; break; }           \
+        case 64 * 16 + 4: { constexpr int L = 64, C = 4; CALL; break; }           \
+        case 64 * 16 + 5: { constexpr int L = 64, C = 5; CALL; break; }           \
+        case 64 * 16 + 6: { constexpr int L = 64, C = 6; CALL; break; }           \
+        case 64 * 16 + 7: { constexpr int L = 64, C = 7; CALL; break; }           \
+        case 64 * 16 + 8: { constexpr int L = 64, C = 8; CALL; break; }           \
+        default: return hipErrorInvalidConfiguration;                              \
+    }
+
+constexpr int ROWS_NW = 4;   // waves per rows workgroup
+
+// waves per gate/up workgroup: 8 lanes per row cover the 64-row slab in one
+// pass with 8 waves; wider rows use 4 waves and several passes
+static int gu_waves(int lpr) { return lpr == 8 ? 8 : 4; }
+
 template <int FMT, bool TAP>
-static hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, const GUArgs& a, hipStream_t st) {
+static hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a,
+                              hipStream_t st) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
-        constexpr int NW = GU_NW;
-        constexpr int PASSES = 64 / (NW * (64 / L));
-        if constexpr (PASSES == 1 || C <= 5)
-            hipLaunchKernelGGL((k_gate_up_mv<FMT, L, C, NW, TAP>), grid, dim3(NW * 64), 0, st, a);
-        else
-            return hipErrorInvalidConfiguration;
+        constexpr int NW = L == 8 ? 8 : 4;
+        hipLaunchKernelGGL((k_gate_up_mv<FMT, L, C, NW, TAP>), grid, dim3(NW * 64), lds, st, a);
     }));
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
-                             const Buckets& b, ActPtr hq, const Taps& taps, hipStream_t st) {
+                             const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
+                             const Taps& taps, hipStream_t st) {
     int lpr, cpl;
     if (!pick_gu(nchunks(m.kin, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
+    if (64 % (gu_waves(lpr) * (64 / lpr))) return hipErrorInvalidConfiguration;
     GUArgs a;
     a.experts = experts;
     a.eb = m.expert_bytes;
     a.gu_scales_off = m.gu.scales_off;
     a.K = m.kin; a.F = m.F; a.k = m.k; a.T = T;
-    a.ain = ain; a.b = b; a.hq = hq; a.taps = taps;
+    a.tch = pick_tch(m.kin);
+    a.ain = ain; a.ain_f32 = ain_f32; a.keep = keep;
+    a.b = b; a.hq = hq; a.taps = taps;
+    const size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 64 * 4 + (size_t)a.tch * 8;
     int slots = std::min(m.E, T * m.k);
     dim3 grid(slots * (m.F / QK));
     bool tap = taps.h || taps.isum_gu;
     if (m.fmt == MOE_FMT_Q4_0)
-        return tap ? gate_up_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, a, st)
-                   : gate_up_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, a, st);
-    return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, a, st)
-               : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, a, st);
+        return tap ? gate_up_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st)
+                   : gate_up_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st);
+    return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
+               : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
 
-constexpr int ROWS_NW = 8;
-
 template <int FMT, bool TAP>
-static hipError_t rows_fmt(int lpr, int cpl, int ngroups, const RowsArgs& a, hipStream_t st) {
+static hipError_t rows_fmt(int lpr, int cpl, dim3 grid, size_t lds, const RowsArgs& a,
+                           hipStream_t st) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
-        constexpr int RT = ROWS_NW * (64 / L);
-        dim3 grid(ngroups * (a.rows / RT));
-        hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), 0, st, a);
+        hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), lds, st, a);
     }));
     return hipGetLastError();
 }
 
-static hipError_t rows_dispatch(int fmt, int ngroups, const RowsArgs& a, hipStream_t st) {
+// rows per workgroup: a multiple of the rows one pass covers, dividing `rows`,
+// small enough to give about 512 workgroups
+static int pick_rt(int rows, int groups, int rpp) {
+    int rt = rpp;
+    while (rt * 2 <= 64 && rows % (rt * 2) == 0 && (long)groups * (rows / (rt * 2)) >= 512) rt *= 2;
+    return rt;
+}
+
+static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st) {
     int lpr, cpl;
     if (!pick(nchunks(a.K, fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
-    if (a.rows % (ROWS_NW * (64 / lpr))) return hipErrorInvalidConfiguration;
+    const int rpp = ROWS_NW * (64 / lpr);
+    if (a.rows % rpp) return hipErrorInvalidConfiguration;
+    a.rt = pick_rt(a.rows, groups, rpp);
+    a.tch = pick_tch(a.K);
+    const size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 4;
+    dim3 grid(groups * (a.rows / a.rt));
     bool tap = a.isum_tap != nullptr;
     if (fmt == MOE_FMT_Q4_0)
-        return tap ? rows_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, ngroups, a, st)
-                   : rows_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, ngroups, a, st);
-    return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, ngroups, a, st)
-               : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, ngroups, a, st);
+        return tap ? rows_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st);
+    return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
+               : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
 
 hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st) {
-    RowsArgs a;
+    RowsArgs a{};
     a.base = experts;
     a.group_stride = m.expert_bytes;
     a.codes_off = m.dn_off + m.dn.codes_off;
     a.scales_off = m.dn_off + m.dn.scales_off;
     a.rows = m.kout; a.K = m.F; a.T = T;
-    a.b = b; a.ain = hq; a.out = y;
+    a.b = b; a.ain = hq; a.ain_f32 = nullptr; a.keep = ActPtr{}; a.out = y;
     a.tap_div = m.k; a.isum_tap = taps.isum_dn; a.tap_tokens = taps.tap_tokens;
     return rows_dispatch(m.fmt, std::min(m.E, T * m.k), a, st);
 }
 
-hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
-                           int32_t* isum_tap, int tap_tokens, hipStream_t st) {
-    RowsArgs a;
+hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
+                           const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
+                           int tap_tokens, hipStream_t st) {
+    RowsArgs a{};
     a.base = base;
     a.group_stride = 0;
     a.codes_off = W.codes_off;
     a.scales_off = W.scales_off;
     a.rows = W.rows; a.K = W.nblk * QK; a.T = T;
     a.b = Buckets{};
-    a.ain = ain; a.out = out;
+    a.ain = ain; a.ain_f32 = ain_f32; a.keep = keep; a.out = out;
     a.tap_div = 1; a.isum_tap = isum_tap; a.tap_tokens = tap_tokens;
     return rows_dispatch(W.fmt, 1, a, st);
 }
 
-constexpr int DT_NW = 8;
-
 template <int FMT, bool TAP>
 static hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream_t st) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
-        constexpr int RT = DT_NW * (64 / L);
-        if (a.Kout % RT) return hipErrorInvalidConfiguration;
-        dim3 grid(T * (a.Kout / RT));
-        hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, DT_NW, TAP>), grid, dim3(DT_NW * 64), 0, st, a);
+        if constexpr (DT_RT % (64 / L) == 0) {
+            dim3 grid(T * (a.Kout / DT_RT));
+            hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), 0, st, a);
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
     }));
     return hipGetLastError();
 }
@@ -508,6 +677,7 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActP
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
     int lpr, cpl;
     if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
+    if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;
     DownTokArgs a;
     a.experts = experts;
     a.eb = m.expert_bytes;

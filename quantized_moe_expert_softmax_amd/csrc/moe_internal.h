@@ -85,6 +85,7 @@ enum CtrlWord {
     CW_BUCKET_ARRIVE = 0,   // arrivals of the per-expert bucketing workgroups
     CW_N_ACTIVE = 1,        // experts with at least one token
     CW_N_TILES = 2,         // token tiles over all active experts (grouped GEMM)
+    CW_ROUTE_ARRIVE = 3,    // arrivals of the decode routing logits workgroups
     CW_COUNT = 64
 };
 
@@ -101,9 +102,12 @@ struct WsLayout {
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+constexpr int DECODE_T = 8;  // T up to this routes in one fused kernel
+
 inline int router_splits(const Dims& m, int T) {
-    // enough workgroups to spread the router matrix at small T
-    if (T > 32) return 1;
+    // enough workgroups to spread the router matrix at small T; the fused
+    // decode router computes whole logits
+    if (T > 32 || T <= DECODE_T) return 1;
     int s = 1;
     while (s < ROUTER_SPLIT_MAX && (m.E / 4) * s * 2 <= 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
     return s;
