@@ -325,6 +325,8 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
     }
     const bool down_tok = T <= DOWN_TOK_MAX_T;
+    // many tokens: grouped matrix-core GEMMs over token tiles
+    const bool gemm = T > MV_MAX_T;
     if (taps && down_tok) tp.y = taps->y;
     const ActPtr none{nullptr, nullptr, nullptr};
 
@@ -343,15 +345,24 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     bool bucketed = false;
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
                      &bucketed, st), "router");
-    if (!bucketed) CK(launch_bucket(m, w, ws, T, 32, st), "bucketing");
+    if (!bucketed) CK(launch_bucket(m, w, ws, T, st), "bucketing");
     EV(MOE_EV_ROUTED);
+    const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
-        // z = D . Q8_1(x), fp32; the gate/up kernel quantises it on the way in
-        CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
-                           tp.tap_tokens, st), "D");
+        // z = D . Q8_1(x), fp32
+        if (gemm) {
+            CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
+            CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
+        } else {
+            // the gate/up kernel quantises z on the way in
+            CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
+                               tp.tap_tokens, st), "D");
+        }
     }
     EV(MOE_EV_EXPERT_IN);
-    if (m.L)
+    if (gemm)
+        CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st), "gate/up");
+    else if (m.L)
         CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st), "gate/up");
     else
         CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st), "gate/up");
@@ -360,14 +371,23 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     if (down_tok) {
         CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st), "down+combine");
     } else {
-        CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
+        if (gemm)
+            CK(launch_down_mfma(m, T, ex, hq, b, tile_map, y, tp, st), "down");
+        else
+            CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
         CK(launch_combine(y, b.wts, T, m.k, m.kout, comb, st), "combine");
     }
     EV(MOE_EV_DOWN);
     if (m.L) {
-        // out = U . Q8_1(y_lat); the U kernel quantises y_lat on the way in
-        CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, none, ylat, taps ? ylq : none, out,
-                           tp.isum_u, tp.tap_tokens, st), "U");
+        // out = U . Q8_1(y_lat)
+        if (gemm) {
+            CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
+            CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
+        } else {
+            // the U kernel quantises y_lat on the way in
+            CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, none, ylat, taps ? ylq : none, out,
+                               tp.isum_u, tp.tap_tokens, st), "U");
+        }
     }
     EV(MOE_EV_END);
     if (taps) {

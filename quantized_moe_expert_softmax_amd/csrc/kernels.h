@@ -34,8 +34,9 @@ hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStr
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
                          ActPtr xq, bool* bucketed, hipStream_t st);
-hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, int tile_m,
-                         hipStream_t st);
+// Per-expert assignment lists in token order, the active experts, and the
+// token tiles (GEMM_TILE_M assignments) of each, numbered in tile_map.
+hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, hipStream_t st);
 hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R, float* out,
                           hipStream_t st);
 hipError_t launch_tap_q8_1(ActPtr a, long rows, int K, uint8_t* out, hipStream_t st);
@@ -57,5 +58,17 @@ hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, Act
 hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
                            const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
                            int tap_tokens, hipStream_t st);
+
+// Many-token path: grouped int8 matrix-core GEMM over the token tiles that the
+// bucketing kernel numbered in tile_map (tiles of GEMM_TILE_M assignments).
+bool mfma_config_ok(int rows, int K);
+hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+                               const Buckets& b, const int32_t* tile_map, ActPtr hq,
+                               const Taps& taps, hipStream_t st);
+hipError_t launch_down_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+                            const Buckets& b, const int32_t* tile_map, float* y, const Taps& taps,
+                            hipStream_t st);
+hipError_t launch_dense_mfma(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
+                             int32_t* isum_tap, int tap_tokens, hipStream_t st);
 
 }  // namespace moe

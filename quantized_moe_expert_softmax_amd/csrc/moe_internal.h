@@ -90,7 +90,7 @@ enum CtrlWord {
 };
 
 struct WsLayout {
-    size_t ctrl, logit_part, ids, wts, counts, active, tile_start, lists;
+    size_t ctrl, logit_part, ids, wts, counts, active, tile_start, tile_map, lists;
     size_t xq_q, xq_ds, xq_sq;
     size_t z, zq_q, zq_ds, zq_sq;
     size_t hq_q, hq_ds, hq_sq;
@@ -103,6 +103,15 @@ struct WsLayout {
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr int DECODE_T = 8;  // T up to this routes in one fused kernel
+constexpr int MV_MAX_T = 32; // T up to this runs the matrix-vector expert kernels
+constexpr int GEMM_TILE_M = 64;  // token tile of the grouped matrix-core GEMM
+
+// Upper bound of the token tiles over all active experts: every expert adds at
+// most one partial tile.
+inline int gemm_max_tiles(int T, int k, int E) {
+    const long A = (long)T * k;
+    return (int)((A + GEMM_TILE_M - 1) / GEMM_TILE_M + (A < E ? A : E));
+}
 
 inline int router_splits(const Dims& m, int T) {
     // enough workgroups to spread the router matrix at small T; the fused
@@ -127,6 +136,7 @@ inline WsLayout ws_layout(const Dims& m, int T) {
     w.counts = take(sizeof(int32_t) * m.E);
     w.active = take(sizeof(int32_t) * m.E);
     w.tile_start = take(sizeof(int32_t) * (m.E + 1));
+    w.tile_map = take(sizeof(int32_t) * gemm_max_tiles(T, m.k, m.E));
     w.lists = take(sizeof(int32_t) * (size_t)m.E * T);
     w.xq_q = take((size_t)T * m.H);
     w.xq_ds = take(sizeof(uint32_t) * T * (m.H / QK));

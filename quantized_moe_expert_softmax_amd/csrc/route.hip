@@ -518,8 +518,10 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
         s_cnt[i] = 0;
         s_mask[i] = 0u;
     }
-    if (G > 0)
+    if (G > 0) {
         for (int i = tid; i < T * 64; i += SEL_NT) s_gkey[i / 64][i % 64] = 0ull;
+        if (tid < T) s_nallow[tid] = 0;
+    }
     __syncthreads();
     if (G > 0) {
         for (int i = tid; i < TE; i += SEL_NT) {
@@ -540,34 +542,45 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
             s_gsel[t][g] = r < A.TG;
         }
         __syncthreads();
+        // allowed experts, counted per token with LDS atomics
         for (int i = tid; i < TE; i += SEL_NT) {
-            const int t = i / E, e = i - t * E;
-            const unsigned gl = (unsigned)A.groups[e];
-            s_allow[i] = gl < (unsigned)G && s_gsel[t][gl];
-        }
-        __syncthreads();
-        if (tid < T) {
-            int n = 0;
-            for (int h = 0; h < E; ++h) n += s_allow[tid * E + h];
-            s_nallow[tid] = n;
+            const int t = i / E;
+            const unsigned gl = (unsigned)A.groups[i - t * E];
+            const bool al = gl < (unsigned)G && s_gsel[t][gl];
+            s_allow[i] = al;
+            if (al) atomicAdd(&s_nallow[t], 1);
         }
         __syncthreads();
     }
-    // exact ranks; a token with fewer than k allowed experts (labels that break
-    // the equal-size-groups contract) ranks every expert instead
-    for (int i = tid; i < TE; i += SEL_NT) {
-        const int t = i / E, e = i - t * E;
-        const double* lt = s_l + t * E;
-        const unsigned char* at = s_allow + t * E;
-        const bool all = G == 0 || s_nallow[t] < k;
-        if (!all && !at[e]) continue;
-        const double le = lt[e];
-        int r = 0;
-        for (int h = 0; h < E; ++h) {
-            const double lh = lt[h];
-            r += (all || at[h]) && ((lh > le) || (lh == le && h < e));
+    // exact ranks, P lanes per (token, expert) pair each scanning E/P rivals; a
+    // token with fewer than k allowed experts (labels that break the
+    // equal-size-groups contract) ranks every expert instead
+    int P = 1;
+    while (P < 64 && TE * P * 2 <= SEL_NT) P *= 2;
+    const int lp = 31 - __clz(P);
+    for (int b0 = 0; b0 < (TE << lp); b0 += SEL_NT) {
+        const int gi = b0 + tid;
+        const int i = gi >> lp, part = gi & (P - 1);
+        int r = 0, t = 0, e = 0;
+        bool cand = false;
+        if (i < TE) {
+            t = i / E;
+            e = i - t * E;
+            const double* lt = s_l + t * E;
+            const unsigned char* at = s_allow + t * E;
+            const bool all = G == 0 || s_nallow[t] < k;
+            cand = all || at[e];
+            if (cand) {
+                const double le = lt[e];
+#pragma unroll 4
+                for (int h = part; h < E; h += P) {
+                    const double lh = lt[h];
+                    r += (all || at[h]) && ((lh > le) || (lh == le && h < e));
+                }
+            }
         }
-        if (r < k) s_sel[t][r] = e;
+        for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+        if (cand && part == 0 && r < k) s_sel[t][r] = e;
     }
     __syncthreads();
     // softmax over the chosen logits, rank order, fp64
@@ -622,7 +635,8 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ lists,
                                                 uint32_t* __restrict__ ctrl,
                                                 int32_t* __restrict__ active,
-                                                int32_t* __restrict__ tile_start) {
+                                                int32_t* __restrict__ tile_start,
+                                                int32_t* __restrict__ tile_map) {
     __shared__ int wsum[4];
     __shared__ int base;
     __shared__ int is_last;
@@ -673,8 +687,19 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids,
     }
     int slot = sc[tid] - act;           // exclusive
     int tl = tiles[tid] - til;
-    if (c0 > 0) { active[slot] = e0; tile_start[slot] = tl; ++slot; tl += (c0 + tile_m - 1) / tile_m; }
-    if (c1 > 0) { active[slot] = e1; tile_start[slot] = tl; }
+    // tile map entry: expert | (tile index within the expert << 16)
+    if (c0 > 0) {
+        active[slot] = e0;
+        tile_start[slot] = tl;
+        for (int i = 0; i < (c0 + tile_m - 1) / tile_m; ++i) tile_map[tl + i] = e0 | (i << 16);
+        ++slot;
+        tl += (c0 + tile_m - 1) / tile_m;
+    }
+    if (c1 > 0) {
+        active[slot] = e1;
+        tile_start[slot] = tl;
+        for (int i = 0; i < (c1 + tile_m - 1) / tile_m; ++i) tile_map[tl + i] = e1 | (i << 16);
+    }
     if (tid == 255) {
         ctrl[CW_N_ACTIVE] = sc[255];
         ctrl[CW_N_TILES] = tiles[255];
@@ -778,12 +803,12 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     return hipGetLastError();
 }
 
-hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, int tile_m,
+hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T,
                          hipStream_t st) {
     hipLaunchKernelGGL(k_bucket, dim3(m.E), dim3(256), 0, st, (const int32_t*)(ws + w.ids), T * m.k,
-                       T, m.E, tile_m, (int32_t*)(ws + w.counts), (int32_t*)(ws + w.lists),
+                       T, m.E, GEMM_TILE_M, (int32_t*)(ws + w.counts), (int32_t*)(ws + w.lists),
                        (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active),
-                       (int32_t*)(ws + w.tile_start));
+                       (int32_t*)(ws + w.tile_start), (int32_t*)(ws + w.tile_map));
     return hipGetLastError();
 }
 

@@ -95,6 +95,31 @@ def test_variants(kw):
     _report(str(kw), w.tokens, rep)
 
 
+# many-token path (grouped matrix-core GEMM): several row tiles, ragged token
+# tiles, both weight formats, latent D/U, group-limited routing
+@pytest.mark.parametrize("kw,sample,taps", [
+    (dict(expert_fmt=synth.Q4_0, tokens=100), None, 4),
+    (dict(top_k=8, tokens=65), None, 3),
+    (dict(n_experts=1, top_k=1, tokens=129), None, 3),
+    (dict(latent=256, n_experts=16, top_k=4, n_groups=4, topk_groups=2, tokens=70), None, 3),
+    (dict(latent=256, expert_fmt=synth.Q4_0, n_experts=16, top_k=4, tokens=97), None, 3),
+    (dict(hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300, bias=True),
+     [0, 1, 77, 150, 298, 299], 2),
+])
+def test_gemm_variants(kw, sample, taps):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tokens=sample, tap_tokens=taps)
+    _report("gemm " + str(kw), w.tokens, rep)
+
+
+@pytest.mark.parametrize("name,T", [("latent_q8", 48), ("latent_q4", 40)])
+def test_latent_gemm_sampled(name, T):
+    layer, inp = _layer(name, T)
+    rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp,
+                        tokens=[0, 1, 17, T - 1])
+    _report(name, T, rep)
+
+
 def test_zero_input_uniform_weights_zero_output():
     w = _variant(tokens=3)
     inp = gh.make_inputs(w)
