@@ -9,6 +9,10 @@
 //     so its int32 result is the exact block sum of 32 weight rows against 32
 //     token columns; the block is then scaled by d_w * d_a in fp32 and added to
 //     an fp32 accumulator (the block sums are never merged across blocks);
+//   * the 32 x 32 scale products d_w[row] * d_a[token] of a block come from an
+//     f16 matrix-core outer product (v_mfma_f32_32x32x16_f16 with one non-zero
+//     k), exact in fp32 because two binary16 significands need 22 bits; so the
+//     vector ALU spends one convert and one FMA per block result;
 //   * weights are the row operand, tokens the column operand, so a lane holds
 //     one token and 16 weight rows: the 32 outputs of one Q8_1 block of h sit in
 //     one lane pair, which makes the SwiGLU + requantisation epilogue local;
@@ -26,12 +30,18 @@
 namespace moe {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int MF_MT = GEMM_TILE_M;        // token columns per workgroup
 constexpr int MF_NT = 128;                // weight rows per workgroup
 constexpr int MF_KB = 4;                  // blocks of 32 per LDS stage
 constexpr int MF_ROWB = MF_KB * QK + 16;  // LDS bytes per staged row (padded)
 constexpr int MF_THREADS = 256;
+// binary16 scales of a stage: [block][MF_NT + 32] and [block][MF_MT + 32]; the
+// last 32 entries of each row stay zero (the f16 outer product reads them in
+// lanes 32..63)
+constexpr int MF_SWR = MF_NT + 32, MF_SAR = MF_MT + 32;
 
 struct MfArgs {
     const uint8_t* base;          // expert packs (group mode) or the dense matrix
@@ -66,7 +76,7 @@ template <int FMT, bool SWIGLU, bool TAP>
 __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
     constexpr int QB = FMT == MOE_FMT_Q4_0 ? 16 : 32;   // code bytes per block
     constexpr int WBYTES = MF_NT * MF_ROWB, XBYTES = MF_MT * MF_ROWB;
-    constexpr int STAGE = WBYTES + XBYTES + MF_KB * MF_NT * 4 + MF_KB * MF_MT * 4;
+    constexpr int STAGE = WBYTES + XBYTES + MF_KB * MF_SWR * 2 + MF_KB * MF_SAR * 2;
     __shared__ __align__(16) char smem[2 * STAGE];
     __shared__ int s_row[MF_MT], s_orow[MF_MT];
 
@@ -95,6 +105,13 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
     }
     const int ncol = min(MF_MT, cnt - m0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    {
+        // zero tails of the scale rows, both stage buffers
+        const int buf = tid >> 7, kb = (tid >> 5) & 3, z = tid & 31;
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(smem + buf * STAGE + WBYTES + XBYTES);
+        sdw[kb * MF_SWR + MF_NT + z] = 0;
+        sdw[MF_KB * MF_SWR + kb * MF_SAR + MF_MT + z] = 0;
+    }
     if (tid < MF_MT) {
         const int c = min(tid, ncol - 1);
         const int o = lst ? lst[m0 + c] : m0 + c;
@@ -139,8 +156,8 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
         char* st = smem + buf * STAGE;
         int8_t* sw = reinterpret_cast<int8_t*>(st);
         int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
-        float* sdw = reinterpret_cast<float*>(st + WBYTES + XBYTES);
-        float* sda = sdw + MF_KB * MF_NT;
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(st + WBYTES + XBYTES);
+        uint16_t* sda = sdw + MF_KB * MF_SWR;
 #pragma unroll
         for (int j = 0; j < WCH; ++j) {
             const int ch = tid + j * MF_THREADS;
@@ -167,66 +184,79 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
             *reinterpret_cast<v4i*>(sx + c * MF_ROWB + p * 16) = rx[j];
         }
         if (tid < MF_NT) {
-            sdw[0 * MF_NT + tid] = h2f(rdw.x & 0xffffu);
-            sdw[1 * MF_NT + tid] = h2f(rdw.x >> 16);
-            sdw[2 * MF_NT + tid] = h2f(rdw.y & 0xffffu);
-            sdw[3 * MF_NT + tid] = h2f(rdw.y >> 16);
+            sdw[0 * MF_SWR + tid] = (uint16_t)(rdw.x & 0xffffu);
+            sdw[1 * MF_SWR + tid] = (uint16_t)(rdw.x >> 16);
+            sdw[2 * MF_SWR + tid] = (uint16_t)(rdw.y & 0xffffu);
+            sdw[3 * MF_SWR + tid] = (uint16_t)(rdw.y >> 16);
         } else if (tid < MF_NT + MF_MT) {
             const int c = tid - MF_NT;
-            const bool ok = c < ncol;
+            const bool ok = c < ncol;      // columns past the tile's tokens get d_a = 0
 #pragma unroll
             for (int q = 0; q < MF_KB; ++q)
-                sda[q * MF_MT + c] = ok ? h2f((uint32_t)rda[q] & 0xffffu) : 0.0f;
+                sda[q * MF_SAR + c] = ok ? (uint16_t)((uint32_t)rda[q] & 0xffffu) : (uint16_t)0;
         }
     };
 
     // ---- the wave's tile: rows wr*64 + [0,32) and + [32,64), token columns wc*32 + [0,32)
     const int wr = wave & 1, wc = wave >> 1;
     const int half = lane >> 5, l32 = lane & 31;
+    // scale entries of this lane (the zero tails in lanes 32..63)
+    const int o_w0 = half ? MF_NT + l32 : wr * 64 + l32;
+    const int o_w1 = half ? MF_NT + l32 : wr * 64 + 32 + l32;
+    const int o_a = half ? MF_MT + l32 : wc * 32 + l32;
+    // a wave whose 32 token columns are all past the tile's tokens only stages
+    const bool busy = wc * 32 < ncol;
     float acc0[16], acc1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
 
     const int stages = nb / MF_KB;
     auto compute = [&](int buf, int s) {
+        if (!busy) return;
         const char* st = smem + buf * STAGE;
         const int8_t* sw = reinterpret_cast<const int8_t*>(st);
         const int8_t* sx = reinterpret_cast<const int8_t*>(st + WBYTES);
-        const float* sdw = reinterpret_cast<const float*>(st + WBYTES + XBYTES);
-        const float* sda = sdw + MF_KB * MF_NT;
+        const uint16_t* sdw = reinterpret_cast<const uint16_t*>(st + WBYTES + XBYTES);
+        const uint16_t* sda = sdw + MF_KB * MF_SWR;
         // block kb's products are issued one block ahead of their rescale
         auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
             a0 = *reinterpret_cast<const v4i*>(sw + (wr * 64 + l32) * MF_ROWB + kb * QK + half * 16);
             a1 = *reinterpret_cast<const v4i*>(sw + (wr * 64 + 32 + l32) * MF_ROWB + kb * QK + half * 16);
             bx = *reinterpret_cast<const v4i*>(sx + (wc * 32 + l32) * MF_ROWB + kb * QK + half * 16);
         };
+        // scale operands: lanes 0..31 give row / column l32 its binary16 d at k = 0
+        auto sfrag = [&](int kb, h8& d0, h8& d1, h8& dc) {
+            const v4i w0 = {(int)sdw[kb * MF_SWR + o_w0], 0, 0, 0};
+            const v4i w1 = {(int)sdw[kb * MF_SWR + o_w1], 0, 0, 0};
+            const v4i c0 = {(int)sda[kb * MF_SAR + o_a], 0, 0, 0};
+            d0 = __builtin_bit_cast(h8, w0);
+            d1 = __builtin_bit_cast(h8, w1);
+            dc = __builtin_bit_cast(h8, c0);
+        };
         v4i a0, a1, bx;
+        h8 d0, d1, dc;
         frag(0, a0, a1, bx);
+        sfrag(0, d0, d1, dc);
         v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
         v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
+        v16f s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d0, dc, v16f{}, 0, 0, 0);
+        v16f s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d1, dc, v16f{}, 0, 0, 0);
 #pragma unroll
         for (int kb = 0; kb < MF_KB; ++kb) {
             v16i n0, n1;
+            v16f t0, t1;
             if (kb + 1 < MF_KB) {
                 frag(kb + 1, a0, a1, bx);
+                sfrag(kb + 1, d0, d1, dc);
                 n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
                 n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
+                t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d0, dc, v16f{}, 0, 0, 0);
+                t1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d1, dc, v16f{}, 0, 0, 0);
             }
-            const float da = sda[kb * MF_MT + wc * 32 + l32];
-            const float* dw0 = sdw + kb * MF_NT + wr * 64 + half * 4;
-            const float* dw1 = dw0 + 32;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 w0 = *reinterpret_cast<const float4*>(dw0 + q * 8);
-                const float4 w1 = *reinterpret_cast<const float4*>(dw1 + q * 8);
-                acc0[4 * q + 0] = fmaf((float)i0[4 * q + 0], w0.x * da, acc0[4 * q + 0]);
-                acc0[4 * q + 1] = fmaf((float)i0[4 * q + 1], w0.y * da, acc0[4 * q + 1]);
-                acc0[4 * q + 2] = fmaf((float)i0[4 * q + 2], w0.z * da, acc0[4 * q + 2]);
-                acc0[4 * q + 3] = fmaf((float)i0[4 * q + 3], w0.w * da, acc0[4 * q + 3]);
-                acc1[4 * q + 0] = fmaf((float)i1[4 * q + 0], w1.x * da, acc1[4 * q + 0]);
-                acc1[4 * q + 1] = fmaf((float)i1[4 * q + 1], w1.y * da, acc1[4 * q + 1]);
-                acc1[4 * q + 2] = fmaf((float)i1[4 * q + 2], w1.z * da, acc1[4 * q + 2]);
-                acc1[4 * q + 3] = fmaf((float)i1[4 * q + 3], w1.w * da, acc1[4 * q + 3]);
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] = fmaf((float)i0[i], s0[i], acc0[i]);
+                acc1[i] = fmaf((float)i1[i], s1[i], acc1[i]);
             }
             if constexpr (TAP) {
                 const int c = wc * 32 + l32;
@@ -248,6 +278,8 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
             if (kb + 1 < MF_KB) {
                 i0 = n0;
                 i1 = n1;
+                s0 = t0;
+                s1 = t1;
             }
             // the block's rescale happens here, not sunk past later stores
 #pragma unroll

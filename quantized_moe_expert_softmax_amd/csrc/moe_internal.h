@@ -114,11 +114,17 @@ inline int gemm_max_tiles(int T, int k, int E) {
 }
 
 inline int router_splits(const Dims& m, int T) {
-    // enough workgroups to spread the router matrix at small T; the fused
-    // decode router computes whole logits
-    if (T > 32 || T <= DECODE_T) return 1;
+    // K slices of the router logits: enough workgroups to spread the router
+    // matrix (small T) or the token x expert tiles (many tokens); the decode
+    // router computes whole logits
+    if (T <= DECODE_T) return 1;
     int s = 1;
-    while (s < ROUTER_SPLIT_MAX && (m.E / 4) * s * 2 <= 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
+    if (T <= MV_MAX_T) {
+        while (s < ROUTER_SPLIT_MAX && (m.E / 4) * s * 2 <= 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
+    } else {
+        const long tiles = (long)((T + 63) / 64) * ((m.E + 63) / 64);
+        while (s < ROUTER_SPLIT_MAX && tiles * s < 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
+    }
     return s;
 }
 

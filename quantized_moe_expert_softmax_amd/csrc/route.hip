@@ -81,6 +81,89 @@ __global__ __launch_bounds__(256) void k_route_logits(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Many-token router logits: a workgroup computes a 64-token x 64-expert tile of
+// one K slice.  x and W_r tiles are staged in LDS as fp64 (k-major), each thread
+// accumulates 4 tokens x 4 experts in fp64 (products of two floats are exact in
+// fp64).  Trailing workgroups quantise x to Q8_1, as in k_route_logits.
+constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 2;
+
+__global__ __launch_bounds__(256) void k_route_logits_tiled(const float* __restrict__ x,
+                                                            const float* __restrict__ W, int T,
+                                                            int H, int E, int S,
+                                                            double* __restrict__ part,
+                                                            int n_logit_wg, ActPtr xq) {
+    if ((int)blockIdx.x >= n_logit_wg) {
+        const int nb = H / QK;
+        const long blk = (long)(blockIdx.x - n_logit_wg) * 8 + threadIdx.x / 32;
+        if (blk >= (long)T * nb) return;
+        const int l = threadIdx.x % 32;
+        const long r = blk / nb, b = blk % nb;
+        quant_q8_1_32(x[r * H + b * QK + l], l, xq.q + r * H + b * QK, xq.ds + r * nb + b,
+                      xq.sq + r * nb + b);
+        return;
+    }
+    __shared__ __align__(16) double sx[RT_K][RT_M + RT_PAD];
+    __shared__ __align__(16) double sw[RT_K][RT_N + RT_PAD];
+    const int gm = (T + RT_M - 1) / RT_M, gn = (E + RT_N - 1) / RT_N;
+    int b = blockIdx.x;
+    const int tm = b % gm;
+    b /= gm;
+    const int tn = b % gn;
+    const int s = b / gn;
+    const int slice = H / S, k0 = s * slice;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int kk = k0; kk < k0 + slice; kk += RT_K) {
+        // 64 rows x 32 floats of x and of W_r: two float4 per thread each
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = threadIdx.x + j * 256;
+            const int row = idx >> 3, c4 = idx & 7;
+            const int t = min(tm * RT_M + row, T - 1), e = min(tn * RT_N + row, E - 1);
+            const float4 xv = *reinterpret_cast<const float4*>(x + (size_t)t * H + kk + c4 * 4);
+            const float4 wv = *reinterpret_cast<const float4*>(W + (size_t)e * H + kk + c4 * 4);
+            sx[c4 * 4 + 0][row] = xv.x;
+            sx[c4 * 4 + 1][row] = xv.y;
+            sx[c4 * 4 + 2][row] = xv.z;
+            sx[c4 * 4 + 3][row] = xv.w;
+            sw[c4 * 4 + 0][row] = wv.x;
+            sw[c4 * 4 + 1][row] = wv.y;
+            sw[c4 * 4 + 2][row] = wv.z;
+            sw[c4 * 4 + 3][row] = wv.w;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < RT_K; ++k) {
+            double xa[4], wb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xa[i] = sx[k][ty * 4 + i];
+                wb[i] = sw[k][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(xa[i], wb[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = tm * RT_M + ty * 4 + i;
+        if (t >= T) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tn * RT_N + tx * 4 + j;
+            if (e < E) part[((size_t)s * T + t) * E + e] = acc[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Selection for one token by one wave: sum the K-slice partials (in slice
 // order), add the bias, apply the group limit, top-k with ties to the lower id,
 // softmax over the chosen logits in fp64.  Lane j < k returns rank j's expert
@@ -638,26 +721,31 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ tile_start,
                                                 int32_t* __restrict__ tile_map) {
     __shared__ int wsum[4];
-    __shared__ int base;
     __shared__ int is_last;
     const int e = blockIdx.x, tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    if (tid == 0) base = 0;
-    __syncthreads();
-    for (int a0 = 0; a0 < A; a0 += 256) {
-        int a = a0 + tid;
-        bool f = a < A && ids[a] == e;
-        uint64_t m = __ballot(f);
-        int pre = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) wsum[wave] = __popcll(m);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wave; ++w) off += wsum[w];
-        if (f) lists[(size_t)e * T + off + pre] = a;
-        __syncthreads();
-        if (tid == 0) base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        __syncthreads();
+    // wave w owns the contiguous quarter [q0, q1) of the assignments: count its
+    // matches, then (after one exchange of the wave totals) list them in order
+    const int Q = (A + 3) / 4;
+    const int q0 = min(wave * Q, A), q1 = min(q0 + Q, A);
+    int cnt = 0;
+#pragma unroll 4
+    for (int a0 = q0; a0 < q1; a0 += 64) {
+        const int a = a0 + lane;
+        cnt += __popcll(__ballot(a < q1 && ids[a] == e));
     }
-    if (tid == 0) counts[e] = base;
+    if (lane == 0) wsum[wave] = cnt;
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+#pragma unroll 4
+    for (int a0 = q0; a0 < q1; a0 += 64) {
+        const int a = a0 + lane;
+        const bool f = a < q1 && ids[a] == e;
+        const unsigned long long m = __ballot(f);
+        if (f) lists[(size_t)e * T + off + __popcll(m & ((1ull << lane) - 1ull))] = a;
+        off += __popcll(m);
+    }
+    if (tid == 0) counts[e] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __threadfence();
     __syncthreads();
     if (tid == 0) is_last = atomicAdd(&ctrl[CW_BUCKET_ARRIVE], 1u) == (unsigned)(E - 1);
@@ -782,9 +870,13 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
         const int nl = ge * S * ((T + 7) / 8);
         hipLaunchKernelGGL(k_route_logits<8>, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H, m.E,
                            S, part, nl, xq);
-    } else {
+    } else if (T <= MV_MAX_T) {
         const int nl = ge * S * ((T + 31) / 32);
         hipLaunchKernelGGL(k_route_logits<32>, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H,
+                           m.E, S, part, nl, xq);
+    } else {
+        const int nl = ((T + RT_M - 1) / RT_M) * ((m.E + RT_N - 1) / RT_N) * S;
+        hipLaunchKernelGGL(k_route_logits_tiled, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H,
                            m.E, S, part, nl, xq);
     }
     hipError_t e = hipGetLastError();
