@@ -11,9 +11,15 @@ copies of the expert weights and a pool of token batches so that a step cannot
 be served from the 256 MB MALL by an earlier one.
 
 Prints one JSON line: tokens/s (value), the dominant kernel's achieved HBM
-bandwidth against the 8 TB/s peak (roofline, from HIP events recorded on the
-library's stream around that kernel), and the CPU oracle's throughput on a
-bounded sample of the same workload (cpu_baseline).
+bandwidth against the 8 TB/s peak (roofline; the kernel's duration comes from
+two HIP events recorded by that kernel's own dispatch on the library's stream),
+the CPU oracle's throughput on a bounded sample of the same workload
+(cpu_baseline), and, unless --no-prefill, the 2048-token prefill layer with the
+int8 matrix-core utilisation of its grouped gate/up GEMM.
+
+Traffic (roofline.traffic) comes from two rocprofv3 counter runs of this script
+with --calibration-copy (FETCH_SIZE, then WRITE_SIZE), summarised by
+--write-traffic into profiles/traffic_gate_up_<workload>_T<T>.json.
 """
 from __future__ import annotations
 
@@ -28,7 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix peak
 Q8_1_BLOCK = 36
+METRIC = "MoE-layer tokens/s + expert-weight GB/s (% of HBM peak), decode & prefill"
+COPY_BYTES = 256 << 20       # the calibration copy kernel moves this many bytes each way
 
 
 def parse():
@@ -45,6 +54,15 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile-steps", action="store_true",
                    help="also print per-stage milliseconds to stderr")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="end with three copy kernels of 256 MiB each way (x * 1.0 in fp32), "
+                        "the calibration of the HBM byte counters")
+    p.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                        "script with --calibration-copy for --workload/--tokens, print the "
+                        "record that bench.py reads from profiles/ and exit")
     return p.parse_args()
 
 
@@ -114,55 +132,45 @@ def algorithmic_bytes(w, T, n_active):
     return gate_up, layer, n_active * (gu_w + dn_w)
 
 
-def main():
-    a = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if a.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only: the layer is a "
-                          "single-GPU kernel path; see DESIGN.md for how it would shard",
-                          "n_gpus": a.gpus}))
-        sys.exit(2)
-
+def measure(w, T, steps, warmup, pool, copies, profile=False):
+    """Whole-layer steps of workload w at T tokens: wall-clock throughput over
+    `steps` steps, then the same steps with stage events and the gate/up
+    kernel's own dispatch events.  Inputs are resident before timing starts."""
     import numpy as np
     import torch
 
     from quantized_moe_expert_softmax_amd import moe, synth
 
-    w0 = synth.WORKLOADS[a.workload]
-    T = a.tokens or w0.tokens
-    w = synth.Workload(**{**w0.__dict__, "tokens": T})
     dev = torch.device("cuda", 0)
     # keep the token pool within 512 MB of device memory
-    pool = max(2, min(a.pool, (512 << 20) // (T * w.hidden * 4)))
-    a.pool = pool
+    pool = max(2, min(pool, (512 << 20) // (T * w.hidden * 4)))
     t_gen = time.time()
     inp = synth.gen_layer(w)
-    xs = [synth.gen_x(w, batch=b) for b in range(a.pool)]
+    xs = [synth.gen_x(w, batch=b) for b in range(pool)]
     t_gen = time.time() - t_gen
 
     desc = moe.desc_of(w, max_tokens=T)
     layer = moe.MoeLayer(desc, inp, device=0)
-    copies = a.copies or (1 if w.expert_bytes * w.n_experts * T > (1 << 33) else 4)
+    if copies is None:
+        copies = 1 if w.expert_bytes * w.n_experts * T > (1 << 33) else 4
     ex = [layer.experts] + [layer.experts.clone() for _ in range(copies - 1)]
     Ds = [layer.D] + ([layer.D.clone() for _ in range(copies - 1)] if w.latent else [None] * (copies - 1))
     Us = [layer.U] + ([layer.U.clone() for _ in range(copies - 1)] if w.latent else [None] * (copies - 1))
     xd = torch.from_numpy(np.stack(xs)).to(dev)
     out = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
     ws = layer.workspace(T)
-    stream = torch.cuda.current_stream(dev)
-    st = stream.cuda_stream
+    st = torch.cuda.current_stream(dev).cuda_stream
     P = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    base = (layer.handle,)
 
     def args(i):
         c = i % copies
-        return (layer.handle, xd[i % a.pool].data_ptr(), T, layer.router_w.data_ptr(),
+        return (layer.handle, xd[i % pool].data_ptr(), T, layer.router_w.data_ptr(),
                 P(layer.router_b), P(layer.groups), ex[c].data_ptr(), P(Ds[c]), P(Us[c]),
                 w.top_k, out.data_ptr(), ws.data_ptr(), ws.numel(), st)
 
     # distinct experts per batch (for the byte counts), from the routing tap
     n_active = []
-    for b in range(a.pool):
+    for b in range(pool):
         ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
         taps = moe.moe_taps()
         taps.ids = ids.data_ptr()
@@ -170,32 +178,31 @@ def main():
         torch.cuda.synchronize()
         n_active.append(len(np.unique(ids.cpu().numpy())))
     mean_active = float(np.mean(n_active))
-    del base
 
     # timed region: whole-layer steps
-    for i in range(a.warmup):
+    for i in range(warmup):
         moe.moe_layer_forward(*args(i))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
+    for i in range(steps):
         moe.moe_layer_forward(*args(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / a.steps
 
-    # the same steps again with HIP events on the library's stream at stage boundaries
+    # the same steps again with HIP events on the library's stream
     he = HipEvents()
-    evs = [[he.create() for _ in range(moe.MOE_EV_COUNT)] for _ in range(a.steps)]
-    for i in range(a.warmup):
+    evs = [[he.create() for _ in range(moe.MOE_EV_COUNT)] for _ in range(steps)]
+    for i in range(warmup):
         moe.moe_layer_forward(*args(i))
-    for i in range(a.steps):
+    for i in range(steps):
         moe.moe_layer_forward_events(*args(i), evs[i])
     torch.cuda.synchronize()
 
     def stage(i0, i1):
-        return float(np.mean([he.elapsed_ms(evs[s][i0], evs[s][i1]) for s in range(a.steps)]))
+        return float(np.mean([he.elapsed_ms(evs[s][i0], evs[s][i1]) for s in range(steps)]))
 
-    st_ms = {"route": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_ROUTED),
+    st_ms = {"gate_up_kernel": stage(moe.MOE_EV_GATE_UP_KSTART, moe.MOE_EV_GATE_UP_KEND),
+             "route": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_ROUTED),
              "dense_in": stage(moe.MOE_EV_ROUTED, moe.MOE_EV_EXPERT_IN),
              "gate_up": stage(moe.MOE_EV_EXPERT_IN, moe.MOE_EV_GATE_UP),
              "down": stage(moe.MOE_EV_GATE_UP, moe.MOE_EV_DOWN),
@@ -204,12 +211,78 @@ def main():
     for row in evs:
         for e in row:
             he.destroy(e)
-    if a.profile_steps:
-        print(json.dumps({"stage_ms": st_ms}), file=sys.stderr)
+    if profile:
+        print(json.dumps({"workload": w.name, "stage_ms": st_ms}), file=sys.stderr)
+    layer.close()
+    return dict(tokens_s=T * steps / (t1 - t0), ms_step=(t1 - t0) * 1e3 / steps, st_ms=st_ms,
+                mean_active=mean_active, copies=copies, pool=pool, t_gen=t_gen, inp=inp, xs=xs)
 
-    gu_bytes, layer_bytes, expert_bytes = algorithmic_bytes(w, T, mean_active)
-    gu_gbs = gu_bytes / (st_ms["gate_up"] * 1e-3) / 1e9
-    tokens_s = T * a.steps / (t1 - t0)
+
+def gemm_int8_ops(w, T):
+    """int8 multiply-adds (as 2 ops) of the grouped gate/up GEMM: every
+    assignment against 2F rows of Kin."""
+    return 2.0 * T * w.top_k * 2 * w.n_ff * w.k_in
+
+
+def write_traffic(fetch_dir, write_dir):
+    """profiles/traffic_gate_up_<workload>_T<T>.json from two rocprofv3 --pmc runs
+    of this script with --calibration-copy: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the gate/up kernel, scaled by what the same counters read for
+    the plain copy kernel of COPY_BYTES each way."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        acc = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    res = {}
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        acc = per_kernel(d, counter)
+        gu = [v for k, vs in acc.items() if "gate_up" in k or "k_mfma<8, true" in k for v in vs]
+        cp = [v for k, vs in acc.items() if "MulFunctor" in k for v in vs]
+        if not gu or not cp:
+            raise SystemExit(f"{d}: no gate/up or calibration dispatches with {counter}")
+        kib_gu = sum(gu) / len(gu)
+        kib_cp = sum(cp) / len(cp)
+        scale = COPY_BYTES / (kib_cp * 1024.0)
+        res[name] = dict(kib_per_dispatch=kib_gu, copy_kib=kib_cp, scale=scale,
+                         bytes_per_launch=kib_gu * 1024.0 * scale, dispatches=len(gu))
+    res["bytes_per_launch"] = res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]
+    res["src_hash"] = src_hash()
+    return res
+
+
+def main():
+    a = parse()
+    if a.write_traffic:
+        res = write_traffic(*a.write_traffic)
+        print(json.dumps(res))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the layer is a "
+                          "single-GPU kernel path; see DESIGN.md for how it would shard",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from quantized_moe_expert_softmax_amd import synth
+
+    w0 = synth.WORKLOADS[a.workload]
+    T = a.tokens or w0.tokens
+    w = synth.Workload(**{**w0.__dict__, "tokens": T})
+    m = measure(w, T, a.steps, a.warmup, a.pool, a.copies, a.profile_steps)
+    st_ms = m["st_ms"]
+
+    gu_bytes, layer_bytes, expert_bytes = algorithmic_bytes(w, T, m["mean_active"])
+    gu_gbs = gu_bytes / (st_ms["gate_up_kernel"] * 1e-3) / 1e9
 
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_gate_up_{a.workload}_T{T}.json")
@@ -221,31 +294,58 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         import oracle
+        inp, xs, pool = m["inp"], m["xs"], m["pool"]
         ncores = 1
         chunk = min(T, 8)
         t_c0 = time.perf_counter()
         done = 0
         b = 0
         while time.perf_counter() - t_c0 < a.cpu_seconds:
-            toks = list(range((b // a.pool) * chunk % T, (b // a.pool) * chunk % T + chunk))
-            oracle.layer_forward(w, xs[b % a.pool], inp["router_w"], inp["router_b"],
+            first = (b // pool) * chunk % T
+            oracle.layer_forward(w, xs[b % pool], inp["router_w"], inp["router_b"],
                                  inp["groups"], inp["experts"], inp["D"], inp["U"],
-                                 tokens=[t % T for t in toks], nthreads=ncores)
+                                 tokens=[(first + t) % T for t in range(chunk)], nthreads=ncores)
             done += chunk
             b += 1
         el = time.perf_counter() - t_c0
         cpu = {"value": done / el, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
                "sample": f"{done} tokens ({b} calls of {chunk} tokens from the batches of "
                          f"this workload), {el:.1f} s on one host thread"}
+    m.pop("inp"), m.pop("xs")
+
+    prefill = None
+    if not a.no_prefill and a.workload != "prefill":
+        wp = synth.WORKLOADS["prefill"]
+        mp = measure(wp, wp.tokens, a.prefill_steps, 3, 4, 1, a.profile_steps)
+        mp.pop("inp"), mp.pop("xs")
+        ops = gemm_int8_ops(wp, wp.tokens)
+        k_ms = mp["st_ms"]["gate_up_kernel"]
+        gb, _, eb = algorithmic_bytes(wp, wp.tokens, mp["mean_active"])
+        prefill = {"workload": "prefill", "tokens_per_step": wp.tokens,
+                   "tokens_per_s": mp["tokens_s"], "ms_per_step": mp["ms_step"],
+                   "mean_active_experts": mp["mean_active"],
+                   "int8_mfma": {"kernel": "gate_up (grouped int8 GEMM + SwiGLU + Q8_1)",
+                                 "int8_ops_per_launch": ops, "avg_launch_ms": k_ms,
+                                 "achieved": ops / (k_ms * 1e-3) / 1e12, "peak": INT8_PEAK_TOPS,
+                                 "unit": "TOP/s", "frac": ops / (k_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS},
+                   "gate_up_gbs": gb / (k_ms * 1e-3) / 1e9,
+                   "stage_ms": mp["st_ms"]}
+
+    if a.calibration_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
 
     res = {
-        "metric": "MoE-layer tokens/s (decode), expert-weight GB/s as % of HBM peak",
-        "value": tokens_s,
+        "metric": METRIC,
+        "value": m["tokens_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -254,21 +354,21 @@ def main():
         "config": {"workload": a.workload, "hidden": w.hidden, "n_experts": w.n_experts,
                    "top_k": w.top_k, "n_ff": w.n_ff, "latent": w.latent,
                    "expert_fmt": "Q4_0" if w.expert_fmt == synth.Q4_0 else "Q8_0",
-                   "tokens_per_step": T, "weight_copies": copies, "token_batches": a.pool,
-                   "mean_active_experts": mean_active},
+                   "tokens_per_step": T, "weight_copies": m["copies"], "token_batches": m["pool"],
+                   "mean_active_experts": m["mean_active"]},
         "roofline": {"bound": "hbm", "kernel": "gate_up (grouped gate/up + SwiGLU + Q8_1)",
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gu_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": gu_bytes,
-                     "avg_launch_ms": st_ms["gate_up"]},
-        "layer_gbs": layer_bytes / (ms_step * 1e-3) / 1e9,
-        "expert_gbs": expert_bytes / ((st_ms["gate_up"] + st_ms["down"]) * 1e-3) / 1e9,
+                     "avg_launch_ms": st_ms["gate_up_kernel"]},
+        "layer_gbs": layer_bytes / (m["ms_step"] * 1e-3) / 1e9,
+        "expert_gbs": expert_bytes / ((st_ms["gate_up_kernel"] + st_ms["down"]) * 1e-3) / 1e9,
         "stage_ms": st_ms,
+        "prefill": prefill,
         "cpu_baseline": cpu,
-        "input_generation_s": t_gen,
+        "input_generation_s": m["t_gen"],
     }
     print(json.dumps(res))
-    layer.close()
 
 
 if __name__ == "__main__":

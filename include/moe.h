@@ -180,10 +180,14 @@ moe_status moe_layer_forward_taps(const moe_layer* layer, const float* x, int T,
  *   MOE_EV_GATE_UP  after the grouped gate/up + SwiGLU + requantisation
  *   MOE_EV_DOWN     after the grouped down projection and the combine
  *   MOE_EV_END      after the last kernel (latent: after U)
+ *   MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND
+ *                   the start and end of the grouped gate/up kernel itself,
+ *                   recorded by its own dispatch (no event packets around it),
+ *                   so their elapsed time is that kernel's duration
  * The kernels and out are those of moe_layer_forward.
  */
 enum { MOE_EV_BEGIN = 0, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN,
-       MOE_EV_END, MOE_EV_COUNT };
+       MOE_EV_END, MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND, MOE_EV_COUNT };
 
 moe_status moe_layer_forward_events(const moe_layer* layer, const float* x, int T,
                                     const float* router_w, const float* router_b,

@@ -360,12 +360,17 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         }
     }
     EV(MOE_EV_EXPERT_IN);
+    KEvents gev;
+    if (events) {
+        gev.start = (hipEvent_t)events[MOE_EV_GATE_UP_KSTART];
+        gev.stop = (hipEvent_t)events[MOE_EV_GATE_UP_KEND];
+    }
     if (gemm)
-        CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st), "gate/up");
+        CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st, gev), "gate/up");
     else if (m.L)
-        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st), "gate/up");
+        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev), "gate/up");
     else
-        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st), "gate/up");
+        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev), "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs
     if (down_tok) {

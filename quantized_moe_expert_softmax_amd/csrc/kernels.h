@@ -1,5 +1,6 @@
 // Kernel launchers of libmoe (host side of the HIP translation units).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "device.h"
@@ -17,6 +18,21 @@ struct Buckets {
     const int32_t* ids;       // [T][k]
     const float* wts;         // [T][k]
 };
+
+// Events recorded by one kernel's own dispatch (its start and end), for timing
+// that kernel alone; both null = a plain launch.
+struct KEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                     const KEvents& ev, Args... args) {
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
 
 struct Taps {                 // device pointers, NULL = off
     float* h = nullptr;       // [A][F]
@@ -50,7 +66,7 @@ bool mv_config_ok(int K, int fmt, bool gate_up);
 // the kernel (ain_f32, with `keep` receiving the Q8_1 blocks when non-null).
 hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
-                             const Taps& taps, hipStream_t st);
+                             const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{});
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st);
 hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
@@ -64,7 +80,7 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 bool mfma_config_ok(int rows, int K);
 hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
                                const Buckets& b, const int32_t* tile_map, ActPtr hq,
-                               const Taps& taps, hipStream_t st);
+                               const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{});
 hipError_t launch_down_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                             const Buckets& b, const int32_t* tile_map, float* y, const Taps& taps,
                             hipStream_t st);

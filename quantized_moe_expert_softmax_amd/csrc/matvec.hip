@@ -565,17 +565,17 @@ static int gu_waves(int lpr) { return lpr == 8 ? 8 : 4; }
 
 template <int FMT, bool TAP>
 static hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a,
-                              hipStream_t st) {
+                              hipStream_t st, const KEvents& ev) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         constexpr int NW = L == 8 ? 8 : 4;
-        hipLaunchKernelGGL((k_gate_up_mv<FMT, L, C, NW, TAP>), grid, dim3(NW * 64), lds, st, a);
+        launch_k(k_gate_up_mv<FMT, L, C, NW, TAP>, grid, dim3(NW * 64), lds, st, ev, a);
     }));
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
-                             const Taps& taps, hipStream_t st) {
+                             const Taps& taps, hipStream_t st, const KEvents& ev) {
     int lpr, cpl;
     if (!pick_gu(nchunks(m.kin, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (64 % (gu_waves(lpr) * (64 / lpr))) return hipErrorInvalidConfiguration;
@@ -592,10 +592,10 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     dim3 grid(slots * (m.F / QK));
     bool tap = taps.h || taps.isum_gu;
     if (m.fmt == MOE_FMT_Q4_0)
-        return tap ? gate_up_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st)
-                   : gate_up_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st);
-    return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
-               : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
+        return tap ? gate_up_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st, ev);
+    return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
+               : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
 
 template <int FMT, bool TAP>

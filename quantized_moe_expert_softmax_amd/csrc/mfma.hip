@@ -368,27 +368,28 @@ bool mfma_config_ok(int rows, int K) { return rows % MF_NT == 0 && K % (MF_KB * 
 
 
 template <int FMT, bool SWIGLU>
-static hipError_t mfma_launch(const MfArgs& a, bool tap, hipStream_t st) {
+static hipError_t mfma_launch(const MfArgs& a, bool tap, hipStream_t st, const KEvents& ev) {
     long blocks = (long)(a.rows / MF_NT) * a.max_tiles;
     blocks = (blocks + 7) & ~7L;
     if (blocks == 0) return hipSuccess;
     if (tap)
-        hipLaunchKernelGGL((k_mfma<FMT, SWIGLU, true>), dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, a);
+        launch_k(k_mfma<FMT, SWIGLU, true>, dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, ev, a);
     else
-        hipLaunchKernelGGL((k_mfma<FMT, SWIGLU, false>), dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, a);
+        launch_k(k_mfma<FMT, SWIGLU, false>, dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, ev, a);
     return hipGetLastError();
 }
 
 template <bool SWIGLU>
-static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st) {
+static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
+                           const KEvents& ev = KEvents{}) {
     if (!mfma_config_ok(a.rows, a.K)) return hipErrorInvalidConfiguration;
-    if (fmt == MOE_FMT_Q4_0) return mfma_launch<MOE_FMT_Q4_0, SWIGLU>(a, tap, st);
-    return mfma_launch<MOE_FMT_Q8_0, SWIGLU>(a, tap, st);
+    if (fmt == MOE_FMT_Q4_0) return mfma_launch<MOE_FMT_Q4_0, SWIGLU>(a, tap, st, ev);
+    return mfma_launch<MOE_FMT_Q8_0, SWIGLU>(a, tap, st, ev);
 }
 
 hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
                                const Buckets& b, const int32_t* tile_map, ActPtr hq,
-                               const Taps& taps, hipStream_t st) {
+                               const Taps& taps, hipStream_t st, const KEvents& ev) {
     MfArgs a{};
     a.base = experts;
     a.group_stride = m.expert_bytes;
@@ -401,7 +402,7 @@ hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, Act
     a.ain = ain;
     a.F = m.F; a.hq = hq;
     a.tap_h = taps.h; a.tap_isum = taps.isum_gu; a.tap_tokens = taps.tap_tokens; a.tap_div = m.k;
-    return mfma_fmt<true>(m.fmt, a, taps.h || taps.isum_gu, st);
+    return mfma_fmt<true>(m.fmt, a, taps.h || taps.isum_gu, st, ev);
 }
 
 hipError_t launch_down_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr hq,

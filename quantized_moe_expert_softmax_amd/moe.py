@@ -25,8 +25,9 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_
            "moe_pack_host", "moe_unpack_host", "moe_pack", "moe_workspace_bytes",
            "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
            "moe_last_error", "moe_version"]
-MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END = range(6)
-MOE_EV_COUNT = 6
+(MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END,
+ MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND) = range(8)
+MOE_EV_COUNT = 8
 
 
 class MoeError(RuntimeError):
