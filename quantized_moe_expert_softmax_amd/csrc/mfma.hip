@@ -10,20 +10,23 @@
 //     token columns; the block is then scaled by d_w * d_a in fp32 and added to
 //     an fp32 accumulator (the block sums are never merged across blocks);
 //   * the 32 x 32 scale products d_w[row] * d_a[token] of a block come from an
-//     f16 matrix-core outer product (v_mfma_f32_32x32x16_f16 with one non-zero
+//     f16 matrix-core outer product (v_mfma_f32_32x32x8f16 with one non-zero
 //     k), exact in fp32 because two binary16 significands need 22 bits; so the
 //     vector ALU spends one convert and one FMA per block result;
 //   * weights are the row operand, tokens the column operand, so a lane holds
 //     one token and 16 weight rows: the 32 outputs of one Q8_1 block of h sit in
 //     one lane pair, which makes the SwiGLU + requantisation epilogue local;
-//   * a workgroup computes 128 weight rows x 64 tokens, staging 4 blocks of K
-//     at a time in LDS (double-buffered, rows padded by 16 bytes against bank
-//     conflicts); Q4_0 codes are widened to int8 (c - 8) while staged, so the
-//     inner loop is the same for both formats;
+//   * a workgroup computes 128 weight rows x 64 tokens, 4 blocks of K per LDS
+//     stage.  Q8_0 weights stream into a three-stage LDS ring with direct
+//     global->LDS loads (no registers, two stages in flight behind the one in
+//     use; rows XOR-swizzled against bank conflicts).  Q4_0 weights go through
+//     registers into two padded LDS stages, widened to int8 (c - 8) on the way,
+//     so the inner loop is the same for both formats;
 //   * the token tiles of all active experts are numbered by the bucketing
 //     kernel (tile_map); block ids are spread so that one XCD works on
 //     consecutive token tiles of the same weight rows, which then hit its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -31,17 +34,13 @@ namespace moe {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int MF_MT = GEMM_TILE_M;        // token columns per workgroup
 constexpr int MF_NT = 128;                // weight rows per workgroup
 constexpr int MF_KB = 4;                  // blocks of 32 per LDS stage
-constexpr int MF_ROWB = MF_KB * QK + 16;  // LDS bytes per staged row (padded)
 constexpr int MF_THREADS = 256;
-// binary16 scales of a stage: [block][MF_NT + 32] and [block][MF_MT + 32]; the
-// last 32 entries of each row stay zero (the f16 outer product reads them in
-// lanes 32..63)
-constexpr int MF_SWR = MF_NT + 32, MF_SAR = MF_MT + 32;
 
 struct MfArgs {
     const uint8_t* base;          // expert packs (group mode) or the dense matrix
@@ -72,241 +71,137 @@ __device__ __forceinline__ uint32_t q4_widen(uint32_t nib) {
     return v | (neg * 0x1Eu);
 }
 
-template <int FMT, bool SWIGLU, bool TAP>
-__global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
-    constexpr int QB = FMT == MOE_FMT_Q4_0 ? 16 : 32;   // code bytes per block
-    constexpr int WBYTES = MF_NT * MF_ROWB, XBYTES = MF_MT * MF_ROWB;
-    constexpr int STAGE = WBYTES + XBYTES + MF_KB * MF_SWR * 2 + MF_KB * MF_SAR * 2;
-    __shared__ __align__(16) char smem[2 * STAGE];
-    __shared__ int s_row[MF_MT], s_orow[MF_MT];
+// ---------------------------------------------------------------------------
+// Shared pieces of both kernels.
 
-    // block id -> (row tile, token tile); consecutive ids of one XCD share row tiles
+// The workgroup's tile: block id -> (row tile nt, token tile); the rows of its
+// token columns go to s_row (activation rows) and s_orow (output rows).
+// Returns false when the workgroup has no tile.  Consecutive ids of one XCD
+// (ids are dealt to the 8 XCDs round-robin) get consecutive token tiles of the
+// same row tile.
+struct MfTile {
+    const uint8_t* mat;
+    int nt, m0, ncol;
+};
+
+__device__ __forceinline__ bool mf_tile(const MfArgs& A, MfTile& t, int* s_row, int* s_orow) {
     const int nb_all = gridDim.x;
     const int lid = (blockIdx.x & 7) * (nb_all >> 3) + (blockIdx.x >> 3);
-    const int NTI = A.rows / MF_NT;
-    const int nt = lid / A.max_tiles, g = lid - nt * A.max_tiles;
-    if (nt >= NTI) return;
-    const uint8_t* mat;
+    t.nt = lid / A.max_tiles;
+    const int g = lid - t.nt * A.max_tiles;
+    if (t.nt >= A.rows / MF_NT) return false;
     const int32_t* lst = nullptr;
-    int cnt, m0;
+    int cnt;
     if (A.b.ctrl) {
-        if (g >= (int)A.b.ctrl[CW_N_TILES]) return;
+        if (g >= (int)A.b.ctrl[CW_N_TILES]) return false;
         const int tm = A.tile_map[g];
         const int e = tm & 0xffff;
-        m0 = (tm >> 16) * MF_MT;
+        t.m0 = (tm >> 16) * MF_MT;
         cnt = A.b.counts[e];
         lst = A.b.lists + (size_t)e * A.T;
-        mat = A.base + (size_t)e * A.group_stride;
+        t.mat = A.base + (size_t)e * A.group_stride;
     } else {
-        m0 = g * MF_MT;
-        if (m0 >= A.T) return;
+        t.m0 = g * MF_MT;
+        if (t.m0 >= A.T) return false;
         cnt = A.T;
-        mat = A.base;
+        t.mat = A.base;
     }
-    const int ncol = min(MF_MT, cnt - m0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    {
-        // zero tails of the scale rows, both stage buffers
-        const int buf = tid >> 7, kb = (tid >> 5) & 3, z = tid & 31;
-        uint16_t* sdw = reinterpret_cast<uint16_t*>(smem + buf * STAGE + WBYTES + XBYTES);
-        sdw[kb * MF_SWR + MF_NT + z] = 0;
-        sdw[MF_KB * MF_SWR + kb * MF_SAR + MF_MT + z] = 0;
+    t.ncol = min(MF_MT, cnt - t.m0);
+    if ((int)threadIdx.x < MF_MT) {
+        const int c = min((int)threadIdx.x, t.ncol - 1);   // columns past the tokens repeat the last
+        const int o = lst ? lst[t.m0 + c] : t.m0 + c;
+        s_orow[threadIdx.x] = o;
+        s_row[threadIdx.x] = o / A.act_div;
     }
-    if (tid < MF_MT) {
-        const int c = min(tid, ncol - 1);
-        const int o = lst ? lst[m0 + c] : m0 + c;
-        s_orow[tid] = o;
-        s_row[tid] = o / A.act_div;
-    }
-    __syncthreads();
+    return true;
+}
 
-    const int K = A.K, nb = K / QK;
-    const size_t rowb = (size_t)nb * QB;
-    const uint8_t* codes = mat + A.codes_off + (size_t)nt * MF_NT * rowb;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.scales_off) + (size_t)nt * MF_NT * nb;
+// The wave's place in the tile: rows wr*64 + [0,32) (accumulator 0) and
+// + [32,64) (accumulator 1), token columns wc*32 + [0,32).
+struct MfWave {
+    int wr, wc, half, l32;
+};
 
-    // ---- global -> registers -> LDS staging of one stage (blocks kb0 .. kb0+MF_KB)
-    constexpr int WCH = FMT == MOE_FMT_Q4_0 ? 2 : 4;   // 16-byte weight chunks per thread
-    constexpr int WCPR = MF_KB * QB / 16;            // chunks per weight row per stage
-    v4i rw[WCH];
-    v4i rx[2];
-    uint2 rdw;
-    v4i rda;
-    auto gload = [&](int kb0) {
-#pragma unroll
-        for (int j = 0; j < WCH; ++j) {
-            const int ch = tid + j * MF_THREADS;
-            const int r = ch / WCPR, p = ch - r * WCPR;
-            rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * QB + p * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ch = tid + j * MF_THREADS;
-            const int c = ch >> 3, p = ch & 7;
-            rx[j] = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)kb0 * QK + p * 16);
-        }
-        if (tid < MF_NT) {
-            rdw = *reinterpret_cast<const uint2*>(scl + (size_t)tid * nb + kb0);
-        } else if (tid < MF_NT + MF_MT) {
-            const int c = tid - MF_NT;
-            rda = *reinterpret_cast<const v4i*>(A.ain.ds + (size_t)s_row[c] * nb + kb0);
-        }
-    };
-    auto lstore = [&](int buf) {
-        char* st = smem + buf * STAGE;
-        int8_t* sw = reinterpret_cast<int8_t*>(st);
-        int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
-        uint16_t* sdw = reinterpret_cast<uint16_t*>(st + WBYTES + XBYTES);
-        uint16_t* sda = sdw + MF_KB * MF_SWR;
-#pragma unroll
-        for (int j = 0; j < WCH; ++j) {
-            const int ch = tid + j * MF_THREADS;
-            const int r = ch / WCPR, p = ch - r * WCPR;
-            if constexpr (FMT == MOE_FMT_Q4_0) {
-                // one Q4_0 block (16 bytes) -> 32 int8: elements 0..15, then 16..31
-                v4i lo, hi;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t w = (uint32_t)rw[j][d];
-                    lo[d] = (int)q4_widen(w & 0x0F0F0F0Fu);
-                    hi[d] = (int)q4_widen((w >> 4) & 0x0F0F0F0Fu);
-                }
-                *reinterpret_cast<v4i*>(sw + r * MF_ROWB + p * 32) = lo;
-                *reinterpret_cast<v4i*>(sw + r * MF_ROWB + p * 32 + 16) = hi;
-            } else {
-                *reinterpret_cast<v4i*>(sw + r * MF_ROWB + p * 16) = rw[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ch = tid + j * MF_THREADS;
-            const int c = ch >> 3, p = ch & 7;
-            *reinterpret_cast<v4i*>(sx + c * MF_ROWB + p * 16) = rx[j];
-        }
-        if (tid < MF_NT) {
-            sdw[0 * MF_SWR + tid] = (uint16_t)(rdw.x & 0xffffu);
-            sdw[1 * MF_SWR + tid] = (uint16_t)(rdw.x >> 16);
-            sdw[2 * MF_SWR + tid] = (uint16_t)(rdw.y & 0xffffu);
-            sdw[3 * MF_SWR + tid] = (uint16_t)(rdw.y >> 16);
-        } else if (tid < MF_NT + MF_MT) {
-            const int c = tid - MF_NT;
-            const bool ok = c < ncol;      // columns past the tile's tokens get d_a = 0
-#pragma unroll
-            for (int q = 0; q < MF_KB; ++q)
-                sda[q * MF_SAR + c] = ok ? (uint16_t)((uint32_t)rda[q] & 0xffffu) : (uint16_t)0;
-        }
-    };
+// One stage (MF_KB blocks) of a wave: frag(kb, a0, a1, bx) fetches the code
+// operands of block kb, sfrag(kb, d0, d1, dc) the binary16 scale operands
+// (row / column l32's d at k = 0 in lanes 0..31, zero elsewhere; a zero-
+// extended 16-bit load gives the first register, the second is zero).  Block
+// kb+1's products are issued before block kb is rescaled.
+__device__ __forceinline__ h4 scale_op(uint32_t d16) { return __builtin_bit_cast(h4, v2i{(int)d16, 0}); }
 
-    // ---- the wave's tile: rows wr*64 + [0,32) and + [32,64), token columns wc*32 + [0,32)
-    const int wr = wave & 1, wc = wave >> 1;
-    const int half = lane >> 5, l32 = lane & 31;
-    // scale entries of this lane (the zero tails in lanes 32..63)
-    const int o_w0 = half ? MF_NT + l32 : wr * 64 + l32;
-    const int o_w1 = half ? MF_NT + l32 : wr * 64 + 32 + l32;
-    const int o_a = half ? MF_MT + l32 : wc * 32 + l32;
-    // a wave whose 32 token columns are all past the tile's tokens only stages
-    const bool busy = wc * 32 < ncol;
-    float acc0[16], acc1[16];
+template <bool SWIGLU, bool TAP, class Frag, class SFrag>
+__device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const MfWave& w, int s,
+                                         const int* s_orow, Frag frag, SFrag sfrag,
+                                         float (&acc0)[16], float (&acc1)[16]) {
+    v4i a0, a1, bx;
+    h4 d0, d1, dc;
+    frag(0, a0, a1, bx);
+    sfrag(0, d0, d1, dc);
+    v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
+    v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
+    v16f s0 = __builtin_amdgcn_mfma_f32_32x32x8f16(d0, dc, v16f{}, 0, 0, 0);
+    v16f s1 = __builtin_amdgcn_mfma_f32_32x32x8f16(d1, dc, v16f{}, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
-
-    const int stages = nb / MF_KB;
-    auto compute = [&](int buf, int s) {
-        if (!busy) return;
-        const char* st = smem + buf * STAGE;
-        const int8_t* sw = reinterpret_cast<const int8_t*>(st);
-        const int8_t* sx = reinterpret_cast<const int8_t*>(st + WBYTES);
-        const uint16_t* sdw = reinterpret_cast<const uint16_t*>(st + WBYTES + XBYTES);
-        const uint16_t* sda = sdw + MF_KB * MF_SWR;
-        // block kb's products are issued one block ahead of their rescale
-        auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
-            a0 = *reinterpret_cast<const v4i*>(sw + (wr * 64 + l32) * MF_ROWB + kb * QK + half * 16);
-            a1 = *reinterpret_cast<const v4i*>(sw + (wr * 64 + 32 + l32) * MF_ROWB + kb * QK + half * 16);
-            bx = *reinterpret_cast<const v4i*>(sx + (wc * 32 + l32) * MF_ROWB + kb * QK + half * 16);
-        };
-        // scale operands: lanes 0..31 give row / column l32 its binary16 d at k = 0
-        auto sfrag = [&](int kb, h8& d0, h8& d1, h8& dc) {
-            const v4i w0 = {(int)sdw[kb * MF_SWR + o_w0], 0, 0, 0};
-            const v4i w1 = {(int)sdw[kb * MF_SWR + o_w1], 0, 0, 0};
-            const v4i c0 = {(int)sda[kb * MF_SAR + o_a], 0, 0, 0};
-            d0 = __builtin_bit_cast(h8, w0);
-            d1 = __builtin_bit_cast(h8, w1);
-            dc = __builtin_bit_cast(h8, c0);
-        };
-        v4i a0, a1, bx;
-        h8 d0, d1, dc;
-        frag(0, a0, a1, bx);
-        sfrag(0, d0, d1, dc);
-        v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
-        v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
-        v16f s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d0, dc, v16f{}, 0, 0, 0);
-        v16f s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d1, dc, v16f{}, 0, 0, 0);
+    for (int kb = 0; kb < MF_KB; ++kb) {
+        v16i n0, n1;
+        v16f t0, t1;
+        if (kb + 1 < MF_KB) {
+            frag(kb + 1, a0, a1, bx);
+            sfrag(kb + 1, d0, d1, dc);
+            n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
+            n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
+            t0 = __builtin_amdgcn_mfma_f32_32x32x8f16(d0, dc, v16f{}, 0, 0, 0);
+            t1 = __builtin_amdgcn_mfma_f32_32x32x8f16(d1, dc, v16f{}, 0, 0, 0);
+        }
 #pragma unroll
-        for (int kb = 0; kb < MF_KB; ++kb) {
-            v16i n0, n1;
-            v16f t0, t1;
-            if (kb + 1 < MF_KB) {
-                frag(kb + 1, a0, a1, bx);
-                sfrag(kb + 1, d0, d1, dc);
-                n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
-                n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
-                t0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d0, dc, v16f{}, 0, 0, 0);
-                t1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(d1, dc, v16f{}, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                acc0[i] = fmaf((float)i0[i], s0[i], acc0[i]);
-                acc1[i] = fmaf((float)i1[i], s1[i], acc1[i]);
-            }
-            if constexpr (TAP) {
-                const int c = wc * 32 + l32;
-                const int o = s_orow[c];
-                if (A.tap_isum && c < ncol && o / A.tap_div < A.tap_tokens) {
-                    const int blk = s * MF_KB + kb;
-                    for (int i = 0; i < 16; ++i) {
-                        for (int t = 0; t < 2; ++t) {
-                            const int pr = nt * MF_NT + wr * 64 + t * 32 + mf_row_of(i, half);
-                            // canonical row: gate/up rows are stored as 32 gate + 32 up per slab
-                            const int cr = SWIGLU ? ((pr & 63) < 32 ? (pr >> 6) * 32 + (pr & 31)
-                                                                    : A.F + (pr >> 6) * 32 + (pr & 31))
-                                                  : pr;
-                            A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = t ? i1[i] : i0[i];
-                        }
+        for (int i = 0; i < 16; ++i) {
+            acc0[i] = fmaf((float)i0[i], s0[i], acc0[i]);
+            acc1[i] = fmaf((float)i1[i], s1[i], acc1[i]);
+        }
+        if constexpr (TAP) {
+            const int c = w.wc * 32 + w.l32;
+            const int o = s_orow[c];
+            if (A.tap_isum && c < t.ncol && o / A.tap_div < A.tap_tokens) {
+                const int nb = A.K / QK;
+                const int blk = s * MF_KB + kb;
+                for (int i = 0; i < 16; ++i) {
+                    for (int q = 0; q < 2; ++q) {
+                        const int pr = t.nt * MF_NT + w.wr * 64 + q * 32 + mf_row_of(i, w.half);
+                        // canonical row: gate/up rows are stored as 32 gate + 32 up per slab
+                        const int cr = SWIGLU ? ((pr & 63) < 32 ? (pr >> 6) * 32 + (pr & 31)
+                                                                : A.F + (pr >> 6) * 32 + (pr & 31))
+                                              : pr;
+                        A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = q ? i1[i] : i0[i];
                     }
                 }
             }
-            if (kb + 1 < MF_KB) {
-                i0 = n0;
-                i1 = n1;
-                s0 = t0;
-                s1 = t1;
-            }
-            // the block's rescale happens here, not sunk past later stores
-#pragma unroll
-            for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(acc0[i]), "+v"(acc1[i]));
-            // keep the two-deep pipeline: no hoisting of later blocks' reads
-            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    gload(0);
-    lstore(0);
-    __syncthreads();
-#pragma unroll 1
-    for (int s = 0; s + 1 < stages; ++s) {
-        gload((s + 1) * MF_KB);
-        compute(s & 1, s);
-        lstore((s + 1) & 1);
-        __syncthreads();
+        if (kb + 1 < MF_KB) {
+            i0 = n0;
+            i1 = n1;
+            s0 = t0;
+            s1 = t1;
+        }
+        // the block's rescale happens here, not sunk past later stores
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(acc0[i]), "+v"(acc1[i]));
+        // keep the two-deep pipeline: no hoisting of later blocks' reads
+        __builtin_amdgcn_sched_barrier(0);
     }
-    compute((stages - 1) & 1, stages - 1);
+}
 
-    // ---- epilogue
-    const int c = wc * 32 + l32;
-    const bool valid = c < ncol;
+// Epilogue: SwiGLU + Q8_1 of h (gate/up), or the fp32 rows (down, dense).
+template <bool SWIGLU, bool TAP>
+__device__ __forceinline__ void mf_epilogue(const MfArgs& A, const MfTile& t, const MfWave& w,
+                                            const int* s_orow, const float (&acc0)[16],
+                                            const float (&acc1)[16]) {
+    const int c = w.wc * 32 + w.l32;
+    const bool valid = c < t.ncol;
     const int o = s_orow[c];
+    const int half = w.half;
     if constexpr (SWIGLU) {
         // rows wr*64 + [0,32) are gate rows f, + [32,64) the up rows of the same f
-        const int fb = nt * 2 + wr;     // Q8_1 block of h along F
+        const int fb = t.nt * 2 + w.wr;     // Q8_1 block of h along F
         float h[16];
         float amax = 0.0f;
 #pragma unroll
@@ -351,7 +246,7 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
         }
     } else {
         if (valid) {
-            float* orow = A.out + (size_t)o * A.rows + nt * MF_NT + wr * 64 + half * 4;
+            float* orow = A.out + (size_t)o * A.rows + t.nt * MF_NT + w.wr * 64 + half * 4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<float4*>(orow + q * 8) =
@@ -364,27 +259,331 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma(MfArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-bool mfma_config_ok(int rows, int K) { return rows % MF_NT == 0 && K % (MF_KB * QK) == 0; }
+// Q8_0: three-stage LDS ring filled by direct global->LDS loads.
+//
+// Stage layout (bytes): codes W [128 rows][128] at 0, codes X [64 tokens][128]
+// at 16384, d_w [128 rows][4 x binary16] at 24576, d_a [64 tokens][4 x u32
+// (d16 | s16 << 16)] at 25600.  A load instruction writes 64 lanes x 16 bytes
+// (x 4 bytes for d_w) contiguously, so the code rows cannot be padded; the
+// 16-byte chunk c of row r sits in slot c ^ mf_swz(r) instead.  mf_swz gives
+// distinct slots to rows 0..7 (and 8..15), and to the even and the odd rows of
+// 0..15, so the fragment reads (16 lanes = rows r..r+15 of one chunk) hit
+// distinct banks with either 32 or 64 LDS banks.
+constexpr int MD_W = 0, MD_X = MF_NT * 128, MD_DW = MD_X + MF_MT * 128, MD_DA = MD_DW + MF_NT * 8;
+constexpr int MD_STAGE = MD_DA + MF_MT * 16;   // 26624
+constexpr int MD_NS = 3;                       // stages in the ring
 
+__device__ __forceinline__ int mf_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int FMT, bool SWIGLU>
-static hipError_t mfma_launch(const MfArgs& a, bool tap, hipStream_t st, const KEvents& ev) {
-    long blocks = (long)(a.rows / MF_NT) * a.max_tiles;
-    blocks = (blocks + 7) & ~7L;
-    if (blocks == 0) return hipSuccess;
-    if (tap)
-        launch_k(k_mfma<FMT, SWIGLU, true>, dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, ev, a);
-    else
-        launch_k(k_mfma<FMT, SWIGLU, false>, dim3((unsigned)blocks), dim3(MF_THREADS), 0, st, ev, a);
-    return hipGetLastError();
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Direct global->LDS loads: lane i writes its 16 (4) bytes at LDS address
+// lds + 16 i (4 i).  Issued from asm so that the compiler does not add its own
+// wait for all such loads before every later LDS read (it cannot tell the
+// ring's stages apart); the kernel's wait_stage() is the only wait.  The loads
+// write no registers: the address registers are read when the load issues.
+__device__ __forceinline__ uint32_t lds_addr(const char* l) {
+    return (uint32_t)(uintptr_t)(const lds_char*)l;
 }
+// reads at an LDS byte address
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ v4i lds_ld16(uint32_t a) { return *(const lds_v4i*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t lds_ldu16(uint32_t a) { return *(const lds_u16*)(uintptr_t)a; }
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <bool SWIGLU, bool TAP>
+__global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_dma(MfArgs A) {
+    __shared__ __align__(16) char ring[MD_NS * MD_STAGE];
+    __shared__ __align__(16) char zero16[16];
+    __shared__ int s_row[MF_MT], s_orow[MF_MT];
+
+    MfTile t;
+    if (!mf_tile(A, t, s_row, s_orow)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
+    __syncthreads();
+
+    const int K = A.K, nb = K / QK;
+    const size_t rowb = (size_t)nb * 32;
+    const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
+    const uint8_t* scl = t.mat + A.scales_off + (size_t)t.nt * MF_NT * nb * 2;
+
+    // this wave's loads of a stage, as per-lane sources at stage 0 (a stage
+    // advances codes by 128 bytes, d_w by 8 and d_a by 16):
+    //   codes W: instructions 4*wave .. 4*wave+3, rows 8i + lane/8, chunk (lane%8) ^ swz
+    //   codes X: instructions 2*wave, 2*wave+1, token rows 8i + lane/8
+    //   d_w:     instruction wave, rows 32*wave + lane/2, 4 bytes (lane%2)
+    //   d_a:     wave 0, token lane, 16 bytes
+    const uint8_t* srcW[4];
+    const int8_t* srcX[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (4 * wave + j) + (lane >> 3);
+        const int c = (lane & 7) ^ mf_swz(r);
+        srcW[j] = codes + (size_t)r * rowb + c * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = 8 * (2 * wave + j) + (lane >> 3);
+        const int c = (lane & 7) ^ mf_swz(r);
+        srcX[j] = A.ain.q + (size_t)s_row[r] * K + c * 16;
+    }
+    const uint8_t* srcDW = scl + ((size_t)(32 * wave + (lane >> 1)) * nb) * 2 + (lane & 1) * 4;
+    const uint32_t* srcDA = A.ain.ds + (size_t)s_row[lane] * nb;
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int s) {
+        const uint32_t st = ring0 + (uint32_t)(s % MD_NS) * MD_STAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(srcW[j] + s * 128, st + MD_W + (4 * wv + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(srcX[j] + s * 128, st + MD_X + (2 * wv + j) * 1024);
+        dma4(srcDW + s * 8, st + MD_DW + wv * 256);
+        if (wv == 0) dma16(srcDA + s * MF_KB, st + MD_DA);
+    };
+    // wait until this wave's loads of the stage about to be used have landed
+    // (at most one later stage of loads may stay in flight), then a barrier so
+    // that every wave's loads have, and every wave is done with the buffer the
+    // next loads refill: a wave issues 8 (wave 0) or 7 loads per stage.  The
+    // tapped kernel also stores inside the loop, so it drains every time.
+    auto wait_stage = [&](bool later) {
+        if (TAP || !later) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else if (wave == 0) {
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    };
+
+    MfWave w{wave & 1, wave >> 1, lane >> 5, lane & 31};
+    const bool busy = w.wc * 32 < t.ncol;   // a wave past the tile's tokens only loads
+    // chunk c = 2kb + half of row r sits in slot c ^ swz(r): byte offset
+    // (2kb * 16) ^ ((half ^ swz(r)) * 16) within the row
+    const int ra = w.wr * 64 + w.l32, rb = w.wc * 32 + w.l32;
+    const int fa = (w.half ^ mf_swz(ra)) * 16, fbx = (w.half ^ mf_swz(rb)) * 16;
+    int offA[MF_KB], offB[MF_KB];
+#pragma unroll
+    for (int kb = 0; kb < MF_KB; ++kb) {
+        offA[kb] = lds_addr(ring) + MD_W + ra * 128 + ((kb * 32) ^ fa);
+        offB[kb] = lds_addr(ring) + MD_X + rb * 128 + ((kb * 32) ^ fbx);
+    }
+    // scale entries: lanes 32..63 read zeros
+    const uint32_t oW0 = w.half ? lds_addr(zero16) : lds_addr(ring) + MD_DW + ra * 8;
+    const uint32_t oW1 = w.half ? lds_addr(zero16) : lds_addr(ring) + MD_DW + (ra + 32) * 8;
+    const uint32_t oDA = w.half ? lds_addr(zero16) : lds_addr(ring) + MD_DA + rb * 16;
+    const int kw2 = w.half ? 0 : 2, kw4 = w.half ? 0 : 4;   // per-block steps of those entries
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+
+    // stage s of the ring buffer B (= s % MD_NS, a constant in each copy)
+    auto stage = [&](int s, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        const int stages = nb / MF_KB;
+        wait_stage(s + 1 < stages);
+        if (s + 2 < stages) issue(s + 2);
+        if (!busy) return;
+        const uint32_t sb = (uint32_t)B * MD_STAGE;                     // buffer base
+        const uint32_t sbz = w.half ? 0u : sb;                          // zero entries stay put
+        auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
+            a0 = lds_ld16(offA[kb] + sb);
+            a1 = lds_ld16(offA[kb] + sb + 32 * 128);
+            bx = lds_ld16(offB[kb] + sb);
+        };
+        auto sfrag = [&](int kb, h4& d0, h4& d1, h4& dc) {
+            d0 = scale_op(lds_ldu16(oW0 + sbz + kb * kw2));
+            d1 = scale_op(lds_ldu16(oW1 + sbz + kb * kw2));
+            dc = scale_op(lds_ldu16(oDA + sbz + kb * kw4));
+        };
+        mf_stage<SWIGLU, TAP>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+    };
+
+    const int stages = nb / MF_KB;
+    issue(0);
+    if (stages > 1) issue(1);
+    for (int s = 0; s < stages; s += MD_NS) {
+        stage(s, std::integral_constant<int, 0>{});
+        if (s + 1 < stages) stage(s + 1, std::integral_constant<int, 1>{});
+        if (s + 2 < stages) stage(s + 2, std::integral_constant<int, 2>{});
+    }
+    mf_epilogue<SWIGLU, TAP>(A, t, w, s_orow, acc0, acc1);
+}
+
+// ---------------------------------------------------------------------------
+// Q4_0: two padded LDS stages filled through registers, codes widened to int8.
+constexpr int MS_ROWB = MF_KB * QK + 16;  // LDS bytes per staged row (padded)
+// binary16 scales of a stage: [block][MF_NT + 32] and [block][MF_MT + 32]; the
+// last 32 entries of each row stay zero (the f16 outer product reads them in
+// lanes 32..63)
+constexpr int MS_SWR = MF_NT + 32, MS_SAR = MF_MT + 32;
+
+template <bool SWIGLU, bool TAP>
+__global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
+    constexpr int QB = 16;                                // code bytes per Q4_0 block
+    constexpr int WBYTES = MF_NT * MS_ROWB, XBYTES = MF_MT * MS_ROWB;
+    constexpr int STAGE = WBYTES + XBYTES + MF_KB * MS_SWR * 2 + MF_KB * MS_SAR * 2;
+    __shared__ __align__(16) char smem[2 * STAGE];
+    __shared__ int s_row[MF_MT], s_orow[MF_MT];
+
+    MfTile t;
+    if (!mf_tile(A, t, s_row, s_orow)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    {
+        // zero tails of the scale rows, both stage buffers
+        const int buf = tid >> 7, kb = (tid >> 5) & 3, z = tid & 31;
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(smem + buf * STAGE + WBYTES + XBYTES);
+        sdw[kb * MS_SWR + MF_NT + z] = 0;
+        sdw[MF_KB * MS_SWR + kb * MS_SAR + MF_MT + z] = 0;
+    }
+    __syncthreads();
+
+    const int K = A.K, nb = K / QK;
+    const size_t rowb = (size_t)nb * QB;
+    const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
+    const uint16_t* scl = reinterpret_cast<const uint16_t*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
+
+    // ---- global -> registers -> LDS staging of one stage (blocks kb0 .. kb0+MF_KB)
+    constexpr int WCH = 2;                     // 16-byte chunks (= Q4_0 blocks) per thread
+    constexpr int WCPR = MF_KB * QB / 16;      // chunks per weight row per stage
+    v4i rw[WCH];
+    v4i rx[2];
+    uint2 rdw;
+    v4i rda;
+    auto gload = [&](int kb0) {
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int r = ch / WCPR, p = ch - r * WCPR;
+            rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * QB + p * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int c = ch >> 3, p = ch & 7;
+            rx[j] = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)kb0 * QK + p * 16);
+        }
+        if (tid < MF_NT) {
+            rdw = *reinterpret_cast<const uint2*>(scl + (size_t)tid * nb + kb0);
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+            rda = *reinterpret_cast<const v4i*>(A.ain.ds + (size_t)s_row[c] * nb + kb0);
+        }
+    };
+    auto lstore = [&](int buf) {
+        char* st = smem + buf * STAGE;
+        int8_t* sw = reinterpret_cast<int8_t*>(st);
+        int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(st + WBYTES + XBYTES);
+        uint16_t* sda = sdw + MF_KB * MS_SWR;
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int r = ch / WCPR, p = ch - r * WCPR;
+            // one Q4_0 block (16 bytes) -> 32 int8: elements 0..15, then 16..31
+            v4i lo, hi;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t x = (uint32_t)rw[j][d];
+                lo[d] = (int)q4_widen(x & 0x0F0F0F0Fu);
+                hi[d] = (int)q4_widen((x >> 4) & 0x0F0F0F0Fu);
+            }
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32) = lo;
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32 + 16) = hi;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int c = ch >> 3, p = ch & 7;
+            *reinterpret_cast<v4i*>(sx + c * MS_ROWB + p * 16) = rx[j];
+        }
+        if (tid < MF_NT) {
+            sdw[0 * MS_SWR + tid] = (uint16_t)(rdw.x & 0xffffu);
+            sdw[1 * MS_SWR + tid] = (uint16_t)(rdw.x >> 16);
+            sdw[2 * MS_SWR + tid] = (uint16_t)(rdw.y & 0xffffu);
+            sdw[3 * MS_SWR + tid] = (uint16_t)(rdw.y >> 16);
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+#pragma unroll
+            for (int q = 0; q < MF_KB; ++q) sda[q * MS_SAR + c] = (uint16_t)((uint32_t)rda[q] & 0xffffu);
+        }
+    };
+
+    MfWave w{wave & 1, wave >> 1, lane >> 5, lane & 31};
+    // scale entries of this lane (the zero tails in lanes 32..63)
+    const int o_w0 = w.half ? MF_NT + w.l32 : w.wr * 64 + w.l32;
+    const int o_w1 = w.half ? MF_NT + w.l32 : w.wr * 64 + 32 + w.l32;
+    const int o_a = w.half ? MF_MT + w.l32 : w.wc * 32 + w.l32;
+    const bool busy = w.wc * 32 < t.ncol;   // a wave past the tile's tokens only stages
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+
+    const int stages = nb / MF_KB;
+    auto compute = [&](int buf, int s) {
+        if (!busy) return;
+        const char* st = smem + buf * STAGE;
+        const int8_t* sw = reinterpret_cast<const int8_t*>(st);
+        const int8_t* sx = reinterpret_cast<const int8_t*>(st + WBYTES);
+        const uint16_t* sdw = reinterpret_cast<const uint16_t*>(st + WBYTES + XBYTES);
+        const uint16_t* sda = sdw + MF_KB * MS_SWR;
+        auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
+            a0 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            a1 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            bx = *reinterpret_cast<const v4i*>(sx + (w.wc * 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+        };
+        auto sfrag = [&](int kb, h4& d0, h4& d1, h4& dc) {
+            d0 = scale_op(sdw[kb * MS_SWR + o_w0]);
+            d1 = scale_op(sdw[kb * MS_SWR + o_w1]);
+            dc = scale_op(sda[kb * MS_SAR + o_a]);
+        };
+        mf_stage<SWIGLU, TAP>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+    };
+    gload(0);
+    lstore(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s + 1 < stages; ++s) {
+        gload((s + 1) * MF_KB);
+        compute(s & 1, s);
+        lstore((s + 1) & 1);
+        __syncthreads();
+    }
+    compute((stages - 1) & 1, stages - 1);
+    mf_epilogue<SWIGLU, TAP>(A, t, w, s_orow, acc0, acc1);
+}
+
+// ---------------------------------------------------------------------------
+bool mfma_config_ok(int rows, int K) { return rows % MF_NT == 0 && K % (MF_KB * QK) == 0; }
 
 template <bool SWIGLU>
 static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
                            const KEvents& ev = KEvents{}) {
     if (!mfma_config_ok(a.rows, a.K)) return hipErrorInvalidConfiguration;
-    if (fmt == MOE_FMT_Q4_0) return mfma_launch<MOE_FMT_Q4_0, SWIGLU>(a, tap, st, ev);
-    return mfma_launch<MOE_FMT_Q8_0, SWIGLU>(a, tap, st, ev);
+    long blocks = (long)(a.rows / MF_NT) * a.max_tiles;
+    blocks = (blocks + 7) & ~7L;
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(MF_THREADS);
+    if (fmt == MOE_FMT_Q4_0) {
+        if (tap)
+            launch_k(k_mfma_q4<SWIGLU, true>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_q4<SWIGLU, false>, grid, block, 0, st, ev, a);
+    } else {
+        if (tap)
+            launch_k(k_mfma_dma<SWIGLU, true>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_dma<SWIGLU, false>, grid, block, 0, st, ev, a);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
