@@ -576,9 +576,10 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
                                                              int32_t* __restrict__ lists,
                                                              uint32_t* __restrict__ ctrl,
                                                              int32_t* __restrict__ active) {
-    __shared__ double s_l[DECODE_T * 512];
+    // logits live as ordered keys (dkey of l + 0.0: -0 and +0 compare equal as
+    // doubles and get one key); dkey_inv gives the logit back for the softmax
+    __shared__ unsigned long long s_key[DECODE_T * 512];
     __shared__ unsigned long long s_gkey[DECODE_T][64];
-    __shared__ unsigned char s_allow[DECODE_T * 512];
     __shared__ unsigned char s_gsel[DECODE_T][64];
     __shared__ int s_nallow[DECODE_T];
     __shared__ int s_sel[DECODE_T][32];
@@ -590,12 +591,11 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int TE = T * E;
     for (int i = tid; i < TE; i += SEL_NT) {
-        const int t = i / E, e = i - t * E;
+        const int e = i % E;
         double v = A.part[i];
         if (A.bias) v += (double)A.bias[e];
-        s_l[i] = v;
+        s_key[i] = dkey(v + 0.0);
         if (A.logits_tap) A.logits_tap[i] = v;
-        s_allow[i] = 1;
     }
     for (int i = tid; i < E; i += SEL_NT) {
         s_cnt[i] = 0;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
         for (int i = tid; i < TE; i += SEL_NT) {
             const int t = i / E, e = i - t * E;
             const unsigned gl = (unsigned)A.groups[e];
-            if (gl < (unsigned)G) atomicMax(&s_gkey[t][gl], dkey(s_l[i] + 0.0));   // -0 -> +0
+            if (gl < (unsigned)G) atomicMax(&s_gkey[t][gl], s_key[i]);
         }
         __syncthreads();
         // group rank among the token's groups (key desc, group asc); keep rank < TG
@@ -620,24 +620,37 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
             int r = 0;
             for (int h = 0; h < G; ++h) {
                 const unsigned long long kh = s_gkey[t][h];
-                r += (kh > kg) || (kh == kg && h < g);
+                r += (int)(kh > kg) | ((int)(kh == kg) & (int)(h < g));
             }
             s_gsel[t][g] = r < A.TG;
         }
         __syncthreads();
-        // allowed experts, counted per token with LDS atomics
+        // allowed experts per token: one LDS atomic per wave and token run
+        for (int b0 = 0; b0 < TE; b0 += SEL_NT) {
+            const int i = b0 + tid;
+            int t = -1;
+            bool al = false;
+            if (i < TE) {
+                t = i / E;
+                const unsigned gl = (unsigned)A.groups[i - t * E];
+                al = gl < (unsigned)G && s_gsel[t][gl];
+            }
+            if (al) atomicAdd(&s_nallow[t], 1);
+        }
+        __syncthreads();
+        // an excluded expert gets key 0: below every logit's key, so it never
+        // beats another and is never chosen; a token with fewer than k allowed
+        // experts (labels that break the equal-size-groups contract) keeps all
         for (int i = tid; i < TE; i += SEL_NT) {
             const int t = i / E;
             const unsigned gl = (unsigned)A.groups[i - t * E];
             const bool al = gl < (unsigned)G && s_gsel[t][gl];
-            s_allow[i] = al;
-            if (al) atomicAdd(&s_nallow[t], 1);
+            if (!al && s_nallow[t] >= k) s_key[i] = 0ull;
         }
         __syncthreads();
     }
-    // exact ranks, P lanes per (token, expert) pair each scanning E/P rivals; a
-    // token with fewer than k allowed experts (labels that break the
-    // equal-size-groups contract) ranks every expert instead
+    // exact ranks: P lanes per (token, expert) pair each count the rivals
+    // (key desc, id asc) among E/P of them, eight loads at a time, no branches
     int P = 1;
     while (P < 64 && TE * P * 2 <= SEL_NT) P *= 2;
     const int lp = 31 - __clz(P);
@@ -645,20 +658,24 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
         const int gi = b0 + tid;
         const int i = gi >> lp, part = gi & (P - 1);
         int r = 0, t = 0, e = 0;
-        bool cand = false;
+        unsigned long long ke = 0ull;
         if (i < TE) {
             t = i / E;
             e = i - t * E;
-            const double* lt = s_l + t * E;
-            const unsigned char* at = s_allow + t * E;
-            const bool all = G == 0 || s_nallow[t] < k;
-            cand = all || at[e];
-            if (cand) {
-                const double le = lt[e];
-#pragma unroll 4
-                for (int h = part; h < E; h += P) {
-                    const double lh = lt[h];
-                    r += (all || at[h]) && ((lh > le) || (lh == le && h < e));
+            ke = s_key[i];
+        }
+        const bool cand = ke != 0ull;
+        if (cand) {
+            constexpr int U = 8;
+            const unsigned long long* kt = s_key + t * E;
+            for (int h0 = part; h0 < E; h0 += U * P) {
+                unsigned long long kh[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) kh[u] = kt[min(h0 + u * P, E - 1)];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int h = h0 + u * P;
+                    r += (int)(h < E) & ((int)(kh[u] > ke) | ((int)(kh[u] == ke) & (int)(h < e)));
                 }
             }
         }
@@ -669,7 +686,7 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
     // softmax over the chosen logits, rank order, fp64
     for (int i = tid; i < T * k; i += SEL_NT) {
         const int t = i / k, j = i - t * k;
-        s_ex[t][j] = exp(s_l[t * E + s_sel[t][j]] - s_l[t * E + s_sel[t][0]]);
+        s_ex[t][j] = exp(dkey_inv(s_key[t * E + s_sel[t][j]]) - dkey_inv(s_key[t * E + s_sel[t][0]]));
     }
     __syncthreads();
     for (int i = tid; i < T * k; i += SEL_NT) {
