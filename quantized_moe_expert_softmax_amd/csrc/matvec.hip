@@ -355,6 +355,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
     int32_t* s_s = reinterpret_cast<int32_t*>(smem + stage_bytes(TCH, K));
 
+    // the first pass of weights is requested before the activations are staged
+    v4i wA[CPL];
+    uint32_t sA[CPL];
+    {
+        constexpr int RPW = 64 / LPR;
+        const int lane = threadIdx.x & 63;
+        const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, lane % LPR,
+                                nb * Fmt<FMT>::CPB, wA, sA);
+    }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
         const int n = min(TCH, cnt - i0);
         if (threadIdx.x < n) s_s[threadIdx.x] = lst ? lst[i0 + threadIdx.x] : i0 + threadIdx.x;
@@ -370,10 +380,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
             if (s_s[i] / A.tap_div < A.tap_tokens)
                 A.isum_tap[((size_t)s_s[i] * A.rows + r0 + r) * nb + blk] = v;
         };
-        v4i wA[CPL];
-        uint32_t sA[CPL];
         row_tile<FMT, LPR, CPL, NW, TAP>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d, s_sq, emit,
-                                         emit_isum, TAP && A.isum_tap, wA, sA, false);
+                                         emit_isum, TAP && A.isum_tap, wA, sA, i0 == 0);
         __syncthreads();
     }
 }
