@@ -120,6 +120,67 @@ def test_latent_gemm_sampled(name, T):
     _report(name, T, rep)
 
 
+# path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
+# and the largest routing sizes the ABI accepts
+@pytest.mark.parametrize("kw", [
+    dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=8),
+    dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=9),
+    dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=32),
+    dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=33),
+    dict(hidden=256, n_ff=256, n_experts=512, top_k=32, n_groups=64, topk_groups=8, tokens=1),
+    dict(hidden=256, n_ff=256, n_experts=512, top_k=32, n_groups=64, topk_groups=8, tokens=6),
+    dict(hidden=256, n_ff=256, n_experts=512, top_k=32, tokens=33),
+    dict(hidden=8192, n_ff=256, n_experts=2, top_k=1, tokens=1),
+    dict(hidden=8192, n_ff=256, n_experts=2, top_k=1, tokens=40),
+])
+def test_boundaries_and_maximum_sizes(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 2))
+    _report("edge " + str(kw), w.tokens, rep)
+
+
+def _exact_ids(w, inp, T):
+    """GPU ids and the oracle's ids for every token (no near-tie exclusion)."""
+    import oracle
+    layer = gh.gpu_layer(w, inp, T)
+    g = gh.run_taps(layer, w, inp["x"], 0)
+    layer.close()
+    _, rt = oracle.layer_forward(w, inp["x"], inp["router_w"], inp["router_b"], inp["groups"],
+                                 inp["experts"], inp["D"], inp["U"], taps=("ids", "weights"))
+    return g, rt
+
+
+@pytest.mark.parametrize("T", [1, 6, 20, 40])
+def test_exact_expert_ties_go_to_lower_id(T):
+    """Experts 1 and 3 share a router row (exactly equal logits on both sides),
+    scaled so that they often lead: top-1 must pick expert 1, never 3."""
+    w = _variant(tokens=T, top_k=1)
+    inp = gh.make_inputs(w)
+    # a row along the sum of the tokens: a large positive logit for each token
+    lead = (inp["x"].sum(0) * (8.0 / w.hidden)).astype(np.float32)
+    inp["router_w"][1] = lead
+    inp["router_w"][3] = lead
+    g, rt = _exact_ids(w, inp, T)
+    assert np.array_equal(g["ids"], rt["ids"])
+    assert np.all(g["ids"] == 1)
+
+
+@pytest.mark.parametrize("T", [1, 6, 20, 40])
+def test_exact_group_ties_go_to_lower_group(T):
+    """Groups 0 and 2 have identical, dominant router rows: with one group kept,
+    group 0's experts win the tie, never group 2's."""
+    w = _variant(tokens=T, n_experts=16, top_k=2, n_groups=4, topk_groups=1)
+    inp = gh.make_inputs(w)
+    lead = (inp["x"].sum(0) * (1.0 / w.hidden)).astype(np.float32)
+    for j, c in enumerate((8.0, 7.0, 6.0, 5.0)):
+        inp["router_w"][j] = lead * np.float32(c)
+        inp["router_w"][8 + j] = lead * np.float32(c)
+    g, rt = _exact_ids(w, inp, T)
+    assert np.array_equal(g["ids"], rt["ids"])
+    assert np.all(g["ids"] == np.array([0, 1]))
+    assert np.allclose(g["weights"], rt["weights"], rtol=4e-7, atol=0)
+
+
 def test_zero_input_uniform_weights_zero_output():
     w = _variant(tokens=3)
     inp = gh.make_inputs(w)
