@@ -15,7 +15,10 @@ bandwidth against the 8 TB/s peak (roofline; the kernel's duration comes from
 two HIP events recorded by that kernel's own dispatch on the library's stream),
 the CPU oracle's throughput on a bounded sample of the same workload
 (cpu_baseline), and, unless --no-prefill, the 2048-token prefill layer with the
-int8 matrix-core utilisation of its grouped gate/up GEMM.
+int8 matrix-core utilisation of its grouped gate/up GEMM.  Also reported: the
+10th/50th/90th percentiles of the per-step layer time (events), the same steps
+replayed from HIP graphs (graph), and the box's plain torch copy and read rates
+over 1 GiB (hbm_probe) as context for the kernel bandwidths.
 
 Traffic (roofline.traffic) comes from two rocprofv3 counter runs of this script
 with --calibration-copy (FETCH_SIZE, then WRITE_SIZE), summarised by
@@ -132,7 +135,7 @@ def algorithmic_bytes(w, T, n_active):
     return gate_up, layer, n_active * (gu_w + dn_w)
 
 
-def measure(w, T, steps, warmup, pool, copies, profile=False):
+def measure(w, T, steps, warmup, pool, copies, profile=False, graphs=True):
     """Whole-layer steps of workload w at T tokens: wall-clock throughput over
     `steps` steps, then the same steps with stage events and the gate/up
     kernel's own dispatch events.  Inputs are resident before timing starts."""
@@ -201,6 +204,10 @@ def measure(w, T, steps, warmup, pool, copies, profile=False):
     def stage(i0, i1):
         return float(np.mean([he.elapsed_ms(evs[s][i0], evs[s][i1]) for s in range(steps)]))
 
+    layer_ms = np.array([he.elapsed_ms(evs[s][moe.MOE_EV_BEGIN], evs[s][moe.MOE_EV_END])
+                         for s in range(steps)])
+    pct = {f"p{q}": float(np.percentile(layer_ms, q)) for q in (10, 50, 90)}
+
     st_ms = {"gate_up_kernel": stage(moe.MOE_EV_GATE_UP_KSTART, moe.MOE_EV_GATE_UP_KEND),
              "route": stage(moe.MOE_EV_BEGIN, moe.MOE_EV_ROUTED),
              "dense_in": stage(moe.MOE_EV_ROUTED, moe.MOE_EV_EXPERT_IN),
@@ -213,9 +220,66 @@ def measure(w, T, steps, warmup, pool, copies, profile=False):
             he.destroy(e)
     if profile:
         print(json.dumps({"workload": w.name, "stage_ms": st_ms}), file=sys.stderr)
+
+    # the same steps replayed from HIP graphs, one graph per (weight copy, batch)
+    # pair of the rotation, so the host launches one graph per layer call
+    graph_ms = None
+    if graphs:
+        gs = []
+        for i in range(min(steps, 2 * copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                ga = list(args(i))
+                ga[-1] = torch.cuda.current_stream(dev).cuda_stream
+                moe.moe_layer_forward(*ga)
+            gs.append(g)
+        for i in range(warmup):
+            gs[i % len(gs)].replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(steps):
+            gs[i % len(gs)].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t2) * 1e3 / steps
+        del gs
     layer.close()
     return dict(tokens_s=T * steps / (t1 - t0), ms_step=(t1 - t0) * 1e3 / steps, st_ms=st_ms,
+                layer_ms_pct=pct, graph_ms_step=graph_ms,
                 mean_active=mean_active, copies=copies, pool=pool, t_gen=t_gen, inp=inp, xs=xs)
+
+
+def hbm_probe(reps=10):
+    """The same box's plain streaming rates, as context for the kernel figures:
+    torch's copy (read + write) and sum (read) over 1 GiB of fp32, timed with
+    events on torch's stream."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, nbytes in (("copy_gbs", lambda: dst.copy_(src), 8 * n),
+                             ("read_gbs", lambda: src.sum(), 4 * n)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    res["bytes"] = 4 * n
+    return res
+
+
+def graph_rate(T, ms):
+    """Layer calls replayed from HIP graphs: tokens/s and ms per step."""
+    if ms is None:
+        return None
+    return {"tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms}
 
 
 def gemm_int8_ops(w, T):
@@ -244,7 +308,8 @@ def write_traffic(fetch_dir, write_dir):
     res = {}
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         acc = per_kernel(d, counter)
-        gu = [v for k, vs in acc.items() if "gate_up" in k or "k_mfma<8, true" in k for v in vs]
+        gu = [v for k, vs in acc.items()
+              if "gate_up" in k or "k_mfma_dma<true" in k or "k_mfma_q4<true" in k for v in vs]
         cp = [v for k, vs in acc.items() if "MulFunctor" in k for v in vs]
         if not gu or not cp:
             raise SystemExit(f"{d}: no gate/up or calibration dispatches with {counter}")
@@ -329,7 +394,10 @@ def main():
                                  "achieved": ops / (k_ms * 1e-3) / 1e12, "peak": INT8_PEAK_TOPS,
                                  "unit": "TOP/s", "frac": ops / (k_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS},
                    "gate_up_gbs": gb / (k_ms * 1e-3) / 1e9,
-                   "stage_ms": mp["st_ms"]}
+                   "stage_ms": mp["st_ms"], "layer_ms_pct": mp["layer_ms_pct"],
+                   "graph": graph_rate(wp.tokens, mp["graph_ms_step"])}
+
+    probe = hbm_probe()
 
     if a.calibration_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -364,6 +432,9 @@ def main():
         "layer_gbs": layer_bytes / (m["ms_step"] * 1e-3) / 1e9,
         "expert_gbs": expert_bytes / ((st_ms["gate_up_kernel"] + st_ms["down"]) * 1e-3) / 1e9,
         "stage_ms": st_ms,
+        "layer_ms_pct": m["layer_ms_pct"],
+        "graph": graph_rate(T, m["graph_ms_step"]),
+        "hbm_probe": probe,
         "prefill": prefill,
         "cpu_baseline": cpu,
         "input_generation_s": m["t_gen"],

@@ -327,6 +327,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     const bool down_tok = T <= DOWN_TOK_MAX_T;
     // many tokens: grouped matrix-core GEMMs over token tiles
     const bool gemm = T > MV_MAX_T;
+    // latent rows of a single token are quantised by each consumer workgroup as
+    // it stages them (no extra launch); with more tokens every workgroup would
+    // repeat that work, so z and y_lat are quantised once by their own kernel
+    const bool lat_fused_q = T <= LAT_FUSED_Q_MAX_T;
     if (taps && down_tok) tp.y = taps->y;
     const ActPtr none{nullptr, nullptr, nullptr};
 
@@ -354,9 +358,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
             CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
             CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         } else {
-            // the gate/up kernel quantises z on the way in
             CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
                                tp.tap_tokens, st), "D");
+            // one token: the gate/up kernel quantises z on the way in; more: once, here
+            if (!lat_fused_q) CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         }
     }
     EV(MOE_EV_EXPERT_IN);
@@ -367,8 +372,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     if (gemm)
         CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st, gev), "gate/up");
-    else if (m.L)
+    else if (m.L && lat_fused_q)
         CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev), "gate/up");
+    else if (m.L)
+        CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev), "gate/up");
     else
         CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev), "gate/up");
     EV(MOE_EV_GATE_UP);
@@ -388,10 +395,14 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (gemm) {
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
-        } else {
+        } else if (lat_fused_q) {
             // the U kernel quantises y_lat on the way in
             CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, none, ylat, taps ? ylq : none, out,
                                tp.isum_u, tp.tap_tokens, st), "U");
+        } else {
+            CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
+            CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, nullptr, none, out, tp.isum_u,
+                               tp.tap_tokens, st), "U");
         }
     }
     EV(MOE_EV_END);

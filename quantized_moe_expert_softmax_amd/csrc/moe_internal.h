@@ -104,6 +104,7 @@ inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr int DECODE_T = 8;  // T up to this routes in one fused kernel
 constexpr int MV_MAX_T = 32; // T up to this runs the matrix-vector expert kernels
+constexpr int LAT_FUSED_Q_MAX_T = 1;  // latent: consumers quantise z / y_lat up to this T
 constexpr int GEMM_TILE_M = 64;  // token tile of the grouped matrix-core GEMM
 
 // Upper bound of the token tiles over all active experts: every expert adds at
