@@ -102,7 +102,8 @@ struct WsLayout {
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-constexpr int DECODE_T = 8;  // T up to this routes in one fused kernel
+constexpr int DECODE_T = 8;  // largest T the single-token router kernels are sized for
+constexpr int ROUTE_DEC_MAX_T = 1;  // T up to this (<= DECODE_T) takes those kernels
 constexpr int MV_MAX_T = 32; // T up to this runs the matrix-vector expert kernels
 constexpr int LAT_FUSED_Q_MAX_T = 1;  // latent: consumers quantise z / y_lat up to this T
 constexpr int GEMM_TILE_M = 64;  // token tile of the grouped matrix-core GEMM
@@ -114,18 +115,27 @@ inline int gemm_max_tiles(int T, int k, int E) {
     return (int)((A + GEMM_TILE_M - 1) / GEMM_TILE_M + (A < E ? A : E));
 }
 
+// Router logits tile (tokens x experts per workgroup, K chunks split over its
+// waves) by token count; `kind` selects the kernel instance.
+struct RouterTile {
+    int bm, bn, wk, kind;
+};
+inline RouterTile router_tile(int T) {
+    if (T <= 16) return {16, 16, 4, 0};
+    if (T <= 32) return {32, 16, 4, 1};
+    return {64, 64, 1, 2};
+}
+
 inline int router_splits(const Dims& m, int T) {
     // K slices of the router logits: enough workgroups to spread the router
-    // matrix (small T) or the token x expert tiles (many tokens); the decode
+    // matrix (few tokens) or the token x expert tiles (many); the single-token
     // router computes whole logits
-    if (T <= DECODE_T) return 1;
+    if (T <= ROUTE_DEC_MAX_T) return 1;
+    const RouterTile rt = router_tile(T);
+    const long tiles = (long)((T + rt.bm - 1) / rt.bm) * ((m.E + rt.bn - 1) / rt.bn);
+    const int chunks = m.H / 16;
     int s = 1;
-    if (T <= MV_MAX_T) {
-        while (s < ROUTER_SPLIT_MAX && (m.E / 4) * s * 2 <= 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
-    } else {
-        const long tiles = (long)((T + 63) / 64) * ((m.E + 63) / 64);
-        while (s < ROUTER_SPLIT_MAX && tiles * s < 512 && (m.H / (s * 2)) % 256 == 0) s *= 2;
-    }
+    while (s < ROUTER_SPLIT_MAX && tiles * s * 2 <= 512 && chunks % (s * 2 * rt.wk) == 0) s *= 2;
     return s;
 }
 

@@ -81,6 +81,129 @@ __global__ __launch_bounds__(256) void k_route_logits(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Router logits on the fp64 matrix cores, partial over K slices:
+// part[s][t][e] = sum_{i in slice s} x[t,i] W[e,i].  x and W_r are fp32, so
+// their products are exact in fp64 and only the accumulation rounds.
+// One v_mfma_f64_16x16x4f64 takes a 16-token x 4 and a 4 x 16-expert operand,
+// one double per lane: lane l holds row l%16 at k-slot l/16, and the 16x16
+// fp64 result sits as rows l/16 + 4*v, column l%16 (v < 4).  Each lane loads
+// four consecutive floats of its row per 16-wide K chunk and feeds them to
+// four MFMAs as k = 4*(l/16) + j, so a chunk is covered once.
+// A workgroup is four waves on a (16*MT*WM tokens) x (16*NT*WN experts) tile;
+// with WK > 1 the waves split the slice's chunks and are summed in wave order.
+// Trailing workgroups quantise x to Q8_1 as in the other router kernels.
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+template <int MT, int NT, int WM, int WN, int WK>
+__global__ __launch_bounds__(256) void k_route_logits_mf(const float* __restrict__ x,
+                                                         const float* __restrict__ W, int T,
+                                                         int H, int E, int S,
+                                                         double* __restrict__ part,
+                                                         int n_logit_wg, ActPtr xq) {
+    static_assert(WM * WN * WK == 4, "four waves per workgroup");
+    if ((int)blockIdx.x >= n_logit_wg) {
+        const int nb = H / QK;
+        const long blk = (long)(blockIdx.x - n_logit_wg) * 8 + threadIdx.x / 32;
+        if (blk >= (long)T * nb) return;
+        const int l = threadIdx.x % 32;
+        const long r = blk / nb, b = blk % nb;
+        quant_q8_1_32(x[r * H + b * QK + l], l, xq.q + r * H + b * QK, xq.ds + r * nb + b,
+                      xq.sq + r * nb + b);
+        return;
+    }
+    constexpr int BM = 16 * MT * WM, BN = 16 * NT * WN;
+    const int gm = (T + BM - 1) / BM, gn = (E + BN - 1) / BN;
+    int b = blockIdx.x;
+    const int tm = b % gm;
+    b /= gm;
+    const int tn = b % gn;
+    const int s = b / gn;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wk = wave % WK, wm = (wave / WK) % WM, wn = wave / (WK * WM);
+    const int r = lane & 15, q = lane >> 4;
+    const int slice = H / S, nch = slice / 16;
+    const int tb = tm * BM + wm * 16 * MT, eb = tn * BN + wn * 16 * NT;
+    const float* xr[MT];
+    const float* wr[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+        xr[i] = x + (size_t)min(tb + i * 16 + r, T - 1) * H + s * slice + 4 * q;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        wr[j] = W + (size_t)min(eb + j * 16 + r, E - 1) * H + s * slice + 4 * q;
+    d4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
+    // chunks wk, wk + WK, ...; the next chunk is in flight while one is multiplied
+    // (past the last chunk the current one is re-read and not used)
+    float4 a[MT], w[NT];
+    const int c0 = min(wk, nch - 1);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const float4*>(xr[i] + c0 * 16);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) w[j] = *reinterpret_cast<const float4*>(wr[j] + c0 * 16);
+    for (int c = wk; c < nch; c += WK) {
+        const int cn = c + WK < nch ? c + WK : c;
+        float4 an[MT], wn4[NT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) an[i] = *reinterpret_cast<const float4*>(xr[i] + cn * 16);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) wn4[j] = *reinterpret_cast<const float4*>(wr[j] + cn * 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const float av = u == 0 ? a[i].x : u == 1 ? a[i].y : u == 2 ? a[i].z : a[i].w;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const float bv = u == 0 ? w[j].x : u == 1 ? w[j].y : u == 2 ? w[j].z : w[j].w;
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
+                                                                     acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) a[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) w[j] = wn4[j];
+    }
+    if constexpr (WK > 1) {
+        __shared__ double s_red[WK - 1][MT * NT * 4][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s_red[wk - 1][(i * NT + j) * 4 + v][lane] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+#pragma unroll
+        for (int o = 0; o < WK - 1; ++o)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][j][v] += s_red[o][(i * NT + j) * 4 + v][lane];
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int e = eb + j * 16 + r;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = tb + i * 16 + q + 4 * v;
+                if (t < T && e < E) part[((size_t)s * T + t) * E + e] = acc[i][j][v];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Many-token router logits: a workgroup computes a 64-token x 64-expert tile of
 // one K slice.  x and W_r tiles are staged in LDS as fp64 (k-major), each thread
 // accumulates 4 tokens x 4 experts in fp64 (products of two floats are exact in
@@ -727,22 +850,246 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
 }
 
 // ---------------------------------------------------------------------------
+// Per-token selection, one workgroup per token (any T): the token's logits are
+// the K-slice partials summed in slice order plus the bias, held as ordered
+// keys; with group labels the groups are ranked first by their largest member
+// key and the experts outside the chosen groups get key 0; every expert's rank
+// is the number of experts that beat it ((key desc, id asc)); rank < k is the
+// slot.  Softmax over the chosen logits in fp64, rank order.
+// BUCKET (T <= 32, T*k <= 1024): the last workgroup to finish (an arrival
+// counter) buckets every token's assignments, as k_route_select_dec does, and
+// clears the counter for the next call.
+// (NT threads: 1024 when few tokens share the chip, 256 when many do)
+template <bool BUCKET, int TSEL_NT>
+__global__ __launch_bounds__(TSEL_NT) void k_route_select_tok(SelectArgs A,
+                                                              int32_t* __restrict__ ids,
+                                                              float* __restrict__ wts,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ lists,
+                                                              uint32_t* __restrict__ ctrl,
+                                                              int32_t* __restrict__ active) {
+    __shared__ unsigned long long s_key[512];
+    __shared__ unsigned s_khi[512];
+    __shared__ unsigned long long s_gkey[64];
+    __shared__ unsigned char s_gsel[64];
+    __shared__ int s_nallow;
+    __shared__ int s_sel[32];
+    __shared__ double s_ex[32];
+    __shared__ int s_last;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = A.T, E = A.E, k = A.k, G = A.G;
+    for (int e = tid; e < E; e += TSEL_NT) {
+        double ps[ROUTE_SMAX];
+#pragma unroll
+        for (int sl = 0; sl < ROUTE_SMAX; ++sl)
+            ps[sl] = sl < A.S ? A.part[((size_t)sl * T + t) * E + e] : 0.0;
+        double v = 0.0;
+#pragma unroll
+        for (int sl = 0; sl < ROUTE_SMAX; ++sl)
+            if (sl < A.S) v += ps[sl];
+        if (A.bias) v += (double)A.bias[e];
+        if (A.logits_tap) A.logits_tap[(size_t)t * E + e] = v;
+        s_key[e] = dkey(v + 0.0);
+    }
+    if (G > 0) {
+        if (tid < 64) s_gkey[tid] = 0ull;
+        if (tid == 0) s_nallow = 0;
+        __syncthreads();
+        for (int e = tid; e < E; e += TSEL_NT) {
+            const unsigned gl = (unsigned)A.groups[e];
+            if (gl < (unsigned)G) atomicMax(&s_gkey[gl], s_key[e]);
+        }
+        __syncthreads();
+        if (tid < G) {
+            const unsigned long long kg = s_gkey[tid];
+            int r = 0;
+            for (int h = 0; h < G; ++h) {
+                const unsigned long long kh = s_gkey[h];
+                r += (int)(kh > kg) | ((int)(kh == kg) & (int)(h < tid));
+            }
+            s_gsel[tid] = r < A.TG;
+        }
+        __syncthreads();
+        int nal = 0;
+        for (int e = tid; e < E; e += TSEL_NT) {
+            const unsigned gl = (unsigned)A.groups[e];
+            nal += (int)(gl < (unsigned)G && s_gsel[gl]);
+        }
+        for (int o = 32; o > 0; o >>= 1) nal += __shfl_xor(nal, o, 64);
+        if (lane == 0 && nal) atomicAdd(&s_nallow, nal);
+        __syncthreads();
+        // fewer than k allowed (labels that break the equal-size-groups
+        // contract): every expert stays a candidate
+        if (s_nallow >= k) {
+            for (int e = tid; e < E; e += TSEL_NT) {
+                const unsigned gl = (unsigned)A.groups[e];
+                if (!(gl < (unsigned)G && s_gsel[gl])) s_key[e] = 0ull;
+            }
+        }
+    }
+    __syncthreads();
+    // ranks: P lanes per expert each count the rivals among E/P of them, first
+    // on the top 32 bits of the keys (one compare each); an expert that could
+    // be chosen and shares those bits with a rival is ranked again on the
+    // whole keys
+    for (int e = tid; e < E; e += TSEL_NT) s_khi[e] = (unsigned)(s_key[e] >> 32);
+    __syncthreads();
+    int P = 1;
+    while (P < 64 && E * P * 2 <= TSEL_NT) P *= 2;
+    const int lp = 31 - __clz(P);
+    for (int b0 = 0; b0 < (E << lp); b0 += TSEL_NT) {
+        const int gi = b0 + tid;
+        const int e = gi >> lp, pt = gi & (P - 1);
+        const unsigned long long ke = e < E ? s_key[e] : 0ull;
+        const unsigned khi = (unsigned)(ke >> 32);
+        int gt = 0, eq = 0;
+        if (ke != 0ull) {
+            constexpr int U = 8;
+            for (int h0 = pt; h0 < E; h0 += U * P) {
+                unsigned kh[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) kh[u] = s_khi[min(h0 + u * P, E - 1)];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int in = h0 + u * P < E;
+                    gt += in & (int)(kh[u] > khi);
+                    eq += in & (int)(kh[u] == khi);
+                }
+            }
+        }
+        for (int o = 1; o < P; o <<= 1) {
+            gt += __shfl_xor(gt, o);
+            eq += __shfl_xor(eq, o);
+        }
+        int r = gt;
+        const bool exact = ke != 0ull && gt < k && eq > 1;
+        if (__ballot(exact)) {
+            int rx = 0;
+            if (exact) {
+                for (int h = pt; h < E; h += P) {
+                    const unsigned long long kh = s_key[h];
+                    rx += (int)(kh > ke) | ((int)(kh == ke) & (int)(h < e));
+                }
+            }
+            for (int o = 1; o < P; o <<= 1) rx += __shfl_xor(rx, o);
+            if (exact) r = rx;
+        }
+        if (ke != 0ull && pt == 0 && r < k) s_sel[r] = e;
+    }
+    __syncthreads();
+    if (tid < k) {
+        const double l0 = dkey_inv(s_key[s_sel[0]]);
+        s_ex[tid] = exp(dkey_inv(s_key[s_sel[tid]]) - l0);
+    }
+    __syncthreads();
+    if (tid < k) {
+        double den = 0.0;
+        for (int j = 0; j < k; ++j) den += s_ex[j];
+        // ids are read by another workgroup of this grid when bucketing: an
+        // agent-scope store writes through to the device-coherent level
+        if constexpr (BUCKET)
+            __hip_atomic_store(ids + (size_t)t * k + tid, s_sel[tid], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        else
+            ids[(size_t)t * k + tid] = s_sel[tid];
+        wts[(size_t)t * k + tid] = (float)(s_ex[tid] / den);
+    }
+    if constexpr (BUCKET) {
+        __shared__ int s_ids[1024];
+        __shared__ int s_cnt[512];
+        __shared__ unsigned s_mask[512];
+        __shared__ int s_wtot[TSEL_NT / 64];
+        if (T > 1) {
+            // the id stores have completed (vmcnt 0) before this workgroup
+            // counts itself in; the last arrival reads every token's ids with
+            // agent-scope loads
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+                s_last = __hip_atomic_fetch_add(&ctrl[CW_ROUTE_ARRIVE], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(T - 1);
+            __syncthreads();
+            if (!s_last) return;
+        } else {
+            __syncthreads();
+        }
+        const int nA = T * k;
+        for (int e = tid; e < E; e += TSEL_NT) {
+            s_cnt[e] = 0;
+            s_mask[e] = 0u;
+        }
+        for (int i = tid; i < nA; i += TSEL_NT)
+            s_ids[i] = __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        for (int i = tid; i < nA; i += TSEL_NT) {
+            const int id = s_ids[i];
+            atomicAdd(&s_cnt[id], 1);
+            atomicOr(&s_mask[id], 1u << (i / k));
+        }
+        __syncthreads();
+        // counts of every expert; slots of the active ones in id order
+        int c[2], nact = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int e = 2 * tid + h;
+            c[h] = e < E ? s_cnt[e] : 0;
+            nact += c[h] > 0;
+        }
+        // exclusive scan of nact over the workgroup
+        int incl = nact;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) s_wtot[wave] = incl;
+        __syncthreads();
+        int slot = incl - nact;
+        for (int w2 = 0; w2 < wave; ++w2) slot += s_wtot[w2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int e = 2 * tid + h;
+            if (e < E) {
+                counts[e] = c[h];
+                if (c[h] > 0) active[slot++] = e;
+            }
+        }
+        if (tid == 0) {
+            int n = 0;
+            for (int w2 = 0; w2 < TSEL_NT / 64; ++w2) n += s_wtot[w2];
+            ctrl[CW_N_ACTIVE] = n;
+            ctrl[CW_ROUTE_ARRIVE] = 0u;
+        }
+        // list positions: the token's rank among the expert's tokens
+        for (int i = tid; i < nA; i += TSEL_NT) {
+            const int id = s_ids[i], tt = i / k;
+            lists[(size_t)id * T + __popc(s_mask[id] & ((1u << tt) - 1u))] = i;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Bucketing: workgroup e lists the assignments routed to expert e in token order.
 // The last workgroup to finish compacts the experts with tokens into slots and
 // computes each slot's first token tile (tiles of tile_m tokens).
-__global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids, int A, int T,
-                                                int E, int tile_m, int32_t* __restrict__ counts,
-                                                int32_t* __restrict__ lists,
-                                                uint32_t* __restrict__ ctrl,
-                                                int32_t* __restrict__ active,
-                                                int32_t* __restrict__ tile_start,
-                                                int32_t* __restrict__ tile_map) {
-    __shared__ int wsum[4];
+constexpr int BK_NT = 1024;
+
+__global__ __launch_bounds__(BK_NT) void k_bucket(const int32_t* __restrict__ ids, int A, int T,
+                                                  int E, int tile_m, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ lists,
+                                                  uint32_t* __restrict__ ctrl,
+                                                  int32_t* __restrict__ active,
+                                                  int32_t* __restrict__ tile_start,
+                                                  int32_t* __restrict__ tile_map) {
+    constexpr int NWV = BK_NT / 64;
+    __shared__ int wsum[NWV];
+    __shared__ int s_wa[NWV], s_wt[NWV];
     __shared__ int is_last;
     const int e = blockIdx.x, tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    // wave w owns the contiguous quarter [q0, q1) of the assignments: count its
-    // matches, then (after one exchange of the wave totals) list them in order
-    const int Q = (A + 3) / 4;
+    // wave w owns the contiguous w-th sixteenth [q0, q1) of the assignments:
+    // count its matches, then (after one exchange of the wave totals) list
+    // them in order
+    const int Q = (A + NWV - 1) / NWV;
     const int q0 = min(wave * Q, A), q1 = min(q0 + Q, A);
     int cnt = 0;
 #pragma unroll 4
@@ -762,53 +1109,55 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids,
         if (f) lists[(size_t)e * T + off + __popcll(m & ((1ull << lane) - 1ull))] = a;
         off += __popcll(m);
     }
-    if (tid == 0) counts[e] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (tid == 0) {
+        int c = 0;
+        for (int w = 0; w < NWV; ++w) c += wsum[w];
+        counts[e] = c;
+    }
     __threadfence();
     __syncthreads();
     if (tid == 0) is_last = atomicAdd(&ctrl[CW_BUCKET_ARRIVE], 1u) == (unsigned)(E - 1);
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    // compact: slot order = expert id order.  Two experts per thread (E <= 512).
-    __shared__ int sc[512];
-    __shared__ int tiles[512];
-    int c0 = 0, c1 = 0;
-    int e0 = 2 * tid, e1 = 2 * tid + 1;
-    if (e0 < E) c0 = __atomic_load_n(&counts[e0], __ATOMIC_RELAXED);
-    if (e1 < E) c1 = __atomic_load_n(&counts[e1], __ATOMIC_RELAXED);
-    // inclusive scan of (active count, tile count) over threads
-    int act = (c0 > 0) + (c1 > 0);
-    int til = (c0 + tile_m - 1) / tile_m + (c1 + tile_m - 1) / tile_m;
-    sc[tid] = act;
-    tiles[tid] = til;
+    // compact: slot order = expert id order, one expert per thread (E <= 512);
+    // exclusive scans of (active, tiles) over the threads
+    const int c = tid < E ? __atomic_load_n(&counts[tid], __ATOMIC_RELAXED) : 0;
+    const int act = c > 0, til = (c + tile_m - 1) / tile_m;
+    int ia = act, it = til;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int va = __shfl_up(ia, o, 64), vt = __shfl_up(it, o, 64);
+        if (lane >= o) {
+            ia += va;
+            it += vt;
+        }
+    }
+    if (lane == 63) {
+        s_wa[wave] = ia;
+        s_wt[wave] = it;
+    }
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        int va = tid >= o ? sc[tid - o] : 0;
-        int vt = tid >= o ? tiles[tid - o] : 0;
-        __syncthreads();
-        sc[tid] += va;
-        tiles[tid] += vt;
-        __syncthreads();
+    int slot = ia - act, tl = it - til;
+    for (int w = 0; w < wave; ++w) {
+        slot += s_wa[w];
+        tl += s_wt[w];
     }
-    int slot = sc[tid] - act;           // exclusive
-    int tl = tiles[tid] - til;
     // tile map entry: expert | (tile index within the expert << 16)
-    if (c0 > 0) {
-        active[slot] = e0;
+    if (c > 0) {
+        active[slot] = tid;
         tile_start[slot] = tl;
-        for (int i = 0; i < (c0 + tile_m - 1) / tile_m; ++i) tile_map[tl + i] = e0 | (i << 16);
-        ++slot;
-        tl += (c0 + tile_m - 1) / tile_m;
+        for (int i = 0; i < til; ++i) tile_map[tl + i] = tid | (i << 16);
     }
-    if (c1 > 0) {
-        active[slot] = e1;
-        tile_start[slot] = tl;
-        for (int i = 0; i < (c1 + tile_m - 1) / tile_m; ++i) tile_map[tl + i] = e1 | (i << 16);
-    }
-    if (tid == 255) {
-        ctrl[CW_N_ACTIVE] = sc[255];
-        ctrl[CW_N_TILES] = tiles[255];
-        tile_start[sc[255]] = tiles[255];
+    if (tid == 0) {
+        int na = 0, nt = 0;
+        for (int w = 0; w < NWV; ++w) {
+            na += s_wa[w];
+            nt += s_wt[w];
+        }
+        ctrl[CW_N_ACTIVE] = na;
+        ctrl[CW_N_TILES] = nt;
+        tile_start[na] = nt;
         ctrl[CW_BUCKET_ARRIVE] = 0u;    // ready for the next call
     }
 }
@@ -819,12 +1168,21 @@ __global__ __launch_bounds__(256) void k_bucket(const int32_t* __restrict__ ids,
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ wts, int T, int k,
                                                  int R, float* __restrict__ out) {
+    // one float4 of out per thread (R is a multiple of 4)
+    const int R4 = R / 4;
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)T * R) return;
-    const long t = i / R, r = i % R;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) acc = fmaf(wts[t * k + j], y[(t * k + j) * R + r], acc);
-    out[i] = acc;
+    if (i >= (long)T * R4) return;
+    const long t = i / R4, r4 = i % R4;
+    float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; ++j) {
+        const float w = wts[t * k + j];
+        const float4 v = reinterpret_cast<const float4*>(y + (t * k + j) * R)[r4];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(out)[i] = acc;
 }
 
 // Canonical 36-byte Q8_1 blocks from the split activation layout.
@@ -856,23 +1214,14 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
                          ActPtr xq, bool* bucketed, hipStream_t st) {
     double* part = (double*)(ws + w.logit_part);
     const int S = w.S;
-    const int ge = (m.E + 3) / 4;
     const long qblocks = (long)T * (m.H / QK);
     const int qwg = (int)((qblocks + 7) / 8);
     int32_t* ids = (int32_t*)(ws + w.ids);
     float* wts = (float*)(ws + w.wts);
-    const int me = (m.E + 63) / 64;
     SelectArgs a;
     a.part = part; a.S = S; a.T = T; a.E = m.E; a.k = m.k;
     a.bias = br; a.groups = groups; a.G = m.G; a.TG = m.TG; a.logits_tap = logits_tap;
-#define MOE_MAXE(M, CALL)                                  \
-    switch (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8) {     \
-        case 1: { constexpr int ME = 1; CALL; break; }     \
-        case 2: { constexpr int ME = 2; CALL; break; }     \
-        case 4: { constexpr int ME = 4; CALL; break; }     \
-        default: { constexpr int ME = 8; CALL; break; }    \
-    }
-    if (T <= DECODE_T && m.E <= 512 && m.k <= 32) {
+    if (T <= ROUTE_DEC_MAX_T && m.E <= 512 && m.k <= 32) {
         hipLaunchKernelGGL(k_route_logits_dec, dim3(m.E + qwg), dim3(256), 0, st, x, Wr, T, m.H,
                            m.E, part, xq);
         hipError_t e = hipGetLastError();
@@ -883,29 +1232,36 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
         *bucketed = true;
         return hipGetLastError();
     }
-    if (T <= 8) {
-        const int nl = ge * S * ((T + 7) / 8);
-        hipLaunchKernelGGL(k_route_logits<8>, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H, m.E,
-                           S, part, nl, xq);
-    } else if (T <= MV_MAX_T) {
-        const int nl = ge * S * ((T + 31) / 32);
-        hipLaunchKernelGGL(k_route_logits<32>, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H,
-                           m.E, S, part, nl, xq);
-    } else {
-        const int nl = ((T + RT_M - 1) / RT_M) * ((m.E + RT_N - 1) / RT_N) * S;
-        hipLaunchKernelGGL(k_route_logits_tiled, dim3(nl + qwg), dim3(256), 0, st, x, Wr, T, m.H,
-                           m.E, S, part, nl, xq);
+    const RouterTile rt = router_tile(T);
+    const int nl = ((T + rt.bm - 1) / rt.bm) * ((m.E + rt.bn - 1) / rt.bn) * S;
+    const dim3 lg(nl + qwg);
+    switch (rt.kind) {
+        case 0:
+            hipLaunchKernelGGL((k_route_logits_mf<1, 1, 1, 1, 4>), lg, dim3(256), 0, st, x, Wr, T,
+                               m.H, m.E, S, part, nl, xq);
+            break;
+        case 1:
+            hipLaunchKernelGGL((k_route_logits_mf<2, 1, 1, 1, 4>), lg, dim3(256), 0, st, x, Wr, T,
+                               m.H, m.E, S, part, nl, xq);
+            break;
+        default:
+            hipLaunchKernelGGL((k_route_logits_mf<2, 2, 2, 2, 1>), lg, dim3(256), 0, st, x, Wr, T,
+                               m.H, m.E, S, part, nl, xq);
+            break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    int32_t* counts = (int32_t*)(ws + w.counts);
+    int32_t* lists = (int32_t*)(ws + w.lists);
+    uint32_t* ctrl = (uint32_t*)(ws + w.ctrl);
+    int32_t* active = (int32_t*)(ws + w.active);
     if (T <= SMALL_TMAX && T * m.k <= 1024 && m.E <= 512) {
-        MOE_MAXE(me, hipLaunchKernelGGL(k_route_small<ME>, dim3(1), dim3(SMALL_NW * 64), 0, st, a,
-                                        ids, wts, (int32_t*)(ws + w.counts),
-                                        (int32_t*)(ws + w.lists), (uint32_t*)(ws + w.ctrl),
-                                        (int32_t*)(ws + w.active)));
+        hipLaunchKernelGGL((k_route_select_tok<true, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
+                           wts, counts, lists, ctrl, active);
         *bucketed = true;
     } else {
-        MOE_MAXE(me, hipLaunchKernelGGL(k_router_topk<ME>, dim3(T), dim3(64), 0, st, a, ids, wts));
+        hipLaunchKernelGGL((k_route_select_tok<false, 256>), dim3(T), dim3(256), 0, st, a, ids,
+                           wts, counts, lists, ctrl, active);
         *bucketed = false;
     }
 #undef MOE_MAXE
@@ -914,7 +1270,7 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
 
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T,
                          hipStream_t st) {
-    hipLaunchKernelGGL(k_bucket, dim3(m.E), dim3(256), 0, st, (const int32_t*)(ws + w.ids), T * m.k,
+    hipLaunchKernelGGL(k_bucket, dim3(m.E), dim3(BK_NT), 0, st, (const int32_t*)(ws + w.ids), T * m.k,
                        T, m.E, GEMM_TILE_M, (int32_t*)(ws + w.counts), (int32_t*)(ws + w.lists),
                        (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active),
                        (int32_t*)(ws + w.tile_start), (int32_t*)(ws + w.tile_map));
@@ -923,7 +1279,7 @@ hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T,
 
 hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R, float* out,
                           hipStream_t st) {
-    long n = (long)T * R;
+    long n = (long)T * (R / 4);
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, wts, T, k,
                        R, out);
