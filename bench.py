@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--workload", default="decode",
                    help="tiny | decode | latent_q8 | latent_q4 | prefill")
     p.add_argument("--tokens", type=int, default=None, help="tokens per step (default: the workload's)")
+    p.add_argument("--dense-fmt", choices=("q8_0", "q4_0"), default=None,
+                   help="block format of a latent layer's D/U (default: the workload's, Q8_0)")
     p.add_argument("--copies", type=int, default=None, help="device copies of the expert weights")
     p.add_argument("--pool", type=int, default=64, help="distinct token batches")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -130,7 +132,9 @@ def algorithmic_bytes(w, T, n_active):
     gate_up = n_active * gu_w + act_in + hq
     dense = 0
     if L:
-        dense = L * (H // 32) * 34 + H * (L // 32) * 34
+        from quantized_moe_expert_softmax_amd import synth
+        dbb = synth.BLOCK_BYTES[w.dense_fmt]
+        dense = L * (H // 32) * dbb + H * (L // 32) * dbb
     layer = E * H * 4 + T * H * 4 + n_active * (gu_w + dn_w) + dense + T * H * 4
     return gate_up, layer, n_active * (gu_w + dn_w)
 
@@ -342,7 +346,10 @@ def main():
 
     w0 = synth.WORKLOADS[a.workload]
     T = a.tokens or w0.tokens
-    w = synth.Workload(**{**w0.__dict__, "tokens": T})
+    over = {"tokens": T}
+    if a.dense_fmt:
+        over["dense_fmt"] = synth.Q4_0 if a.dense_fmt == "q4_0" else synth.Q8_0
+    w = synth.Workload(**{**w0.__dict__, **over})
     m = measure(w, T, a.steps, a.warmup, a.pool, a.copies, a.profile_steps)
     st_ms = m["st_ms"]
 
@@ -422,6 +429,8 @@ def main():
         "config": {"workload": a.workload, "hidden": w.hidden, "n_experts": w.n_experts,
                    "top_k": w.top_k, "n_ff": w.n_ff, "latent": w.latent,
                    "expert_fmt": "Q4_0" if w.expert_fmt == synth.Q4_0 else "Q8_0",
+                   "dense_fmt": (("Q4_0" if w.dense_fmt == synth.Q4_0 else "Q8_0")
+                                 if w.latent else None),
                    "tokens_per_step": T, "weight_copies": m["copies"], "token_batches": m["pool"],
                    "mean_active_experts": m["mean_active"]},
         "roofline": {"bound": "hbm", "kernel": "gate_up (grouped gate/up + SwiGLU + Q8_1)",

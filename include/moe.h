@@ -71,7 +71,7 @@ typedef struct {
     int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
     int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
     int32_t expert_fmt;   /* MOE_FMT_Q8_0 or MOE_FMT_Q4_0                                 */
-    int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 (ignored when latent == 0)          */
+    int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 or MOE_FMT_Q4_0 (latent == 0: unused)*/
     int32_t n_groups;     /* 0 = no group limit; else divides E                           */
     int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/
     int32_t max_tokens;   /* largest T a forward call may pass: 1..65536                  */

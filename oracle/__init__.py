@@ -36,7 +36,7 @@ def build(force: bool = False) -> str:
 
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("hidden", "n_experts", "top_k", "n_ff", "latent",
-                                            "expert_fmt", "n_groups", "topk_groups")]
+                                            "expert_fmt", "n_groups", "topk_groups", "dense_fmt")]
 
 
 _TAP_FIELDS = [("logits", ctypes.c_void_p), ("ids", ctypes.c_void_p), ("weights", ctypes.c_void_p),
@@ -96,7 +96,7 @@ def _p(a: Optional[np.ndarray]):
 def desc_of(w) -> Desc:
     """Oracle descriptor from a workload (any object with the workload's fields)."""
     return Desc(w.hidden, w.n_experts, w.top_k, w.n_ff, w.latent, w.expert_fmt, w.n_groups,
-                w.topk_groups)
+                w.topk_groups, getattr(w, "dense_fmt", 8))
 
 
 def f16_encode(v: float) -> int:

@@ -17,8 +17,9 @@
  *        port commits: Q8_1 activation bytes match only with a correctly
  *        rounded fp32 divide; per-token top-k routing over the experts.
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
- *        latent-MoE with dense Q8 D/U projections into a 1280/1792-wide latent
- *        space, expert group labels, Q4_0 x Q8_1 rows.
+ *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
+ *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
+ *        the D/U projections is read as Q4_0).
  * Where the pages leave a step open the reading taken is stated at that step.
  *
  * Precision: integer block sums are exact int32; per-block contributions
@@ -41,6 +42,7 @@ typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
     int expert_fmt;           /* ORC_Q8_0 or ORC_Q4_0 */
     int n_groups, topk_groups;/* 0 = no group limit */
+    int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
 
 /* Optional per-step outputs, indexed by position i in the token list. */
@@ -342,7 +344,7 @@ static void run_token(job_t* J, int i) {
     if (L) {                                   /* latent: z = D Q8_1(x), experts on Q8_1(z) */
         z = (float*)malloc(sizeof(float) * L);
         zq = (uint8_t*)malloc((size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
-        orc_matvec(ORC_Q8_0, L, H / ORC_QK, J->D, xq, z, tp ? TAP(tp->isum_d, (size_t)L * (H / ORC_QK)) : NULL);
+        orc_matvec(d->dense_fmt, L, H / ORC_QK, J->D, xq, z, tp ? TAP(tp->isum_d, (size_t)L * (H / ORC_QK)) : NULL);
         orc_quantize_q8_1(z, L, zq);
         if (tp && tp->z) memcpy(tp->z + (size_t)i * L, z, sizeof(float) * L);
         if (tp && tp->zq) memcpy(tp->zq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, zq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
@@ -374,7 +376,7 @@ static void run_token(job_t* J, int i) {
         orc_quantize_q8_1(comb, L, ylq);
         if (tp && tp->ylat) memcpy(tp->ylat + (size_t)i * L, comb, sizeof(float) * L);
         if (tp && tp->ylq) memcpy(tp->ylq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, ylq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
-        orc_matvec(ORC_Q8_0, H, L / ORC_QK, J->U, ylq, J->out + (size_t)i * H,
+        orc_matvec(d->dense_fmt, H, L / ORC_QK, J->U, ylq, J->out + (size_t)i * H,
                    tp ? TAP(tp->isum_u, (size_t)H * (L / ORC_QK)) : NULL);
         free(ylq);
         free(comb);
@@ -414,6 +416,7 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     if (!d || !x || !Wr || !experts || !out || n < 0) return -1;
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
+    if (d->latent && d->dense_fmt != ORC_Q8_0 && d->dense_fmt != ORC_Q4_0) return -1;
     if (d->n_groups > 0) {                     /* every group holds E / n_groups experts */
         int G = d->n_groups;
         if (!groups || d->n_experts % G || d->topk_groups < 1 || d->topk_groups > G ||

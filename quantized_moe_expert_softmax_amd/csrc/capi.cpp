@@ -53,9 +53,10 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (!d) return fail(MOE_EINVAL, "desc is NULL");
     if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0)
         return fail(MOE_EUNSUPPORTED, "expert_fmt %d is neither Q8_0 (8) nor Q4_0 (2)", d->expert_fmt);
-    if (d->latent && d->dense_fmt != MOE_FMT_Q8_0)
-        return fail(MOE_EUNSUPPORTED, "dense_fmt %d: the D/U projections support Q8_0 (8) only",
-                    d->dense_fmt);
+    // edge0-strata README, changes from upstream Strata: the latent D/U
+    // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
+    if (d->latent && d->dense_fmt != MOE_FMT_Q8_0 && d->dense_fmt != MOE_FMT_Q4_0)
+        return fail(MOE_EUNSUPPORTED, "dense_fmt %d is neither Q8_0 (8) nor Q4_0 (2)", d->dense_fmt);
     if (!mult(d->hidden, 256) || d->hidden > 8192)
         return fail(d->hidden <= 0 ? MOE_EINVAL : MOE_EUNSUPPORTED,
                     "hidden %d must be a positive multiple of 256, at most 8192", d->hidden);
@@ -90,8 +91,8 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
                     d->expert_fmt == MOE_FMT_Q4_0 ? "Q4_0" : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
-    if (d->latent && (!mv_config_ok(d->hidden, MOE_FMT_Q8_0, false) ||
-                      !mv_config_ok(d->latent, MOE_FMT_Q8_0, false)))
+    if (d->latent && (!mv_config_ok(d->hidden, d->dense_fmt, false) ||
+                      !mv_config_ok(d->latent, d->dense_fmt, false)))
         return fail(MOE_EUNSUPPORTED, "no D/U kernel for hidden %d, latent %d", d->hidden,
                     d->latent);
     g_err.clear();

@@ -55,15 +55,15 @@ inline Dims make_dims(const moe_desc& d) {
     m.H = d.hidden; m.E = d.n_experts; m.k = d.top_k; m.F = d.n_ff; m.L = d.latent;
     m.kin = d.latent ? d.latent : d.hidden;
     m.kout = m.kin;
-    m.fmt = d.expert_fmt; m.dfmt = MOE_FMT_Q8_0;
+    m.fmt = d.expert_fmt; m.dfmt = d.latent ? d.dense_fmt : MOE_FMT_Q8_0;
     m.G = d.n_groups; m.TG = d.topk_groups; m.max_tokens = d.max_tokens;
     m.gu = mat_layout(2 * m.F, m.kin / QK, m.fmt);
     m.dn = mat_layout(m.kout, m.F / QK, m.fmt);
     m.dn_off = m.gu.bytes();
     m.expert_bytes = m.gu.bytes() + m.dn.bytes();
     if (m.L) {
-        m.D = mat_layout(m.L, m.H / QK, MOE_FMT_Q8_0);
-        m.U = mat_layout(m.H, m.L / QK, MOE_FMT_Q8_0);
+        m.D = mat_layout(m.L, m.H / QK, m.dfmt);
+        m.U = mat_layout(m.H, m.L / QK, m.dfmt);
     }
     return m;
 }

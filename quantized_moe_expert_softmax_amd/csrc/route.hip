@@ -136,38 +136,50 @@ __global__ __launch_bounds__(256) void k_route_logits_mf(const float* __restrict
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
-    // chunks wk, wk + WK, ...; the next chunk is in flight while one is multiplied
-    // (past the last chunk the current one is re-read and not used)
-    float4 a[MT], w[NT];
-    const int c0 = min(wk, nch - 1);
+    // the wave's chunks are wk, wk + WK, ...; they are taken CG at a time into
+    // two register sets used in turn (no copies between them, so a set's loads
+    // stay in flight while the other set is multiplied).  A chunk past the
+    // last is loaded from the last chunk and not multiplied.
+    constexpr int CG = 2;
+    float4 a0[CG][MT], w0[CG][NT], a1[CG][MT], w1[CG][NT];
+    auto load_set = [&](float4 (&as)[CG][MT], float4 (&ws)[CG][NT], int c) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const float4*>(xr[i] + c0 * 16);
+        for (int g = 0; g < CG; ++g) {
+            const int cc = min(c + g * WK, nch - 1);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) w[j] = *reinterpret_cast<const float4*>(wr[j] + c0 * 16);
-    for (int c = wk; c < nch; c += WK) {
-        const int cn = c + WK < nch ? c + WK : c;
-        float4 an[MT], wn4[NT];
+            for (int i = 0; i < MT; ++i) as[g][i] = *reinterpret_cast<const float4*>(xr[i] + cc * 16);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) an[i] = *reinterpret_cast<const float4*>(xr[i] + cn * 16);
+            for (int j = 0; j < NT; ++j) ws[g][j] = *reinterpret_cast<const float4*>(wr[j] + cc * 16);
+        }
+    };
+    auto mul_set = [&](const float4 (&as)[CG][MT], const float4 (&ws)[CG][NT], int c) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) wn4[j] = *reinterpret_cast<const float4*>(wr[j] + cn * 16);
+        for (int g = 0; g < CG; ++g) {
+            if (c + g * WK >= nch) break;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 4; ++u) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const float av = u == 0 ? a[i].x : u == 1 ? a[i].y : u == 2 ? a[i].z : a[i].w;
+                for (int i = 0; i < MT; ++i) {
+                    const float4 av4 = as[g][i];
+                    const float av = u == 0 ? av4.x : u == 1 ? av4.y : u == 2 ? av4.z : av4.w;
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const float bv = u == 0 ? w[j].x : u == 1 ? w[j].y : u == 2 ? w[j].z : w[j].w;
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
-                                                                     acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < NT; ++j) {
+                        const float4 bv4 = ws[g][j];
+                        const float bv = u == 0 ? bv4.x : u == 1 ? bv4.y : u == 2 ? bv4.z : bv4.w;
+                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av, (double)bv,
+                                                                         acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) a[i] = an[i];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) w[j] = wn4[j];
+    };
+    constexpr int STEP = CG * WK;
+    load_set(a0, w0, wk);
+    for (int c = wk; c < nch; c += 2 * STEP) {
+        load_set(a1, w1, c + STEP);
+        mul_set(a0, w0, c);
+        load_set(a0, w0, c + 2 * STEP);
+        mul_set(a1, w1, c + STEP);
     }
     if constexpr (WK > 1) {
         __shared__ double s_red[WK - 1][MT * NT * 4][64];
@@ -1109,20 +1121,24 @@ __global__ __launch_bounds__(BK_NT) void k_bucket(const int32_t* __restrict__ id
         if (f) lists[(size_t)e * T + off + __popcll(m & ((1ull << lane) - 1ull))] = a;
         off += __popcll(m);
     }
+    // the count is the only value another workgroup of this grid reads: an
+    // agent-scope store writes it through to the device-coherent level and has
+    // completed (vmcnt 0) before the arrival is counted; the lists are for the
+    // next kernels
     if (tid == 0) {
         int c = 0;
         for (int w = 0; w < NWV; ++w) c += wsum[w];
-        counts[e] = c;
+        __hip_atomic_store(counts + e, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        is_last = __hip_atomic_fetch_add(&ctrl[CW_BUCKET_ARRIVE], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(E - 1);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(&ctrl[CW_BUCKET_ARRIVE], 1u) == (unsigned)(E - 1);
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
     // compact: slot order = expert id order, one expert per thread (E <= 512);
     // exclusive scans of (active, tiles) over the threads
-    const int c = tid < E ? __atomic_load_n(&counts[tid], __ATOMIC_RELAXED) : 0;
+    const int c = tid < E ? __hip_atomic_load(counts + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0;
     const int act = c > 0, til = (c + tile_m - 1) / tile_m;
     int ia = act, it = til;
 #pragma unroll

@@ -109,7 +109,7 @@ def make_desc(hidden, n_experts, top_k, n_ff, latent=0, expert_fmt=MOE_FMT_Q8_0,
 def desc_of(w, max_tokens: Optional[int] = None) -> moe_desc:
     """Descriptor of a synthetic workload (see synth.Workload)."""
     return make_desc(w.hidden, w.n_experts, w.top_k, w.n_ff, w.latent, w.expert_fmt,
-                     MOE_FMT_Q8_0, w.n_groups, w.topk_groups,
+                     getattr(w, "dense_fmt", MOE_FMT_Q8_0), w.n_groups, w.topk_groups,
                      w.tokens if max_tokens is None else max_tokens)
 
 

@@ -136,6 +136,7 @@ class Workload:
     topk_groups: int = 0
     bias: bool = False
     seed: int = 0
+    dense_fmt: int = Q8_0
 
     @property
     def k_in(self) -> int:
@@ -236,12 +237,13 @@ def gen_experts(w: Workload, out: Optional[np.ndarray] = None, threads: int = 8)
 
 
 def gen_dense(w: Workload):
-    """Canonical Q8_0 D [L][H/32] and U [H][L/32]; (None, None) when not latent."""
+    """Canonical D [L][H/32] and U [H][L/32] in w.dense_fmt (the same block
+    distributions as the experts of that format); (None, None) when not latent."""
     if not w.latent:
         return None, None
     res = []
     for i, (rows, nb) in enumerate(w.dense_shapes()):
-        res.append(blocks(Q8_0, w.seed, S_DENSE + 2 * i, S_DENSE + 2 * i + 1, rows * nb))
+        res.append(blocks(w.dense_fmt, w.seed, S_DENSE + 2 * i, S_DENSE + 2 * i + 1, rows * nb))
     return res[0], res[1]
 
 

@@ -147,7 +147,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
     if w.latent:
         H, L = w.hidden, w.latent
         tt = min(tap_tokens, T)
-        z_ref, iss = dense_isums(8, inp["D"], L, H // 32, g["xq"][:tt])
+        z_ref, iss = dense_isums(w.dense_fmt, inp["D"], L, H // 32, g["xq"][:tt])
         assert np.array_equal(g["isum_d"][:tt], iss)
         assert np.allclose(g["z"][:tt], z_ref, rtol=0, atol=1e-5 * np.abs(z_ref).max())
         assert np.array_equal(g["zq"], oracle.quantize_q8_1(g["z"]))
@@ -181,7 +181,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
             assert rel_max(g["y"][a], y_dn) < 1e-5
     if w.latent:
         H, L = w.hidden, w.latent
-        _, iss = dense_isums(8, inp["U"], H, L // 32, g["ylq"][:tt])
+        _, iss = dense_isums(w.dense_fmt, inp["U"], H, L // 32, g["ylq"][:tt])
         assert np.array_equal(g["isum_u"][:tt], iss)
 
     # the layer output, token by token
@@ -211,7 +211,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
         comb = (g["weights"][t].astype(np.float64)[:, None] * y_own).sum(0)
         if w.latent:
             assert rel_max(g["ylat"][t], comb) < 1e-5, t
-            out_own = oracle.matvec(8, inp["U"], w.hidden, w.latent // 32, g["ylq"][t].reshape(-1))
+            out_own = oracle.matvec(w.dense_fmt, inp["U"], w.hidden, w.latent // 32, g["ylq"][t].reshape(-1))
         else:
             out_own = comb
         assert rel_max(g["out"][t], out_own) < 1e-5, (t, rel_max(g["out"][t], out_own))

@@ -57,7 +57,7 @@ def test_desc_refusals_name_the_cause(L):
     _refused(moe.make_desc(**{**ok, "n_groups": 4, "topk_groups": 0}), moe.MOE_EINVAL, "topk_groups")
     _refused(moe.make_desc(**{**ok, "n_groups": 4, "topk_groups": 5}), moe.MOE_EINVAL, "topk_groups")
     _refused(moe.make_desc(**{**ok, "n_groups": 8, "topk_groups": 1}), moe.MOE_EINVAL, "top_k")
-    _refused(moe.make_desc(**{**ok, "latent": 256, "dense_fmt": 2}), moe.MOE_EUNSUPPORTED, "dense_fmt")
+    _refused(moe.make_desc(**{**ok, "latent": 256, "dense_fmt": 7}), moe.MOE_EUNSUPPORTED, "dense_fmt")
     _refused(moe.make_desc(**{**ok, "latent": 300}), moe.MOE_EUNSUPPORTED, "latent")
     _refused(moe.make_desc(**{**ok, "hidden": 8192 + 256}), moe.MOE_EUNSUPPORTED, "hidden")
     assert L.moe_desc_check(None) == moe.MOE_EINVAL

@@ -120,6 +120,24 @@ def test_latent_gemm_sampled(name, T):
     _report(name, T, rep)
 
 
+# latent D/U in Q4_0 (the Q4 choice of the D/U projections): the single-token
+# path, a decode window, the 9..32-token matrix-vector path and the GEMM path
+@pytest.mark.parametrize("kw", [
+    dict(latent=256, dense_fmt=synth.Q4_0, n_experts=16, top_k=4, n_groups=4, topk_groups=2,
+         tokens=1),
+    dict(latent=256, dense_fmt=synth.Q4_0, n_experts=16, top_k=4, tokens=6),
+    dict(latent=256, dense_fmt=synth.Q4_0, expert_fmt=synth.Q4_0, n_experts=16, top_k=4,
+         tokens=20),
+    dict(latent=256, dense_fmt=synth.Q4_0, n_experts=16, top_k=4, tokens=70),
+    dict(hidden=1280, latent=512, dense_fmt=synth.Q4_0, expert_fmt=synth.Q4_0, n_experts=32,
+         top_k=8, n_groups=8, topk_groups=4, tokens=40),
+])
+def test_q4_0_dense_projections(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("dense q4_0 " + str(kw), w.tokens, rep)
+
+
 # path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [

@@ -556,6 +556,40 @@ def test_latent_selection_dense(orc, synth):
         assert np.array_equal(taps["z"][t], deq[:64].astype(np.float32))
 
 
+def test_latent_selection_dense_q4_0(orc, synth):
+    """Q4_0 D and U as selections (d = 1, code 9 = +1 on the diagonal, code 8 = 0
+    elsewhere; low nibble = element j, high nibble = element j + 16): z is the
+    dequantised Q8_1(x) prefix and out is the dequantised Q8_1(y_lat) followed
+    by zeros, exactly."""
+    H, L = 128, 64
+    w = _wl(hidden=H, n_experts=4, top_k=2, n_ff=64, tokens=3, latent=L, seed=5,
+            dense_fmt=synth.Q4_0)
+    inp = _layer_inputs(synth, w)
+
+    def selection(rows, nblk):
+        m = np.full((rows, nblk, 18), 0x88, np.uint8)
+        m[:, :, 0] = 0x00
+        m[:, :, 1] = 0x3C
+        for r in range(min(rows, nblk * 32)):
+            p = r % 32
+            m[r, r // 32, 2 + p % 16] = 0x89 if p < 16 else 0x98
+        return m.reshape(-1)
+
+    out, taps = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                                  D=selection(L, H // 32), U=selection(H, L // 32),
+                                  taps=("xq", "z", "ylq"))
+
+    def deq(q8_1_blocks):
+        return np.concatenate([orc.f16_decode(int(b[0]) | int(b[1]) << 8)
+                               * b[4:].view(np.int8).astype(np.float64) for b in q8_1_blocks])
+
+    for t in range(3):
+        assert np.array_equal(taps["z"][t], deq(taps["xq"][t])[:L].astype(np.float32))
+        want = np.zeros(H, np.float32)
+        want[:L] = deq(taps["ylq"][t]).astype(np.float32)
+        assert np.array_equal(out[t], want)
+
+
 def test_oracle_refuses_bad_groups(orc, synth):
     w = _wl(n_experts=8, top_k=3, n_groups=4, topk_groups=1)   # 1 group of 2 < k = 3
     inp = _layer_inputs(synth, dataclasses.replace(w, n_groups=0, topk_groups=0))
