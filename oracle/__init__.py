@@ -20,6 +20,7 @@ _lib = None
 
 Q8_0 = 8
 Q4_0 = 2
+Q5_1 = 7
 Q8_1_BYTES = 36
 
 
@@ -67,6 +68,10 @@ def lib():
         L.orc_isum_q8_0.restype = ctypes.c_int32
         L.orc_isum_q4_0.argtypes = [vp, vp]
         L.orc_isum_q4_0.restype = ctypes.c_int32
+        L.orc_isum_q5_1.argtypes = [vp, vp]
+        L.orc_isum_q5_1.restype = ctypes.c_int32
+        L.orc_q5_1_code.argtypes = [vp, i32]
+        L.orc_q5_1_code.restype = ctypes.c_int
         L.orc_dequant_weight.argtypes = [i32, vp, i32]
         L.orc_dequant_weight.restype = ctypes.c_double
         L.orc_row_dot.argtypes = [i32, vp, vp, i32, vp]
@@ -120,8 +125,13 @@ def quantize_q8_1(v: np.ndarray) -> np.ndarray:
 def isum(fmt: int, wblk: np.ndarray, ablk: np.ndarray) -> int:
     wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
     ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
-    f = lib().orc_isum_q8_0 if fmt == Q8_0 else lib().orc_isum_q4_0
+    f = {Q8_0: lib().orc_isum_q8_0, Q4_0: lib().orc_isum_q4_0, Q5_1: lib().orc_isum_q5_1}[fmt]
     return int(f(_p(wblk), _p(ablk)))
+
+
+def q5_1_code(wblk: np.ndarray, j: int) -> int:
+    wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
+    return int(lib().orc_q5_1_code(_p(wblk), j))
 
 
 def dequant_weight(fmt: int, wblk: np.ndarray, j: int) -> float:

@@ -16,6 +16,10 @@
  *   [SY] "Sync upstream Strata v0.1.39 into Lanes" (pull request 24), the SYCL
  *        port commits: Q8_1 activation bytes match only with a correctly
  *        rounded fp32 divide; per-token top-k routing over the experts.
+ *   [Q5] same page, the K-quant follow-up commit: Q5_1 experts (llama.cpp's
+ *        Q5_1 blocks), whose min term multiplies the sum of the QUANTISED
+ *        activations of the Q8_1 block (the ggml CPU convention), not the
+ *        float sum of the activations.
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
  *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
  *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
@@ -35,12 +39,13 @@
 
 #define ORC_Q8_0 8
 #define ORC_Q4_0 2
+#define ORC_Q5_1 7
 #define ORC_QK 32
 #define ORC_Q8_1_BYTES 36
 
 typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
-    int expert_fmt;           /* ORC_Q8_0 or ORC_Q4_0 */
+    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0 or ORC_Q5_1 */
     int n_groups, topk_groups;/* 0 = no group limit */
     int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
@@ -172,21 +177,47 @@ int32_t orc_isum_q4_0(const uint8_t* w, const uint8_t* a) {
     return s;
 }
 
-static inline int fmt_bytes(int fmt) { return fmt == ORC_Q4_0 ? 18 : 34; }
+/*
+ * Q5_1: binary16 d, binary16 m, a 32-bit little-endian qh, then 16 bytes.
+ * Element j < 16 takes the low nibble of byte j and bit j of qh as its fifth
+ * bit; element j + 16 the high nibble of byte j and bit j + 16 of qh.  The
+ * weight value is d * q + m with q in [0, 31] [Q5].
+ */
+static inline uint32_t rd32(const uint8_t* p) {
+    return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+int orc_q5_1_code(const uint8_t* w, int j) {
+    uint32_t qh = rd32(w + 4);
+    int nib = j < 16 ? (w[8 + j] & 0x0F) : (w[8 + j - 16] >> 4);
+    return nib | (int)((qh >> j) & 1u) << 4;
+}
+
+/* integer part of the Q5_1 x Q8_1 block dot: sum q_w * q_a */
+int32_t orc_isum_q5_1(const uint8_t* w, const uint8_t* a) {
+    int32_t s = 0;
+    for (int j = 0; j < ORC_QK; ++j) s += orc_q5_1_code(w, j) * (int32_t)(int8_t)a[4 + j];
+    return s;
+}
+
+static inline int fmt_bytes(int fmt) { return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34; }
 
 /* Dequantised value of element j of a weight block, for the cross-check tests. */
 double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
     double d = orc_f16_decode(rd16(w));
     if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
+    if (fmt == ORC_Q5_1) return d * (double)orc_q5_1_code(w, j) + orc_f16_decode(rd16(w + 2));
     int c = j < 16 ? (w[2 + j] & 0x0F) : (w[2 + j - 16] >> 4);
     return d * (double)(c - 8);
 }
 
 /*
  * One output of a quantised matrix-vector product:
- *   y = sum_b f16(d_w,b) * f16(d_a,b) * isum_b
- * Each term is exact in double (22-bit scale product times a 20-bit integer);
- * the terms are added in block order in double and the sum rounded to float.
+ *   y = sum_b f16(d_w,b) * f16(d_a,b) * isum_b  (+ f16(m_w,b) * f16(s_a,b) for Q5_1)
+ * Each term is exact in double (22-bit scale product times a 20-bit integer;
+ * two binary16 values); a block's terms and then the blocks are added in order
+ * in double and the sum rounded to float.  The Q5_1 min term takes s, the
+ * Q8_1 block's stored d * sum(q) [Q5], [KQ].
  */
 float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
     int bb = fmt_bytes(fmt);
@@ -194,9 +225,12 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
     for (int b = 0; b < nblk; ++b) {
         const uint8_t* w = row + (size_t)b * bb;
         const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
-        int32_t is = fmt == ORC_Q8_0 ? orc_isum_q8_0(w, a) : orc_isum_q4_0(w, a);
+        int32_t is = fmt == ORC_Q8_0 ? orc_isum_q8_0(w, a)
+                   : fmt == ORC_Q5_1 ? orc_isum_q5_1(w, a) : orc_isum_q4_0(w, a);
         if (isum_tap) isum_tap[b] = is;
-        acc += orc_f16_decode(rd16(w)) * orc_f16_decode(rd16(a)) * (double)is;
+        double c = orc_f16_decode(rd16(w)) * orc_f16_decode(rd16(a)) * (double)is;
+        if (fmt == ORC_Q5_1) c += orc_f16_decode(rd16(w + 2)) * orc_f16_decode(rd16(a + 2));
+        acc += c;
     }
     return (float)acc;
 }
@@ -416,6 +450,7 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     if (!d || !x || !Wr || !experts || !out || n < 0) return -1;
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
+    if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1) return -1;
     if (d->latent && d->dense_fmt != ORC_Q8_0 && d->dense_fmt != ORC_Q4_0) return -1;
     if (d->n_groups > 0) {                     /* every group holds E / n_groups experts */
         int G = d->n_groups;

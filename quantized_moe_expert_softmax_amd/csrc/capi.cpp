@@ -51,8 +51,10 @@ static bool mult(int v, int m) { return v > 0 && v % m == 0; }
 
 extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (!d) return fail(MOE_EINVAL, "desc is NULL");
-    if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0)
-        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is neither Q8_0 (8) nor Q4_0 (2)", d->expert_fmt);
+    if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0 &&
+        d->expert_fmt != MOE_FMT_Q5_1)
+        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7)",
+                    d->expert_fmt);
     // edge0-strata README, changes from upstream Strata: the latent D/U
     // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
     if (d->latent && d->dense_fmt != MOE_FMT_Q8_0 && d->dense_fmt != MOE_FMT_Q4_0)
@@ -88,7 +90,7 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     const int kin = d->latent ? d->latent : d->hidden;
     if (!mv_config_ok(kin, d->expert_fmt, true))
         return fail(MOE_EUNSUPPORTED, "no gate/up kernel for %d-wide %s rows", kin,
-                    d->expert_fmt == MOE_FMT_Q4_0 ? "Q4_0" : "Q8_0");
+                    d->expert_fmt == MOE_FMT_Q4_0 ? "Q4_0" : d->expert_fmt == MOE_FMT_Q5_1 ? "Q5_1" : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
     if (d->latent && (!mv_config_ok(d->hidden, d->dense_fmt, false) ||
@@ -160,7 +162,7 @@ static int gate_up_row(int p, int F) {
 // One matrix: canonical blocks (rows in canonical order) <-> packed codes/scales.
 static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t* canon,
                            uint8_t* packed, bool to_packed) {
-    const int bb = block_bytes(M.fmt), cb = code_bytes(M.fmt);
+    const int bb = block_bytes(M.fmt), cb = code_bytes(M.fmt), sb = side_bytes(M.fmt);
     uint8_t* codes = packed + M.codes_off;
     uint8_t* scales = packed + M.scales_off;
     for (int p = 0; p < M.rows; ++p) {
@@ -169,12 +171,12 @@ static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t*
             const size_t cpos = ((size_t)r * M.nblk + b) * bb;
             const size_t ppos = ((size_t)p * M.nblk + b);
             if (to_packed) {
-                memcpy(scales + 2 * ppos, canon + cpos, 2);
-                memcpy(codes + ppos * cb, canon + cpos + 2, cb);
+                memcpy(scales + sb * ppos, canon + cpos, sb);
+                memcpy(codes + ppos * cb, canon + cpos + sb, cb);
             } else {
                 uint8_t* c = const_cast<uint8_t*>(canon);
-                memcpy(c + cpos, scales + 2 * ppos, 2);
-                memcpy(c + cpos + 2, codes + ppos * cb, cb);
+                memcpy(c + cpos, scales + sb * ppos, sb);
+                memcpy(c + cpos + sb, codes + ppos * cb, cb);
             }
         }
     }
@@ -327,7 +329,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     const bool down_tok = T <= DOWN_TOK_MAX_T;
     // many tokens: grouped matrix-core GEMMs over token tiles
-    const bool gemm = T > MV_MAX_T;
+    // (Q5_1 experts have no matrix-core kernel: every T runs the matrix-vector
+    // kernels, which loop over an expert's tokens)
+    const bool gemm = T > MV_MAX_T && m.fmt != MOE_FMT_Q5_1;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

@@ -37,6 +37,26 @@ __device__ __forceinline__ int dot16(const v4i& w, const v4i& a) {
 // in the high nibble) against 32 int8 activations a_lo (elements 0..15) and
 // a_hi (16..31): sum_j c_j a_j, codes unsigned 0..15.  The caller subtracts
 // 8 * sum(a) to centre the codes.
+// bits 0..3 of x moved to bit 4 of bytes 0..3 (bit i to byte i): the four
+// copies x << 7i put bit i at bit 8i and nowhere else a byte starts
+__device__ __forceinline__ int spread4(uint32_t x) {
+    return (int)(((x * 0x00204081u) & 0x01010101u) << 4);
+}
+
+// Q5_1 block (16 nibble bytes w, fifth bits qh: element j at bit j) against
+// Q8_1 codes: elements 0..15 in a_lo, 16..31 in a_hi; codes are 0..31
+__device__ __forceinline__ int dot_q5(const v4i& w, uint32_t qh, const v4i& a_lo, const v4i& a_hi) {
+    const int m = 0x0F0F0F0F;
+    int s = dot4((w.x & m) | spread4(qh & 15u), a_lo.x, 0);
+    s = dot4((w.y & m) | spread4((qh >> 4) & 15u), a_lo.y, s);
+    s = dot4((w.z & m) | spread4((qh >> 8) & 15u), a_lo.z, s);
+    s = dot4((w.w & m) | spread4((qh >> 12) & 15u), a_lo.w, s);
+    s = dot4(((w.x >> 4) & m) | spread4((qh >> 16) & 15u), a_hi.x, s);
+    s = dot4(((w.y >> 4) & m) | spread4((qh >> 20) & 15u), a_hi.y, s);
+    s = dot4(((w.z >> 4) & m) | spread4((qh >> 24) & 15u), a_hi.z, s);
+    return dot4(((w.w >> 4) & m) | spread4(qh >> 28), a_hi.w, s);
+}
+
 __device__ __forceinline__ int dot_q4(const v4i& w, const v4i& a_lo, const v4i& a_hi) {
     const int m = 0x0F0F0F0F;
     int s = dot4(w.x & m, a_lo.x, 0);

@@ -16,6 +16,7 @@
 //   * rows are reduced with DPP row ops and the gfx950 row swaps.
 // Integer block sums are exact; scale products and row sums are fp32.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -23,9 +24,19 @@ namespace moe {
 
 template <int FMT>
 struct Fmt {
-    static constexpr int QB = FMT == MOE_FMT_Q4_0 ? 16 : 32;  // code bytes per block
-    static constexpr int CPB = FMT == MOE_FMT_Q4_0 ? 1 : 2;   // 16-byte chunks per block
+    static constexpr bool NIB = FMT != MOE_FMT_Q8_0;          // 16 nibble bytes per block
+    static constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
+    static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block
+    static constexpr int CPB = NIB ? 1 : 2;                   // 16-byte chunks per block
+    // a block's side data in memory and in registers: the binary16 d, or for
+    // Q5_1 {d | m << 16, qh}
+    using SideMem = std::conditional_t<Q5, uint2, uint16_t>;
+    using Side = std::conditional_t<Q5, uint2, uint32_t>;
 };
+
+// d of a block's side data
+__device__ __forceinline__ uint32_t side_d(uint32_t s) { return s; }
+__device__ __forceinline__ uint32_t side_d(uint2 s) { return s.x; }
 
 // Q8_1 of one value per lane of a 32-lane group (see quant_q8_1_32), returned
 // to every lane: code, (d, s) binary16 pair, code sum.
@@ -52,8 +63,10 @@ __device__ __forceinline__ Q81 q8_1_lane(float v) {
 // LDS staging of the activation rows a workgroup works on.
 //   s_q  int8  [n][K]
 //   s_d  float [n][K/32]   the binary16 d of each block, as float
-//   s_sq int   [n][K/32]   code sums (used by Q4_0 weights)
+//   s_sq int   [n][K/32]   code sums (used by Q4_0 weights); with S_VAL the
+//                          block's stored s as float bits instead (Q5_1 weights)
 // src_row[i] is the row of the source buffer that becomes LDS row i.
+template <bool S_VAL>
 __device__ __forceinline__ void stage_q(const ActPtr& a, int K, const int32_t* src_row, int n,
                                         int8_t* s_q, float* s_d, int32_t* s_sq) {
     const int nb = K / QK, c16 = K / 16;
@@ -65,12 +78,13 @@ __device__ __forceinline__ void stage_q(const ActPtr& a, int K, const int32_t* s
         const int i = idx / nb, b = idx - i * nb;
         const size_t g = (size_t)src_row[i] * nb + b;
         s_d[idx] = h2f(a.ds[g]);
-        s_sq[idx] = a.sq[g];
+        s_sq[idx] = S_VAL ? __float_as_int(h2f(a.ds[g] >> 16)) : a.sq[g];
     }
 }
 
 // fp32 rows quantised to Q8_1 straight into LDS; one 32-lane group per block.
 // When `keep` has a q pointer the blocks are also written to it (row src_row[i]).
+template <bool S_VAL>
 __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t* src_row, int n,
                                           int8_t* s_q, float* s_d, int32_t* s_sq, ActPtr keep) {
     const int nb = K / QK;
@@ -82,7 +96,7 @@ __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t
         s_q[i * K + b * QK + l] = (int8_t)r.q;
         if (l == 0) {
             s_d[blk] = h2f(r.ds);
-            s_sq[blk] = r.sum;
+            s_sq[blk] = S_VAL ? __float_as_int(h2f(r.ds >> 16)) : r.sum;
         }
         if (keep.q) {
             keep.q[row * K + b * QK + l] = (int8_t)r.q;
@@ -102,8 +116,9 @@ __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t
 // chunk and its contribution masked later), and the scale stays as raw binary16
 // bits until it is used, so no load waits on another.
 template <int FMT, int LPR, int CPL>
-__device__ __forceinline__ void load_row(const uint8_t* row, const uint16_t* rscl, int sl, int NCH,
-                                         v4i (&wq)[CPL], uint32_t (&wsc)[CPL]) {
+__device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<FMT>::SideMem* rscl,
+                                         int sl, int NCH, v4i (&wq)[CPL],
+                                         typename Fmt<FMT>::Side (&wsc)[CPL]) {
     using F = Fmt<FMT>;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -114,9 +129,13 @@ __device__ __forceinline__ void load_row(const uint8_t* row, const uint16_t* rsc
 }
 
 template <int FMT>
-__device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const int8_t* arow, const int32_t* asq,
-                                              int c) {
-    if constexpr (FMT == MOE_FMT_Q4_0) {
+__device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const typename Fmt<FMT>::Side& side,
+                                              const int8_t* arow, const int32_t* asq, int c) {
+    if constexpr (FMT == MOE_FMT_Q5_1) {
+        const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
+        const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
+        return dot_q5(wq, side.y, lo, hi);
+    } else if constexpr (FMT == MOE_FMT_Q4_0) {
         const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
         const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
         return dot_q4(wq, lo, hi) - 8 * asq[c];
@@ -128,7 +147,7 @@ __device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const int8_t* arow,
 
 // One pass: the rows of this pass (weights in wq/wsc) against the n staged rows.
 template <int FMT, int LPR, int CPL, bool TAP, class Emit, class EmitIsum>
-__device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const uint32_t (&wsc)[CPL], int r,
+__device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fmt<FMT>::Side (&wsc)[CPL], int r,
                                          int sl, int NCH, int nb, int n, int K,
                                          const int8_t* s_q, const float* s_d,
                                          const int32_t* s_sq, Emit& emit, EmitIsum& emit_isum,
@@ -145,8 +164,12 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const uint32_t (&
             const bool valid = j * LPR + sl < NCH;
             const int c = min(j * LPR + sl, NCH - 1);
             const int blk = c / F::CPB;
-            const int is = chunk_isum_lds<FMT>(wq[j], arow, asq, c);
-            acc = fmaf((float)is, valid ? h2f(wsc[j]) * ad[blk] : 0.0f, acc);
+            const int is = chunk_isum_lds<FMT>(wq[j], wsc[j], arow, asq, c);
+            acc = fmaf((float)is, valid ? h2f(side_d(wsc[j])) * ad[blk] : 0.0f, acc);
+            if constexpr (F::Q5) {
+                // min term: m_w times the activation block's stored s
+                acc = fmaf(valid ? h2f(wsc[j].x >> 16) : 0.0f, __int_as_float(asq[blk]), acc);
+            }
             if constexpr (TAP) {
                 if (tap) {
                     int full = is;
@@ -166,11 +189,12 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const uint32_t (&
 // pass's rows (it is never used) so that every load is unconditional.  On
 // entry A must hold pass 0 when `a_loaded`.
 template <int FMT, int LPR, int CPL, int NW, bool TAP, int PASSES = 0, class Emit, class EmitIsum>
-__device__ __forceinline__ void row_tile(const uint8_t* codes, const uint16_t* scl, size_t rowb,
+__device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fmt<FMT>::SideMem* scl,
+                                         size_t rowb,
                                          int nb, int rows, int n, int K, const int8_t* s_q,
                                          const float* s_d, const int32_t* s_sq, Emit emit,
                                          EmitIsum emit_isum, bool tap, v4i (&wA)[CPL],
-                                         uint32_t (&sA)[CPL], bool a_loaded) {
+                                         typename Fmt<FMT>::Side (&sA)[CPL], bool a_loaded) {
     using F = Fmt<FMT>;
     constexpr int RPW = 64 / LPR;
     const int NCH = nb * F::CPB;
@@ -187,7 +211,7 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const uint16_t* s
     }
     auto row_of = [&](int p) { return (min(p, passes - 1) * NW + wave) * RPW + rg; };
     v4i wB[CPL];
-    uint32_t sB[CPL];
+    typename F::Side sB[CPL];
     if (!a_loaded) {
         const int r = row_of(0);
         load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
@@ -246,7 +270,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
     const uint8_t* ebase = A.experts + (size_t)e * A.eb;
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * nb;
+    using SM = typename Fmt<FMT>::SideMem;
+    const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * nb;
 
     int8_t* s_q = reinterpret_cast<int8_t*>(smem);
     float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
 
     // the first pass of weights is requested before the activations are staged
     v4i wA[CPL];
-    uint32_t sA[CPL];
+    typename Fmt<FMT>::Side sA[CPL];
     {
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
@@ -274,9 +299,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         }
         __syncthreads();
         if (A.ain_f32)
-            stage_f32(A.ain_f32, K, s_t, n, s_q, s_d, s_sq, fb == 0 ? A.keep : ActPtr{});
+            stage_f32<Fmt<FMT>::Q5>(A.ain_f32, K, s_t, n, s_q, s_d, s_sq, fb == 0 ? A.keep : ActPtr{});
         else
-            stage_q(A.ain, K, s_t, n, s_q, s_d, s_sq);
+            stage_q<Fmt<FMT>::Q5>(A.ain, K, s_t, n, s_q, s_d, s_sq);
         __syncthreads();
         const bool tap = TAP && A.taps.isum_gu;
         auto emit = [&](int i, int r, float v) { s_gu[i * 64 + r] = v; };
@@ -349,7 +374,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     const int K = A.K, nb = K / QK, TCH = A.tch;
     const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
     const uint8_t* codes = mat + A.codes_off + (size_t)rt * A.rt * rowb;
-    const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.scales_off) + (size_t)rt * A.rt * nb;
+    using SM = typename Fmt<FMT>::SideMem;
+    const SM* scl = reinterpret_cast<const SM*>(mat + A.scales_off) + (size_t)rt * A.rt * nb;
     int8_t* s_q = reinterpret_cast<int8_t*>(smem);
     float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
     int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
@@ -357,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
 
     // the first pass of weights is requested before the activations are staged
     v4i wA[CPL];
-    uint32_t sA[CPL];
+    typename Fmt<FMT>::Side sA[CPL];
     {
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
@@ -370,9 +396,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
         if (threadIdx.x < n) s_s[threadIdx.x] = lst ? lst[i0 + threadIdx.x] : i0 + threadIdx.x;
         __syncthreads();
         if (A.ain_f32)
-            stage_f32(A.ain_f32, K, s_s, n, s_q, s_d, s_sq, rt == 0 ? A.keep : ActPtr{});
+            stage_f32<Fmt<FMT>::Q5>(A.ain_f32, K, s_s, n, s_q, s_d, s_sq, rt == 0 ? A.keep : ActPtr{});
         else
-            stage_q(A.ain, K, s_s, n, s_q, s_d, s_sq);
+            stage_q<Fmt<FMT>::Q5>(A.ain, K, s_s, n, s_q, s_d, s_sq);
         __syncthreads();
         const int r0 = rt * A.rt;
         auto emit = [&](int i, int r, float v) { A.out[(size_t)s_s[i] * A.rows + r0 + r] = v; };
@@ -424,9 +450,10 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         const int e = A.b.ids[a];
         const uint8_t* mat = A.experts + (size_t)e * A.eb + A.dn_off;
         const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
-        const uint16_t* scl = reinterpret_cast<const uint16_t*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * nb;
+        using SM = typename F::SideMem;
+        const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * nb;
         v4i wq[CPL], wn[CPL];
-        uint32_t wsc[CPL], wsn[CPL];
+        typename F::Side wsc[CPL], wsn[CPL];
         load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * nb, sl, NCH, wq, wsc);
         // this rank's activation chunks, the same for every row
         v4i act[CPL][NA];
@@ -438,7 +465,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
             const int c = min(jj * LPR + sl, NCH - 1);
 #pragma unroll
             for (int h = 0; h < NA; ++h) act[jj][h] = ld16(arow + c * 16 * NA + h * 16);
-            asq[jj] = F::CPB == 1 ? A.hq.sq[(size_t)a * nb + c] : 0;
+            asq[jj] = F::CPB == 1 && !F::Q5 ? A.hq.sq[(size_t)a * nb + c] : 0;
             ads[jj] = A.hq.ds[(size_t)a * nb + c / F::CPB];
         }
 #pragma unroll
@@ -453,11 +480,17 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
                 const int c = jj * LPR + sl;
                 const bool valid = c < NCH;
                 int is;
-                if constexpr (F::CPB == 1)
+                if constexpr (F::Q5)
+                    is = dot_q5(wq[jj], wsc[jj].y, act[jj][0], act[jj][NA - 1]);
+                else if constexpr (F::CPB == 1)
                     is = dot_q4(wq[jj], act[jj][0], act[jj][NA - 1]) - 8 * asq[jj];
                 else
                     is = dot16(wq[jj], act[jj][0]);
-                acc = fmaf((float)is, valid ? h2f(wsc[jj]) * h2f(ads[jj]) : 0.0f, acc);
+                acc = fmaf((float)is, valid ? h2f(side_d(wsc[jj])) * h2f(ads[jj]) : 0.0f, acc);
+                if constexpr (F::Q5) {
+                    // min term: m_w times the block's stored s
+                    acc = fmaf(valid ? h2f(wsc[jj].x >> 16) : 0.0f, h2f(ads[jj] >> 16), acc);
+                }
                 if constexpr (TAP) {
                     if (tap) {
                         int full = is;
@@ -503,7 +536,7 @@ static bool pick(int nch, int& lpr, int& cpl) {
     return false;
 }
 
-static int nchunks(int K, int fmt) { return fmt == MOE_FMT_Q4_0 ? K / 32 : K / 16; }
+static int nchunks(int K, int fmt) { return fmt == MOE_FMT_Q8_0 ? K / 16 : K / 32; }
 
 // gate/up: two passes of weights live at once, so at most 5 chunks per lane
 // (4 preferred: whole 4 KB rows per wave at K = 4096)
@@ -602,6 +635,9 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     if (m.fmt == MOE_FMT_Q4_0)
         return tap ? gate_up_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st, ev)
                    : gate_up_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st, ev);
+    if (m.fmt == MOE_FMT_Q5_1)
+        return tap ? gate_up_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, grid, lds, a, st, ev);
     return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
                : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
@@ -636,6 +672,9 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (fmt == MOE_FMT_Q4_0)
         return tap ? rows_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st)
                    : rows_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, grid, lds, a, st);
+    if (fmt == MOE_FMT_Q5_1)
+        return tap ? rows_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, grid, lds, a, st);
     return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
@@ -697,6 +736,9 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActP
     if (m.fmt == MOE_FMT_Q4_0)
         return tap ? down_tok_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, T, a, st)
                    : down_tok_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, T, a, st);
+    if (m.fmt == MOE_FMT_Q5_1)
+        return tap ? down_tok_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, T, a, st)
+                   : down_tok_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, T, a, st);
     return tap ? down_tok_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, T, a, st)
                : down_tok_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, T, a, st);
 }

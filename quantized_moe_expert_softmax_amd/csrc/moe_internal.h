@@ -2,9 +2,11 @@
 // library only; the public ABI is include/moe.h).
 //
 // Packed block matrix [rows][nblk] (any format): the codes of all rows first,
-// row-major (32 bytes per Q8_0 block, 16 per Q4_0 block, in element order for
-// Q8_0 and in the canonical nibble-byte order for Q4_0), then the binary16
-// scales, row-major [row][block].  Same byte count as the canonical blocks.
+// row-major (32 bytes per Q8_0 block, 16 per Q4_0 or Q5_1 block, in element
+// order for Q8_0 and in the canonical nibble-byte order otherwise), then each
+// block's side data, row-major [row][block]: the binary16 d (2 bytes), or for
+// Q5_1 d, m and qh (8 bytes, as in the canonical block).  The canonical block
+// is [side data][codes] in every format, and the byte count is the same.
 //
 // Packed expert: gate/up matrix of 2F rows then the down matrix [Kout][F/32].
 // The gate/up rows come in pairs of 32-row tiles: packed row fb*64 + r holds
@@ -21,8 +23,9 @@ namespace moe {
 constexpr int QK = 32;              // elements per block
 constexpr int Q8_1_CANON = 36;      // canonical Q8_1 block bytes
 
-inline int code_bytes(int fmt) { return fmt == MOE_FMT_Q4_0 ? 16 : 32; }
-inline int block_bytes(int fmt) { return code_bytes(fmt) + 2; }
+inline int code_bytes(int fmt) { return fmt == MOE_FMT_Q8_0 ? 32 : 16; }
+inline int side_bytes(int fmt) { return fmt == MOE_FMT_Q5_1 ? 8 : 2; }
+inline int block_bytes(int fmt) { return code_bytes(fmt) + side_bytes(fmt); }
 
 struct MatLayout {                  // one packed block matrix
     int rows = 0, nblk = 0, fmt = MOE_FMT_Q8_0;

@@ -37,7 +37,9 @@ _lib = None
 
 Q8_0 = 8
 Q4_0 = 2
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18}
+Q5_1 = 7
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24}
+S_MIN = 1 << 40      # added to a block set's scale stream for its Q5_1 minimums
 
 
 def build_synth(force: bool = False) -> str:
@@ -99,7 +101,7 @@ def absnormal_f64(seed: int, stream: int, n: int, scale: float, first: int = 0) 
 
 def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
            out: Optional[np.ndarray] = None) -> np.ndarray:
-    """nblk canonical weight blocks of format fmt, as a uint8 array of nblk * 34 (or 18) bytes."""
+    """nblk canonical weight blocks of format fmt, as a uint8 array of nblk * 34 (18, 24) bytes."""
     lib = _L()
     if fmt == Q8_0:
         pay = 32
@@ -111,6 +113,15 @@ def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
         payload = np.empty(nblk * pay, dtype=np.uint8)
         lib.synth_nibble_bytes(seed, q_stream, 0, nblk * pay, _ptr(payload))
         scale = absnormal_f64(seed, d_stream, nblk, 0.02 / 8.0)
+    elif fmt == Q5_1:
+        # binary16 m, then qh (4 bytes) and the 16 nibble bytes, all bits uniform
+        pay = 22
+        raw = np.empty(nblk * 20, dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, q_stream, 0, nblk * 20, _ptr(raw))
+        scale = absnormal_f64(seed, d_stream, nblk, 0.02 / 16.0)
+        mins = -absnormal_f64(seed, d_stream + S_MIN, nblk, 0.02 / 2.0)
+        m16 = mins.astype(np.float16).view(np.uint8).reshape(nblk, 2)
+        payload = np.ascontiguousarray(np.concatenate([m16, raw.reshape(nblk, 20)], axis=1)).reshape(-1)
     else:
         raise ValueError(f"unknown block format {fmt}")
     d16 = scale.astype(np.float16).view(np.uint16)
@@ -180,6 +191,8 @@ WORKLOADS = {
                           latent=1792, expert_fmt=Q4_0, n_groups=16, topk_groups=4, seed=1003),
     "prefill": Workload("prefill", hidden=4096, n_experts=128, top_k=8, n_ff=1536, tokens=2048,
                         bias=True, seed=1004),
+    "decode_q5_1": Workload("decode_q5_1", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
+                            tokens=1, expert_fmt=Q5_1, seed=1005),
 }
 
 

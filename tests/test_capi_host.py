@@ -46,6 +46,7 @@ def _refused(desc, status, word):
 def test_desc_refusals_name_the_cause(L):
     ok = dict(hidden=512, n_experts=8, top_k=2, n_ff=256, max_tokens=4)
     _refused(moe.make_desc(**{**ok, "expert_fmt": 6}), moe.MOE_EUNSUPPORTED, "expert_fmt")
+    _refused(moe.make_desc(**{**ok, "latent": 256, "dense_fmt": 7}), moe.MOE_EUNSUPPORTED, "dense_fmt")
     _refused(moe.make_desc(**{**ok, "hidden": 500}), moe.MOE_EUNSUPPORTED, "hidden")
     _refused(moe.make_desc(**{**ok, "hidden": 0}), moe.MOE_EINVAL, "hidden")
     _refused(moe.make_desc(**{**ok, "n_ff": 384}), moe.MOE_EUNSUPPORTED, "n_ff")
@@ -94,7 +95,7 @@ def _small(fmt=8, latent=0):
                           latent=latent, expert_fmt=fmt, seed=77)
 
 
-@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (8, 256), (2, 256)])
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (8, 256), (2, 256), (7, 256)])
 def test_pack_roundtrip(L, fmt, latent):
     w = _small(fmt, latent)
     d = moe.desc_of(w)
@@ -115,17 +116,18 @@ def test_pack_roundtrip(L, fmt, latent):
             assert np.array_equal(b, t)
 
 
-@pytest.mark.parametrize("fmt", [8, 2])
+@pytest.mark.parametrize("fmt", [8, 2, 7])
 def test_pack_layout_positions(L, fmt):
-    """Spot-check the documented packed layout: codes of all rows, then binary16 scales;
-    gate/up rows interleaved in 32-row tiles."""
+    """Spot-check the documented packed layout: codes of all rows, then each block's side
+    data (binary16 d; for Q5_1 d, m and qh); gate/up rows interleaved in 32-row tiles."""
     w = _small(fmt)
     d = moe.desc_of(w)
     ex = synth.gen_experts(w)
     packed = np.empty_like(ex)
     moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
-    bb = 34 if fmt == 8 else 18
-    cb = bb - 2
+    bb = {8: 34, 2: 18, 7: 24}[fmt]
+    sb = 8 if fmt == 7 else 2
+    cb = bb - sb
     F, K = w.n_ff, w.hidden
     nb = K // 32
     e = 2
@@ -137,8 +139,8 @@ def test_pack_layout_positions(L, fmt):
                                     (F + 33, 97), (F - 1, 64 * (F // 32 - 1) + 31)]:
         for b in (0, nb - 1, 5):
             cblk = blob[(canon_row * nb + b) * bb:(canon_row * nb + b + 1) * bb]
-            assert np.array_equal(codes_gu[(packed_row * nb + b) * cb:(packed_row * nb + b + 1) * cb], cblk[2:])
-            assert np.array_equal(scales_gu[(packed_row * nb + b) * 2:(packed_row * nb + b) * 2 + 2], cblk[:2])
+            assert np.array_equal(codes_gu[(packed_row * nb + b) * cb:(packed_row * nb + b + 1) * cb], cblk[sb:])
+            assert np.array_equal(scales_gu[(packed_row * nb + b) * sb:(packed_row * nb + b) * sb + sb], cblk[:sb])
     # down matrix: rows in order
     dn_c = blob[2 * F * nb * bb:]
     dn_p = pk[2 * F * nb * bb:]
@@ -146,9 +148,9 @@ def test_pack_layout_positions(L, fmt):
     rows = w.k_out
     for r, b in [(0, 0), (rows - 1, nbf - 1), (17, 3)]:
         cblk = dn_c[(r * nbf + b) * bb:(r * nbf + b + 1) * bb]
-        assert np.array_equal(dn_p[(r * nbf + b) * cb:(r * nbf + b + 1) * cb], cblk[2:])
-        off = rows * nbf * cb + (r * nbf + b) * 2
-        assert np.array_equal(dn_p[off:off + 2], cblk[:2])
+        assert np.array_equal(dn_p[(r * nbf + b) * cb:(r * nbf + b + 1) * cb], cblk[sb:])
+        off = rows * nbf * cb + (r * nbf + b) * sb
+        assert np.array_equal(dn_p[off:off + sb], cblk[:sb])
 
 
 def test_forward_argument_checks_without_gpu(L):

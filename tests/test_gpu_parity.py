@@ -138,6 +138,25 @@ def test_q4_0_dense_projections(kw):
     _report("dense q4_0 " + str(kw), w.tokens, rep)
 
 
+# Q5_1 experts (the min term takes the Q8_1 block's stored s): decode, a verify
+# window, the 9..32-token path, more than 32 tokens (still the matrix-vector
+# kernels), latent layers, wider rows
+@pytest.mark.parametrize("kw", [
+    dict(expert_fmt=synth.Q5_1, tokens=1),
+    dict(expert_fmt=synth.Q5_1, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
+    dict(expert_fmt=synth.Q5_1, tokens=20),
+    dict(expert_fmt=synth.Q5_1, tokens=70, bias=True),
+    dict(expert_fmt=synth.Q5_1, latent=256, n_experts=16, top_k=4, tokens=6),
+    dict(expert_fmt=synth.Q5_1, latent=256, n_experts=16, top_k=4, tokens=40),
+    dict(expert_fmt=synth.Q5_1, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
+    dict(expert_fmt=synth.Q5_1, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=6),
+])
+def test_q5_1_experts(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("q5_1 " + str(kw), w.tokens, rep)
+
+
 # path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [

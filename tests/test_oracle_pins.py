@@ -294,6 +294,81 @@ def test_isum_q4_0_bruteforce(orc):
         assert orc.isum(2, w[i], a[i]) == ref
 
 
+def _q5_1_block(c):
+    w = np.zeros(24, np.uint8)
+    d, m = int(c["d16"], 16), int(c["m16"], 16)
+    w[0], w[1], w[2], w[3] = d & 0xFF, d >> 8, m & 0xFF, m >> 8
+    w[4:8] = np.frombuffer(bytes.fromhex(c["qh"]), np.uint8)
+    w[8:] = np.frombuffer(bytes.fromhex(c["qs"]), np.uint8)
+    return w
+
+
+def test_q5_1_golden_blocks(orc):
+    """Hand-derived Q5_1 blocks: bit and nibble order of the codes, the little-endian qh, and
+    the min term, which multiplies the Q8_1 block's stored s (not d_a * sum(q_a))."""
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    assert len(g["q5_1"]) == 7
+    for c in g["q5_1"]:
+        w = _q5_1_block(c)
+        a = np.zeros(36, np.uint8)
+        ad, as_ = int(c["a_d16"], 16), int(c["a_s16"], 16)
+        a[0], a[1], a[2], a[3] = ad & 0xFF, ad >> 8, as_ & 0xFF, as_ >> 8
+        a[4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+        assert orc.isum(7, w, a) == c["isum"], c["name"]
+        y = orc.matvec(7, w, 1, 1, a)
+        assert y[0] == np.float32(c["y"]), (c["name"], y[0])
+
+
+def _rand_q5_1(rng, n):
+    b = np.zeros((n, 24), np.uint8)
+    d = (np.abs(rng.standard_normal(n)) * 0.02 / 16).astype(np.float16).view(np.uint16)
+    m = (-np.abs(rng.standard_normal(n)) * 0.01).astype(np.float16).view(np.uint16)
+    b[:, 0], b[:, 1] = d & 0xFF, d >> 8
+    b[:, 2], b[:, 3] = m & 0xFF, m >> 8
+    b[:, 4:] = rng.integers(0, 256, (n, 20)).astype(np.uint8)
+    return b
+
+
+def test_isum_q5_1_bruteforce(orc):
+    """The integer part against numpy bit arithmetic on random blocks."""
+    rng = np.random.default_rng(24)
+    w = _rand_q5_1(rng, 200)
+    a = _rand_q8_1(orc, rng, 200)
+    for i in range(200):
+        qh = int.from_bytes(bytes(w[i, 4:8]), "little")
+        nib = np.concatenate([w[i, 8:] & 0x0F, w[i, 8:] >> 4]).astype(np.int64)
+        hi = np.array([(qh >> j) & 1 for j in range(32)], np.int64)
+        ref = int(np.dot(nib | (hi << 4), a[i, 4:].view(np.int8).astype(np.int64)))
+        assert orc.isum(7, w[i], a[i]) == ref
+
+
+def test_q5_1_row_is_dequantised_dot_with_the_stored_s(orc):
+    """A Q5_1 row equals the fp64 dot of the dequantised weights (d*q + m) with the Q8_1
+    activations when the activation sum is taken as each block's stored s: the d*q part is
+    exact per block and the m part is m * s."""
+    rng = np.random.default_rng(25)
+    nblk = 10
+    W = _rand_q5_1(rng, 3 * nblk)
+    A = _rand_q8_1(orc, rng, nblk)
+    y, isum = orc.matvec(7, W.reshape(-1), 3, nblk, A.reshape(-1), with_isum=True)
+    for r in range(3):
+        acc = 0.0
+        for b in range(nblk):
+            wb = W[r * nblk + b]
+            da = orc.f16_decode(int(A[b, 0]) | int(A[b, 1]) << 8)
+            sa = orc.f16_decode(int(A[b, 2]) | int(A[b, 3]) << 8)
+            dw = orc.f16_decode(int(wb[0]) | int(wb[1]) << 8)
+            mw = orc.f16_decode(int(wb[2]) | int(wb[3]) << 8)
+            qa = A[b, 4:].view(np.int8).astype(np.int64)
+            # d*q part: the dequantised codes times the dequantised activations, exact
+            part = math.fsum((orc.dequant_weight(7, wb, j) - mw) * da * int(qa[j]) for j in range(32))
+            assert part == dw * da * isum[r, b]
+            # the stored s is d * sum(q_a) (fp32 d, rounded to binary16), not the float sum
+            assert sa == pytest.approx(da * int(qa.sum()), rel=2 ** -9, abs=2 ** -24)
+            acc += part + mw * sa
+        assert y[r] == np.float32(acc)
+
+
 @pytest.mark.parametrize("fmt", [8, 2])
 def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
     """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
