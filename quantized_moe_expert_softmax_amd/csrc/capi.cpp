@@ -329,9 +329,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     const bool down_tok = T <= DOWN_TOK_MAX_T;
     // many tokens: grouped matrix-core GEMMs over token tiles
-    // (Q5_1 experts have no matrix-core kernel: every T runs the matrix-vector
-    // kernels, which loop over an expert's tokens)
-    const bool gemm = T > MV_MAX_T && m.fmt != MOE_FMT_Q5_1;
+    const bool gemm = T > MV_MAX_T;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

@@ -11,8 +11,10 @@
 //   * a group of LPR lanes owns a weight row; lane sl loads the 16-byte chunks
 //     c = j*LPR + sl (j < CPL), so each wave's loads are contiguous; one pass of
 //     rows sits in registers while the next pass is already being loaded;
-//   * each chunk is 16 int8 codes (half a Q8_0 block) or one Q4_0 block, dotted
-//     with v_dot4 against the LDS activations, scaled by d_w * d_a per block;
+//   * each chunk is 16 int8 codes (half a Q8_0 block) or one Q4_0 / Q5_1 block
+//     (Q5_1's fifth bits from the block's side data), dotted with v_dot4
+//     against the LDS activations, scaled by d_w * d_a per block (plus Q5_1's
+//     m_w * s_a);
 //   * rows are reduced with DPP row ops and the gfx950 row swaps.
 // Integer block sums are exact; scale products and row sums are fp32.
 #include <algorithm>

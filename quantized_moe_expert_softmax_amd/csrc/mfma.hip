@@ -426,11 +426,18 @@ constexpr int MS_ROWB = MF_KB * QK + 16;  // LDS bytes per staged row (padded)
 // lanes 32..63)
 constexpr int MS_SWR = MF_NT + 32, MS_SAR = MF_MT + 32;
 
-template <bool SWIGLU, bool TAP>
+// Q5_1 (FMT): the fifth bits come from each block's side data {d | m << 16, qh},
+// the codes widen to int8 0..31, and each stage adds the min terms
+// sum_b m_w[r][b] * s_a[t][b] with one more f16 outer product per row tile:
+// the four blocks' m and s in the k slots 0..3 of lanes 0..31.
+template <bool SWIGLU, bool TAP, int FMT>
 __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
-    constexpr int QB = 16;                                // code bytes per Q4_0 block
+    constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
+    constexpr int QB = 16;                                // code bytes per Q4_0 / Q5_1 block
     constexpr int WBYTES = MF_NT * MS_ROWB, XBYTES = MF_MT * MS_ROWB;
-    constexpr int STAGE = WBYTES + XBYTES + MF_KB * MS_SWR * 2 + MF_KB * MS_SAR * 2;
+    constexpr int SCB = MF_KB * MS_SWR * 2 + MF_KB * MS_SAR * 2;
+    constexpr int MINB = Q5 ? (MF_NT + MF_MT) * MF_KB * 2 : 0;   // m_w [row][4], s_a [col][4]
+    constexpr int STAGE = WBYTES + XBYTES + SCB + MINB;
     __shared__ __align__(16) char smem[2 * STAGE];
     __shared__ int s_row[MF_MT], s_orow[MF_MT];
 
@@ -450,13 +457,16 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
     const size_t rowb = (size_t)nb * QB;
     const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
     const uint16_t* scl = reinterpret_cast<const uint16_t*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
+    const uint2* side = reinterpret_cast<const uint2*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
 
     // ---- global -> registers -> LDS staging of one stage (blocks kb0 .. kb0+MF_KB)
-    constexpr int WCH = 2;                     // 16-byte chunks (= Q4_0 blocks) per thread
+    constexpr int WCH = 2;                     // 16-byte chunks (= blocks) per thread
     constexpr int WCPR = MF_KB * QB / 16;      // chunks per weight row per stage
     v4i rw[WCH];
+    uint32_t rq[WCH];                          // Q5_1: qh of each chunk's block
     v4i rx[2];
     uint2 rdw;
+    v4i rsd[2];                                // Q5_1: the row's side data, 4 blocks
     v4i rda;
     auto gload = [&](int kb0) {
 #pragma unroll
@@ -464,6 +474,7 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             const int ch = tid + j * MF_THREADS;
             const int r = ch / WCPR, p = ch - r * WCPR;
             rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * QB + p * 16);
+            if constexpr (Q5) rq[j] = side[(size_t)r * nb + kb0 + p].y;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -472,7 +483,12 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             rx[j] = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)kb0 * QK + p * 16);
         }
         if (tid < MF_NT) {
-            rdw = *reinterpret_cast<const uint2*>(scl + (size_t)tid * nb + kb0);
+            if constexpr (Q5) {
+                rsd[0] = ld16(side + (size_t)tid * nb + kb0);
+                rsd[1] = ld16(side + (size_t)tid * nb + kb0 + 2);
+            } else {
+                rdw = *reinterpret_cast<const uint2*>(scl + (size_t)tid * nb + kb0);
+            }
         } else if (tid < MF_NT + MF_MT) {
             const int c = tid - MF_NT;
             rda = *reinterpret_cast<const v4i*>(A.ain.ds + (size_t)s_row[c] * nb + kb0);
@@ -488,13 +504,18 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
         for (int j = 0; j < WCH; ++j) {
             const int ch = tid + j * MF_THREADS;
             const int r = ch / WCPR, p = ch - r * WCPR;
-            // one Q4_0 block (16 bytes) -> 32 int8: elements 0..15, then 16..31
+            // one block (16 bytes) -> 32 int8: elements 0..15, then 16..31
             v4i lo, hi;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t x = (uint32_t)rw[j][d];
-                lo[d] = (int)q4_widen(x & 0x0F0F0F0Fu);
-                hi[d] = (int)q4_widen((x >> 4) & 0x0F0F0F0Fu);
+                if constexpr (Q5) {
+                    lo[d] = (int)(x & 0x0F0F0F0Fu) | spread4((rq[j] >> (4 * d)) & 15u);
+                    hi[d] = (int)((x >> 4) & 0x0F0F0F0Fu) | spread4((rq[j] >> (16 + 4 * d)) & 15u);
+                } else {
+                    lo[d] = (int)q4_widen(x & 0x0F0F0F0Fu);
+                    hi[d] = (int)q4_widen((x >> 4) & 0x0F0F0F0Fu);
+                }
             }
             *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32) = lo;
             *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32 + 16) = hi;
@@ -506,14 +527,32 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             *reinterpret_cast<v4i*>(sx + c * MS_ROWB + p * 16) = rx[j];
         }
         if (tid < MF_NT) {
-            sdw[0 * MS_SWR + tid] = (uint16_t)(rdw.x & 0xffffu);
-            sdw[1 * MS_SWR + tid] = (uint16_t)(rdw.x >> 16);
-            sdw[2 * MS_SWR + tid] = (uint16_t)(rdw.y & 0xffffu);
-            sdw[3 * MS_SWR + tid] = (uint16_t)(rdw.y >> 16);
+            if constexpr (Q5) {
+                // side words: {d | m << 16, qh} per block; blocks 0,1 in rsd[0], 2,3 in rsd[1]
+                const uint32_t dm[4] = {(uint32_t)rsd[0].x, (uint32_t)rsd[0].z, (uint32_t)rsd[1].x,
+                                        (uint32_t)rsd[1].z};
+                uint16_t* smw = sda + MF_KB * MS_SAR;
+#pragma unroll
+                for (int q = 0; q < MF_KB; ++q) sdw[q * MS_SWR + tid] = (uint16_t)(dm[q] & 0xffffu);
+                *reinterpret_cast<uint2*>(smw + tid * MF_KB) =
+                    uint2{(dm[0] >> 16) | (dm[1] & 0xffff0000u), (dm[2] >> 16) | (dm[3] & 0xffff0000u)};
+            } else {
+                sdw[0 * MS_SWR + tid] = (uint16_t)(rdw.x & 0xffffu);
+                sdw[1 * MS_SWR + tid] = (uint16_t)(rdw.x >> 16);
+                sdw[2 * MS_SWR + tid] = (uint16_t)(rdw.y & 0xffffu);
+                sdw[3 * MS_SWR + tid] = (uint16_t)(rdw.y >> 16);
+            }
         } else if (tid < MF_NT + MF_MT) {
             const int c = tid - MF_NT;
 #pragma unroll
             for (int q = 0; q < MF_KB; ++q) sda[q * MS_SAR + c] = (uint16_t)((uint32_t)rda[q] & 0xffffu);
+            if constexpr (Q5) {
+                // the activation blocks' stored s (high halves of ds)
+                uint16_t* sas = sda + MF_KB * MS_SAR + MF_NT * MF_KB;
+                *reinterpret_cast<uint2*>(sas + c * MF_KB) =
+                    uint2{((uint32_t)rda[0] >> 16) | ((uint32_t)rda[1] & 0xffff0000u),
+                          ((uint32_t)rda[2] >> 16) | ((uint32_t)rda[3] & 0xffff0000u)};
+            }
         }
     };
 
@@ -546,6 +585,24 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             dc = scale_op(sda[kb * MS_SAR + o_a]);
         };
         mf_stage<SWIGLU, TAP>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+        if constexpr (Q5) {
+            // min terms of the stage's four blocks (k slots 0..3; lanes 32..63 zero)
+            const uint16_t* smw = sda + MF_KB * MS_SAR;
+            const uint16_t* sas = smw + MF_NT * MF_KB;
+            const h4 z{};
+            const h4 m0 = *reinterpret_cast<const h4*>(smw + (w.wr * 64 + w.l32) * MF_KB);
+            const h4 m1 = *reinterpret_cast<const h4*>(smw + (w.wr * 64 + 32 + w.l32) * MF_KB);
+            const h4 sv = *reinterpret_cast<const h4*>(sas + (w.wc * 32 + w.l32) * MF_KB);
+            const v16f p0 = __builtin_amdgcn_mfma_f32_32x32x8f16(w.half ? z : m0, w.half ? z : sv,
+                                                                 v16f{}, 0, 0, 0);
+            const v16f p1 = __builtin_amdgcn_mfma_f32_32x32x8f16(w.half ? z : m1, w.half ? z : sv,
+                                                                 v16f{}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] += p0[i];
+                acc1[i] += p1[i];
+            }
+        }
     };
     gload(0);
     lstore(0);
@@ -574,9 +631,14 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
     const dim3 grid((unsigned)blocks), block(MF_THREADS);
     if (fmt == MOE_FMT_Q4_0) {
         if (tap)
-            launch_k(k_mfma_q4<SWIGLU, true>, grid, block, 0, st, ev, a);
+            launch_k(k_mfma_q4<SWIGLU, true, MOE_FMT_Q4_0>, grid, block, 0, st, ev, a);
         else
-            launch_k(k_mfma_q4<SWIGLU, false>, grid, block, 0, st, ev, a);
+            launch_k(k_mfma_q4<SWIGLU, false, MOE_FMT_Q4_0>, grid, block, 0, st, ev, a);
+    } else if (fmt == MOE_FMT_Q5_1) {
+        if (tap)
+            launch_k(k_mfma_q4<SWIGLU, true, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_q4<SWIGLU, false, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
     } else {
         if (tap)
             launch_k(k_mfma_dma<SWIGLU, true>, grid, block, 0, st, ev, a);
