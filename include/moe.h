@@ -63,8 +63,12 @@ typedef enum {
  * commit: Q5_1 experts): 24-byte blocks of binary16 d, binary16 m, a 32-bit
  * little-endian qh of fifth bits and 16 nibble bytes, value d*q + m; its dot
  * with a Q8_1 block adds m times the block's stored s (d times the sum of the
- * quantised activations).  Q5_1 is an expert format only. */
-enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7 };
+ * quantised activations).  Q4_K (same commit: Q4_K experts): 144-byte
+ * super-blocks of 256 (binary16 d and dmin, 12 bytes of 6-bit sub-block scales
+ * and mins, 128 nibble bytes), value d*scale*q - dmin*min, the min term on
+ * each Q8_1 block's code sum times its d; it needs Kin and n_ff to be
+ * multiples of 256.  Q5_1 and Q4_K are expert formats only. */
+enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12 };
 
 /* Which packed tensor a pack call is about. */
 enum { MOE_PACK_EXPERTS = 0, MOE_PACK_D = 1, MOE_PACK_U = 2 };
@@ -75,7 +79,7 @@ typedef struct {
     int32_t top_k;        /* k: 1..min(E, 32)                                             */
     int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
     int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
-    int32_t expert_fmt;   /* MOE_FMT_Q8_0, MOE_FMT_Q4_0 or MOE_FMT_Q5_1                   */
+    int32_t expert_fmt;   /* MOE_FMT_Q8_0, MOE_FMT_Q4_0, MOE_FMT_Q5_1 or MOE_FMT_Q4_K     */
     int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 or MOE_FMT_Q4_0 (latent == 0: unused)*/
     int32_t n_groups;     /* 0 = no group limit; else divides E                           */
     int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/

@@ -21,6 +21,7 @@ _lib = None
 Q8_0 = 8
 Q4_0 = 2
 Q5_1 = 7
+Q4_K = 12
 Q8_1_BYTES = 36
 
 
@@ -72,6 +73,12 @@ def lib():
         L.orc_isum_q5_1.restype = ctypes.c_int32
         L.orc_q5_1_code.argtypes = [vp, i32]
         L.orc_q5_1_code.restype = ctypes.c_int
+        L.orc_q4_k_code.argtypes = [vp, i32]
+        L.orc_q4_k_code.restype = ctypes.c_int
+        L.orc_q4_k_scale_min.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+        L.orc_q4_k_scale_min.restype = None
+        L.orc_isum_q4_k.argtypes = [vp, i32, vp]
+        L.orc_isum_q4_k.restype = ctypes.c_int32
         L.orc_dequant_weight.argtypes = [i32, vp, i32]
         L.orc_dequant_weight.restype = ctypes.c_double
         L.orc_row_dot.argtypes = [i32, vp, vp, i32, vp]
@@ -127,6 +134,24 @@ def isum(fmt: int, wblk: np.ndarray, ablk: np.ndarray) -> int:
     ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
     f = {Q8_0: lib().orc_isum_q8_0, Q4_0: lib().orc_isum_q4_0, Q5_1: lib().orc_isum_q5_1}[fmt]
     return int(f(_p(wblk), _p(ablk)))
+
+
+def q4_k_code(sblk: np.ndarray, e: int) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    return int(lib().orc_q4_k_code(_p(sblk), e))
+
+
+def q4_k_scale_min(sblk: np.ndarray, b: int):
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    sc, mn = ctypes.c_int(), ctypes.c_int()
+    lib().orc_q4_k_scale_min(_p(sblk), b, ctypes.byref(sc), ctypes.byref(mn))
+    return sc.value, mn.value
+
+
+def isum_q4_k(sblk: np.ndarray, b: int, ablk: np.ndarray) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
+    return int(lib().orc_isum_q4_k(_p(sblk), b, _p(ablk)))
 
 
 def q5_1_code(wblk: np.ndarray, j: int) -> int:

@@ -20,6 +20,8 @@
  *        Q5_1 blocks), whose min term multiplies the sum of the QUANTISED
  *        activations of the Q8_1 block (the ggml CPU convention), not the
  *        float sum of the activations.
+ *   [QK] same commit: Q4_K experts, whose dot is llama.cpp's q4_K x q8_1 (the
+ *        min term on the sum of the quantised activations of each Q8_1 block).
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
  *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
  *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
@@ -40,12 +42,13 @@
 #define ORC_Q8_0 8
 #define ORC_Q4_0 2
 #define ORC_Q5_1 7
+#define ORC_Q4_K 12
 #define ORC_QK 32
 #define ORC_Q8_1_BYTES 36
 
 typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
-    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0 or ORC_Q5_1 */
+    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1 or ORC_Q4_K */
     int n_groups, topk_groups;/* 0 = no group limit */
     int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
@@ -200,13 +203,53 @@ int32_t orc_isum_q5_1(const uint8_t* w, const uint8_t* a) {
     return s;
 }
 
-static inline int fmt_bytes(int fmt) { return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34; }
+/*
+ * Q4_K: super-blocks of 256 elements (8 sub-blocks of 32) in 144 bytes:
+ * binary16 d, binary16 dmin, 12 bytes of 6-bit sub-block scales and mins, 128
+ * nibble bytes.  Sub-block b < 4: scale = s[b] & 63, min = s[b + 4] & 63; b >= 4:
+ * scale = (s[b + 4] & 15) | (s[b - 4] >> 6) << 4, min = (s[b + 4] >> 4) |
+ * (s[b] >> 6) << 4.  Element i of sub-block b is byte 32 * (b / 2) + i of the
+ * nibble bytes, its low nibble for even b and its high nibble for odd b.  The
+ * value is d * scale * q - dmin * min [QK] (llama.cpp's Q4_K).
+ */
+void orc_q4_k_scale_min(const uint8_t* sb, int b, int* sc, int* mn) {
+    const uint8_t* s = sb + 4;
+    if (b < 4) {
+        *sc = s[b] & 63;
+        *mn = s[b + 4] & 63;
+    } else {
+        *sc = (s[b + 4] & 15) | (s[b - 4] >> 6) << 4;
+        *mn = (s[b + 4] >> 4) | (s[b] >> 6) << 4;
+    }
+}
+
+int orc_q4_k_code(const uint8_t* sb, int e) {
+    int b = e / 32, i = e % 32;
+    uint8_t v = sb[16 + 32 * (b / 2) + i];
+    return b % 2 ? v >> 4 : v & 0x0F;
+}
+
+/* integer part of sub-block b against one Q8_1 block: sum q * q_a */
+int32_t orc_isum_q4_k(const uint8_t* sb, int b, const uint8_t* a) {
+    int32_t s = 0;
+    for (int i = 0; i < ORC_QK; ++i) s += orc_q4_k_code(sb, 32 * b + i) * (int32_t)(int8_t)a[4 + i];
+    return s;
+}
+
+static inline int fmt_bytes(int fmt) {
+    return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34;   /* per 32; Q4_K: 144 per 256 */
+}
 
 /* Dequantised value of element j of a weight block, for the cross-check tests. */
 double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
     double d = orc_f16_decode(rd16(w));
     if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
     if (fmt == ORC_Q5_1) return d * (double)orc_q5_1_code(w, j) + orc_f16_decode(rd16(w + 2));
+    if (fmt == ORC_Q4_K) {                         /* w: the super-block, j < 256 */
+        int sc, mn;
+        orc_q4_k_scale_min(w, j / 32, &sc, &mn);
+        return d * sc * (double)orc_q4_k_code(w, j) - orc_f16_decode(rd16(w + 2)) * mn;
+    }
     int c = j < 16 ? (w[2 + j] & 0x0F) : (w[2 + j - 16] >> 4);
     return d * (double)(c - 8);
 }
@@ -220,8 +263,29 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
  * Q8_1 block's stored d * sum(q) [Q5], [KQ].
  */
 float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
-    int bb = fmt_bytes(fmt);
     double acc = 0.0;
+    if (fmt == ORC_Q4_K) {
+        /*
+         * Sub-block b against Q8_1 block b: d * scale_b * d_a * isum_b minus
+         * dmin * min_b * d_a * sum(q_a), the activation sum taken from the
+         * codes (llama.cpp's q4_K x q8_1); each term exact in double.
+         */
+        for (int b = 0; b < nblk; ++b) {
+            const uint8_t* sb = row + (size_t)(b / 8) * 144;
+            const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
+            int sc, mn;
+            orc_q4_k_scale_min(sb, b % 8, &sc, &mn);
+            int32_t is = orc_isum_q4_k(sb, b % 8, a), qs = 0;
+            for (int i = 0; i < ORC_QK; ++i) qs += (int8_t)a[4 + i];
+            if (isum_tap) isum_tap[b] = is;
+            double da = orc_f16_decode(rd16(a));
+            double c = orc_f16_decode(rd16(sb)) * sc * da * (double)is;
+            c -= orc_f16_decode(rd16(sb + 2)) * mn * da * (double)qs;
+            acc += c;
+        }
+        return (float)acc;
+    }
+    int bb = fmt_bytes(fmt);
     for (int b = 0; b < nblk; ++b) {
         const uint8_t* w = row + (size_t)b * bb;
         const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
@@ -236,9 +300,13 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
 }
 
 /* rows outputs of a [rows][nblk] block matrix times a Q8_1 vector */
+static size_t row_bytes(int fmt, int nblk) {
+    return fmt == ORC_Q4_K ? (size_t)(nblk / 8) * 144 : (size_t)nblk * fmt_bytes(fmt);
+}
+
 void orc_matvec(int fmt, int rows, int nblk, const uint8_t* W, const uint8_t* act, float* y,
                 int32_t* isum_tap) {
-    size_t rb = (size_t)nblk * fmt_bytes(fmt);
+    size_t rb = row_bytes(fmt, nblk);
     for (int r = 0; r < rows; ++r)
         y[r] = orc_row_dot(fmt, W + r * rb, act, nblk, isum_tap ? isum_tap + (size_t)r * nblk : NULL);
 }
@@ -307,8 +375,8 @@ void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const f
 static size_t expert_bytes(const orc_desc* d) {
     int kin = d->latent ? d->latent : d->hidden;
     int kout = kin;
-    size_t blocks = (size_t)2 * d->n_ff * (kin / ORC_QK) + (size_t)kout * (d->n_ff / ORC_QK);
-    return blocks * fmt_bytes(d->expert_fmt);
+    return 2 * d->n_ff * row_bytes(d->expert_fmt, kin / ORC_QK) +
+           (size_t)kout * row_bytes(d->expert_fmt, d->n_ff / ORC_QK);
 }
 
 size_t orc_expert_bytes(const orc_desc* d) { return expert_bytes(d); }
@@ -324,7 +392,7 @@ void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, f
     int fmt = d->expert_fmt, F = d->n_ff;
     int kin = d->latent ? d->latent : d->hidden, kout = kin;
     int nbi = kin / ORC_QK, nbf = F / ORC_QK;
-    size_t rbi = (size_t)nbi * fmt_bytes(fmt);
+    size_t rbi = row_bytes(fmt, nbi);
     const uint8_t* gate = blob;
     const uint8_t* up = gate + (size_t)F * rbi;
     const uint8_t* down = up + (size_t)F * rbi;
@@ -450,7 +518,10 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     if (!d || !x || !Wr || !experts || !out || n < 0) return -1;
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
-    if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1) return -1;
+    if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1 &&
+        d->expert_fmt != ORC_Q4_K) return -1;
+    if (d->expert_fmt == ORC_Q4_K && ((d->latent ? d->latent : d->hidden) % 256 || d->n_ff % 256))
+        return -1;
     if (d->latent && d->dense_fmt != ORC_Q8_0 && d->dense_fmt != ORC_Q4_0) return -1;
     if (d->n_groups > 0) {                     /* every group holds E / n_groups experts */
         int G = d->n_groups;

@@ -52,8 +52,8 @@ static bool mult(int v, int m) { return v > 0 && v % m == 0; }
 extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (!d) return fail(MOE_EINVAL, "desc is NULL");
     if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0 &&
-        d->expert_fmt != MOE_FMT_Q5_1)
-        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7)",
+        d->expert_fmt != MOE_FMT_Q5_1 && d->expert_fmt != MOE_FMT_Q4_K)
+        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12)",
                     d->expert_fmt);
     // edge0-strata README, changes from upstream Strata: the latent D/U
     // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
@@ -90,7 +90,10 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     const int kin = d->latent ? d->latent : d->hidden;
     if (!mv_config_ok(kin, d->expert_fmt, true))
         return fail(MOE_EUNSUPPORTED, "no gate/up kernel for %d-wide %s rows", kin,
-                    d->expert_fmt == MOE_FMT_Q4_0 ? "Q4_0" : d->expert_fmt == MOE_FMT_Q5_1 ? "Q5_1" : "Q8_0");
+                    d->expert_fmt == MOE_FMT_Q4_0   ? "Q4_0"
+                    : d->expert_fmt == MOE_FMT_Q5_1 ? "Q5_1"
+                    : d->expert_fmt == MOE_FMT_Q4_K ? "Q4_K"
+                                                    : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
     if (d->latent && (!mv_config_ok(d->hidden, d->dense_fmt, false) ||
@@ -162,14 +165,16 @@ static int gate_up_row(int p, int F) {
 // One matrix: canonical blocks (rows in canonical order) <-> packed codes/scales.
 static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t* canon,
                            uint8_t* packed, bool to_packed) {
-    const int bb = block_bytes(M.fmt), cb = code_bytes(M.fmt), sb = side_bytes(M.fmt);
+    // canonical units ([side data][codes]) of ub blocks of 32
+    const int ub = unit_blocks(M.fmt), nu = M.nblk / ub;
+    const int bb = block_bytes(M.fmt) * ub, cb = code_bytes(M.fmt) * ub, sb = side_bytes(M.fmt) * ub;
     uint8_t* codes = packed + M.codes_off;
     uint8_t* scales = packed + M.scales_off;
     for (int p = 0; p < M.rows; ++p) {
         const int r = map(p, F);
-        for (int b = 0; b < M.nblk; ++b) {
-            const size_t cpos = ((size_t)r * M.nblk + b) * bb;
-            const size_t ppos = ((size_t)p * M.nblk + b);
+        for (int b = 0; b < nu; ++b) {
+            const size_t cpos = ((size_t)r * nu + b) * bb;
+            const size_t ppos = ((size_t)p * nu + b);
             if (to_packed) {
                 memcpy(scales + sb * ppos, canon + cpos, sb);
                 memcpy(codes + ppos * cb, canon + cpos + sb, cb);
@@ -327,9 +332,12 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         tp.tap_tokens = std::min(std::max(taps->tap_tokens, 0), T);
         if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
     }
-    const bool down_tok = T <= DOWN_TOK_MAX_T;
+    const bool down_tok = T <= DOWN_TOK_MAX_T && m.fmt != MOE_FMT_Q4_K;
     // many tokens: grouped matrix-core GEMMs over token tiles
-    const bool gemm = T > MV_MAX_T;
+    // (Q4_K experts have no matrix-core kernel: every T runs the matrix-vector
+    // kernels, which loop over an expert's tokens, and their down projection
+    // is per slot)
+    const bool gemm = T > MV_MAX_T && m.fmt != MOE_FMT_Q4_K;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

@@ -28,13 +28,67 @@ template <int FMT>
 struct Fmt {
     static constexpr bool NIB = FMT != MOE_FMT_Q8_0;          // 16 nibble bytes per block
     static constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
-    static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block
-    static constexpr int CPB = NIB ? 1 : 2;                   // 16-byte chunks per block
-    // a block's side data in memory and in registers: the binary16 d, or for
-    // Q5_1 {d | m << 16, qh}
-    using SideMem = std::conditional_t<Q5, uint2, uint16_t>;
-    using Side = std::conditional_t<Q5, uint2, uint32_t>;
+    static constexpr bool K4 = FMT == MOE_FMT_Q4_K;
+    static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block of 32
+    static constexpr int CPB = NIB ? 1 : 2;                   // 16-byte chunks per block of 32
+    static constexpr int SBLK = K4 ? 8 : 1;                   // blocks of 32 per side-data unit
+    static constexpr int CPSIDE = CPB * SBLK;                 // chunks per side-data unit
+    // a unit's side data in memory and in registers: the binary16 d; for Q5_1
+    // {d | m << 16, qh}; for a Q4_K super-block {d | dmin << 16, scale bytes 0..11}
+    using SideMem = std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint16_t>>;
+    using Side = std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint32_t>>;
 };
+
+// Q4_K sub-block b's 6-bit scale and min from a super-block's side data
+// (scale bytes 0..3 in y, 4..7 in z, 8..11 in w): b < 4 takes the low 6 bits
+// of bytes b and b + 4; b >= 4 the nibbles of byte b + 4 under the top two bits
+// of bytes b - 4 (scale) and b (min).  Both forms are computed and one kept.
+__device__ __forceinline__ void k4_scale_min(const v4i& sd, int b, int& sc, int& mn) {
+    const int j = (b & 3) * 8;
+    const uint32_t s0 = (uint32_t)sd.y >> j, s1 = (uint32_t)sd.z >> j, s2 = (uint32_t)sd.w >> j;
+    const int lo_sc = (int)(s0 & 63u), lo_mn = (int)(s1 & 63u);
+    const int hi_sc = (int)((s2 & 15u) | ((s0 >> 6) & 3u) << 4);
+    const int hi_mn = (int)(((s2 >> 4) & 15u) | ((s1 >> 6) & 3u) << 4);
+    sc = b < 4 ? lo_sc : hi_sc;
+    mn = b < 4 ? lo_mn : hi_mn;
+}
+
+// A Q4_K chunk c (16 nibble bytes) of a row: super-block c / 8; within it
+// nibble bytes 16 * (c % 8) .. + 16, i.e. elements 16 * (c % 2) .. + 16 of the
+// sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles), g = (c % 8) / 2.
+// Its value against the LDS activations: the two scaled integer sums, and for
+// the first half of each sub-block (c even) the min terms on the whole blocks'
+// code sums.  isum0 / isum1 return the two integer sums (for taps).
+__device__ __forceinline__ float k4_chunk(const v4i& w, const v4i& sd, int c, bool valid,
+                                          const int8_t* arow, const float* ad, const int32_t* asq,
+                                          float acc, int& isum0, int& isum1) {
+    const int sbk = c >> 3, cc = c & 7, g = cc >> 1, h = cc & 1;
+    const int B0 = sbk * 8 + 2 * g, B1 = B0 + 1;
+    const v4i a0 = *reinterpret_cast<const v4i*>(arow + B0 * 32 + 16 * h);
+    const v4i a1 = *reinterpret_cast<const v4i*>(arow + B1 * 32 + 16 * h);
+    const int m = 0x0F0F0F0F;
+    int i0 = dot4(w.x & m, a0.x, 0);
+    i0 = dot4(w.y & m, a0.y, i0);
+    i0 = dot4(w.z & m, a0.z, i0);
+    i0 = dot4(w.w & m, a0.w, i0);
+    int i1 = dot4((w.x >> 4) & m, a1.x, 0);
+    i1 = dot4((w.y >> 4) & m, a1.y, i1);
+    i1 = dot4((w.z >> 4) & m, a1.z, i1);
+    i1 = dot4((w.w >> 4) & m, a1.w, i1);
+    int sc0, mn0, sc1, mn1;
+    k4_scale_min(sd, 2 * g, sc0, mn0);
+    k4_scale_min(sd, 2 * g + 1, sc1, mn1);
+    const float dd = h2f((uint32_t)sd.x), dmin = h2f((uint32_t)sd.x >> 16);
+    const float da0 = ad[B0], da1 = ad[B1];
+    acc = fmaf((float)i0, valid ? dd * (float)sc0 * da0 : 0.0f, acc);
+    acc = fmaf((float)i1, valid ? dd * (float)sc1 * da1 : 0.0f, acc);
+    const bool first = valid && h == 0;
+    acc = fmaf((float)asq[B0], first ? -(dmin * (float)mn0 * da0) : 0.0f, acc);
+    acc = fmaf((float)asq[B1], first ? -(dmin * (float)mn1 * da1) : 0.0f, acc);
+    isum0 = i0;
+    isum1 = i1;
+    return acc;
+}
 
 // d of a block's side data
 __device__ __forceinline__ uint32_t side_d(uint32_t s) { return s; }
@@ -112,7 +166,7 @@ __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t
 
 // ---------------------------------------------------------------------------
 // The row-tile engine: for `rows` rows of a packed block matrix (codes at
-// codes + r*rowb, binary16 scales at scl + r*nb) and the n LDS activation rows,
+// codes + r*rowb, side data at scl + r*nb/SBLK) and the n LDS activation rows,
 // emit(i, r, W[r] . act[i]) from lane 0 of each row's lane group.
 // Loads are unconditional (a chunk index past the row is clamped to the last
 // chunk and its contribution masked later), and the scale stays as raw binary16
@@ -126,14 +180,16 @@ __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<
     for (int j = 0; j < CPL; ++j) {
         const int c = min(j * LPR + sl, NCH - 1);
         wq[j] = ld16(row + (size_t)c * 16);
-        wsc[j] = rscl[c / F::CPB];
+        wsc[j] = rscl[c / F::CPSIDE];
     }
 }
 
 template <int FMT>
 __device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const typename Fmt<FMT>::Side& side,
                                               const int8_t* arow, const int32_t* asq, int c) {
-    if constexpr (FMT == MOE_FMT_Q5_1) {
+    if constexpr (FMT == MOE_FMT_Q4_K) {
+        return 0;   // (Q4_K chunks go through k4_chunk)
+    } else if constexpr (FMT == MOE_FMT_Q5_1) {
         const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
         const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
         return dot_q5(wq, side.y, lo, hi);
@@ -165,18 +221,34 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
         for (int j = 0; j < CPL; ++j) {
             const bool valid = j * LPR + sl < NCH;
             const int c = min(j * LPR + sl, NCH - 1);
-            const int blk = c / F::CPB;
-            const int is = chunk_isum_lds<FMT>(wq[j], wsc[j], arow, asq, c);
-            acc = fmaf((float)is, valid ? h2f(side_d(wsc[j])) * ad[blk] : 0.0f, acc);
-            if constexpr (F::Q5) {
-                // min term: m_w times the activation block's stored s
-                acc = fmaf(valid ? h2f(wsc[j].x >> 16) : 0.0f, __int_as_float(asq[blk]), acc);
-            }
-            if constexpr (TAP) {
-                if (tap) {
-                    int full = is;
-                    if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
-                    if (valid && (F::CPB == 1 || (sl & 1) == 0)) emit_isum(i, r, blk, full);
+            if constexpr (F::K4) {
+                int i0, i1;
+                acc = k4_chunk(wq[j], wsc[j], c, valid, arow, ad, asq, acc, i0, i1);
+                if constexpr (TAP) {
+                    if (tap) {
+                        // the two halves of each sub-block sit in lanes sl, sl ^ 1
+                        const int f0 = i0 + __shfl_xor(i0, 1, 64), f1 = i1 + __shfl_xor(i1, 1, 64);
+                        const int B0 = (c >> 3) * 8 + 2 * ((c & 7) >> 1);
+                        if (valid && (sl & 1) == 0) {
+                            emit_isum(i, r, B0, f0);
+                            emit_isum(i, r, B0 + 1, f1);
+                        }
+                    }
+                }
+            } else {
+                const int blk = c / F::CPB;
+                const int is = chunk_isum_lds<FMT>(wq[j], wsc[j], arow, asq, c);
+                acc = fmaf((float)is, valid ? h2f(side_d(wsc[j])) * ad[blk] : 0.0f, acc);
+                if constexpr (F::Q5) {
+                    // min term: m_w times the activation block's stored s
+                    acc = fmaf(valid ? h2f(wsc[j].x >> 16) : 0.0f, __int_as_float(asq[blk]), acc);
+                }
+                if constexpr (TAP) {
+                    if (tap) {
+                        int full = is;
+                        if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
+                        if (valid && (F::CPB == 1 || (sl & 1) == 0)) emit_isum(i, r, blk, full);
+                    }
                 }
             }
         }
@@ -206,7 +278,7 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
     if constexpr (PASSES == 1) {
         // a single pass: one buffer
         const int r = wave * RPW + rg;
-        if (!a_loaded) load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+        if (!a_loaded) load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, r, sl, NCH, nb, n, K, s_q, s_d, s_sq, emit, emit_isum,
                                      tap);
         return;
@@ -216,18 +288,18 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
     typename F::Side sB[CPL];
     if (!a_loaded) {
         const int r = row_of(0);
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
     }
     for (int p = 0; p < passes; p += 2) {
         {
             const int r = row_of(p + 1);
-            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wB, sB);
+            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wB, sB);
         }
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, row_of(p), sl, NCH, nb, n, K, s_q, s_d, s_sq, emit,
                                      emit_isum, tap);
         {
             const int r = row_of(p + 2);
-            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, sl, NCH, wA, sA);
+            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
         }
         if (p + 1 < passes)
             pass_dot<FMT, LPR, CPL, TAP>(wB, sB, row_of(p + 1), sl, NCH, nb, n, K, s_q, s_d, s_sq,
@@ -273,7 +345,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     const uint8_t* ebase = A.experts + (size_t)e * A.eb;
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
     using SM = typename Fmt<FMT>::SideMem;
-    const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * nb;
+    const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * (nb / Fmt<FMT>::SBLK);
 
     int8_t* s_q = reinterpret_cast<int8_t*>(smem);
     float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
@@ -289,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
         const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, lane % LPR,
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
                                 nb * Fmt<FMT>::CPB, wA, sA);
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
@@ -377,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
     const uint8_t* codes = mat + A.codes_off + (size_t)rt * A.rt * rowb;
     using SM = typename Fmt<FMT>::SideMem;
-    const SM* scl = reinterpret_cast<const SM*>(mat + A.scales_off) + (size_t)rt * A.rt * nb;
+    const SM* scl = reinterpret_cast<const SM*>(mat + A.scales_off) + (size_t)rt * A.rt * (nb / Fmt<FMT>::SBLK);
     int8_t* s_q = reinterpret_cast<int8_t*>(smem);
     float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
     int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
@@ -390,7 +462,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
         const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * nb, lane % LPR,
+        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
                                 nb * Fmt<FMT>::CPB, wA, sA);
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
@@ -453,10 +525,10 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         const uint8_t* mat = A.experts + (size_t)e * A.eb + A.dn_off;
         const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
         using SM = typename F::SideMem;
-        const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * nb;
+        const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);
         v4i wq[CPL], wn[CPL];
         typename F::Side wsc[CPL], wsn[CPL];
-        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * nb, sl, NCH, wq, wsc);
+        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
         // this rank's activation chunks, the same for every row
         v4i act[CPL][NA];
         int asq[CPL];
@@ -474,7 +546,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         for (int p = 0; p < PASSES; ++p) {
             const int r = p * RPW + rg;
             if (p + 1 < PASSES)
-                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * nb, sl,
+                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
                                         NCH, wn, wsn);
             float acc = 0.0f;
 #pragma unroll
@@ -640,6 +712,9 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     if (m.fmt == MOE_FMT_Q5_1)
         return tap ? gate_up_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, grid, lds, a, st, ev)
                    : gate_up_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, grid, lds, a, st, ev);
+    if (m.fmt == MOE_FMT_Q4_K)
+        return tap ? gate_up_fmt<MOE_FMT_Q4_K, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_Q4_K, false>(lpr, cpl, grid, lds, a, st, ev);
     return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
                : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
@@ -677,6 +752,9 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (fmt == MOE_FMT_Q5_1)
         return tap ? rows_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, grid, lds, a, st)
                    : rows_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, grid, lds, a, st);
+    if (fmt == MOE_FMT_Q4_K)
+        return tap ? rows_fmt<MOE_FMT_Q4_K, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_Q4_K, false>(lpr, cpl, grid, lds, a, st);
     return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
@@ -724,6 +802,7 @@ static hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hi
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
+    if (m.fmt == MOE_FMT_Q4_K) return hipErrorInvalidConfiguration;   // (down per slot instead)
     int lpr, cpl;
     if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;

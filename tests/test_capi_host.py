@@ -95,7 +95,7 @@ def _small(fmt=8, latent=0):
                           latent=latent, expert_fmt=fmt, seed=77)
 
 
-@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (8, 256), (2, 256), (7, 256)])
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (8, 256), (2, 256), (7, 256), (12, 256)])
 def test_pack_roundtrip(L, fmt, latent):
     w = _small(fmt, latent)
     d = moe.desc_of(w)
@@ -151,6 +151,28 @@ def test_pack_layout_positions(L, fmt):
         assert np.array_equal(dn_p[(r * nbf + b) * cb:(r * nbf + b + 1) * cb], cblk[sb:])
         off = rows * nbf * cb + (r * nbf + b) * sb
         assert np.array_equal(dn_p[off:off + sb], cblk[:sb])
+
+
+def test_pack_layout_q4_k(L):
+    """Q4_K super-blocks pack as 128 code bytes per super-block (row-major codes of all rows)
+    and 16 bytes of side data (d, dmin, the 12 scale bytes) per super-block after them."""
+    w = _small(12)
+    d = moe.desc_of(w)
+    ex = synth.gen_experts(w)
+    packed = np.empty_like(ex)
+    moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
+    F, K = w.n_ff, w.hidden
+    nsb = K // 256
+    e = 1
+    blob = ex[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    pk = packed[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    rows = 2 * F
+    for canon_row, packed_row in [(0, 0), (F + 0, 32), (33, 65)]:
+        for u in (0, nsb - 1):
+            c = blob[(canon_row * nsb + u) * 144:(canon_row * nsb + u + 1) * 144]
+            assert np.array_equal(pk[(packed_row * nsb + u) * 128:(packed_row * nsb + u + 1) * 128], c[16:])
+            off = rows * nsb * 128 + (packed_row * nsb + u) * 16
+            assert np.array_equal(pk[off:off + 16], c[:16])
 
 
 def test_forward_argument_checks_without_gpu(L):

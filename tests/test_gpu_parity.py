@@ -160,6 +160,25 @@ def test_q5_1_experts(kw):
     _report("q5_1 " + str(kw), w.tokens, rep)
 
 
+# Q4_K experts (super-blocks of 256; the min term on each activation block's
+# code sum): decode, a verify window, the 9..32-token path, more than 32 tokens,
+# latent, decode-sized rows
+@pytest.mark.parametrize("kw", [
+    dict(expert_fmt=synth.Q4_K, tokens=1),
+    dict(expert_fmt=synth.Q4_K, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
+    dict(expert_fmt=synth.Q4_K, tokens=20),
+    dict(expert_fmt=synth.Q4_K, tokens=70, bias=True),
+    dict(expert_fmt=synth.Q4_K, latent=256, n_experts=16, top_k=4, tokens=6),
+    dict(expert_fmt=synth.Q4_K, latent=256, n_experts=16, top_k=4, tokens=40),
+    dict(expert_fmt=synth.Q4_K, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
+    dict(expert_fmt=synth.Q4_K, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=6),
+])
+def test_q4_k_experts(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("q4_k " + str(kw), w.tokens, rep)
+
+
 # path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [

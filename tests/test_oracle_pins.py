@@ -369,6 +369,83 @@ def test_q5_1_row_is_dequantised_dot_with_the_stored_s(orc):
         assert y[r] == np.float32(acc)
 
 
+def _q4_k_superblock(d16=0, dmin16=0, scales="00" * 12, qs=()):
+    sb = np.zeros(144, np.uint8)
+    sb[0], sb[1], sb[2], sb[3] = d16 & 0xFF, d16 >> 8, dmin16 & 0xFF, dmin16 >> 8
+    sb[4:16] = np.frombuffer(bytes.fromhex(scales), np.uint8)
+    for i, v in qs:
+        sb[16 + i] = v
+    return sb
+
+
+def test_q4_k_golden_superblocks(orc):
+    """Hand-derived Q4_K super-blocks: the 6-bit scale and min unpacking of sub-blocks below
+    and above 4, the nibble order of the codes, and one row value whose min term takes the
+    activation block's code sum."""
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    for c in g["q4_k"]:
+        sb = _q4_k_superblock(scales=c["scales"])
+        assert orc.q4_k_scale_min(sb, c["b"]) == (c["scale"], c["min"]), c["name"]
+    c = g["q4_k_codes"]
+    sb = _q4_k_superblock(qs=[(c["qs_byte"], int(c["value"], 16))])
+    a = np.zeros(36, np.uint8)
+    a[4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+    assert orc.isum_q4_k(sb, 2, a) == c["isum_b2"]
+    assert orc.isum_q4_k(sb, 3, a) == c["isum_b3"]
+    assert orc.isum_q4_k(sb, 0, a) == 0 and orc.isum_q4_k(sb, 1, a) == 0
+    c = g["q4_k_row"]
+    sb = _q4_k_superblock(int(c["d16"], 16), int(c["dmin16"], 16), c["scales"],
+                          [(c["qs_byte"], int(c["value"], 16))])
+    act = np.zeros((8, 36), np.uint8)
+    ad = int(c["a_d16"], 16)
+    act[c["active_block"], 0], act[c["active_block"], 1] = ad & 0xFF, ad >> 8
+    act[c["active_block"], 4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+    y = orc.matvec(12, sb, 1, 8, act.reshape(-1))
+    assert y[0] == np.float32(c["y"])
+
+
+def _rand_q4_k(rng, n):
+    sb = rng.integers(0, 256, (n, 144)).astype(np.uint8)
+    d = (np.abs(rng.standard_normal(n)) * 0.02 / 512).astype(np.float16).view(np.uint16)
+    dm = (np.abs(rng.standard_normal(n)) * 0.02 / 128).astype(np.float16).view(np.uint16)
+    sb[:, 0], sb[:, 1], sb[:, 2], sb[:, 3] = d & 0xFF, d >> 8, dm & 0xFF, dm >> 8
+    return sb
+
+
+def test_q4_k_bruteforce_and_dequantised_dot(orc):
+    """Integer sums against numpy bit arithmetic, and each sub-block's contribution equal,
+    exactly, to the fp64 dot of the dequantised weights d*scale*q - dmin*min with the
+    dequantised activations; the row sums the sub-blocks in order."""
+    rng = np.random.default_rng(26)
+    n = 6
+    W = _rand_q4_k(rng, 2 * n)
+    A = _rand_q8_1(orc, rng, 8 * n)
+    y = orc.matvec(12, W.reshape(-1), 2, 8 * n, A.reshape(-1))
+    for r in range(2):
+        acc = 0.0
+        for b in range(8 * n):
+            sb = W[r * n + b // 8]
+            j = b % 8
+            sbytes = sb[4:16].astype(np.int64)
+            if j < 4:
+                sc, mn = sbytes[j] & 63, sbytes[j + 4] & 63
+            else:
+                sc = (sbytes[j + 4] & 15) | (sbytes[j - 4] >> 6) << 4
+                mn = (sbytes[j + 4] >> 4) | (sbytes[j] >> 6) << 4
+            assert orc.q4_k_scale_min(sb, j) == (sc, mn)
+            nib = sb[16 + 32 * (j // 2):16 + 32 * (j // 2) + 32].astype(np.int64)
+            q = (nib >> 4) if j % 2 else (nib & 15)
+            qa = A[b, 4:].view(np.int8).astype(np.int64)
+            assert orc.isum_q4_k(sb, j, A[b]) == int(np.dot(q, qa))
+            da = orc.f16_decode(int(A[b, 0]) | int(A[b, 1]) << 8)
+            part = math.fsum(orc.dequant_weight(12, sb, 32 * j + i) * da * int(qa[i]) for i in range(32))
+            d = orc.f16_decode(int(sb[0]) | int(sb[1]) << 8)
+            dmin = orc.f16_decode(int(sb[2]) | int(sb[3]) << 8)
+            assert part == d * sc * da * int(np.dot(q, qa)) - dmin * mn * da * int(qa.sum())
+            acc += part
+        assert y[r] == np.float32(acc)
+
+
 @pytest.mark.parametrize("fmt", [8, 2])
 def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
     """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
