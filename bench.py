@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--steps", type=int, default=300)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="decode",
-                   help="tiny | decode | latent_q8 | latent_q4 | prefill | decode_q5_1 | decode_q4_k")
+                   help="tiny | decode | latent_q8 | latent_q4 | prefill | decode_q5_1 | decode_q4_k | "
+                        "decode_q5_k")
     p.add_argument("--tokens", type=int, default=None, help="tokens per step (default: the workload's)")
     p.add_argument("--dense-fmt", choices=("q8_0", "q4_0"), default=None,
                    help="block format of a latent layer's D/U (default: the workload's, Q8_0)")
@@ -428,8 +429,8 @@ def main():
         "data": "synthetic, seeded (counter-based splitmix64)",
         "config": {"workload": a.workload, "hidden": w.hidden, "n_experts": w.n_experts,
                    "top_k": w.top_k, "n_ff": w.n_ff, "latent": w.latent,
-                   "expert_fmt": {synth.Q4_0: "Q4_0", synth.Q5_1: "Q5_1",
-                                  synth.Q4_K: "Q4_K"}.get(w.expert_fmt, "Q8_0"),
+                   "expert_fmt": {synth.Q4_0: "Q4_0", synth.Q5_1: "Q5_1", synth.Q4_K: "Q4_K",
+                                  synth.Q5_K: "Q5_K"}.get(w.expert_fmt, "Q8_0"),
                    "dense_fmt": (("Q4_0" if w.dense_fmt == synth.Q4_0 else "Q8_0")
                                  if w.latent else None),
                    "tokens_per_step": T, "weight_copies": m["copies"], "token_batches": m["pool"],

@@ -67,8 +67,11 @@ typedef enum {
  * super-blocks of 256 (binary16 d and dmin, 12 bytes of 6-bit sub-block scales
  * and mins, 128 nibble bytes), value d*scale*q - dmin*min, the min term on
  * each Q8_1 block's code sum times its d; it needs Kin and n_ff to be
- * multiples of 256.  Q5_1 and Q4_K are expert formats only. */
-enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12 };
+ * multiples of 256.  Q5_K (same commit): 176-byte super-blocks, the Q4_K
+ * header and scales, 32 bytes of fifth bits (bit b of byte i for element i of
+ * sub-block b), then the nibbles; same value and dot as Q4_K with q in 0..31.
+ * Q5_1, Q4_K and Q5_K are expert formats only. */
+enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12, MOE_FMT_Q5_K = 13 };
 
 /* Which packed tensor a pack call is about. */
 enum { MOE_PACK_EXPERTS = 0, MOE_PACK_D = 1, MOE_PACK_U = 2 };
@@ -79,7 +82,7 @@ typedef struct {
     int32_t top_k;        /* k: 1..min(E, 32)                                             */
     int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
     int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
-    int32_t expert_fmt;   /* MOE_FMT_Q8_0, MOE_FMT_Q4_0, MOE_FMT_Q5_1 or MOE_FMT_Q4_K     */
+    int32_t expert_fmt;   /* MOE_FMT_Q8_0, _Q4_0, _Q5_1, _Q4_K or _Q5_K                  */
     int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 or MOE_FMT_Q4_0 (latent == 0: unused)*/
     int32_t n_groups;     /* 0 = no group limit; else divides E                           */
     int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/

@@ -22,6 +22,7 @@ Q8_0 = 8
 Q4_0 = 2
 Q5_1 = 7
 Q4_K = 12
+Q5_K = 13
 Q8_1_BYTES = 36
 
 
@@ -79,6 +80,10 @@ def lib():
         L.orc_q4_k_scale_min.restype = None
         L.orc_isum_q4_k.argtypes = [vp, i32, vp]
         L.orc_isum_q4_k.restype = ctypes.c_int32
+        L.orc_q5_k_code.argtypes = [vp, i32]
+        L.orc_q5_k_code.restype = ctypes.c_int
+        L.orc_isum_q5_k.argtypes = [vp, i32, vp]
+        L.orc_isum_q5_k.restype = ctypes.c_int32
         L.orc_dequant_weight.argtypes = [i32, vp, i32]
         L.orc_dequant_weight.restype = ctypes.c_double
         L.orc_row_dot.argtypes = [i32, vp, vp, i32, vp]
@@ -139,6 +144,17 @@ def isum(fmt: int, wblk: np.ndarray, ablk: np.ndarray) -> int:
 def q4_k_code(sblk: np.ndarray, e: int) -> int:
     sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
     return int(lib().orc_q4_k_code(_p(sblk), e))
+
+
+def q5_k_code(sblk: np.ndarray, e: int) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    return int(lib().orc_q5_k_code(_p(sblk), e))
+
+
+def isum_q5_k(sblk: np.ndarray, b: int, ablk: np.ndarray) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
+    return int(lib().orc_isum_q5_k(_p(sblk), b, _p(ablk)))
 
 
 def q4_k_scale_min(sblk: np.ndarray, b: int):

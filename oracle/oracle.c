@@ -20,8 +20,9 @@
  *        Q5_1 blocks), whose min term multiplies the sum of the QUANTISED
  *        activations of the Q8_1 block (the ggml CPU convention), not the
  *        float sum of the activations.
- *   [QK] same commit: Q4_K experts, whose dot is llama.cpp's q4_K x q8_1 (the
- *        min term on the sum of the quantised activations of each Q8_1 block).
+ *   [QK] same commit: Q4_K and Q5_K experts, whose dots are llama.cpp's q4_K /
+ *        q5_K x q8_1 (the min term on the sum of the quantised activations of
+ *        each Q8_1 block).
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
  *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
  *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
@@ -43,12 +44,13 @@
 #define ORC_Q4_0 2
 #define ORC_Q5_1 7
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_QK 32
 #define ORC_Q8_1_BYTES 36
 
 typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
-    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1 or ORC_Q4_K */
+    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1, ORC_Q4_K or ORC_Q5_K */
     int n_groups, topk_groups;/* 0 = no group limit */
     int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
@@ -236,6 +238,27 @@ int32_t orc_isum_q4_k(const uint8_t* sb, int b, const uint8_t* a) {
     return s;
 }
 
+/*
+ * Q5_K: 176-byte super-blocks: binary16 d, binary16 dmin, the 12 scale bytes of
+ * Q4_K, 32 bytes qh, 128 nibble bytes.  Element i of sub-block b takes its
+ * nibble as in Q4_K (nibble byte 32 * (b / 2) + i) and as its fifth bit bit b of
+ * qh byte i; the value is d * scale * q - dmin * min, q in [0, 31] [QK].
+ */
+int orc_q5_k_code(const uint8_t* sb, int e) {
+    int b = e / 32, i = e % 32;
+    uint8_t v = sb[48 + 32 * (b / 2) + i];
+    int nib = b % 2 ? v >> 4 : v & 0x0F;
+    return nib | ((sb[16 + i] >> b) & 1) << 4;
+}
+
+int32_t orc_isum_q5_k(const uint8_t* sb, int b, const uint8_t* a) {
+    int32_t s = 0;
+    for (int i = 0; i < ORC_QK; ++i) s += orc_q5_k_code(sb, 32 * b + i) * (int32_t)(int8_t)a[4 + i];
+    return s;
+}
+
+static inline int kq_bytes(int fmt) { return fmt == ORC_Q5_K ? 176 : 144; }
+
 static inline int fmt_bytes(int fmt) {
     return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34;   /* per 32; Q4_K: 144 per 256 */
 }
@@ -245,10 +268,11 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
     double d = orc_f16_decode(rd16(w));
     if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
     if (fmt == ORC_Q5_1) return d * (double)orc_q5_1_code(w, j) + orc_f16_decode(rd16(w + 2));
-    if (fmt == ORC_Q4_K) {                         /* w: the super-block, j < 256 */
+    if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {      /* w: the super-block, j < 256 */
         int sc, mn;
         orc_q4_k_scale_min(w, j / 32, &sc, &mn);
-        return d * sc * (double)orc_q4_k_code(w, j) - orc_f16_decode(rd16(w + 2)) * mn;
+        int q = fmt == ORC_Q4_K ? orc_q4_k_code(w, j) : orc_q5_k_code(w, j);
+        return d * sc * (double)q - orc_f16_decode(rd16(w + 2)) * mn;
     }
     int c = j < 16 ? (w[2 + j] & 0x0F) : (w[2 + j - 16] >> 4);
     return d * (double)(c - 8);
@@ -264,18 +288,19 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
  */
 float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
     double acc = 0.0;
-    if (fmt == ORC_Q4_K) {
+    if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {
         /*
          * Sub-block b against Q8_1 block b: d * scale_b * d_a * isum_b minus
          * dmin * min_b * d_a * sum(q_a), the activation sum taken from the
-         * codes (llama.cpp's q4_K x q8_1); each term exact in double.
+         * codes (llama.cpp's q4_K / q5_K x q8_1); each term exact in double.
          */
         for (int b = 0; b < nblk; ++b) {
-            const uint8_t* sb = row + (size_t)(b / 8) * 144;
+            const uint8_t* sb = row + (size_t)(b / 8) * kq_bytes(fmt);
             const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
             int sc, mn;
             orc_q4_k_scale_min(sb, b % 8, &sc, &mn);
-            int32_t is = orc_isum_q4_k(sb, b % 8, a), qs = 0;
+            int32_t is = fmt == ORC_Q4_K ? orc_isum_q4_k(sb, b % 8, a) : orc_isum_q5_k(sb, b % 8, a);
+            int32_t qs = 0;
             for (int i = 0; i < ORC_QK; ++i) qs += (int8_t)a[4 + i];
             if (isum_tap) isum_tap[b] = is;
             double da = orc_f16_decode(rd16(a));
@@ -301,7 +326,8 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
 
 /* rows outputs of a [rows][nblk] block matrix times a Q8_1 vector */
 static size_t row_bytes(int fmt, int nblk) {
-    return fmt == ORC_Q4_K ? (size_t)(nblk / 8) * 144 : (size_t)nblk * fmt_bytes(fmt);
+    return fmt == ORC_Q4_K || fmt == ORC_Q5_K ? (size_t)(nblk / 8) * kq_bytes(fmt)
+                                              : (size_t)nblk * fmt_bytes(fmt);
 }
 
 void orc_matvec(int fmt, int rows, int nblk, const uint8_t* W, const uint8_t* act, float* y,
@@ -519,8 +545,9 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
     if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1 &&
-        d->expert_fmt != ORC_Q4_K) return -1;
-    if (d->expert_fmt == ORC_Q4_K && ((d->latent ? d->latent : d->hidden) % 256 || d->n_ff % 256))
+        d->expert_fmt != ORC_Q4_K && d->expert_fmt != ORC_Q5_K) return -1;
+    if ((d->expert_fmt == ORC_Q4_K || d->expert_fmt == ORC_Q5_K) &&
+        ((d->latent ? d->latent : d->hidden) % 256 || d->n_ff % 256))
         return -1;
     if (d->latent && d->dense_fmt != ORC_Q8_0 && d->dense_fmt != ORC_Q4_0) return -1;
     if (d->n_groups > 0) {                     /* every group holds E / n_groups experts */

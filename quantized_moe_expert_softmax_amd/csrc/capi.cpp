@@ -52,8 +52,9 @@ static bool mult(int v, int m) { return v > 0 && v % m == 0; }
 extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (!d) return fail(MOE_EINVAL, "desc is NULL");
     if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0 &&
-        d->expert_fmt != MOE_FMT_Q5_1 && d->expert_fmt != MOE_FMT_Q4_K)
-        return fail(MOE_EUNSUPPORTED, "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12)",
+        d->expert_fmt != MOE_FMT_Q5_1 && !kquant(d->expert_fmt))
+        return fail(MOE_EUNSUPPORTED,
+                    "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12), Q5_K (13)",
                     d->expert_fmt);
     // edge0-strata README, changes from upstream Strata: the latent D/U
     // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
@@ -93,6 +94,7 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
                     d->expert_fmt == MOE_FMT_Q4_0   ? "Q4_0"
                     : d->expert_fmt == MOE_FMT_Q5_1 ? "Q5_1"
                     : d->expert_fmt == MOE_FMT_Q4_K ? "Q4_K"
+                    : d->expert_fmt == MOE_FMT_Q5_K ? "Q5_K"
                                                     : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
@@ -332,12 +334,12 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         tp.tap_tokens = std::min(std::max(taps->tap_tokens, 0), T);
         if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
     }
-    const bool down_tok = T <= DOWN_TOK_MAX_T && m.fmt != MOE_FMT_Q4_K;
+    const bool down_tok = T <= DOWN_TOK_MAX_T && !kquant(m.fmt);
     // many tokens: grouped matrix-core GEMMs over token tiles
-    // (Q4_K experts have no matrix-core kernel: every T runs the matrix-vector
+    // (K-quant experts have no matrix-core kernel: every T runs the matrix-vector
     // kernels, which loop over an expert's tokens, and their down projection
     // is per slot)
-    const bool gemm = T > MV_MAX_T && m.fmt != MOE_FMT_Q4_K;
+    const bool gemm = T > MV_MAX_T && !kquant(m.fmt);
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

@@ -24,19 +24,30 @@
 
 namespace moe {
 
+struct __align__(16) K5SideMem {
+    v4i s, qh0, qh1;
+};
+struct K5Side {
+    v4i s, qh;
+};
+
 template <int FMT>
 struct Fmt {
     static constexpr bool NIB = FMT != MOE_FMT_Q8_0;          // 16 nibble bytes per block
     static constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
-    static constexpr bool K4 = FMT == MOE_FMT_Q4_K;
+    static constexpr bool K5 = FMT == MOE_FMT_Q5_K;
+    static constexpr bool K4 = FMT == MOE_FMT_Q4_K || K5;      // super-blocks of 256
     static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block of 32
     static constexpr int CPB = NIB ? 1 : 2;                   // 16-byte chunks per block of 32
     static constexpr int SBLK = K4 ? 8 : 1;                   // blocks of 32 per side-data unit
     static constexpr int CPSIDE = CPB * SBLK;                 // chunks per side-data unit
     // a unit's side data in memory and in registers: the binary16 d; for Q5_1
-    // {d | m << 16, qh}; for a Q4_K super-block {d | dmin << 16, scale bytes 0..11}
-    using SideMem = std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint16_t>>;
-    using Side = std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint32_t>>;
+    // {d | m << 16, qh}; for a Q4_K super-block {d | dmin << 16, scale bytes
+    // 0..11}; for Q5_K that and its 32 qh bytes (a chunk keeps its 16)
+    using SideMem = std::conditional_t<
+        K5, K5SideMem, std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint16_t>>>;
+    using Side = std::conditional_t<
+        K5, K5Side, std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint32_t>>>;
 };
 
 // Q4_K sub-block b's 6-bit scale and min from a super-block's side data
@@ -59,22 +70,39 @@ __device__ __forceinline__ void k4_scale_min(const v4i& sd, int b, int& sc, int&
 // Its value against the LDS activations: the two scaled integer sums, and for
 // the first half of each sub-block (c even) the min terms on the whole blocks'
 // code sums.  isum0 / isum1 return the two integer sums (for taps).
-__device__ __forceinline__ float k4_chunk(const v4i& w, const v4i& sd, int c, bool valid,
-                                          const int8_t* arow, const float* ad, const int32_t* asq,
-                                          float acc, int& isum0, int& isum1) {
+// Q5_K (K5): qh holds the chunk's 16 qh bytes; bit b of qh byte i is the fifth
+// bit of element i of sub-block b.
+template <bool K5>
+__device__ __forceinline__ float k4_chunk(const v4i& w, const v4i& sd, const v4i& qh, int c,
+                                          bool valid, const int8_t* arow, const float* ad,
+                                          const int32_t* asq, float acc, int& isum0, int& isum1) {
     const int sbk = c >> 3, cc = c & 7, g = cc >> 1, h = cc & 1;
     const int B0 = sbk * 8 + 2 * g, B1 = B0 + 1;
     const v4i a0 = *reinterpret_cast<const v4i*>(arow + B0 * 32 + 16 * h);
     const v4i a1 = *reinterpret_cast<const v4i*>(arow + B1 * 32 + 16 * h);
     const int m = 0x0F0F0F0F;
-    int i0 = dot4(w.x & m, a0.x, 0);
-    i0 = dot4(w.y & m, a0.y, i0);
-    i0 = dot4(w.z & m, a0.z, i0);
-    i0 = dot4(w.w & m, a0.w, i0);
-    int i1 = dot4((w.x >> 4) & m, a1.x, 0);
-    i1 = dot4((w.y >> 4) & m, a1.y, i1);
-    i1 = dot4((w.z >> 4) & m, a1.z, i1);
-    i1 = dot4((w.w >> 4) & m, a1.w, i1);
+    v4i lo, hi;
+    lo.x = w.x & m; lo.y = w.y & m; lo.z = w.z & m; lo.w = w.w & m;
+    hi.x = (w.x >> 4) & m; hi.y = (w.y >> 4) & m; hi.z = (w.z >> 4) & m; hi.w = (w.w >> 4) & m;
+    if constexpr (K5) {
+        const int b0 = 2 * g, b1 = b0 + 1;
+        lo.x |= (int)((((uint32_t)qh.x >> b0) & 0x01010101u) << 4);
+        lo.y |= (int)((((uint32_t)qh.y >> b0) & 0x01010101u) << 4);
+        lo.z |= (int)((((uint32_t)qh.z >> b0) & 0x01010101u) << 4);
+        lo.w |= (int)((((uint32_t)qh.w >> b0) & 0x01010101u) << 4);
+        hi.x |= (int)((((uint32_t)qh.x >> b1) & 0x01010101u) << 4);
+        hi.y |= (int)((((uint32_t)qh.y >> b1) & 0x01010101u) << 4);
+        hi.z |= (int)((((uint32_t)qh.z >> b1) & 0x01010101u) << 4);
+        hi.w |= (int)((((uint32_t)qh.w >> b1) & 0x01010101u) << 4);
+    }
+    int i0 = dot4(lo.x, a0.x, 0);
+    i0 = dot4(lo.y, a0.y, i0);
+    i0 = dot4(lo.z, a0.z, i0);
+    i0 = dot4(lo.w, a0.w, i0);
+    int i1 = dot4(hi.x, a1.x, 0);
+    i1 = dot4(hi.y, a1.y, i1);
+    i1 = dot4(hi.z, a1.z, i1);
+    i1 = dot4(hi.w, a1.w, i1);
     int sc0, mn0, sc1, mn1;
     k4_scale_min(sd, 2 * g, sc0, mn0);
     k4_scale_min(sd, 2 * g + 1, sc1, mn1);
@@ -180,15 +208,22 @@ __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<
     for (int j = 0; j < CPL; ++j) {
         const int c = min(j * LPR + sl, NCH - 1);
         wq[j] = ld16(row + (size_t)c * 16);
-        wsc[j] = rscl[c / F::CPSIDE];
+        if constexpr (F::K5) {
+            // the super-block's scales and the qh half of this chunk
+            const v4i* u = reinterpret_cast<const v4i*>(rscl + c / F::CPSIDE);
+            wsc[j].s = u[0];
+            wsc[j].qh = u[1 + (c & 1)];
+        } else {
+            wsc[j] = rscl[c / F::CPSIDE];
+        }
     }
 }
 
 template <int FMT>
 __device__ __forceinline__ int chunk_isum_lds(const v4i& wq, const typename Fmt<FMT>::Side& side,
                                               const int8_t* arow, const int32_t* asq, int c) {
-    if constexpr (FMT == MOE_FMT_Q4_K) {
-        return 0;   // (Q4_K chunks go through k4_chunk)
+    if constexpr (FMT == MOE_FMT_Q4_K || FMT == MOE_FMT_Q5_K) {
+        return 0;   // (K-quant chunks go through k4_chunk)
     } else if constexpr (FMT == MOE_FMT_Q5_1) {
         const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
         const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
@@ -223,7 +258,10 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
             const int c = min(j * LPR + sl, NCH - 1);
             if constexpr (F::K4) {
                 int i0, i1;
-                acc = k4_chunk(wq[j], wsc[j], c, valid, arow, ad, asq, acc, i0, i1);
+                if constexpr (F::K5)
+                    acc = k4_chunk<true>(wq[j], wsc[j].s, wsc[j].qh, c, valid, arow, ad, asq, acc, i0, i1);
+                else
+                    acc = k4_chunk<false>(wq[j], wsc[j], wsc[j], c, valid, arow, ad, asq, acc, i0, i1);
                 if constexpr (TAP) {
                     if (tap) {
                         // the two halves of each sub-block sit in lanes sl, sl ^ 1
@@ -715,6 +753,9 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     if (m.fmt == MOE_FMT_Q4_K)
         return tap ? gate_up_fmt<MOE_FMT_Q4_K, true>(lpr, cpl, grid, lds, a, st, ev)
                    : gate_up_fmt<MOE_FMT_Q4_K, false>(lpr, cpl, grid, lds, a, st, ev);
+    if (m.fmt == MOE_FMT_Q5_K)
+        return tap ? gate_up_fmt<MOE_FMT_Q5_K, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_Q5_K, false>(lpr, cpl, grid, lds, a, st, ev);
     return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
                : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
@@ -755,6 +796,9 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (fmt == MOE_FMT_Q4_K)
         return tap ? rows_fmt<MOE_FMT_Q4_K, true>(lpr, cpl, grid, lds, a, st)
                    : rows_fmt<MOE_FMT_Q4_K, false>(lpr, cpl, grid, lds, a, st);
+    if (fmt == MOE_FMT_Q5_K)
+        return tap ? rows_fmt<MOE_FMT_Q5_K, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_Q5_K, false>(lpr, cpl, grid, lds, a, st);
     return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
@@ -802,7 +846,8 @@ static hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hi
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
-    if (m.fmt == MOE_FMT_Q4_K) return hipErrorInvalidConfiguration;   // (down per slot instead)
+    if (m.fmt == MOE_FMT_Q4_K || m.fmt == MOE_FMT_Q5_K)
+        return hipErrorInvalidConfiguration;   // (down per slot instead)
     int lpr, cpl;
     if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;

@@ -24,12 +24,14 @@ constexpr int QK = 32;              // elements per block
 constexpr int Q8_1_CANON = 36;      // canonical Q8_1 block bytes
 
 // per block of 32 elements (a Q4_K super-block of 256 has 128 code bytes and
-// 16 bytes of side data: 16 and 2 per 32)
+// 16 bytes of side data: 16 and 2 per 32; Q5_K's 48 bytes of side data carry
+// the fifth bits as well: 6 per 32)
 inline int code_bytes(int fmt) { return fmt == MOE_FMT_Q8_0 ? 32 : 16; }
-inline int side_bytes(int fmt) { return fmt == MOE_FMT_Q5_1 ? 8 : 2; }
+inline int side_bytes(int fmt) { return fmt == MOE_FMT_Q5_1 ? 8 : fmt == MOE_FMT_Q5_K ? 6 : 2; }
 inline int block_bytes(int fmt) { return code_bytes(fmt) + side_bytes(fmt); }
 // blocks of 32 per canonical unit (a Q4_K super-block is one unit of 8)
-inline int unit_blocks(int fmt) { return fmt == MOE_FMT_Q4_K ? 8 : 1; }
+inline int unit_blocks(int fmt) { return fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K ? 8 : 1; }
+inline bool kquant(int fmt) { return fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K; }
 
 struct MatLayout {                  // one packed block matrix
     int rows = 0, nblk = 0, fmt = MOE_FMT_Q8_0;

@@ -39,8 +39,9 @@ Q8_0 = 8
 Q4_0 = 2
 Q5_1 = 7
 Q4_K = 12
-# bytes per 32 elements (Q4_K: 144-byte super-blocks of 256)
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18}
+Q5_K = 13
+# bytes per 32 elements (Q4_K / Q5_K: 144 / 176-byte super-blocks of 256)
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18, Q5_K: 22}
 S_MIN = 1 << 40      # added to a block set's scale stream for its Q5_1 minimums
 
 
@@ -124,22 +125,23 @@ def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
         mins = -absnormal_f64(seed, d_stream + S_MIN, nblk, 0.02 / 2.0)
         m16 = mins.astype(np.float16).view(np.uint8).reshape(nblk, 2)
         payload = np.ascontiguousarray(np.concatenate([m16, raw.reshape(nblk, 20)], axis=1)).reshape(-1)
-    elif fmt == Q4_K:
-        # super-blocks: binary16 d, binary16 dmin, then 12 scale bytes and 128
-        # nibble bytes, all bits uniform
+    elif fmt in (Q4_K, Q5_K):
+        # super-blocks: binary16 d, binary16 dmin, then 12 scale bytes, (Q5_K:
+        # 32 qh bytes,) 128 nibble bytes, all bits uniform
         assert nblk % 8 == 0
         nsb = nblk // 8
-        raw = np.empty(nsb * 140, dtype=np.uint8)
-        lib.synth_nibble_bytes(seed, q_stream, 0, nsb * 140, _ptr(raw))
-        scale = absnormal_f64(seed, d_stream, nsb, 0.02 / 512.0)
+        sbb = 144 if fmt == Q4_K else 176
+        raw = np.empty(nsb * (sbb - 4), dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, q_stream, 0, nsb * (sbb - 4), _ptr(raw))
+        scale = absnormal_f64(seed, d_stream, nsb, 0.02 / (512.0 if fmt == Q4_K else 1024.0))
         mins = absnormal_f64(seed, d_stream + S_MIN, nsb, 0.02 / 128.0)
         dm16 = mins.astype(np.float16).view(np.uint8).reshape(nsb, 2)
-        payload = np.ascontiguousarray(np.concatenate([dm16, raw.reshape(nsb, 140)], axis=1)).reshape(-1)
+        payload = np.ascontiguousarray(np.concatenate([dm16, raw.reshape(nsb, sbb - 4)], axis=1)).reshape(-1)
         d16 = scale.astype(np.float16).view(np.uint16)
         if out is None:
-            out = np.empty(nsb * 144, dtype=np.uint8)
-        assert out.nbytes == nsb * 144
-        lib.synth_interleave_blocks(nsb, _ptr(d16), _ptr(payload), 142, _ptr(out))
+            out = np.empty(nsb * sbb, dtype=np.uint8)
+        assert out.nbytes == nsb * sbb
+        lib.synth_interleave_blocks(nsb, _ptr(d16), _ptr(payload), sbb - 2, _ptr(out))
         return out
     else:
         raise ValueError(f"unknown block format {fmt}")
@@ -214,6 +216,8 @@ WORKLOADS = {
                             tokens=1, expert_fmt=Q5_1, seed=1005),
     "decode_q4_k": Workload("decode_q4_k", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
                             tokens=1, expert_fmt=Q4_K, seed=1006),
+    "decode_q5_k": Workload("decode_q5_k", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
+                            tokens=1, expert_fmt=Q5_K, seed=1007),
 }
 
 

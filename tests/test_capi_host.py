@@ -95,7 +95,8 @@ def _small(fmt=8, latent=0):
                           latent=latent, expert_fmt=fmt, seed=77)
 
 
-@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (8, 256), (2, 256), (7, 256), (12, 256)])
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (13, 0), (8, 256), (2, 256),
+                                        (7, 256), (12, 256), (13, 256)])
 def test_pack_roundtrip(L, fmt, latent):
     w = _small(fmt, latent)
     d = moe.desc_of(w)
@@ -153,10 +154,13 @@ def test_pack_layout_positions(L, fmt):
         assert np.array_equal(dn_p[off:off + sb], cblk[:sb])
 
 
-def test_pack_layout_q4_k(L):
-    """Q4_K super-blocks pack as 128 code bytes per super-block (row-major codes of all rows)
-    and 16 bytes of side data (d, dmin, the 12 scale bytes) per super-block after them."""
-    w = _small(12)
+@pytest.mark.parametrize("fmt", [12, 13])
+def test_pack_layout_kquant(L, fmt):
+    """K-quant super-blocks pack as 128 code bytes per super-block (row-major codes of all
+    rows) and the side data per super-block after them: d, dmin and the 12 scale bytes
+    (Q4_K, 16 bytes), and the 32 qh bytes too (Q5_K, 48 bytes)."""
+    w = _small(fmt)
+    sbb, sd = (144, 16) if fmt == 12 else (176, 48)
     d = moe.desc_of(w)
     ex = synth.gen_experts(w)
     packed = np.empty_like(ex)
@@ -169,10 +173,10 @@ def test_pack_layout_q4_k(L):
     rows = 2 * F
     for canon_row, packed_row in [(0, 0), (F + 0, 32), (33, 65)]:
         for u in (0, nsb - 1):
-            c = blob[(canon_row * nsb + u) * 144:(canon_row * nsb + u + 1) * 144]
-            assert np.array_equal(pk[(packed_row * nsb + u) * 128:(packed_row * nsb + u + 1) * 128], c[16:])
-            off = rows * nsb * 128 + (packed_row * nsb + u) * 16
-            assert np.array_equal(pk[off:off + 16], c[:16])
+            c = blob[(canon_row * nsb + u) * sbb:(canon_row * nsb + u + 1) * sbb]
+            assert np.array_equal(pk[(packed_row * nsb + u) * 128:(packed_row * nsb + u + 1) * 128], c[sd:])
+            off = rows * nsb * 128 + (packed_row * nsb + u) * sd
+            assert np.array_equal(pk[off:off + sd], c[:sd])
 
 
 def test_forward_argument_checks_without_gpu(L):

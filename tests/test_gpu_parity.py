@@ -179,6 +179,21 @@ def test_q4_k_experts(kw):
     _report("q4_k " + str(kw), w.tokens, rep)
 
 
+# Q5_K experts (Q4_K with fifth bits from qh): the same paths
+@pytest.mark.parametrize("kw", [
+    dict(expert_fmt=synth.Q5_K, tokens=1),
+    dict(expert_fmt=synth.Q5_K, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
+    dict(expert_fmt=synth.Q5_K, tokens=20),
+    dict(expert_fmt=synth.Q5_K, tokens=70, bias=True),
+    dict(expert_fmt=synth.Q5_K, latent=256, n_experts=16, top_k=4, tokens=6),
+    dict(expert_fmt=synth.Q5_K, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
+])
+def test_q5_k_experts(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("q5_k " + str(kw), w.tokens, rep)
+
+
 # path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [

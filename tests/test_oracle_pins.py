@@ -446,6 +446,51 @@ def test_q4_k_bruteforce_and_dequantised_dot(orc):
         assert y[r] == np.float32(acc)
 
 
+def test_q5_k_golden_fifth_bits(orc):
+    """Hand-derived Q5_K codes: the fifth bit of element i of sub-block b is bit b of qh byte
+    i, on top of the Q4_K nibble order."""
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    c = g["q5_k_codes"]
+    sb = np.zeros(176, np.uint8)
+    sb[16 + c["qh_byte"]] = int(c["qh"], 16)
+    sb[48 + c["qs_byte"]] = int(c["qs"], 16)
+    a = np.zeros(36, np.uint8)
+    a[4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+    for b in (2, 3, 4, 5):
+        assert orc.isum_q5_k(sb, b, a) == c[f"isum_b{b}"], b
+    assert orc.isum_q5_k(sb, 0, a) == 0
+
+
+def test_q5_k_bruteforce_and_dequantised_dot(orc):
+    """Q5_K integer sums against numpy bit arithmetic, and the sub-block contribution equal,
+    exactly, to the dequantised fp64 dot; the row sums the sub-blocks in order."""
+    rng = np.random.default_rng(27)
+    n = 4
+    W = rng.integers(0, 256, (2 * n, 176)).astype(np.uint8)
+    d = (np.abs(rng.standard_normal(2 * n)) * 0.02 / 1024).astype(np.float16).view(np.uint16)
+    dm = (np.abs(rng.standard_normal(2 * n)) * 0.02 / 128).astype(np.float16).view(np.uint16)
+    W[:, 0], W[:, 1], W[:, 2], W[:, 3] = d & 0xFF, d >> 8, dm & 0xFF, dm >> 8
+    A = _rand_q8_1(orc, rng, 8 * n)
+    y = orc.matvec(13, W.reshape(-1), 2, 8 * n, A.reshape(-1))
+    for r in range(2):
+        acc = 0.0
+        for b in range(8 * n):
+            sb = W[r * n + b // 8]
+            j = b % 8
+            sc, mn = orc.q4_k_scale_min(sb, j)
+            nib = sb[48 + 32 * (j // 2):48 + 32 * (j // 2) + 32].astype(np.int64)
+            q = ((nib >> 4) if j % 2 else (nib & 15)) | ((sb[16:48].astype(np.int64) >> j) & 1) << 4
+            qa = A[b, 4:].view(np.int8).astype(np.int64)
+            assert orc.isum_q5_k(sb, j, A[b]) == int(np.dot(q, qa))
+            da = orc.f16_decode(int(A[b, 0]) | int(A[b, 1]) << 8)
+            part = math.fsum(orc.dequant_weight(13, sb, 32 * j + i) * da * int(qa[i]) for i in range(32))
+            dd = orc.f16_decode(int(sb[0]) | int(sb[1]) << 8)
+            dmin = orc.f16_decode(int(sb[2]) | int(sb[3]) << 8)
+            assert part == dd * sc * da * int(np.dot(q, qa)) - dmin * mn * da * int(qa.sum())
+            acc += part
+        assert y[r] == np.float32(acc)
+
+
 @pytest.mark.parametrize("fmt", [8, 2])
 def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
     """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
