@@ -334,12 +334,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         tp.tap_tokens = std::min(std::max(taps->tap_tokens, 0), T);
         if (!tp.isum_gu && !tp.isum_dn && !tp.isum_d && !tp.isum_u) tp.tap_tokens = 0;
     }
+    // (K-quant experts take the per-slot down projection at every T)
     const bool down_tok = T <= DOWN_TOK_MAX_T && !kquant(m.fmt);
     // many tokens: grouped matrix-core GEMMs over token tiles
-    // (K-quant experts have no matrix-core kernel: every T runs the matrix-vector
-    // kernels, which loop over an expert's tokens, and their down projection
-    // is per slot)
-    const bool gemm = T > MV_MAX_T && !kquant(m.fmt);
+    const bool gemm = T > MV_MAX_T;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

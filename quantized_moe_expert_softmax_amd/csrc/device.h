@@ -37,6 +37,20 @@ __device__ __forceinline__ int dot16(const v4i& w, const v4i& a) {
 // in the high nibble) against 32 int8 activations a_lo (elements 0..15) and
 // a_hi (16..31): sum_j c_j a_j, codes unsigned 0..15.  The caller subtracts
 // 8 * sum(a) to centre the codes.
+// Q4_K sub-block b's 6-bit scale and min from a super-block's side data
+// (scale bytes 0..3 in y, 4..7 in z, 8..11 in w): b < 4 takes the low 6 bits
+// of bytes b and b + 4; b >= 4 the nibbles of byte b + 4 under the top two bits
+// of bytes b - 4 (scale) and b (min).  Both forms are computed and one kept.
+__device__ __forceinline__ void k4_scale_min(const v4i& sd, int b, int& sc, int& mn) {
+    const int j = (b & 3) * 8;
+    const uint32_t s0 = (uint32_t)sd.y >> j, s1 = (uint32_t)sd.z >> j, s2 = (uint32_t)sd.w >> j;
+    const int lo_sc = (int)(s0 & 63u), lo_mn = (int)(s1 & 63u);
+    const int hi_sc = (int)((s2 & 15u) | ((s0 >> 6) & 3u) << 4);
+    const int hi_mn = (int)(((s2 >> 4) & 15u) | ((s1 >> 6) & 3u) << 4);
+    sc = b < 4 ? lo_sc : hi_sc;
+    mn = b < 4 ? lo_mn : hi_mn;
+}
+
 // bits 0..3 of x moved to bit 4 of bytes 0..3 (bit i to byte i): the four
 // copies x << 7i put bit i at bit 8i and nowhere else a byte starts
 __device__ __forceinline__ int spread4(uint32_t x) {

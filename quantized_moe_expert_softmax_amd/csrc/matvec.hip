@@ -50,20 +50,6 @@ struct Fmt {
         K5, K5Side, std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint32_t>>>;
 };
 
-// Q4_K sub-block b's 6-bit scale and min from a super-block's side data
-// (scale bytes 0..3 in y, 4..7 in z, 8..11 in w): b < 4 takes the low 6 bits
-// of bytes b and b + 4; b >= 4 the nibbles of byte b + 4 under the top two bits
-// of bytes b - 4 (scale) and b (min).  Both forms are computed and one kept.
-__device__ __forceinline__ void k4_scale_min(const v4i& sd, int b, int& sc, int& mn) {
-    const int j = (b & 3) * 8;
-    const uint32_t s0 = (uint32_t)sd.y >> j, s1 = (uint32_t)sd.z >> j, s2 = (uint32_t)sd.w >> j;
-    const int lo_sc = (int)(s0 & 63u), lo_mn = (int)(s1 & 63u);
-    const int hi_sc = (int)((s2 & 15u) | ((s0 >> 6) & 3u) << 4);
-    const int hi_mn = (int)(((s2 >> 4) & 15u) | ((s1 >> 6) & 3u) << 4);
-    sc = b < 4 ? lo_sc : hi_sc;
-    mn = b < 4 ? lo_mn : hi_mn;
-}
-
 // A Q4_K chunk c (16 nibble bytes) of a row: super-block c / 8; within it
 // nibble bytes 16 * (c % 8) .. + 16, i.e. elements 16 * (c % 2) .. + 16 of the
 // sub-blocks 2g (low nibbles) and 2g + 1 (high nibbles), g = (c % 8) / 2.

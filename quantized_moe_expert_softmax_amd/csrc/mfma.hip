@@ -129,18 +129,27 @@ struct MfWave {
 // kb+1's products are issued before block kb is rescaled.
 __device__ __forceinline__ h4 scale_op(uint32_t d16) { return __builtin_bit_cast(h4, v2i{(int)d16, 0}); }
 
-template <bool SWIGLU, bool TAP, class Frag, class SFrag>
+// the scale outer product: binary16 operands (exact in fp32), or fp32 operands
+// (one k of v_mfma_f32_32x32x2_f32: lanes 0..31 carry the values, 32..63 zero)
+__device__ __forceinline__ v16f scale_mfma(h4 a, h4 b) {
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, v16f{}, 0, 0, 0);
+}
+__device__ __forceinline__ v16f scale_mfma(float a, float b) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, v16f{}, 0, 0, 0);
+}
+
+template <bool SWIGLU, bool TAP, class SOp = h4, class Frag, class SFrag>
 __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const MfWave& w, int s,
                                          const int* s_orow, Frag frag, SFrag sfrag,
                                          float (&acc0)[16], float (&acc1)[16]) {
     v4i a0, a1, bx;
-    h4 d0, d1, dc;
+    SOp d0, d1, dc;
     frag(0, a0, a1, bx);
     sfrag(0, d0, d1, dc);
     v16i i0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
     v16i i1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
-    v16f s0 = __builtin_amdgcn_mfma_f32_32x32x8f16(d0, dc, v16f{}, 0, 0, 0);
-    v16f s1 = __builtin_amdgcn_mfma_f32_32x32x8f16(d1, dc, v16f{}, 0, 0, 0);
+    v16f s0 = scale_mfma(d0, dc);
+    v16f s1 = scale_mfma(d1, dc);
 #pragma unroll
     for (int kb = 0; kb < MF_KB; ++kb) {
         v16i n0, n1;
@@ -150,8 +159,8 @@ __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const
             sfrag(kb + 1, d0, d1, dc);
             n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bx, v16i{}, 0, 0, 0);
             n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bx, v16i{}, 0, 0, 0);
-            t0 = __builtin_amdgcn_mfma_f32_32x32x8f16(d0, dc, v16f{}, 0, 0, 0);
-            t1 = __builtin_amdgcn_mfma_f32_32x32x8f16(d1, dc, v16f{}, 0, 0, 0);
+            t0 = scale_mfma(d0, dc);
+            t1 = scale_mfma(d1, dc);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -619,6 +628,188 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// Q4_K / Q5_K (FMT): a stage of four blocks is half a super-block.  Its 64
+// nibble bytes widen to int8 (plus Q5_K's fifth bits from qh): nibble byte
+// 32g' + i of the stage gives element i of stage block 2g' (low nibble) and of
+// 2g' + 1 (high nibble).  A row's scale for stage block q is d * scale_b and
+// its min product dmin * min_b (b = the sub-block), both exact in fp32 and
+// taken to the matrix cores as fp32 (v_mfma_f32_32x32x2_f32): the rescale uses
+// d * scale_b x d_a, and each stage subtracts sum_q dmin*min_q[r] x d_a*sum(q_a)[t]
+// with two more fp32 outer products (two blocks each, in the two k slots).
+template <bool SWIGLU, bool TAP, int FMT>
+__global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_kq(MfArgs A) {
+    constexpr bool K5 = FMT == MOE_FMT_Q5_K;
+    constexpr int SIDE = K5 ? 48 : 16;                   // side bytes per super-block
+    constexpr int WBYTES = MF_NT * MS_ROWB, XBYTES = MF_MT * MS_ROWB;
+    constexpr int SW32 = MF_KB * MS_SWR * 4, SA32 = MF_KB * MS_SAR * 4;
+    constexpr int MW32 = MF_KB * MF_NT * 4, MA32 = MF_KB * MF_MT * 4;
+    constexpr int STAGE = WBYTES + XBYTES + SW32 + SA32 + MW32 + MA32;
+    __shared__ __align__(16) char smem[2 * STAGE];
+    __shared__ int s_row[MF_MT], s_orow[MF_MT];
+
+    MfTile t;
+    if (!mf_tile(A, t, s_row, s_orow)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    {
+        // zero tails of the fp32 scale rows, both stage buffers
+        const int buf = tid >> 7, kb = (tid >> 5) & 3, z = tid & 31;
+        float* sdw = reinterpret_cast<float*>(smem + buf * STAGE + WBYTES + XBYTES);
+        sdw[kb * MS_SWR + MF_NT + z] = 0.0f;
+        sdw[MF_KB * MS_SWR + kb * MS_SAR + MF_MT + z] = 0.0f;
+    }
+    __syncthreads();
+
+    const int K = A.K, nb = K / QK, nsb = nb / 8;
+    const size_t rowb = (size_t)nb * 16;
+    const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
+    const uint8_t* side = t.mat + A.scales_off + (size_t)t.nt * MF_NT * nsb * SIDE;
+
+    constexpr int WCH = 2;                      // 16-byte chunks per thread (4 per row per stage)
+    v4i rw[WCH], rqh[WCH];
+    v4i rx[2];
+    v4i rsd, rda, rsq;
+    auto gload = [&](int kb0) {
+        const int sbk = kb0 >> 3;
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int r = ch >> 2, p = ch & 3;
+            rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * 16 + p * 16);
+            if constexpr (K5) rqh[j] = ld16(side + ((size_t)r * nsb + sbk) * SIDE + 16 + 16 * (p & 1));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int c = ch >> 3, p = ch & 7;
+            rx[j] = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)kb0 * QK + p * 16);
+        }
+        if (tid < MF_NT) {
+            rsd = ld16(side + ((size_t)tid * nsb + sbk) * SIDE);
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+            rda = *reinterpret_cast<const v4i*>(A.ain.ds + (size_t)s_row[c] * nb + kb0);
+            rsq = *reinterpret_cast<const v4i*>(A.ain.sq + (size_t)s_row[c] * nb + kb0);
+        }
+    };
+    auto lstore = [&](int buf, int kb0) {
+        const int half = (kb0 >> 2) & 1;                  // which half of the super-block
+        char* st = smem + buf * STAGE;
+        int8_t* sw = reinterpret_cast<int8_t*>(st);
+        int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
+        float* sdw = reinterpret_cast<float*>(st + WBYTES + XBYTES);
+        float* sda = sdw + MF_KB * MS_SWR;
+        float* smw = sda + MF_KB * MS_SAR;
+        float* sas = smw + MF_KB * MF_NT;
+#pragma unroll
+        for (int j = 0; j < WCH; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int r = ch >> 2, p = ch & 3;
+            const int q0 = 2 * (p >> 1), h = p & 1;       // stage blocks q0 (low), q0 + 1 (high)
+            const int gb = 4 * half + q0;                 // the low nibbles' sub-block
+            v4i lo, hi;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t x = (uint32_t)rw[j][d];
+                uint32_t l = x & 0x0F0F0F0Fu, hh = (x >> 4) & 0x0F0F0F0Fu;
+                if constexpr (K5) {
+                    const uint32_t qb = (uint32_t)rqh[j][d];
+                    l |= ((qb >> gb) & 0x01010101u) << 4;
+                    hh |= ((qb >> (gb + 1)) & 0x01010101u) << 4;
+                }
+                lo[d] = (int)l;
+                hi[d] = (int)hh;
+            }
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + q0 * QK + 16 * h) = lo;
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + (q0 + 1) * QK + 16 * h) = hi;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ch = tid + j * MF_THREADS;
+            const int c = ch >> 3, p = ch & 7;
+            *reinterpret_cast<v4i*>(sx + c * MS_ROWB + p * 16) = rx[j];
+        }
+        if (tid < MF_NT) {
+            const float dd = h2f((uint32_t)rsd.x), dmin = h2f((uint32_t)rsd.x >> 16);
+#pragma unroll
+            for (int q = 0; q < MF_KB; ++q) {
+                int sc, mn;
+                k4_scale_min(rsd, 4 * half + q, sc, mn);
+                sdw[q * MS_SWR + tid] = dd * (float)sc;
+                smw[q * MF_NT + tid] = dmin * (float)mn;
+            }
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+#pragma unroll
+            for (int q = 0; q < MF_KB; ++q) {
+                const float da = h2f((uint32_t)rda[q]);
+                sda[q * MS_SAR + c] = da;
+                sas[q * MF_MT + c] = da * (float)rsq[q];
+            }
+        }
+    };
+
+    MfWave w{wave & 1, wave >> 1, lane >> 5, lane & 31};
+    const int o_w0 = w.half ? MF_NT + w.l32 : w.wr * 64 + w.l32;
+    const int o_w1 = w.half ? MF_NT + w.l32 : w.wr * 64 + 32 + w.l32;
+    const int o_a = w.half ? MF_MT + w.l32 : w.wc * 32 + w.l32;
+    const bool busy = w.wc * 32 < t.ncol;
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+
+    const int stages = nb / MF_KB;
+    auto compute = [&](int buf, int s) {
+        if (!busy) return;
+        const char* st = smem + buf * STAGE;
+        const int8_t* sw = reinterpret_cast<const int8_t*>(st);
+        const int8_t* sx = reinterpret_cast<const int8_t*>(st + WBYTES);
+        const float* sdw = reinterpret_cast<const float*>(st + WBYTES + XBYTES);
+        const float* sda = sdw + MF_KB * MS_SWR;
+        const float* smw = sda + MF_KB * MS_SAR;
+        const float* sas = smw + MF_KB * MF_NT;
+        auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
+            a0 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            a1 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            bx = *reinterpret_cast<const v4i*>(sx + (w.wc * 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+        };
+        auto sfrag = [&](int kb, float& d0, float& d1, float& dc) {
+            d0 = sdw[kb * MS_SWR + o_w0];
+            d1 = sdw[kb * MS_SWR + o_w1];
+            dc = sda[kb * MS_SAR + o_a];
+        };
+        mf_stage<SWIGLU, TAP, float>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+        // min terms: blocks (0, 1) then (2, 3), one per k slot (lane half)
+        v16f p0 = v16f{}, p1 = v16f{};
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int q = 2 * pr + w.half;
+            const float m0 = smw[q * MF_NT + w.wr * 64 + w.l32];
+            const float m1 = smw[q * MF_NT + w.wr * 64 + 32 + w.l32];
+            const float sv = sas[q * MF_MT + w.wc * 32 + w.l32];
+            p0 = __builtin_amdgcn_mfma_f32_32x32x2f32(m0, sv, p0, 0, 0, 0);
+            p1 = __builtin_amdgcn_mfma_f32_32x32x2f32(m1, sv, p1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc0[i] -= p0[i];
+            acc1[i] -= p1[i];
+        }
+    };
+    gload(0);
+    lstore(0, 0);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s + 1 < stages; ++s) {
+        gload((s + 1) * MF_KB);
+        compute(s & 1, s);
+        lstore((s + 1) & 1, (s + 1) * MF_KB);
+        __syncthreads();
+    }
+    compute((stages - 1) & 1, stages - 1);
+    mf_epilogue<SWIGLU, TAP>(A, t, w, s_orow, acc0, acc1);
+}
+
+// ---------------------------------------------------------------------------
 bool mfma_config_ok(int rows, int K) { return rows % MF_NT == 0 && K % (MF_KB * QK) == 0; }
 
 template <bool SWIGLU>
@@ -639,6 +830,16 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
             launch_k(k_mfma_q4<SWIGLU, true, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
         else
             launch_k(k_mfma_q4<SWIGLU, false, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
+    } else if (fmt == MOE_FMT_Q4_K) {
+        if (tap)
+            launch_k(k_mfma_kq<SWIGLU, true, MOE_FMT_Q4_K>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_kq<SWIGLU, false, MOE_FMT_Q4_K>, grid, block, 0, st, ev, a);
+    } else if (fmt == MOE_FMT_Q5_K) {
+        if (tap)
+            launch_k(k_mfma_kq<SWIGLU, true, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_kq<SWIGLU, false, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
     } else {
         if (tap)
             launch_k(k_mfma_dma<SWIGLU, true>, grid, block, 0, st, ev, a);

@@ -108,6 +108,9 @@ def test_variants(kw):
     (dict(expert_fmt=synth.Q5_1, tokens=100), None, 4),
     (dict(expert_fmt=synth.Q5_1, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300),
      [0, 5, 150, 299], 2),
+    (dict(expert_fmt=synth.Q4_K, tokens=100), None, 4),
+    (dict(expert_fmt=synth.Q5_K, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300),
+     [0, 5, 150, 299], 2),
 ])
 def test_gemm_variants(kw, sample, taps):
     w = _variant(**kw)
