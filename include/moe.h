@@ -187,7 +187,8 @@ moe_status moe_layer_forward_taps(const moe_layer* layer, const float* x, int T,
  * hipEvent_t created by the caller, passed as void*; NULL entries are skipped)
  * on `stream` at these points of the kernel sequence:
  *   MOE_EV_BEGIN    before the first kernel
- *   MOE_EV_ROUTED   after quantising x, routing and bucketing
+ *   MOE_EV_ROUTED   after quantising x, routing and bucketing (T == 1: after the
+ *                   router logits; the selection runs in the gate/up kernel)
  *   MOE_EV_EXPERT_IN after the latent D projection (== ROUTED when latent == 0)
  *   MOE_EV_GATE_UP  after the grouped gate/up + SwiGLU + requantisation
  *   MOE_EV_DOWN     after the grouped down projection and the combine

@@ -357,10 +357,15 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     } while (0)
 
     EV(MOE_EV_BEGIN);
-    bool bucketed = false;
+    RouteDone routed;
+    SelectArgs sel;
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
-                     &bucketed, st), "router");
-    if (!bucketed) CK(launch_bucket(m, w, ws, T, st), "bucketing");
+                     &routed, &sel, st), "router");
+    if (routed == ROUTE_SELECTED) CK(launch_bucket(m, w, ws, T, st), "bucketing");
+    // a single token is selected and bucketed by the gate/up kernel's prologue
+    const SelectArgs* gu_route = routed == ROUTE_LOGITS ? &sel : nullptr;
+    RouteOut rout{(int32_t*)(ws + w.ids), (float*)(ws + w.wts), (int32_t*)(ws + w.counts),
+                  (int32_t*)(ws + w.lists), (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active)};
     EV(MOE_EV_ROUTED);
     const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
@@ -384,11 +389,14 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     if (gemm)
         CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st, gev), "gate/up");
     else if (m.L && lat_fused_q)
-        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev), "gate/up");
+        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev, gu_route, &rout),
+           "gate/up");
     else if (m.L)
-        CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev), "gate/up");
+        CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout),
+           "gate/up");
     else
-        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev), "gate/up");
+        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout),
+           "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs
     if (down_tok) {

@@ -34,6 +34,30 @@ inline void launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st
         hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
+// Router logits and selection parameters: part[s][t][e] are the logits'
+// K-slice partials (S slices, summed in slice order), bias [E] or null, group
+// labels [E] when G > 0, TG groups kept; logits_tap [T][E] or null.
+constexpr int ROUTE_SMAX = 16;
+struct SelectArgs {
+    const double* part;
+    int S, T, E, k;
+    const float* bias;
+    const int32_t* groups;
+    int G, TG;
+    double* logits_tap;
+};
+
+// Where a kernel that routes a single token itself publishes the result (the
+// same content as the router and bucketing kernels write).
+struct RouteOut {
+    int32_t* ids;
+    float* wts;
+    int32_t* counts;
+    int32_t* lists;
+    uint32_t* ctrl;
+    int32_t* active;
+};
+
 struct Taps {                 // device pointers, NULL = off
     float* h = nullptr;       // [A][F]
     float* y = nullptr;       // [A][Kout]
@@ -45,11 +69,14 @@ struct Taps {                 // device pointers, NULL = off
 };
 
 hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStream_t st);
-// Q8_1(x) and the router logits; then top-k and softmax per token, and for
-// decode sizes the bucketing too (*bucketed = true).
+// Q8_1(x) and the router logits; then, from two tokens on, top-k and softmax
+// per token, and up to 32 tokens the bucketing too.  *done tells how far the
+// launched kernels go; *sel receives the selection parameters (for a single
+// token the gate/up kernel selects in its prologue from them).
+enum RouteDone { ROUTE_LOGITS, ROUTE_SELECTED, ROUTE_BUCKETED };
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, bool* bucketed, hipStream_t st);
+                         ActPtr xq, RouteDone* done, SelectArgs* sel, hipStream_t st);
 // Per-expert assignment lists in token order, the active experts, and the
 // token tiles (GEMM_TILE_M assignments) of each, numbered in tile_map.
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, hipStream_t st);
@@ -64,9 +91,13 @@ bool mv_config_ok(int K, int fmt, bool gate_up);
 // Decode-path expert and dense kernels (matrix-vector, one pass over the weights).
 // The expert input is either quantised rows (ain) or fp32 rows quantised inside
 // the kernel (ain_f32, with `keep` receiving the Q8_1 blocks when non-null).
+// route != null (T == 1 only): every workgroup selects the token's experts
+// from the router logits in its prologue and workgroup 0 publishes ids,
+// weights and buckets to *rout; b is then not read.
 hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
-                             const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{});
+                             const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
+                             const SelectArgs* route = nullptr, const RouteOut* rout = nullptr);
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st);
 hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,

@@ -1,0 +1,87 @@
+// Matrix-vector path of libmoe: the arguments of its kernels and the per-format
+// launch functions that the launchers (matvec.hip) call.  The kernels themselves
+// (matvec_kern.h) are instantiated one format per translation unit (mv_*.hip).
+#pragma once
+#include "kernels.h"
+#include "select.h"
+
+namespace moe {
+
+// LDS bytes of n staged rows of K elements (codes, d, sums), 16-byte aligned.
+__host__ __device__ constexpr size_t stage_bytes(int n, int K) {
+    return (size_t)n * K + 2 * (size_t)n * (K / QK) * 4;
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU + Q8_1.  Workgroup = (slot, fb): the 64-row slab of gate
+// rows fb*32.. and up rows fb*32.. of the slot's expert, for every token routed
+// to it.  Output: hq rows a = t*k + j, block fb.
+struct GUArgs {
+    const uint8_t* experts;
+    size_t eb, gu_scales_off;
+    int K, F, k, T, tch;
+    ActPtr ain;           // quantised expert input rows [T][K], or
+    const float* ain_f32; // fp32 rows [T][K] quantised in the prologue (latent z)
+    ActPtr keep;          // where the prologue also stores Q8_1(z) (taps), q == nullptr: off
+    Buckets b;
+    ActPtr hq;
+    Taps taps;
+    SelectArgs route;     // route.part != null: one token, routed in the prologue
+    RouteOut rout;
+};
+
+
+// ---------------------------------------------------------------------------
+// Rows kernel: out[s][r] = W_g[r] . act[s] for a tile of rows of a block matrix.
+// Expert mode (b.ctrl != nullptr): group = slot, W_g = the down matrix of expert
+// active[slot], act/out rows = the expert's assignments (hq rows).  Dense mode:
+// one matrix, act/out rows = tokens 0..T-1 (D on Q8_1(x), U on Q8_1(y_lat)).
+struct RowsArgs {
+    const uint8_t* base;
+    size_t group_stride, codes_off, scales_off;
+    int rows, K, T, rt, tch;
+    Buckets b;                 // b.ctrl == nullptr: dense mode
+    ActPtr ain;                // quantised act rows, or
+    const float* ain_f32;      // fp32 act rows quantised in the prologue
+    ActPtr keep;               // Q8_1 of the fp32 rows, stored for taps (q == nullptr: off)
+    float* out;                // [act row][rows]
+    int tap_div;               // token of act row s = s / tap_div
+    int32_t* isum_tap;         // [act row][rows][K/32]
+    int tap_tokens;
+};
+
+// ---------------------------------------------------------------------------
+// Down projection with the combine fused, one workgroup per (token, 16-row
+// tile); wave j computes rank j's expert rows, then the tile is combined in
+// rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).
+struct DownTokArgs {
+    const uint8_t* experts;
+    size_t eb, dn_off, dn_scales_off;
+    int F, Kout, k;
+    ActPtr hq;
+    Buckets b;
+    float* out;              // [T][Kout]: the layer output, or y_lat for a latent layer
+    Taps taps;
+};
+
+constexpr int DT_RT = 16;    // output rows per workgroup
+constexpr int DT_NW = 8;     // waves per workgroup (ranks in parallel)
+constexpr int DT_KMAX = 32;  // largest top_k
+
+constexpr int ROWS_NW = 4;   // waves per rows workgroup
+
+// waves per gate/up workgroup: 8 lanes per row cover the 64-row slab in one
+// pass with 8 waves; wider rows use 4 waves and several passes
+inline int gu_waves(int lpr) { return lpr == 8 ? 8 : 4; }
+
+// Launch one instance by (lanes per row, 16-byte chunks per lane); defined and
+// instantiated for every format in mv_*.hip (down_tok_fmt for Q8_0, Q4_0, Q5_1).
+template <int FMT, bool TAP>
+hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a, hipStream_t st,
+                       const KEvents& ev);
+template <int FMT, bool TAP>
+hipError_t rows_fmt(int lpr, int cpl, dim3 grid, size_t lds, const RowsArgs& a, hipStream_t st);
+template <int FMT, bool TAP>
+hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream_t st);
+
+}  // namespace moe

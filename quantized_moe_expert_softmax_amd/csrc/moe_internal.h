@@ -111,8 +111,10 @@ struct WsLayout {
 
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-constexpr int DECODE_T = 8;  // largest T the single-token router kernels are sized for
-constexpr int ROUTE_DEC_MAX_T = 1;  // T up to this (<= DECODE_T) takes those kernels
+constexpr int DECODE_T = 8;  // largest T the few-token router logits kernel is sized for
+// T up to this takes that kernel and leaves top-k, softmax and bucketing to the
+// gate/up kernel's prologue, which routes a single token
+constexpr int ROUTE_DEC_MAX_T = 1;
 constexpr int MV_MAX_T = 32; // T up to this runs the matrix-vector expert kernels
 constexpr int LAT_FUSED_Q_MAX_T = 1;  // latent: consumers quantise z / y_lat up to this T
 constexpr int GEMM_TILE_M = 64;  // token tile of the grouped matrix-core GEMM

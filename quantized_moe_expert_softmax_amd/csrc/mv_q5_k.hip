@@ -1,0 +1,6 @@
+// Matrix-vector kernel instances for Q5_K rows.
+#include "matvec_kern.h"
+
+namespace moe {
+MOE_MV_INSTANCES(MOE_FMT_Q5_K)
+}  // namespace moe

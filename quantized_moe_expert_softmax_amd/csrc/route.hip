@@ -9,6 +9,7 @@
 // expert gets the list of its assignments a = t*k + j in token order, and the
 // experts with tokens are compacted into slots in id order.
 #include "kernels.h"
+#include "select.h"
 
 namespace moe {
 
@@ -23,61 +24,6 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x,
     const long r = blk / nb, b = blk % nb;
     float v = x[r * K + b * QK + l];
     quant_q8_1_32(v, l, out.q + r * K + b * QK, out.ds + r * nb + b, out.sq + r * nb + b);
-}
-
-// ---------------------------------------------------------------------------
-// Router logits, partial over K slices: part[s][t][e] = sum_{i in slice s} x[t,i] W[e,i],
-// plus the Q8_1 quantisation of x in the trailing workgroups of the same grid.
-// A logits workgroup = 4 waves = 4 experts for TT tokens of one K slice.
-// Products of two floats are exact in fp64; only the additions round.
-template <int TT>
-__global__ __launch_bounds__(256) void k_route_logits(const float* __restrict__ x,
-                                                      const float* __restrict__ W, int T, int H,
-                                                      int E, int S, double* __restrict__ part,
-                                                      int n_logit_wg, ActPtr xq) {
-    if ((int)blockIdx.x >= n_logit_wg) {
-        // x -> Q8_1, one 32-lane group per block
-        const int nb = H / QK;
-        const long blk = (long)(blockIdx.x - n_logit_wg) * 8 + threadIdx.x / 32;
-        if (blk >= (long)T * nb) return;
-        const int l = threadIdx.x % 32;
-        const long r = blk / nb, b = blk % nb;
-        quant_q8_1_32(x[r * H + b * QK + l], l, xq.q + r * H + b * QK, xq.ds + r * nb + b,
-                      xq.sq + r * nb + b);
-        return;
-    }
-    const int ge = (E + 3) / 4;
-    const int bx = blockIdx.x % ge, s = (blockIdx.x / ge) % S, tz = blockIdx.x / (ge * S);
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int e = bx * 4 + wave;
-    const int t0 = tz * TT;
-    if (e >= E) return;
-    const int nt = min(TT, T - t0);
-    const int slice = H / S, k0 = s * slice;
-    double acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.0;
-    const float* wrow = W + (size_t)e * H;
-    for (int i = k0 + lane * 4; i < k0 + slice; i += 256) {
-        const float4 w = *reinterpret_cast<const float4*>(wrow + i);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            if (t < nt) {
-                const float4 xv = *reinterpret_cast<const float4*>(x + (size_t)(t0 + t) * H + i);
-                acc[t] = fma((double)xv.x, (double)w.x, acc[t]);
-                acc[t] = fma((double)xv.y, (double)w.y, acc[t]);
-                acc[t] = fma((double)xv.z, (double)w.z, acc[t]);
-                acc[t] = fma((double)xv.w, (double)w.w, acc[t]);
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t < nt) {
-            const double v = wave_sum_d(acc[t]);
-            if (lane == 0) part[((size_t)s * T + t0 + t) * E + e] = v;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -216,428 +162,8 @@ __global__ __launch_bounds__(256) void k_route_logits_mf(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Many-token router logits: a workgroup computes a 64-token x 64-expert tile of
-// one K slice.  x and W_r tiles are staged in LDS as fp64 (k-major), each thread
-// accumulates 4 tokens x 4 experts in fp64 (products of two floats are exact in
-// fp64).  Trailing workgroups quantise x to Q8_1, as in k_route_logits.
-constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 2;
-
-__global__ __launch_bounds__(256) void k_route_logits_tiled(const float* __restrict__ x,
-                                                            const float* __restrict__ W, int T,
-                                                            int H, int E, int S,
-                                                            double* __restrict__ part,
-                                                            int n_logit_wg, ActPtr xq) {
-    if ((int)blockIdx.x >= n_logit_wg) {
-        const int nb = H / QK;
-        const long blk = (long)(blockIdx.x - n_logit_wg) * 8 + threadIdx.x / 32;
-        if (blk >= (long)T * nb) return;
-        const int l = threadIdx.x % 32;
-        const long r = blk / nb, b = blk % nb;
-        quant_q8_1_32(x[r * H + b * QK + l], l, xq.q + r * H + b * QK, xq.ds + r * nb + b,
-                      xq.sq + r * nb + b);
-        return;
-    }
-    __shared__ __align__(16) double sx[RT_K][RT_M + RT_PAD];
-    __shared__ __align__(16) double sw[RT_K][RT_N + RT_PAD];
-    const int gm = (T + RT_M - 1) / RT_M, gn = (E + RT_N - 1) / RT_N;
-    int b = blockIdx.x;
-    const int tm = b % gm;
-    b /= gm;
-    const int tn = b % gn;
-    const int s = b / gn;
-    const int slice = H / S, k0 = s * slice;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int kk = k0; kk < k0 + slice; kk += RT_K) {
-        // 64 rows x 32 floats of x and of W_r: two float4 per thread each
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int idx = threadIdx.x + j * 256;
-            const int row = idx >> 3, c4 = idx & 7;
-            const int t = min(tm * RT_M + row, T - 1), e = min(tn * RT_N + row, E - 1);
-            const float4 xv = *reinterpret_cast<const float4*>(x + (size_t)t * H + kk + c4 * 4);
-            const float4 wv = *reinterpret_cast<const float4*>(W + (size_t)e * H + kk + c4 * 4);
-            sx[c4 * 4 + 0][row] = xv.x;
-            sx[c4 * 4 + 1][row] = xv.y;
-            sx[c4 * 4 + 2][row] = xv.z;
-            sx[c4 * 4 + 3][row] = xv.w;
-            sw[c4 * 4 + 0][row] = wv.x;
-            sw[c4 * 4 + 1][row] = wv.y;
-            sw[c4 * 4 + 2][row] = wv.z;
-            sw[c4 * 4 + 3][row] = wv.w;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int k = 0; k < RT_K; ++k) {
-            double xa[4], wb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xa[i] = sx[k][ty * 4 + i];
-                wb[i] = sw[k][tx * 4 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(xa[i], wb[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = tm * RT_M + ty * 4 + i;
-        if (t >= T) break;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = tn * RT_N + tx * 4 + j;
-            if (e < E) part[((size_t)s * T + t) * E + e] = acc[i][j];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Selection for one token by one wave: sum the K-slice partials (in slice
-// order), add the bias, apply the group limit, top-k with ties to the lower id,
-// softmax over the chosen logits in fp64.  Lane j < k returns rank j's expert
-// and weight; other lanes return id -1.
-// (value, index) pair of lane `src` moved in by one cross-lane step: DPP row
-// ops inside a 16-lane row, the gfx950 row swaps across rows.  The reduction
-// below is a max over (value, -index), which is associative and commutative,
-// so mirrored partners reduce as well as butterflies do.
-template <int STEP>
-__device__ __forceinline__ void xlane(double v, int i, double& ov, int& oi) {
-    const long long b = __double_as_longlong(v);
-    int lo = (int)(b & 0xFFFFFFFFll), hi = (int)(b >> 32);
-    if constexpr (STEP < 4) {
-        constexpr int CTRL = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
-        lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xf, 0xf, false);
-        hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xf, 0xf, false);
-        oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
-    } else if constexpr (STEP == 4) {
-        auto a = __builtin_amdgcn_permlane16_swap((unsigned)lo, (unsigned)lo, false, false);
-        auto c = __builtin_amdgcn_permlane16_swap((unsigned)hi, (unsigned)hi, false, false);
-        auto d = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
-        // the swap hands each lane its partner row's value in one of the two results
-        const bool odd_row = (threadIdx.x & 16) != 0;
-        lo = (int)(odd_row ? a[0] : a[1]);
-        hi = (int)(odd_row ? c[0] : c[1]);
-        oi = (int)(odd_row ? d[0] : d[1]);
-    } else {
-        auto a = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)lo, false, false);
-        auto c = __builtin_amdgcn_permlane32_swap((unsigned)hi, (unsigned)hi, false, false);
-        auto d = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
-        const bool upper = (threadIdx.x & 32) != 0;
-        lo = (int)(upper ? a[0] : a[1]);
-        hi = (int)(upper ? c[0] : c[1]);
-        oi = (int)(upper ? d[0] : d[1]);
-    }
-    ov = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-template <int STEP>
-__device__ __forceinline__ void argmax_step(double& v, int& i) {
-    double ov;
-    int oi;
-    xlane<STEP>(v, i, ov, oi);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-}
-
-template <int STEP>
-__device__ __forceinline__ void argmax_step_f(float& v, int& i) {
-    float ov;
-    int oi;
-    if constexpr (STEP < 4) {
-        constexpr int CTRL = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
-        ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-        oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
-    } else if constexpr (STEP == 4) {
-        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        auto d = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
-        const bool odd_row = (threadIdx.x & 16) != 0;
-        ov = __uint_as_float(odd_row ? a[0] : a[1]);
-        oi = (int)(odd_row ? d[0] : d[1]);
-    } else {
-        auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-        auto d = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
-        const bool upper = (threadIdx.x & 32) != 0;
-        ov = __uint_as_float(upper ? a[0] : a[1]);
-        oi = (int)(upper ? d[0] : d[1]);
-    }
-    // (value desc, id asc); an empty lane (id 0x7fffffff) loses to any candidate
-    if (oi != 0x7fffffff && (i == 0x7fffffff || ov > v || (ov == v && oi < i))) { v = ov; i = oi; }
-}
-
-__device__ __forceinline__ void argmax_f(float& v, int& i) {
-    argmax_step_f<0>(v, i);
-    argmax_step_f<1>(v, i);
-    argmax_step_f<2>(v, i);
-    argmax_step_f<3>(v, i);
-    argmax_step_f<4>(v, i);
-    argmax_step_f<5>(v, i);
-}
-
-__device__ __forceinline__ void argmax_pair(double& v, int& i) {
-    argmax_step<0>(v, i);
-    argmax_step<1>(v, i);
-    argmax_step<2>(v, i);
-    argmax_step<3>(v, i);
-    argmax_step<4>(v, i);
-    argmax_step<5>(v, i);
-}
-
-// order-preserving map of a double to an unsigned 64-bit key
-__device__ __forceinline__ unsigned long long dkey(double v) {
-    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-__device__ __forceinline__ double dkey_inv(unsigned long long k) {
-    const unsigned long long b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-    return __longlong_as_double((long long)b);
-}
-
-constexpr int ROUTE_SMAX = 16; // K slices
-
-struct SelectArgs {
-    const double* part;
-    int S, T, E, k;
-    const float* bias;
-    const int32_t* groups;
-    int G, TG;
-    double* logits_tap;
-};
-
-// gkey: 64 words of LDS private to the calling wave.  MAXE_LANE = experts per
-// lane (E <= 64 * MAXE_LANE).
-template <int MAXE_LANE>
-__device__ __forceinline__ void select_token(const SelectArgs& A, int t,
-                                             unsigned long long* gkey, int& my_id,
-                                             float& my_w) {
-    const int lane = threadIdx.x & 63;
-    const double NEG = -__builtin_huge_val();
-    double l[MAXE_LANE];
-    bool ok[MAXE_LANE];
-    bool taken[MAXE_LANE];
-#pragma unroll
-    for (int m = 0; m < MAXE_LANE; ++m) {
-        const int e = lane + 64 * m;
-        l[m] = NEG;
-        ok[m] = e < A.E;
-        taken[m] = e >= A.E;
-        if (e < A.E) {
-            double ps[ROUTE_SMAX];
-#pragma unroll
-            for (int s = 0; s < ROUTE_SMAX; ++s)
-                ps[s] = s < A.S ? A.part[((size_t)s * A.T + t) * A.E + e] : 0.0;
-            double v = 0.0;
-#pragma unroll
-            for (int s = 0; s < ROUTE_SMAX; ++s)
-                if (s < A.S) v += ps[s];
-            if (A.bias) v += (double)A.bias[e];
-            l[m] = v;
-            if (A.logits_tap) A.logits_tap[(size_t)t * A.E + e] = v;
-        }
-    }
-    if (A.G > 0) {
-        // group score = largest member logit, through order-preserving keys
-        gkey[lane] = 0ull;
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int m = 0; m < MAXE_LANE; ++m) {
-            const int e = lane + 64 * m;
-            if (e < A.E) {
-                const unsigned gl = (unsigned)A.groups[e];
-                if (gl < (unsigned)A.G) atomicMax(&gkey[gl], dkey(l[m] + 0.0));   // -0 -> +0
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        const double gs = lane < A.G && gkey[lane] ? dkey_inv(gkey[lane]) : NEG;
-        bool gsel = false;
-        for (int n = 0; n < A.TG; ++n) {
-            double v = (lane < A.G && !gsel) ? gs : NEG;
-            int i = (lane < A.G && !gsel) ? lane : 0x7fffffff;
-            argmax_pair(v, i);
-            if (lane == i) gsel = true;
-        }
-        const unsigned long long sel = __ballot(gsel);
-#pragma unroll
-        for (int m = 0; m < MAXE_LANE; ++m) {
-            const int e = lane + 64 * m;
-            if (e < A.E) {
-                const unsigned gl = (unsigned)A.groups[e];
-                ok[m] = gl < (unsigned)A.G && ((sel >> gl) & 1ull);
-            }
-        }
-    }
-    // Fast path: rank by (fp32(l) desc, id asc) with 32-bit lane exchanges.
-    // fp32 rounding is monotone, so when the k+1 best fp32 values are strictly
-    // decreasing the chosen set and its order are those of the fp64 logits;
-    // otherwise (an fp32 tie among them) rank again in fp64.
-    double top_l = 0.0, mine = 0.0;
-    my_id = -1;
-    float f[MAXE_LANE];
-#pragma unroll
-    for (int m = 0; m < MAXE_LANE; ++m) f[m] = (float)l[m];
-    bool ftaken[MAXE_LANE];
-#pragma unroll
-    for (int m = 0; m < MAXE_LANE; ++m) ftaken[m] = taken[m] || !ok[m];
-    float prev = __builtin_inff();
-    bool strict = true;
-    int fid = -1, found = 0;
-    const int need = A.k + 1;
-    for (int j = 0; j < need; ++j) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int m = 0; m < MAXE_LANE; ++m) {
-            const int e = lane + 64 * m;
-            if (!ftaken[m] && (bi == 0x7fffffff || f[m] > bv)) { bv = f[m]; bi = e; }
-        }
-        argmax_f(bv, bi);
-        if (bi == 0x7fffffff) break;                 // fewer than k+1 candidates
-#pragma unroll
-        for (int m = 0; m < MAXE_LANE; ++m)
-            if (lane + 64 * m == bi) ftaken[m] = true;
-        if (!(bv < prev)) strict = false;
-        prev = bv;
-        if (j < A.k && lane == j) fid = bi;
-        ++found;
-    }
-    if (found < A.k) strict = false;    // too few allowed experts: the fp64 path falls back
-    if (strict) {
-        // fp64 logit of each chosen expert, from the lane that holds it
-        my_id = fid;
-        const int src = fid < 0 ? 0 : fid & 63, slot = fid < 0 ? 0 : fid >> 6;
-        double got = 0.0;
-#pragma unroll
-        for (int m = 0; m < MAXE_LANE; ++m) {
-            const double lm = __shfl(l[m], src, 64);
-            if (m == slot) got = lm;
-        }
-        mine = got;
-        top_l = __shfl(mine, 0, 64);
-    } else {
-        for (int j = 0; j < A.k; ++j) {
-            double bv = NEG;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int m = 0; m < MAXE_LANE; ++m) {
-                const int e = lane + 64 * m;
-                if (ok[m] && !taken[m] && (l[m] > bv || (l[m] == bv && e < bi))) { bv = l[m]; bi = e; }
-            }
-            argmax_pair(bv, bi);
-            if (bi == 0x7fffffff) {
-                // labels that break the equal-size-groups contract left fewer than k
-                // candidates: fall back to every expert not yet chosen (k <= E)
-                bv = NEG;
-#pragma unroll
-                for (int m = 0; m < MAXE_LANE; ++m) {
-                    const int e = lane + 64 * m;
-                    if (!taken[m] && (bi == 0x7fffffff || l[m] > bv || (l[m] == bv && e < bi))) { bv = l[m]; bi = e; }
-                }
-                argmax_pair(bv, bi);
-            }
-#pragma unroll
-            for (int m = 0; m < MAXE_LANE; ++m)
-                if (lane + 64 * m == bi) taken[m] = true;
-            if (j == 0) top_l = bv;
-            if (lane == j) { my_id = bi; mine = bv; }
-        }
-    }
-    const double ex = lane < A.k ? exp(mine - top_l) : 0.0;
-    double den = 0.0;
-    for (int j = 0; j < A.k; ++j) den += __shfl(ex, j, 64);        // rank order
-    my_w = lane < A.k ? (float)(ex / den) : 0.0f;
-}
-
-// One wave per token (any T).
-template <int MAXE_LANE>
-__global__ __launch_bounds__(64) void k_router_topk(SelectArgs A, int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts) {
-    __shared__ unsigned long long gkey[64];
-    const int t = blockIdx.x, lane = threadIdx.x;
-    int id;
-    float wt;
-    select_token<MAXE_LANE>(A, t, gkey, id, wt);
-    if (lane < A.k) {
-        ids[(size_t)t * A.k + lane] = id;
-        wts[(size_t)t * A.k + lane] = wt;
-    }
-}
-
-// Decode sizes (T <= 32, T*k <= 1024): one workgroup routes every token (one wave
-// per token) and buckets the assignments.  Per expert: count, token bitmask;
-// slots = experts with tokens in id order; an assignment's place in its
-// expert's list = its token's rank among that expert's tokens.
-constexpr int SMALL_TMAX = 32;
-constexpr int SMALL_NW = 16;
-
-template <int MAXE_LANE>
-__global__ __launch_bounds__(SMALL_NW * 64) void k_route_small(SelectArgs A, int32_t* __restrict__ ids,
-                                                               float* __restrict__ wts,
-                                                               int32_t* __restrict__ counts,
-                                                               int32_t* __restrict__ lists,
-                                                               uint32_t* __restrict__ ctrl,
-                                                               int32_t* __restrict__ active) {
-    __shared__ unsigned long long gkey[SMALL_NW][64];
-    __shared__ int s_cnt[512];
-    __shared__ unsigned s_mask[512];
-    __shared__ int s_wtot[SMALL_NW];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int e = threadIdx.x; e < A.E; e += blockDim.x) {
-        s_cnt[e] = 0;
-        s_mask[e] = 0u;
-    }
-    __syncthreads();
-    int my_id[2] = {-1, -1};
-    for (int rep = 0; rep < 2; ++rep) {
-        const int t = wave + rep * SMALL_NW;
-        if (t >= A.T) break;
-        float wt;
-        select_token<MAXE_LANE>(A, t, gkey[wave], my_id[rep], wt);
-        if (lane < A.k) {
-            ids[(size_t)t * A.k + lane] = my_id[rep];
-            wts[(size_t)t * A.k + lane] = wt;
-            atomicAdd(&s_cnt[my_id[rep]], 1);
-            atomicOr(&s_mask[my_id[rep]], 1u << t);
-        }
-    }
-    __syncthreads();
-    // counts of every expert; slots of the active ones (prefix over E <= 512 = 8 waves)
-    const int e = threadIdx.x;
-    const int c = e < A.E ? s_cnt[e] : 0;
-    const unsigned long long bal = __ballot(c > 0);
-    if (lane == 0) s_wtot[wave] = __popcll(bal);
-    __syncthreads();
-    if (e < A.E) {
-        counts[e] = c;
-        if (c > 0) {
-            int slot = __popcll(bal & ((1ull << lane) - 1ull));
-            for (int w = 0; w < wave; ++w) slot += s_wtot[w];
-            active[slot] = e;
-        }
-    }
-    if (threadIdx.x == 0) {
-        int n = 0;
-        for (int w = 0; w < SMALL_NW; ++w) n += s_wtot[w];
-        ctrl[CW_N_ACTIVE] = n;
-    }
-    // list positions: the token's rank among the expert's tokens
-    for (int rep = 0; rep < 2; ++rep) {
-        const int t = wave + rep * SMALL_NW;
-        if (t >= A.T) break;
-        if (lane < A.k) {
-            const int id = my_id[rep];
-            const int pos = __popc(s_mask[id] & ((1u << t) - 1u));
-            lists[(size_t)id * A.T + pos] = t * A.k + lane;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Decode routing (T <= DECODE_T), two launches and no cross-workgroup fences.
+// Router logits of a few tokens (T <= DECODE_T; launched for a single token,
+// whose top-k, softmax and bucketing run in the prologue of the gate/up kernel).
 //
 // k_route_logits_dec: workgroups [0, E): expert e = blockIdx.x, 256 threads
 // over the H-wide row of W_r with every load issued at once (indices past the
@@ -697,170 +223,6 @@ __global__ __launch_bounds__(256) void k_route_logits_dec(const float* __restric
     }
 }
 
-// k_route_select_dec: one workgroup.  Every (token, expert) pair computes its
-// rank = the number of allowed experts that beat it ((logit desc, id asc), in
-// fp64, all pairs in parallel); rank < k gives the slot.  With group labels the
-// groups are ranked the same way by their largest member logit first.  Then
-// softmax over the chosen logits (fp64, rank order) and the bucketing.
-constexpr int SEL_NT = 1024;
-
-__global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
-                                                             int32_t* __restrict__ ids,
-                                                             float* __restrict__ wts,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ lists,
-                                                             uint32_t* __restrict__ ctrl,
-                                                             int32_t* __restrict__ active) {
-    // logits live as ordered keys (dkey of l + 0.0: -0 and +0 compare equal as
-    // doubles and get one key); dkey_inv gives the logit back for the softmax
-    __shared__ unsigned long long s_key[DECODE_T * 512];
-    __shared__ unsigned long long s_gkey[DECODE_T][64];
-    __shared__ unsigned char s_gsel[DECODE_T][64];
-    __shared__ int s_nallow[DECODE_T];
-    __shared__ int s_sel[DECODE_T][32];
-    __shared__ double s_ex[DECODE_T][32];
-    __shared__ int s_cnt[512];
-    __shared__ unsigned s_mask[512];
-    __shared__ int s_wtot[SEL_NT / 64];
-    const int T = A.T, E = A.E, k = A.k, G = A.G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int TE = T * E;
-    for (int i = tid; i < TE; i += SEL_NT) {
-        const int e = i % E;
-        double v = A.part[i];
-        if (A.bias) v += (double)A.bias[e];
-        s_key[i] = dkey(v + 0.0);
-        if (A.logits_tap) A.logits_tap[i] = v;
-    }
-    for (int i = tid; i < E; i += SEL_NT) {
-        s_cnt[i] = 0;
-        s_mask[i] = 0u;
-    }
-    if (G > 0) {
-        for (int i = tid; i < T * 64; i += SEL_NT) s_gkey[i / 64][i % 64] = 0ull;
-        if (tid < T) s_nallow[tid] = 0;
-    }
-    __syncthreads();
-    if (G > 0) {
-        for (int i = tid; i < TE; i += SEL_NT) {
-            const int t = i / E, e = i - t * E;
-            const unsigned gl = (unsigned)A.groups[e];
-            if (gl < (unsigned)G) atomicMax(&s_gkey[t][gl], s_key[i]);
-        }
-        __syncthreads();
-        // group rank among the token's groups (key desc, group asc); keep rank < TG
-        for (int i = tid; i < T * G; i += SEL_NT) {
-            const int t = i / G, g = i - t * G;
-            const unsigned long long kg = s_gkey[t][g];
-            int r = 0;
-            for (int h = 0; h < G; ++h) {
-                const unsigned long long kh = s_gkey[t][h];
-                r += (int)(kh > kg) | ((int)(kh == kg) & (int)(h < g));
-            }
-            s_gsel[t][g] = r < A.TG;
-        }
-        __syncthreads();
-        // allowed experts per token: one LDS atomic per wave and token run
-        for (int b0 = 0; b0 < TE; b0 += SEL_NT) {
-            const int i = b0 + tid;
-            int t = -1;
-            bool al = false;
-            if (i < TE) {
-                t = i / E;
-                const unsigned gl = (unsigned)A.groups[i - t * E];
-                al = gl < (unsigned)G && s_gsel[t][gl];
-            }
-            if (al) atomicAdd(&s_nallow[t], 1);
-        }
-        __syncthreads();
-        // an excluded expert gets key 0: below every logit's key, so it never
-        // beats another and is never chosen; a token with fewer than k allowed
-        // experts (labels that break the equal-size-groups contract) keeps all
-        for (int i = tid; i < TE; i += SEL_NT) {
-            const int t = i / E;
-            const unsigned gl = (unsigned)A.groups[i - t * E];
-            const bool al = gl < (unsigned)G && s_gsel[t][gl];
-            if (!al && s_nallow[t] >= k) s_key[i] = 0ull;
-        }
-        __syncthreads();
-    }
-    // exact ranks: P lanes per (token, expert) pair each count the rivals
-    // (key desc, id asc) among E/P of them, eight loads at a time, no branches
-    int P = 1;
-    while (P < 64 && TE * P * 2 <= SEL_NT) P *= 2;
-    const int lp = 31 - __clz(P);
-    for (int b0 = 0; b0 < (TE << lp); b0 += SEL_NT) {
-        const int gi = b0 + tid;
-        const int i = gi >> lp, part = gi & (P - 1);
-        int r = 0, t = 0, e = 0;
-        unsigned long long ke = 0ull;
-        if (i < TE) {
-            t = i / E;
-            e = i - t * E;
-            ke = s_key[i];
-        }
-        const bool cand = ke != 0ull;
-        if (cand) {
-            constexpr int U = 8;
-            const unsigned long long* kt = s_key + t * E;
-            for (int h0 = part; h0 < E; h0 += U * P) {
-                unsigned long long kh[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) kh[u] = kt[min(h0 + u * P, E - 1)];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int h = h0 + u * P;
-                    r += (int)(h < E) & ((int)(kh[u] > ke) | ((int)(kh[u] == ke) & (int)(h < e)));
-                }
-            }
-        }
-        for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
-        if (cand && part == 0 && r < k) s_sel[t][r] = e;
-    }
-    __syncthreads();
-    // softmax over the chosen logits, rank order, fp64
-    for (int i = tid; i < T * k; i += SEL_NT) {
-        const int t = i / k, j = i - t * k;
-        s_ex[t][j] = exp(dkey_inv(s_key[t * E + s_sel[t][j]]) - dkey_inv(s_key[t * E + s_sel[t][0]]));
-    }
-    __syncthreads();
-    for (int i = tid; i < T * k; i += SEL_NT) {
-        const int t = i / k, j = i - t * k;
-        double den = 0.0;
-        for (int jj = 0; jj < k; ++jj) den += s_ex[t][jj];
-        const int id = s_sel[t][j];
-        ids[i] = id;
-        wts[i] = (float)(s_ex[t][j] / den);
-        atomicAdd(&s_cnt[id], 1);
-        atomicOr(&s_mask[id], 1u << t);
-    }
-    __syncthreads();
-    // counts of every expert; slots of the active ones in id order (one expert per thread)
-    const int c = tid < E ? s_cnt[tid] : 0;
-    const unsigned long long bal = __ballot(c > 0);
-    if (lane == 0) s_wtot[wave] = __popcll(bal);
-    __syncthreads();
-    if (tid < E) {
-        counts[tid] = c;
-        if (c > 0) {
-            int slot = __popcll(bal & ((1ull << lane) - 1ull));
-            for (int w = 0; w < wave; ++w) slot += s_wtot[w];
-            active[slot] = tid;
-        }
-    }
-    if (tid == 0) {
-        int n = 0;
-        for (int w = 0; w < SEL_NT / 64; ++w) n += s_wtot[w];
-        ctrl[CW_N_ACTIVE] = n;
-    }
-    // list positions: the token's rank among the expert's tokens
-    for (int i = tid; i < T * k; i += SEL_NT) {
-        const int t = i / k;
-        const int id = s_sel[t][i - t * k];
-        lists[(size_t)id * T + __popc(s_mask[id] & ((1u << t) - 1u))] = i;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Per-token selection, one workgroup per token (any T): the token's logits are
 // the K-slice partials summed in slice order plus the bias, held as ordered
@@ -869,8 +231,10 @@ __global__ __launch_bounds__(SEL_NT) void k_route_select_dec(SelectArgs A,
 // is the number of experts that beat it ((key desc, id asc)); rank < k is the
 // slot.  Softmax over the chosen logits in fp64, rank order.
 // BUCKET (T <= 32, T*k <= 1024): the last workgroup to finish (an arrival
-// counter) buckets every token's assignments, as k_route_select_dec does, and
-// clears the counter for the next call.
+// counter) buckets every token's assignments and clears the counter for the
+// next call: per expert the count and a token bitmask; the slots are the
+// experts with tokens in id order; an assignment's place in its expert's list
+// is its token's rank among that expert's tokens.
 // (NT threads: 1024 when few tokens share the chip, 256 when many do)
 template <bool BUCKET, int TSEL_NT>
 __global__ __launch_bounds__(TSEL_NT) void k_route_select_tok(SelectArgs A,
@@ -1227,7 +591,7 @@ hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStr
 
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, bool* bucketed, hipStream_t st) {
+                         ActPtr xq, RouteDone* done, SelectArgs* sel, hipStream_t st) {
     double* part = (double*)(ws + w.logit_part);
     const int S = w.S;
     const long qblocks = (long)T * (m.H / QK);
@@ -1237,15 +601,11 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     SelectArgs a;
     a.part = part; a.S = S; a.T = T; a.E = m.E; a.k = m.k;
     a.bias = br; a.groups = groups; a.G = m.G; a.TG = m.TG; a.logits_tap = logits_tap;
-    if (T <= ROUTE_DEC_MAX_T && m.E <= 512 && m.k <= 32) {
+    *sel = a;
+    if (T <= ROUTE_DEC_MAX_T) {
         hipLaunchKernelGGL(k_route_logits_dec, dim3(m.E + qwg), dim3(256), 0, st, x, Wr, T, m.H,
                            m.E, part, xq);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_route_select_dec, dim3(1), dim3(SEL_NT), 0, st, a, ids, wts,
-                           (int32_t*)(ws + w.counts), (int32_t*)(ws + w.lists),
-                           (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active));
-        *bucketed = true;
+        *done = ROUTE_LOGITS;
         return hipGetLastError();
     }
     const RouterTile rt = router_tile(T);
@@ -1271,14 +631,14 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     int32_t* lists = (int32_t*)(ws + w.lists);
     uint32_t* ctrl = (uint32_t*)(ws + w.ctrl);
     int32_t* active = (int32_t*)(ws + w.active);
-    if (T <= SMALL_TMAX && T * m.k <= 1024 && m.E <= 512) {
+    if (T <= MV_MAX_T && T * m.k <= 1024 && m.E <= 512) {
         hipLaunchKernelGGL((k_route_select_tok<true, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
                            wts, counts, lists, ctrl, active);
-        *bucketed = true;
+        *done = ROUTE_BUCKETED;
     } else {
         hipLaunchKernelGGL((k_route_select_tok<false, 256>), dim3(T), dim3(256), 0, st, a, ids,
                            wts, counts, lists, ctrl, active);
-        *bucketed = false;
+        *done = ROUTE_SELECTED;
     }
 #undef MOE_MAXE
     return hipGetLastError();
