@@ -19,44 +19,70 @@ __device__ __forceinline__ double dkey_inv(unsigned long long k) {
     return __longlong_as_double((long long)b);
 }
 
-// LDS of the single-token selection (E <= 512, k <= 32, n_groups <= 64).
+// LDS of the single-token selection (E <= 512, k <= 32, n_groups <= 64, at
+// most 8 waves).
 struct RouteLds {
     unsigned long long key[512];    // ordered key of each logit; 0 = excluded
+    unsigned long long ckey[256];   // candidates: wave w's local rank r at w*k + r
     unsigned long long gkey[64];    // group score: largest member key
     double ex[32];                  // exp(l_j - l_0), rank order
+    int cid[256];                   // candidate expert ids
+    int gcnt[64];                   // experts per group label
     int sel[32];                    // rank -> expert
-    int nallow;                     // experts in the kept groups
     unsigned char gsel[64];         // group kept
 };
 
 // Selection for one token by a whole workgroup of NT threads (every thread
 // calls; `weights` uniform over the workgroup), from its logits part[e]
-// (+ bias[e]).  Group limit: the groups are ranked by their largest member
-// key (ties to the lower group) and the experts outside the TG best get key 0,
-// unless that leaves fewer than k (labels that break the equal-size-groups
-// contract).  Every candidate's rank is the number of candidates that beat it
-// ((key desc, id asc)), P threads per expert each counting over E/P rivals;
-// rank < k gives S.sel[rank].  With `weights`, S.ex[j] = exp(l_j - l_0) in fp64
-// and *w (threads j < k) = ex_j / sum of ex in rank order.
+// (+ bias[e]).  Thread t holds experts t and t + NT.
+//  * Group limit: the groups are ranked by their largest member key (ties to
+//    the lower group) and the experts outside the TG best get key 0, unless
+//    that leaves fewer than k (labels that break the equal-size-groups
+//    contract).
+//  * Top-k with ties to the lower id: an expert's rank is the number of
+//    experts whose (key desc, id asc) order beats it; S.sel[rank] for rank < k.
+//    With at least two threads per expert, P threads count one expert's rivals
+//    directly.  Otherwise in two levels: the rank among the experts the wave
+//    holds; those of local rank < k are the candidates, and a candidate's rank
+//    among all candidates is its global rank (every expert that beats a global
+//    top-k member is itself a candidate).
+//  * With `weights`: S.ex[j] = exp(l_j - l_0) in fp64 and *w (threads j < k) =
+//    ex_j / the sum of ex in rank order.
 template <int NT>
 __device__ __forceinline__ void select_wg(const SelectArgs& A, RouteLds& S, bool weights, float* w) {
-    const int tid = threadIdx.x, E = A.E, k = A.k, G = A.G;
-    for (int i = tid; i < E; i += NT) {
-        double v = 0.0 + A.part[i];
-        if (A.bias) v += (double)A.bias[i];
-        S.key[i] = dkey(v + 0.0);      // -0 and +0 get one key
-        if (A.logits_tap) A.logits_tap[i] = v;
-    }
-    if (G > 0) {
-        if (tid < 64) S.gkey[tid] = 0ull;
-        if (tid == 0) S.nallow = 0;
-    }
-    __syncthreads();
-    if (G > 0) {
-        for (int i = tid; i < E; i += NT) {
-            const unsigned gl = (unsigned)A.groups[i];
-            if (gl < (unsigned)G) atomicMax(&S.gkey[gl], S.key[i]);
+    constexpr int MPT = (512 + NT - 1) / NT;      // experts per thread
+    constexpr int NWV = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = A.E, k = A.k, G = A.G;
+    unsigned long long key[MPT];
+    unsigned gl[MPT];
+#pragma unroll
+    for (int m = 0; m < MPT; ++m) {
+        const int i = tid + m * NT;
+        key[m] = 0ull;
+        gl[m] = ~0u;
+        if (i < E) {
+            double v = 0.0 + A.part[i];
+            const float b = A.bias ? A.bias[i] : 0.0f;
+            if (G > 0) gl[m] = (unsigned)A.groups[i];
+            if (A.bias) v += (double)b;
+            key[m] = dkey(v + 0.0);     // -0 and +0 get one key
+            if (A.logits_tap) A.logits_tap[i] = v;
         }
+    }
+    for (int c = tid; c < NWV * k; c += NT) S.ckey[c] = 0ull;
+    if (G > 0) {
+        if (tid < 64) {
+            S.gkey[tid] = 0ull;
+            S.gcnt[tid] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MPT; ++m)
+            if (gl[m] < (unsigned)G) {
+                atomicMax(&S.gkey[gl[m]], key[m]);
+                atomicAdd(&S.gcnt[gl[m]], 1);
+            }
         __syncthreads();
         for (int g = tid; g < G; g += NT) {
             const unsigned long long kg = S.gkey[g];
@@ -68,28 +94,28 @@ __device__ __forceinline__ void select_wg(const SelectArgs& A, RouteLds& S, bool
             S.gsel[g] = r < A.TG;
         }
         __syncthreads();
-        for (int i = tid; i < E; i += NT) {
-            const unsigned gl = (unsigned)A.groups[i];
-            if (gl < (unsigned)G && S.gsel[gl]) atomicAdd(&S.nallow, 1);
+        int nallow = 0;
+        for (int g = 0; g < G; ++g) nallow += S.gsel[g] ? S.gcnt[g] : 0;
+        if (nallow >= k) {
+#pragma unroll
+            for (int m = 0; m < MPT; ++m)
+                if (!(gl[m] < (unsigned)G && S.gsel[gl[m]])) key[m] = 0ull;
         }
-        __syncthreads();
-        for (int i = tid; i < E; i += NT) {
-            const unsigned gl = (unsigned)A.groups[i];
-            const bool al = gl < (unsigned)G && S.gsel[gl];
-            if (!al && S.nallow >= k) S.key[i] = 0ull;
-        }
-        __syncthreads();
     }
-    int P = 1;
-    while (P < 64 && E * P * 2 <= NT) P *= 2;
-    const int lp = 31 - __clz(P);
-    for (int b0 = 0; b0 < (E << lp); b0 += NT) {
-        const int gi = b0 + tid;
-        const int i = gi >> lp, part = gi & (P - 1);
+#pragma unroll
+    for (int m = 0; m < MPT; ++m)
+        if (tid + m * NT < E) S.key[tid + m * NT] = key[m];
+    __syncthreads();
+    if (E * 2 <= NT) {
+        // at least two threads per expert: P of them count the rivals of one
+        // expert over E/P of them each, which gives the global rank directly
+        int P = 2;
+        while (P < 64 && E * P * 2 <= NT) P *= 2;
+        const int lp = 31 - __clz(P);
+        const int i = tid >> lp, part = tid & (P - 1);
         int r = 0;
         const unsigned long long ke = i < E ? S.key[i] : 0ull;
-        const bool cand = ke != 0ull;
-        if (cand) {
+        if (ke != 0ull) {
             constexpr int U = 8;
             for (int h0 = part; h0 < E; h0 += U * P) {
                 unsigned long long kh[U];
@@ -103,9 +129,55 @@ __device__ __forceinline__ void select_wg(const SelectArgs& A, RouteLds& S, bool
             }
         }
         for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
-        if (cand && part == 0 && r < k) S.sel[r] = i;
+        if (ke != 0ull && part == 0 && r < k) S.sel[r] = i;
+        __syncthreads();
+    } else {
+        // level 1: rank among the wave's experts 64*wave + j and NT + 64*wave + j
+        const int nw = 64 * min(MPT, (E + NT - 1) / NT);   // rivals held by the wave
+#pragma unroll
+        for (int m = 0; m < MPT; ++m) {
+            const int i = tid + m * NT;
+            const unsigned long long ke = key[m];
+            int r = 0;
+            if (ke != 0ull) {
+                constexpr int U = 8;
+                for (int h0 = 0; h0 < nw; h0 += U) {
+                    unsigned long long kh[U];
+                    int hi[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int h = h0 + u;
+                        hi[u] = (h >> 6) * NT + 64 * wave + (h & 63);
+                        kh[u] = S.key[min(hi[u], E - 1)];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        r += (int)(hi[u] < E) & ((int)(kh[u] > ke) | ((int)(kh[u] == ke) & (int)(hi[u] < i)));
+                }
+                if (r < k) {
+                    S.ckey[wave * k + r] = ke;
+                    S.cid[wave * k + r] = i;
+                }
+            }
+        }
+        __syncthreads();
+        // level 2: rank among the candidates
+        for (int c = tid; c < NWV * k; c += NT) {
+            const unsigned long long kc = S.ckey[c];
+            if (kc != 0ull) {
+                const int ic = S.cid[c];
+                int r = 0;
+#pragma unroll 8
+                for (int h = 0; h < NWV * k; ++h) {
+                    const unsigned long long kh = S.ckey[h];
+                    const int ih = S.cid[h];
+                    r += (int)(kh != 0ull) & ((int)(kh > kc) | ((int)(kh == kc) & (int)(ih < ic)));
+                }
+                if (r < k) S.sel[r] = ic;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (weights) {
         if (tid < k) S.ex[tid] = exp(dkey_inv(S.key[S.sel[tid]]) - dkey_inv(S.key[S.sel[0]]));
         __syncthreads();

@@ -88,6 +88,11 @@ def _variant(**kw):
     dict(n_experts=1, top_k=1),
     dict(bias=True, tokens=40),
     dict(hidden=1280, n_ff=768, tokens=9),
+    # one token: routed in the gate/up kernel's prologue
+    dict(bias=True, tokens=1),
+    dict(bias=True, n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=1),
+    dict(n_experts=1, top_k=1, tokens=1),
+    dict(top_k=8, tokens=1),
 ])
 def test_variants(kw):
     w = _variant(**kw)
