@@ -29,6 +29,7 @@ struct RouteLds {
     int cid[256];                   // candidate expert ids
     int gcnt[64];                   // experts per group label
     int sel[32];                    // rank -> expert
+    int nallow;                     // experts in the kept groups
     unsigned char gsel[64];         // group kept
 };
 
@@ -84,19 +85,24 @@ __device__ __forceinline__ void select_wg(const SelectArgs& A, RouteLds& S, bool
                 atomicAdd(&S.gcnt[gl[m]], 1);
             }
         __syncthreads();
-        for (int g = tid; g < G; g += NT) {
-            const unsigned long long kg = S.gkey[g];
+        if (tid < 64) {
+            // wave 0, lane g: the group's rank, and the experts the kept groups hold
+            const int g = tid;
+            const unsigned long long kg = g < G ? S.gkey[g] : 0ull;
             int r = 0;
+#pragma unroll 8
             for (int h = 0; h < G; ++h) {
                 const unsigned long long kh = S.gkey[h];
                 r += (int)(kh > kg) | ((int)(kh == kg) & (int)(h < g));
             }
-            S.gsel[g] = r < A.TG;
+            const bool kept = g < G && r < A.TG;
+            if (g < G) S.gsel[g] = kept;
+            int n = kept ? S.gcnt[g] : 0;
+            for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+            if (g == 0) S.nallow = n;
         }
         __syncthreads();
-        int nallow = 0;
-        for (int g = 0; g < G; ++g) nallow += S.gsel[g] ? S.gcnt[g] : 0;
-        if (nallow >= k) {
+        if (S.nallow >= k) {
 #pragma unroll
             for (int m = 0; m < MPT; ++m)
                 if (!(gl[m] < (unsigned)G && S.gsel[gl[m]])) key[m] = 0ull;
