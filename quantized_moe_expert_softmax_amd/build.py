@@ -20,7 +20,6 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["mv_q8_0.hip", "mv_q4_0.hip", "mv_q5_1.hip", "mv_q4_k.hip", "mv_q5_k.hip", "mfma.hip",
            "route.hip", "matvec.hip", "capi.cpp"]
-HEADERS = ["moe_internal.h", "device.h", "kernels.h", "select.h", "matvec.h", "matvec_kern.h"]
 ARCH = "gfx950"
 
 
