@@ -125,9 +125,9 @@ def algorithmic_bytes(w, T, n_active):
     Q8_1 blocks).  Layer: router weights, x, every active expert's blocks, D and
     U, and out."""
     H, E, k, F, L = w.hidden, w.n_experts, w.top_k, w.n_ff, w.latent
-    kin, kout, bb = w.k_in, w.k_out, w.block_bytes
-    gu_w = 2 * F * (kin // 32) * bb
-    dn_w = kout * (F // 32) * bb
+    kin, kout = w.k_in, w.k_out
+    gu_w = w.matrix_bytes(2 * F, kin // 32)
+    dn_w = w.matrix_bytes(kout, F // 32)
     act_in = T * (kin // 32) * Q8_1_BLOCK
     hq = T * k * (F // 32) * Q8_1_BLOCK
     gate_up = n_active * gu_w + act_in + hq
@@ -430,7 +430,7 @@ def main():
         "config": {"workload": a.workload, "hidden": w.hidden, "n_experts": w.n_experts,
                    "top_k": w.top_k, "n_ff": w.n_ff, "latent": w.latent,
                    "expert_fmt": {synth.Q4_0: "Q4_0", synth.Q5_1: "Q5_1", synth.Q4_K: "Q4_K",
-                                  synth.Q5_K: "Q5_K"}.get(w.expert_fmt, "Q8_0"),
+                                  synth.Q5_K: "Q5_K", synth.Q3_K: "Q3_K"}.get(w.expert_fmt, "Q8_0"),
                    "dense_fmt": (("Q4_0" if w.dense_fmt == synth.Q4_0 else "Q8_0")
                                  if w.latent else None),
                    "tokens_per_step": T, "weight_copies": m["copies"], "token_batches": m["pool"],

@@ -70,8 +70,19 @@ typedef enum {
  * multiples of 256.  Q5_K (same commit): 176-byte super-blocks, the Q4_K
  * header and scales, 32 bytes of fifth bits (bit b of byte i for element i of
  * sub-block b), then the nibbles; same value and dot as Q4_K with q in 0..31.
- * Q5_1, Q4_K and Q5_K are expert formats only. */
-enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12, MOE_FMT_Q5_K = 13 };
+ * Q3_K (edge0-strata README, changes from upstream Strata: Q3_K latent
+ * experts; the block is ggml's): 110-byte super-blocks of 256, 32 bytes hmask,
+ * 64 bytes qs, 12 bytes of 6-bit sub-block scales, binary16 d; element e
+ * (half = e/128, j = e%128/32, l = e%32) has low bits (qs[32*half+l] >> 2j) & 3
+ * and high bit (hmask[l] >> (4*half+j)) & 1, code low + 4*high - 4; sub-block i
+ * of 16 has scale (lo | hi << 4) - 32 with lo the low (i < 8) or high (i >= 8)
+ * nibble of byte i % 8 and hi bits 2*(i/4) of byte 8 + i%4; value
+ * d*scale*code; a Q8_1 block's dot is d*d_a times the sum over its two halves
+ * of scale * sum(code * q_a).  Q3_K runs on the matrix-vector kernels at every
+ * T (the D/U projections keep the matrix cores for T > 32).
+ * Q5_1, Q4_K, Q5_K and Q3_K are expert formats only. */
+enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12, MOE_FMT_Q5_K = 13,
+       MOE_FMT_Q3_K = 11 };
 
 /* Which packed tensor a pack call is about. */
 enum { MOE_PACK_EXPERTS = 0, MOE_PACK_D = 1, MOE_PACK_U = 2 };
@@ -82,7 +93,7 @@ typedef struct {
     int32_t top_k;        /* k: 1..min(E, 32)                                             */
     int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
     int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
-    int32_t expert_fmt;   /* MOE_FMT_Q8_0, _Q4_0, _Q5_1, _Q4_K or _Q5_K                  */
+    int32_t expert_fmt;   /* MOE_FMT_Q8_0, _Q4_0, _Q5_1, _Q4_K, _Q5_K or _Q3_K           */
     int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 or MOE_FMT_Q4_0 (latent == 0: unused)*/
     int32_t n_groups;     /* 0 = no group limit; else divides E                           */
     int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/

@@ -23,6 +23,7 @@ Q4_0 = 2
 Q5_1 = 7
 Q4_K = 12
 Q5_K = 13
+Q3_K = 11
 Q8_1_BYTES = 36
 
 
@@ -84,6 +85,12 @@ def lib():
         L.orc_q5_k_code.restype = ctypes.c_int
         L.orc_isum_q5_k.argtypes = [vp, i32, vp]
         L.orc_isum_q5_k.restype = ctypes.c_int32
+        L.orc_q3_k_code.argtypes = [vp, i32]
+        L.orc_q3_k_code.restype = ctypes.c_int
+        L.orc_q3_k_scale.argtypes = [vp, i32]
+        L.orc_q3_k_scale.restype = ctypes.c_int
+        L.orc_isum_q3_k.argtypes = [vp, i32, vp]
+        L.orc_isum_q3_k.restype = ctypes.c_int32
         L.orc_dequant_weight.argtypes = [i32, vp, i32]
         L.orc_dequant_weight.restype = ctypes.c_double
         L.orc_row_dot.argtypes = [i32, vp, vp, i32, vp]
@@ -168,6 +175,22 @@ def isum_q4_k(sblk: np.ndarray, b: int, ablk: np.ndarray) -> int:
     sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
     ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
     return int(lib().orc_isum_q4_k(_p(sblk), b, _p(ablk)))
+
+
+def q3_k_code(sblk: np.ndarray, e: int) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    return int(lib().orc_q3_k_code(_p(sblk), e))
+
+
+def q3_k_scale(sblk: np.ndarray, i: int) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    return int(lib().orc_q3_k_scale(_p(sblk), i))
+
+
+def isum_q3_k(sblk: np.ndarray, b: int, ablk: np.ndarray) -> int:
+    sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
+    ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
+    return int(lib().orc_isum_q3_k(_p(sblk), b, _p(ablk)))
 
 
 def q5_1_code(wblk: np.ndarray, j: int) -> int:

@@ -23,6 +23,11 @@
  *   [QK] same commit: Q4_K and Q5_K experts, whose dots are llama.cpp's q4_K /
  *        q5_K x q8_1 (the min term on the sum of the quantised activations of
  *        each Q8_1 block).
+ *   [Q3] edge0-strata README, section "Changes from upstream Strata": Q3_K
+ *        latent experts.  The pages name the format only; its block is read as
+ *        llama.cpp's Q3_K (the ggml that the same README builds against), and
+ *        its dot against Q8_1 as the block's two 16-element halves, each with
+ *        its signed sub-block scale, times d * d_a (no min term).
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
  *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
  *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
@@ -45,12 +50,13 @@
 #define ORC_Q5_1 7
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
+#define ORC_Q3_K 11
 #define ORC_QK 32
 #define ORC_Q8_1_BYTES 36
 
 typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
-    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1, ORC_Q4_K or ORC_Q5_K */
+    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1, ORC_Q4_K, ORC_Q5_K or ORC_Q3_K */
     int n_groups, topk_groups;/* 0 = no group limit */
     int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
@@ -257,7 +263,45 @@ int32_t orc_isum_q5_k(const uint8_t* sb, int b, const uint8_t* a) {
     return s;
 }
 
-static inline int kq_bytes(int fmt) { return fmt == ORC_Q5_K ? 176 : 144; }
+/*
+ * Q3_K: super-blocks of 256 elements in 110 bytes: 32 bytes hmask, 64 bytes
+ * qs, 12 bytes of 6-bit sub-block scales, binary16 d [Q3].  Element e, with
+ * half = e / 128, j = (e % 128) / 32 and l = e % 32, has its low two bits at
+ * bits 2j, 2j + 1 of qs byte 32 * half + l and its high bit at bit 4 * half + j
+ * of hmask byte l; its code is low + 4 * high - 4, in [-4, 3].  Sixteen
+ * sub-blocks of 16 elements; sub-block i's scale is the 6-bit value with low
+ * nibble s[i] & 15 (i < 8) or s[i - 8] >> 4 (i >= 8) and top two bits
+ * (s[8 + i % 4] >> 2 * (i / 4)) & 3, minus 32.  The value is d * scale * code.
+ */
+int orc_q3_k_code(const uint8_t* sb, int e) {
+    int half = e / 128, j = (e % 128) / 32, l = e % 32;
+    int low = (sb[32 + 32 * half + l] >> (2 * j)) & 3;
+    int high = (sb[l] >> (4 * half + j)) & 1;
+    return low + 4 * high - 4;
+}
+
+int orc_q3_k_scale(const uint8_t* sb, int i) {
+    const uint8_t* s = sb + 96;
+    int lo = i < 8 ? s[i] & 15 : s[i - 8] >> 4;
+    int hi = (s[8 + i % 4] >> (2 * (i / 4))) & 3;
+    return (lo | hi << 4) - 32;
+}
+
+/* integer part of block b (sub-blocks 2b, 2b + 1) against one Q8_1 block:
+ * the sum over the two halves of scale * sum(code * q_a) */
+int32_t orc_isum_q3_k(const uint8_t* sb, int b, const uint8_t* a) {
+    int32_t s = 0;
+    for (int h = 0; h < 2; ++h) {
+        int32_t t = 0;
+        for (int i = 0; i < 16; ++i)
+            t += orc_q3_k_code(sb, 32 * b + 16 * h + i) * (int32_t)(int8_t)a[4 + 16 * h + i];
+        s += orc_q3_k_scale(sb, 2 * b + h) * t;
+    }
+    return s;
+}
+
+static inline int kq_bytes(int fmt) { return fmt == ORC_Q5_K ? 176 : fmt == ORC_Q3_K ? 110 : 144; }
+static inline int is_kq(int fmt) { return fmt == ORC_Q4_K || fmt == ORC_Q5_K || fmt == ORC_Q3_K; }
 
 static inline int fmt_bytes(int fmt) {
     return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34;   /* per 32; Q4_K: 144 per 256 */
@@ -268,6 +312,8 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
     double d = orc_f16_decode(rd16(w));
     if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
     if (fmt == ORC_Q5_1) return d * (double)orc_q5_1_code(w, j) + orc_f16_decode(rd16(w + 2));
+    if (fmt == ORC_Q3_K)                           /* w: the super-block, j < 256 */
+        return orc_f16_decode(rd16(w + 108)) * orc_q3_k_scale(w, j / 16) * (double)orc_q3_k_code(w, j);
     if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {      /* w: the super-block, j < 256 */
         int sc, mn;
         orc_q4_k_scale_min(w, j / 32, &sc, &mn);
@@ -288,6 +334,17 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
  */
 float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
     double acc = 0.0;
+    if (fmt == ORC_Q3_K) {
+        /* block b against Q8_1 block b: d * d_a * isum_b, exact in double [Q3] */
+        for (int b = 0; b < nblk; ++b) {
+            const uint8_t* sb = row + (size_t)(b / 8) * 110;
+            const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
+            int32_t is = orc_isum_q3_k(sb, b % 8, a);
+            if (isum_tap) isum_tap[b] = is;
+            acc += orc_f16_decode(rd16(sb + 108)) * orc_f16_decode(rd16(a)) * (double)is;
+        }
+        return (float)acc;
+    }
     if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {
         /*
          * Sub-block b against Q8_1 block b: d * scale_b * d_a * isum_b minus
@@ -326,8 +383,7 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
 
 /* rows outputs of a [rows][nblk] block matrix times a Q8_1 vector */
 static size_t row_bytes(int fmt, int nblk) {
-    return fmt == ORC_Q4_K || fmt == ORC_Q5_K ? (size_t)(nblk / 8) * kq_bytes(fmt)
-                                              : (size_t)nblk * fmt_bytes(fmt);
+    return is_kq(fmt) ? (size_t)(nblk / 8) * kq_bytes(fmt) : (size_t)nblk * fmt_bytes(fmt);
 }
 
 void orc_matvec(int fmt, int rows, int nblk, const uint8_t* W, const uint8_t* act, float* y,
@@ -545,8 +601,9 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
     if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1 &&
-        d->expert_fmt != ORC_Q4_K && d->expert_fmt != ORC_Q5_K) return -1;
-    if ((d->expert_fmt == ORC_Q4_K || d->expert_fmt == ORC_Q5_K) &&
+        d->expert_fmt != ORC_Q4_K && d->expert_fmt != ORC_Q5_K && d->expert_fmt != ORC_Q3_K)
+        return -1;
+    if (is_kq(d->expert_fmt) &&
         ((d->latent ? d->latent : d->hidden) % 256 || d->n_ff % 256))
         return -1;
     if (d->latent && d->dense_fmt != ORC_Q8_0 && d->dense_fmt != ORC_Q4_0) return -1;

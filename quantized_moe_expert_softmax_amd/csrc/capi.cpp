@@ -54,7 +54,8 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0 &&
         d->expert_fmt != MOE_FMT_Q5_1 && !kquant(d->expert_fmt))
         return fail(MOE_EUNSUPPORTED,
-                    "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12), Q5_K (13)",
+                    "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12), Q5_K (13), "
+                    "Q3_K (11)",
                     d->expert_fmt);
     // edge0-strata README, changes from upstream Strata: the latent D/U
     // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
@@ -95,6 +96,7 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
                     : d->expert_fmt == MOE_FMT_Q5_1 ? "Q5_1"
                     : d->expert_fmt == MOE_FMT_Q4_K ? "Q4_K"
                     : d->expert_fmt == MOE_FMT_Q5_K ? "Q5_K"
+                    : d->expert_fmt == MOE_FMT_Q3_K ? "Q3_K"
                                                     : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
@@ -164,12 +166,55 @@ static int gate_up_row(int p, int F) {
     return r < 32 ? fb * 32 + r : F + fb * 32 + (r - 32);
 }
 
+// Q3_K super-block (canonical: hmask[32], qs[64], scales[12], binary16 d) <->
+// packed codes (eight 12-byte blocks + the 12 scale bytes) and side (d).  The
+// canonical element e = 128*half + 32*j + l has its two low bits at bits 2j of
+// qs[32*half + l] and its high bit at bit 4*half + j of hmask[l]; packed block
+// b, element i = 16h + 4m + p (word h) and i = 4m + p (high-bit word).
+static void q3_k_to_packed(const uint8_t* c, uint8_t* codes, uint8_t* side) {
+    for (int b = 0; b < 8; ++b) {
+        uint32_t w[3] = {0u, 0u, 0u};
+        for (int i = 0; i < 32; ++i) {
+            const int e = 32 * b + i, half = e / 128, j = (e % 128) / 32, l = e % 32;
+            const uint32_t lo = (c[32 + 32 * half + l] >> (2 * j)) & 3u;
+            const uint32_t hi = (c[l] >> (4 * half + j)) & 1u;
+            const int h = i / 16, m = (i % 16) / 4, p = i % 4;
+            w[h] |= lo << (8 * p + 2 * m);
+            w[2] |= hi << (8 * p + i / 4);
+        }
+        for (int k = 0; k < 3; ++k)
+            for (int t = 0; t < 4; ++t) codes[12 * b + 4 * k + t] = (uint8_t)(w[k] >> (8 * t));
+    }
+    memcpy(codes + 96, c + 96, 12);
+    memcpy(side, c + 108, 2);
+}
+
+static void q3_k_to_canonical(const uint8_t* codes, const uint8_t* side, uint8_t* c) {
+    memset(c, 0, 96);
+    for (int b = 0; b < 8; ++b) {
+        uint32_t w[3];
+        for (int k = 0; k < 3; ++k)
+            w[k] = (uint32_t)codes[12 * b + 4 * k] | (uint32_t)codes[12 * b + 4 * k + 1] << 8 |
+                   (uint32_t)codes[12 * b + 4 * k + 2] << 16 | (uint32_t)codes[12 * b + 4 * k + 3] << 24;
+        for (int i = 0; i < 32; ++i) {
+            const int e = 32 * b + i, half = e / 128, j = (e % 128) / 32, l = e % 32;
+            const int h = i / 16, m = (i % 16) / 4, p = i % 4;
+            const uint32_t lo = (w[h] >> (8 * p + 2 * m)) & 3u;
+            const uint32_t hi = (w[2] >> (8 * p + i / 4)) & 1u;
+            c[32 + 32 * half + l] |= (uint8_t)(lo << (2 * j));
+            c[l] |= (uint8_t)(hi << (4 * half + j));
+        }
+    }
+    memcpy(c + 96, codes + 96, 12);
+    memcpy(c + 108, side, 2);
+}
+
 // One matrix: canonical blocks (rows in canonical order) <-> packed codes/scales.
 static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t* canon,
                            uint8_t* packed, bool to_packed) {
-    // canonical units ([side data][codes]) of ub blocks of 32
-    const int ub = unit_blocks(M.fmt), nu = M.nblk / ub;
-    const int bb = block_bytes(M.fmt) * ub, cb = code_bytes(M.fmt) * ub, sb = side_bytes(M.fmt) * ub;
+    // canonical units ([side data][codes], Q3_K: its own block) of ub blocks of 32
+    const int nu = (int)M.units();
+    const int bb = unit_bytes(M.fmt), cb = unit_code_bytes(M.fmt), sb = unit_side_bytes(M.fmt);
     uint8_t* codes = packed + M.codes_off;
     uint8_t* scales = packed + M.scales_off;
     for (int p = 0; p < M.rows; ++p) {
@@ -177,13 +222,18 @@ static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t*
         for (int b = 0; b < nu; ++b) {
             const size_t cpos = ((size_t)r * nu + b) * bb;
             const size_t ppos = ((size_t)p * nu + b);
-            if (to_packed) {
-                memcpy(scales + sb * ppos, canon + cpos, sb);
-                memcpy(codes + ppos * cb, canon + cpos + sb, cb);
+            uint8_t* c = const_cast<uint8_t*>(canon) + cpos;
+            if (M.fmt == MOE_FMT_Q3_K) {
+                if (to_packed)
+                    q3_k_to_packed(c, codes + ppos * cb, scales + sb * ppos);
+                else
+                    q3_k_to_canonical(codes + ppos * cb, scales + sb * ppos, c);
+            } else if (to_packed) {
+                memcpy(scales + sb * ppos, c, sb);
+                memcpy(codes + ppos * cb, c + sb, cb);
             } else {
-                uint8_t* c = const_cast<uint8_t*>(canon);
-                memcpy(c + cpos, scales + sb * ppos, sb);
-                memcpy(c + cpos + sb, codes + ppos * cb, cb);
+                memcpy(c, scales + sb * ppos, sb);
+                memcpy(c + sb, codes + ppos * cb, cb);
             }
         }
     }
@@ -336,8 +386,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     // (K-quant experts take the per-slot down projection at every T)
     const bool down_tok = T <= DOWN_TOK_MAX_T && !kquant(m.fmt);
-    // many tokens: grouped matrix-core GEMMs over token tiles
-    const bool gemm = T > MV_MAX_T;
+    // many tokens: grouped matrix-core GEMMs over token tiles (the D/U
+    // projections always; the experts in the formats that have them)
+    const bool dense_gemm = T > MV_MAX_T;
+    const bool gemm = dense_gemm && has_mfma_path(m.fmt);
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel
@@ -370,7 +422,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
         // z = D . Q8_1(x), fp32
-        if (gemm) {
+        if (dense_gemm) {
             CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
             CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         } else {
@@ -411,7 +463,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     EV(MOE_EV_DOWN);
     if (m.L) {
         // out = U . Q8_1(y_lat)
-        if (gemm) {
+        if (dense_gemm) {
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (lat_fused_q) {

@@ -83,6 +83,9 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     if (m.fmt == MOE_FMT_Q5_K)
         return tap ? gate_up_fmt<MOE_FMT_Q5_K, true>(lpr, cpl, grid, lds, a, st, ev)
                    : gate_up_fmt<MOE_FMT_Q5_K, false>(lpr, cpl, grid, lds, a, st, ev);
+    if (m.fmt == MOE_FMT_Q3_K)
+        return tap ? gate_up_fmt<MOE_FMT_Q3_K, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_Q3_K, false>(lpr, cpl, grid, lds, a, st, ev);
     return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
                : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
@@ -117,6 +120,9 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (fmt == MOE_FMT_Q5_K)
         return tap ? rows_fmt<MOE_FMT_Q5_K, true>(lpr, cpl, grid, lds, a, st)
                    : rows_fmt<MOE_FMT_Q5_K, false>(lpr, cpl, grid, lds, a, st);
+    if (fmt == MOE_FMT_Q3_K)
+        return tap ? rows_fmt<MOE_FMT_Q3_K, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_Q3_K, false>(lpr, cpl, grid, lds, a, st);
     return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
@@ -151,8 +157,7 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
-    if (m.fmt == MOE_FMT_Q4_K || m.fmt == MOE_FMT_Q5_K)
-        return hipErrorInvalidConfiguration;   // (down per slot instead)
+    if (kquant(m.fmt)) return hipErrorInvalidConfiguration;   // (down per slot instead)
     int lpr, cpl;
     if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;

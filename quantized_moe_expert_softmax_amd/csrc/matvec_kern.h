@@ -39,18 +39,59 @@ struct Fmt {
     static constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
     static constexpr bool K5 = FMT == MOE_FMT_Q5_K;
     static constexpr bool K4 = FMT == MOE_FMT_Q4_K || K5;      // super-blocks of 256
+    static constexpr bool K3 = FMT == MOE_FMT_Q3_K;            // super-blocks of 256
     static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block of 32
-    static constexpr int CPB = NIB ? 1 : 2;                   // 16-byte chunks per block of 32
-    static constexpr int SBLK = K4 ? 8 : 1;                   // blocks of 32 per side-data unit
+    static constexpr int CPB = NIB ? 1 : 2;                   // chunks per block of 32
+    static constexpr int SBLK = K4 || K3 ? 8 : 1;             // blocks of 32 per side-data unit
     static constexpr int CPSIDE = CPB * SBLK;                 // chunks per side-data unit
     // a unit's side data in memory and in registers: the binary16 d; for Q5_1
     // {d | m << 16, qh}; for a Q4_K super-block {d | dmin << 16, scale bytes
-    // 0..11}; for Q5_K that and its 32 qh bytes (a chunk keeps its 16)
+    // 0..11}; for Q5_K that and its 32 qh bytes (a chunk keeps its 16); for a
+    // Q3_K super-block d in memory, {scale bytes 0..11, d} in registers
     using SideMem = std::conditional_t<
         K5, K5SideMem, std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint16_t>>>;
     using Side = std::conditional_t<
-        K5, K5Side, std::conditional_t<K4, v4i, std::conditional_t<Q5, uint2, uint32_t>>>;
+        K5, K5Side, std::conditional_t<K4 || K3, v4i, std::conditional_t<Q5, uint2, uint32_t>>>;
+    // packed code bytes of a row of nb blocks (Q3_K: 108 per super-block)
+    __host__ __device__ static constexpr size_t row_bytes(int nb) {
+        return K3 ? (size_t)(nb / 8) * 108 : (size_t)nb * QB;
+    }
 };
+
+// A Q3_K chunk: block c of the row, its 12 packed code bytes in w.x..w.z (two
+// words of 2-bit codes, (word h >> 2m) & 0x03030303 being elements 16h + 4m ..
+// + 3, and a word of high bits, element 4m + p at bit 8p + m) and the
+// super-block's 12 scale bytes in s.x..s.z.  A code is low + 4 * high - 4:
+// per byte, the low bits or'ed with 0xFC where the high bit is clear.  Returns
+// the block's integer sum: each 16-element half's dot times its signed 6-bit
+// sub-block scale (sub-blocks 2b, 2b + 1, b = c % 8).
+__device__ __forceinline__ int k3_isum(const v4i& w, const v4i& s, int c, const int8_t* arow) {
+    const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
+    const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
+    const uint32_t H = (uint32_t)w.z;
+    int t0 = 0, t1 = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t n0 = ((H >> m) & 0x01010101u) ^ 0x01010101u;
+        const uint32_t n1 = ((H >> (4 + m)) & 0x01010101u) ^ 0x01010101u;
+        const int q0 = (int)((((uint32_t)w.x >> (2 * m)) & 0x03030303u) | (n0 * 0xFCu));
+        const int q1 = (int)((((uint32_t)w.y >> (2 * m)) & 0x03030303u) | (n1 * 0xFCu));
+        t0 = dot4(q0, lo[m], t0);
+        t1 = dot4(q1, hi[m], t1);
+    }
+    const int b = c & 7;
+    // the low nibbles: bytes 2b, 2b + 1 (b < 4) or the high nibbles of bytes
+    // 2b - 8, 2b - 7; the top bits: byte 8 + i % 4, bits 2 * (i / 4)
+    const uint32_t wlo = (b & 2) ? (uint32_t)s.y : (uint32_t)s.x;
+    const int sh = 16 * (b & 1);
+    const uint32_t nib = b < 4 ? (wlo >> sh) & 0x0F0Fu : (wlo >> (sh + 4)) & 0x0F0Fu;
+    const int i0 = 2 * b, i1 = i0 + 1;
+    const uint32_t h0 = ((uint32_t)s.z >> (8 * (i0 & 3) + 2 * (i0 >> 2))) & 3u;
+    const uint32_t h1 = ((uint32_t)s.z >> (8 * (i1 & 3) + 2 * (i1 >> 2))) & 3u;
+    const int sc0 = (int)((nib & 0xFu) | h0 << 4) - 32;
+    const int sc1 = (int)((nib >> 8) | h1 << 4) - 32;
+    return sc0 * t0 + sc1 * t1;
+}
 
 // A Q4_K chunk c (16 nibble bytes) of a row: super-block c / 8; within it
 // nibble bytes 16 * (c % 8) .. + 16, i.e. elements 16 * (c % 2) .. + 16 of the
@@ -195,6 +236,16 @@ __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = min(j * LPR + sl, NCH - 1);
+        if constexpr (F::K3) {
+            // the block's 12 code bytes and the super-block's scale bytes (4-byte
+            // aligned), its d from the side data
+            const uint8_t* u = row + (size_t)(c >> 3) * 108;
+            const uint32_t* cw = reinterpret_cast<const uint32_t*>(u + (c & 7) * 12);
+            const uint32_t* sw = reinterpret_cast<const uint32_t*>(u + 96);
+            wq[j] = v4i{(int)cw[0], (int)cw[1], (int)cw[2], 0};
+            wsc[j] = v4i{(int)sw[0], (int)sw[1], (int)sw[2], (int)rscl[c >> 3]};
+            continue;
+        }
         wq[j] = ld16(row + (size_t)c * 16);
         if constexpr (F::K5) {
             // the super-block's scales and the qh half of this chunk
@@ -244,7 +295,13 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
         for (int j = 0; j < CPL; ++j) {
             const bool valid = j * LPR + sl < NCH;
             const int c = min(j * LPR + sl, NCH - 1);
-            if constexpr (F::K4) {
+            if constexpr (F::K3) {
+                const int is = k3_isum(wq[j], wsc[j], c, arow);
+                acc = fmaf((float)is, valid ? h2f((uint32_t)wsc[j].w) * ad[c] : 0.0f, acc);
+                if constexpr (TAP) {
+                    if (tap && valid) emit_isum(i, r, c, is);
+                }
+            } else if constexpr (F::K4) {
                 int i0, i1;
                 if constexpr (F::K5)
                     acc = k4_chunk<true>(wq[j], wsc[j].s, wsc[j].qh, c, valid, arow, ad, asq, acc, i0, i1);
@@ -388,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         cnt = A.b.counts[e];
         lst = A.b.lists + (size_t)e * A.T;
     }
-    const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
+    const size_t rowb = Fmt<FMT>::row_bytes(nb);
     const uint8_t* ebase = A.experts + (size_t)e * A.eb;
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
     using SM = typename Fmt<FMT>::SideMem;
@@ -475,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
         cnt = A.T;
     }
     const int K = A.K, nb = K / QK, TCH = A.tch;
-    const size_t rowb = (size_t)nb * Fmt<FMT>::QB;
+    const size_t rowb = Fmt<FMT>::row_bytes(nb);
     const uint8_t* codes = mat + A.codes_off + (size_t)rt * A.rt * rowb;
     using SM = typename Fmt<FMT>::SideMem;
     const SM* scl = reinterpret_cast<const SM*>(mat + A.scales_off) + (size_t)rt * A.rt * (nb / Fmt<FMT>::SBLK);
@@ -526,7 +583,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     const int t = blockIdx.x / NRT, rt = blockIdx.x - t * NRT;
     const int nb = A.F / QK;
     const int NCH = nb * F::CPB;
-    const size_t rowb = (size_t)nb * F::QB;
+    const size_t rowb = F::row_bytes(nb);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sl = lane % LPR, rg = lane / LPR;
     const bool tap = TAP && t < A.taps.tap_tokens && A.taps.isum_dn;

@@ -840,6 +840,8 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
             launch_k(k_mfma_kq<SWIGLU, true, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
         else
             launch_k(k_mfma_kq<SWIGLU, false, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
+    } else if (fmt != MOE_FMT_Q8_0) {
+        return hipErrorInvalidValue;   // (no matrix-core path for this format)
     } else {
         if (tap)
             launch_k(k_mfma_dma<SWIGLU, true>, grid, block, 0, st, ev, a);

@@ -3,10 +3,18 @@
 //
 // Packed block matrix [rows][nblk] (any format): the codes of all rows first,
 // row-major (32 bytes per Q8_0 block, 16 per Q4_0 or Q5_1 block, in element
-// order for Q8_0 and in the canonical nibble-byte order otherwise), then each
-// block's side data, row-major [row][block]: the binary16 d (2 bytes), or for
-// Q5_1 d, m and qh (8 bytes, as in the canonical block).  The canonical block
-// is [side data][codes] in every format, and the byte count is the same.
+// order for Q8_0 and in the canonical nibble-byte order otherwise; 128 per
+// Q4_K / Q5_K super-block; 108 per Q3_K super-block), then each unit's side
+// data, row-major [row][unit]: the binary16 d (2 bytes), for Q5_1 d, m and qh
+// (8 bytes), for Q4_K / Q5_K the super-block header and scales (16, 48 bytes
+// with Q5_K's qh), for Q3_K the binary16 d.  The canonical unit is [side
+// data][codes] in every format except Q3_K, and the byte count is the same.
+//
+// Packed Q3_K super-block: eight 12-byte blocks, then the 12 canonical scale
+// bytes.  Block b of 32: two little-endian words of 2-bit codes, word h holding
+// element 16h + 4m + p at bits 8p + 2m (so (word >> 2m) & 0x03030303 gives
+// elements 16h + 4m .. + 3 in its bytes), then one word of high bits, element
+// 4m + p at bit 8p + m.
 //
 // Packed expert: gate/up matrix of 2F rows then the down matrix [Kout][F/32].
 // The gate/up rows come in pairs of 32-row tiles: packed row fb*64 + r holds
@@ -23,22 +31,28 @@ namespace moe {
 constexpr int QK = 32;              // elements per block
 constexpr int Q8_1_CANON = 36;      // canonical Q8_1 block bytes
 
-// per block of 32 elements (a Q4_K super-block of 256 has 128 code bytes and
-// 16 bytes of side data: 16 and 2 per 32; Q5_K's 48 bytes of side data carry
-// the fifth bits as well: 6 per 32)
-inline int code_bytes(int fmt) { return fmt == MOE_FMT_Q8_0 ? 32 : 16; }
-inline int side_bytes(int fmt) { return fmt == MOE_FMT_Q5_1 ? 8 : fmt == MOE_FMT_Q5_K ? 6 : 2; }
-inline int block_bytes(int fmt) { return code_bytes(fmt) + side_bytes(fmt); }
-// blocks of 32 per canonical unit (a Q4_K super-block is one unit of 8)
-inline int unit_blocks(int fmt) { return fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K ? 8 : 1; }
-inline bool kquant(int fmt) { return fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K; }
+// Canonical units: unit_blocks(fmt) blocks of 32 (a K-quant super-block is one
+// unit of 8).  Packed bytes per unit: codes, and side data.
+inline bool kquant(int fmt) { return fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K || fmt == MOE_FMT_Q3_K; }
+inline int unit_blocks(int fmt) { return kquant(fmt) ? 8 : 1; }
+inline int unit_code_bytes(int fmt) {
+    return fmt == MOE_FMT_Q8_0 ? 32 : fmt == MOE_FMT_Q3_K ? 108 : 16 * unit_blocks(fmt);
+}
+inline int unit_side_bytes(int fmt) {
+    return fmt == MOE_FMT_Q5_1 ? 8 : fmt == MOE_FMT_Q4_K ? 16 : fmt == MOE_FMT_Q5_K ? 48 : 2;
+}
+inline int unit_bytes(int fmt) { return unit_code_bytes(fmt) + unit_side_bytes(fmt); }
+// matrix-core prefill kernels exist for these formats (the rest run every T on
+// the matrix-vector kernels)
+inline bool has_mfma_path(int fmt) { return fmt != MOE_FMT_Q3_K; }
 
 struct MatLayout {                  // one packed block matrix
     int rows = 0, nblk = 0, fmt = MOE_FMT_Q8_0;
     size_t codes_off = 0;           // from the matrix base
     size_t scales_off = 0;
-    size_t row_code_bytes() const { return (size_t)nblk * code_bytes(fmt); }
-    size_t bytes() const { return (size_t)rows * nblk * block_bytes(fmt); }
+    size_t units() const { return (size_t)nblk / unit_blocks(fmt); }
+    size_t row_code_bytes() const { return units() * unit_code_bytes(fmt); }
+    size_t bytes() const { return (size_t)rows * units() * unit_bytes(fmt); }
 };
 
 inline MatLayout mat_layout(int rows, int nblk, int fmt) {
@@ -47,7 +61,7 @@ inline MatLayout mat_layout(int rows, int nblk, int fmt) {
     m.nblk = nblk;
     m.fmt = fmt;
     m.codes_off = 0;
-    m.scales_off = (size_t)rows * nblk * code_bytes(fmt);
+    m.scales_off = (size_t)rows * m.row_code_bytes();
     return m;
 }
 

@@ -53,7 +53,7 @@ template <int NT>
 __device__ __forceinline__ void select_wg(const SelectArgs& A, RouteLds& S, bool weights, float* w) {
     constexpr int MPT = (512 + NT - 1) / NT;      // experts per thread
     constexpr int NWV = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int E = A.E, k = A.k, G = A.G;
     unsigned long long key[MPT];
     unsigned gl[MPT];

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EDEVICE, MOE_EHIP, MOE_ENOMEM = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EDEVICE",
                 -4: "MOE_EHIP", -5: "MOE_ENOMEM"}
-MOE_FMT_Q8_0, MOE_FMT_Q4_0, MOE_FMT_Q5_1, MOE_FMT_Q4_K, MOE_FMT_Q5_K = 8, 2, 7, 12, 13
+MOE_FMT_Q8_0, MOE_FMT_Q4_0, MOE_FMT_Q5_1, MOE_FMT_Q4_K, MOE_FMT_Q5_K, MOE_FMT_Q3_K = 8, 2, 7, 12, 13, 11
 MOE_PACK_EXPERTS, MOE_PACK_D, MOE_PACK_U = 0, 1, 2
 
 # every function include/moe.h declares

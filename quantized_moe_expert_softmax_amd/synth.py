@@ -40,8 +40,19 @@ Q4_0 = 2
 Q5_1 = 7
 Q4_K = 12
 Q5_K = 13
+Q3_K = 11
 # bytes per 32 elements (Q4_K / Q5_K: 144 / 176-byte super-blocks of 256)
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18, Q5_K: 22}
+# bytes per super-block of 256 elements
+SUPER_BYTES = {Q4_K: 144, Q5_K: 176, Q3_K: 110}
+
+
+def matrix_bytes(fmt: int, rows: int, nblk: int) -> int:
+    """Canonical bytes of a [rows][nblk blocks of 32] matrix of format fmt."""
+    if fmt in SUPER_BYTES:
+        assert nblk % 8 == 0
+        return rows * (nblk // 8) * SUPER_BYTES[fmt]
+    return rows * nblk * BLOCK_BYTES[fmt]
 S_MIN = 1 << 40      # added to a block set's scale stream for its Q5_1 minimums
 
 
@@ -143,6 +154,21 @@ def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
         assert out.nbytes == nsb * sbb
         lib.synth_interleave_blocks(nsb, _ptr(d16), _ptr(payload), sbb - 2, _ptr(out))
         return out
+    elif fmt == Q3_K:
+        # super-blocks: 32 hmask bytes, 64 qs bytes, 12 scale bytes (all bits
+        # uniform), then binary16 d
+        assert nblk % 8 == 0
+        nsb = nblk // 8
+        raw = np.empty(nsb * 108, dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, q_stream, 0, nsb * 108, _ptr(raw))
+        scale = absnormal_f64(seed, d_stream, nsb, 0.02 / 128.0)
+        if out is None:
+            out = np.empty(nsb * 110, dtype=np.uint8)
+        assert out.nbytes == nsb * 110
+        o = out.reshape(nsb, 110)
+        o[:, :108] = raw.reshape(nsb, 108)
+        o[:, 108:] = scale.astype(np.float16).view(np.uint8).reshape(nsb, 2)
+        return out
     else:
         raise ValueError(f"unknown block format {fmt}")
     d16 = scale.astype(np.float16).view(np.uint16)
@@ -189,7 +215,11 @@ class Workload:
 
     @property
     def expert_bytes(self) -> int:
-        return sum(r * b for r, b in self.role_rows()) * self.block_bytes
+        return sum(matrix_bytes(self.expert_fmt, r, b) for r, b in self.role_rows())
+
+    def matrix_bytes(self, rows: int, nblk: int) -> int:
+        """Canonical bytes of an expert matrix of `rows` rows of `nblk` blocks."""
+        return matrix_bytes(self.expert_fmt, rows, nblk)
 
     def with_tokens(self, t: int) -> "Workload":
         return dataclasses.replace(self, tokens=t)
@@ -201,7 +231,7 @@ class Workload:
         return [(self.latent, self.hidden // 32), (self.hidden, self.latent // 32)]
 
 
-# The five layers measured and checked here.
+# The layers measured and checked here.
 WORKLOADS = {
     "tiny": Workload("tiny", hidden=512, n_experts=8, top_k=2, n_ff=256, tokens=4, seed=1000),
     "decode": Workload("decode", hidden=4096, n_experts=128, top_k=8, n_ff=1536, tokens=1,
@@ -218,6 +248,12 @@ WORKLOADS = {
                             tokens=1, expert_fmt=Q4_K, seed=1006),
     "decode_q5_k": Workload("decode_q5_k", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
                             tokens=1, expert_fmt=Q5_K, seed=1007),
+    "decode_q3_k": Workload("decode_q3_k", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
+                            tokens=1, expert_fmt=Q3_K, seed=1008),
+    # the latent_q4 shapes with Q3_K latent experts
+    "latent_q3_k": Workload("latent_q3_k", hidden=7168, n_experts=256, top_k=8, n_ff=1024,
+                            tokens=1, latent=1792, expert_fmt=Q3_K, n_groups=16, topk_groups=4,
+                            seed=1009),
 }
 
 
@@ -250,7 +286,7 @@ def gen_expert(w: Workload, e: int, out: Optional[np.ndarray] = None) -> np.ndar
         out = np.empty(w.expert_bytes, dtype=np.uint8)
     off = 0
     for role, (rows, nb) in enumerate(w.role_rows()):
-        n = rows * nb * w.block_bytes
+        n = w.matrix_bytes(rows, nb)
         blocks(w.expert_fmt, w.seed, S_EXP_Q + 4 * e + role, S_EXP_D + 4 * e + role, rows * nb,
                out=out[off:off + n])
         off += n

@@ -124,7 +124,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
                                    nthreads=8)
     k, F = w.top_k, w.n_ff
     kin, kout = w.k_in, w.k_out
-    bb = w.block_bytes
+    ngu = w.matrix_bytes(2 * F, kin // 32)     # gate/up bytes of one expert
     eb = w.expert_bytes
     nbi, nbf = kin // 32, F // 32
     report = {}
@@ -168,14 +168,14 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
             a = t * k + j
             e = int(g["ids"][t, j])
             blob = inp["experts"][e * eb:(e + 1) * eb]
-            gu = blob[:2 * F * nbi * bb]
+            gu = blob[:ngu]
             y_gu, is_gu = oracle.matvec(w.expert_fmt, gu, 2 * F, nbi, ain[t].reshape(-1), with_isum=True)
             assert np.array_equal(g["isum_gu"][a], is_gu), (t, j)
             # h from the oracle's g and u on the GPU's own input: fp32 order only
             gg, uu = y_gu[:F].astype(np.float64), y_gu[F:].astype(np.float64)
             h_own = (gg / (1.0 + np.exp(-gg)) * uu).astype(np.float32)
             assert rel_max(g["h"][a], h_own) < 1e-4, (t, j, rel_max(g["h"][a], h_own))
-            dn = blob[2 * F * nbi * bb:]
+            dn = blob[ngu:]
             y_dn, is_dn = oracle.matvec(w.expert_fmt, dn, kout, nbf, g["hq"][a].reshape(-1), with_isum=True)
             assert np.array_equal(g["isum_dn"][a], is_dn), (t, j)
             assert rel_max(g["y"][a], y_dn) < 1e-5
@@ -205,7 +205,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
         y_own = []
         for j, a in enumerate(a_t):
             e = int(g["ids"][t, j])
-            dn = inp["experts"][e * eb:(e + 1) * eb][2 * F * nbi * bb:]
+            dn = inp["experts"][e * eb:(e + 1) * eb][ngu:]
             y_own.append(oracle.matvec(w.expert_fmt, dn, kout, nbf, g["hq"][a].reshape(-1)))
         y_own = np.stack(y_own).astype(np.float64)
         comb = (g["weights"][t].astype(np.float64)[:, None] * y_own).sum(0)

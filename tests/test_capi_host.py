@@ -95,8 +95,8 @@ def _small(fmt=8, latent=0):
                           latent=latent, expert_fmt=fmt, seed=77)
 
 
-@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (13, 0), (8, 256), (2, 256),
-                                        (7, 256), (12, 256), (13, 256)])
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (13, 0), (11, 0), (8, 256),
+                                        (2, 256), (7, 256), (12, 256), (13, 256), (11, 256)])
 def test_pack_roundtrip(L, fmt, latent):
     w = _small(fmt, latent)
     d = moe.desc_of(w)
@@ -177,6 +177,40 @@ def test_pack_layout_kquant(L, fmt):
             assert np.array_equal(pk[(packed_row * nsb + u) * 128:(packed_row * nsb + u + 1) * 128], c[sd:])
             off = rows * nsb * 128 + (packed_row * nsb + u) * sd
             assert np.array_equal(pk[off:off + sd], c[:sd])
+
+
+def test_pack_layout_q3_k(L):
+    """Q3_K super-blocks pack as 108 code bytes (eight 12-byte blocks: two words of 2-bit
+    codes, element 16h + 4m + p of word h at bits 8p + 2m, and a word of high bits, element
+    4m + p at bit 8p + m; then the 12 scale bytes) and the binary16 d as side data, the same
+    110 bytes; the packed codes give back every element's code as the oracle reads it from
+    the canonical block."""
+    import oracle
+    w = _small(11)
+    d = moe.desc_of(w)
+    ex = synth.gen_experts(w)
+    packed = np.empty_like(ex)
+    moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
+    F, K = w.n_ff, w.hidden
+    nsb = K // 256
+    e = 1
+    blob = ex[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    pk = packed[e * w.expert_bytes:(e + 1) * w.expert_bytes]
+    rows = 2 * F
+    for canon_row, packed_row in [(0, 0), (F + 0, 32), (33, 65)]:
+        for u in (0, nsb - 1):
+            c = blob[(canon_row * nsb + u) * 110:(canon_row * nsb + u + 1) * 110]
+            pc = pk[(packed_row * nsb + u) * 108:(packed_row * nsb + u + 1) * 108]
+            assert np.array_equal(pc[96:108], c[96:108])
+            off = rows * nsb * 108 + (packed_row * nsb + u) * 2
+            assert np.array_equal(pk[off:off + 2], c[108:110])
+            for b in range(8):
+                wd = pc[12 * b:12 * b + 12].view("<u4").astype(np.int64)
+                for i in range(32):
+                    h, m, p = i // 16, (i % 16) // 4, i % 4
+                    lo = (wd[h] >> (8 * p + 2 * m)) & 3
+                    hi = (wd[2] >> (8 * p + i // 4)) & 1
+                    assert lo + 4 * hi - 4 == oracle.q3_k_code(c, 32 * b + i), (b, i)
 
 
 def test_forward_argument_checks_without_gpu(L):

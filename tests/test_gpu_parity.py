@@ -202,6 +202,27 @@ def test_q5_k_experts(kw):
     _report("q5_k " + str(kw), w.tokens, rep)
 
 
+# Q3_K experts (super-blocks of 256, 3-bit codes, signed 6-bit scales per 16
+# elements): decode, a verify window, the 9..32-token path, more than 32 tokens
+# (which stay on the matrix-vector kernels), latent with group labels and the
+# latent-prefill D/U on the matrix cores, decode-sized rows
+@pytest.mark.parametrize("kw", [
+    dict(expert_fmt=synth.Q3_K, tokens=1),
+    dict(expert_fmt=synth.Q3_K, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
+    dict(expert_fmt=synth.Q3_K, tokens=20),
+    dict(expert_fmt=synth.Q3_K, tokens=70, bias=True),
+    dict(expert_fmt=synth.Q3_K, latent=256, n_experts=16, top_k=4, n_groups=4, topk_groups=2,
+         tokens=1),
+    dict(expert_fmt=synth.Q3_K, latent=256, n_experts=16, top_k=4, tokens=40),
+    dict(expert_fmt=synth.Q3_K, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
+    dict(expert_fmt=synth.Q3_K, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=6),
+])
+def test_q3_k_experts(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("q3_k " + str(kw), w.tokens, rep)
+
+
 # path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [

@@ -491,6 +491,86 @@ def test_q5_k_bruteforce_and_dequantised_dot(orc):
         assert y[r] == np.float32(acc)
 
 
+def _q3_k_superblock(d16=0, scales="00" * 12, qs=(), hmask=()):
+    sb = np.zeros(110, np.uint8)
+    for i, v in hmask:
+        sb[i] = v
+    for i, v in qs:
+        sb[32 + i] = v
+    sb[96:108] = np.frombuffer(bytes.fromhex(scales), np.uint8)
+    sb[108], sb[109] = d16 & 0xFF, d16 >> 8
+    return sb
+
+
+def test_q3_k_golden_superblocks(orc):
+    """Hand-derived Q3_K super-blocks: the 6-bit signed sub-block scales (low nibbles of
+    bytes 0..7 for sub-blocks below 8, high nibbles above, top bits from bytes 8..11), the
+    code order (two bits in qs, the high bit in hmask, minus 4), the two scaled halves of a
+    block, and one row value."""
+    g = json.load(open(os.path.join(GOLD, "quant_blocks.json")))
+    for c in g["q3_k"]:
+        sb = _q3_k_superblock(scales=c["scales"])
+        assert orc.q3_k_scale(sb, c["i"]) == c["scale"], c["name"]
+    c = g["q3_k_codes"]
+    sb = _q3_k_superblock(scales=c["scales"], qs=[(c["qs_byte"], int(c["qs"], 16))],
+                          hmask=[(c["hmask_byte"], int(c["hmask"], 16))])
+    assert orc.q3_k_code(sb, c["element"]) == c["code"]
+    assert orc.q3_k_code(sb, 0) == c["zero_code"]
+    a = np.zeros(36, np.uint8)
+    a[4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+    assert orc.isum_q3_k(sb, 6, a) == c["isum_b6"]
+    assert orc.isum_q3_k(sb, 1, a) == c["isum_b1"]
+    c = g["q3_k_row"]
+    sb = _q3_k_superblock(int(c["d16"], 16), c["scales"], [(c["qs_byte"], int(c["qs"], 16))],
+                          [(c["hmask_byte"], int(c["hmask"], 16))])
+    act = np.zeros((8, 36), np.uint8)
+    ad = int(c["a_d16"], 16)
+    act[c["active_block"], 0], act[c["active_block"], 1] = ad & 0xFF, ad >> 8
+    act[c["active_block"], 4:] = (np.arange(32) + 1).astype(np.int8).view(np.uint8)
+    y = orc.matvec(11, sb, 1, 8, act.reshape(-1))
+    assert y[0] == np.float32(c["y"])
+
+
+def test_q3_k_bruteforce_and_dequantised_dot(orc):
+    """Q3_K codes and scales against numpy bit arithmetic over whole super-blocks, integer
+    block sums against the numpy dot, and each block's contribution equal, exactly, to the
+    fp64 dot of the dequantised weights d * scale * code with the dequantised activations."""
+    rng = np.random.default_rng(28)
+    n = 4
+    W = rng.integers(0, 256, (2 * n, 110)).astype(np.uint8)
+    d = (np.abs(rng.standard_normal(2 * n)) * 0.02 / 128).astype(np.float16).view(np.uint16)
+    W[:, 108], W[:, 109] = d & 0xFF, d >> 8
+    A = _rand_q8_1(orc, rng, 8 * n)
+    y = orc.matvec(11, W.reshape(-1), 2, 8 * n, A.reshape(-1))
+    e = np.arange(256)
+    half, j, l = e // 128, (e % 128) // 32, e % 32
+    for r in range(2):
+        acc = 0.0
+        for sbi in range(n):
+            sb = W[r * n + sbi]
+            s = sb[96:108].astype(np.int64)
+            i = np.arange(16)
+            lo = np.where(i < 8, s[i % 8] & 15, s[i % 8] >> 4)
+            sc = (lo | ((s[8 + i % 4] >> (2 * (i // 4))) & 3) << 4) - 32
+            code = ((sb[32 + 32 * half + l].astype(np.int64) >> (2 * j)) & 3) \
+                + 4 * ((sb[l].astype(np.int64) >> (4 * half + j)) & 1) - 4
+            assert [orc.q3_k_scale(sb, k) for k in range(16)] == list(sc)
+            assert [orc.q3_k_code(sb, k) for k in range(256)] == list(code)
+            dd = orc.f16_decode(int(sb[108]) | int(sb[109]) << 8)
+            for b in range(8):
+                a = A[sbi * 8 + b]
+                qa = a[4:].view(np.int8).astype(np.int64)
+                ref = int(sc[2 * b] * np.dot(code[32 * b:32 * b + 16], qa[:16])
+                          + sc[2 * b + 1] * np.dot(code[32 * b + 16:32 * b + 32], qa[16:]))
+                assert orc.isum_q3_k(sb, b, a) == ref
+                da = orc.f16_decode(int(a[0]) | int(a[1]) << 8)
+                part = math.fsum(orc.dequant_weight(11, sb, 32 * b + k) * da * int(qa[k])
+                                 for k in range(32))
+                assert part == dd * da * ref
+                acc += part
+        assert y[r] == np.float32(acc)
+
+
 @pytest.mark.parametrize("fmt", [8, 2])
 def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
     """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
