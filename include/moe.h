@@ -78,8 +78,7 @@ typedef enum {
  * of 16 has scale (lo | hi << 4) - 32 with lo the low (i < 8) or high (i >= 8)
  * nibble of byte i % 8 and hi bits 2*(i/4) of byte 8 + i%4; value
  * d*scale*code; a Q8_1 block's dot is d*d_a times the sum over its two halves
- * of scale * sum(code * q_a).  Q3_K runs on the matrix-vector kernels at every
- * T (the D/U projections keep the matrix cores for T > 32).
+ * of scale * sum(code * q_a).
  * Q5_1, Q4_K, Q5_K and Q3_K are expert formats only. */
 enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12, MOE_FMT_Q5_K = 13,
        MOE_FMT_Q3_K = 11 };

@@ -386,10 +386,8 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     // (K-quant experts take the per-slot down projection at every T)
     const bool down_tok = T <= DOWN_TOK_MAX_T && !kquant(m.fmt);
-    // many tokens: grouped matrix-core GEMMs over token tiles (the D/U
-    // projections always; the experts in the formats that have them)
-    const bool dense_gemm = T > MV_MAX_T;
-    const bool gemm = dense_gemm && has_mfma_path(m.fmt);
+    // many tokens: grouped matrix-core GEMMs over token tiles
+    const bool gemm = T > MV_MAX_T;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel
@@ -422,7 +420,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
         // z = D . Q8_1(x), fp32
-        if (dense_gemm) {
+        if (gemm) {
             CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
             CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         } else {
@@ -463,7 +461,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     EV(MOE_EV_DOWN);
     if (m.L) {
         // out = U . Q8_1(y_lat)
-        if (dense_gemm) {
+        if (gemm) {
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (lat_fused_q) {

@@ -51,6 +51,21 @@ __device__ __forceinline__ void k4_scale_min(const v4i& sd, int b, int& sc, int&
     mn = b < 4 ? lo_mn : hi_mn;
 }
 
+// Q3_K: the signed 6-bit scales of sub-blocks 2b and 2b + 1 (block b of a
+// super-block) from the 12 scale bytes in s.x..s.z.  The low nibbles are bytes
+// 2b, 2b + 1 (b < 4) or the high nibbles of bytes 2b - 8, 2b - 7; the top two
+// bits of sub-block i are bits 2 * (i / 4) of byte 8 + i % 4; minus 32.
+__device__ __forceinline__ void k3_scales(const v4i& s, int b, int& sc0, int& sc1) {
+    const uint32_t wlo = (b & 2) ? (uint32_t)s.y : (uint32_t)s.x;
+    const int sh = 16 * (b & 1) + (b < 4 ? 0 : 4);
+    const uint32_t nib = (wlo >> sh) & 0x0F0Fu;
+    const int i0 = 2 * b, i1 = i0 + 1;
+    const uint32_t h0 = ((uint32_t)s.z >> (8 * (i0 & 3) + 2 * (i0 >> 2))) & 3u;
+    const uint32_t h1 = ((uint32_t)s.z >> (8 * (i1 & 3) + 2 * (i1 >> 2))) & 3u;
+    sc0 = (int)((nib & 0xFu) | h0 << 4) - 32;
+    sc1 = (int)((nib >> 8) | h1 << 4) - 32;
+}
+
 // bits 0..3 of x moved to bit 4 of bytes 0..3 (bit i to byte i): the four
 // copies x << 7i put bit i at bit 8i and nowhere else a byte starts
 __device__ __forceinline__ int spread4(uint32_t x) {

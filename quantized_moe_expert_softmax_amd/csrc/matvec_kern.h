@@ -79,17 +79,8 @@ __device__ __forceinline__ int k3_isum(const v4i& w, const v4i& s, int c, const 
         t0 = dot4(q0, lo[m], t0);
         t1 = dot4(q1, hi[m], t1);
     }
-    const int b = c & 7;
-    // the low nibbles: bytes 2b, 2b + 1 (b < 4) or the high nibbles of bytes
-    // 2b - 8, 2b - 7; the top bits: byte 8 + i % 4, bits 2 * (i / 4)
-    const uint32_t wlo = (b & 2) ? (uint32_t)s.y : (uint32_t)s.x;
-    const int sh = 16 * (b & 1);
-    const uint32_t nib = b < 4 ? (wlo >> sh) & 0x0F0Fu : (wlo >> (sh + 4)) & 0x0F0Fu;
-    const int i0 = 2 * b, i1 = i0 + 1;
-    const uint32_t h0 = ((uint32_t)s.z >> (8 * (i0 & 3) + 2 * (i0 >> 2))) & 3u;
-    const uint32_t h1 = ((uint32_t)s.z >> (8 * (i1 & 3) + 2 * (i1 >> 2))) & 3u;
-    const int sc0 = (int)((nib & 0xFu) | h0 << 4) - 32;
-    const int sc1 = (int)((nib >> 8) | h1 << 4) - 32;
+    int sc0, sc1;
+    k3_scales(s, c & 7, sc0, sc1);
     return sc0 * t0 + sc1 * t1;
 }
 

@@ -138,7 +138,7 @@ __device__ __forceinline__ v16f scale_mfma(float a, float b) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, v16f{}, 0, 0, 0);
 }
 
-template <bool SWIGLU, bool TAP, class SOp = h4, class Frag, class SFrag>
+template <bool SWIGLU, bool TAP, class SOp = h4, bool NEG = false, class Frag, class SFrag>
 __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const MfWave& w, int s,
                                          const int* s_orow, Frag frag, SFrag sfrag,
                                          float (&acc0)[16], float (&acc1)[16]) {
@@ -180,7 +180,9 @@ __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const
                         const int cr = SWIGLU ? ((pr & 63) < 32 ? (pr >> 6) * 32 + (pr & 31)
                                                                 : A.F + (pr >> 6) * 32 + (pr & 31))
                                               : pr;
-                        A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = q ? i1[i] : i0[i];
+                        // (NEG: the staged codes were negated, so the sum is too)
+                        const int v = q ? i1[i] : i0[i];
+                        A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = NEG ? -v : v;
                     }
                 }
             }
@@ -439,9 +441,16 @@ constexpr int MS_SWR = MF_NT + 32, MS_SAR = MF_MT + 32;
 // the codes widen to int8 0..31, and each stage adds the min terms
 // sum_b m_w[r][b] * s_a[t][b] with one more f16 outer product per row tile:
 // the four blocks' m and s in the k slots 0..3 of lanes 0..31.
+// Q3_K (FMT): a stage of four blocks is half a super-block.  Each element
+// widens to w = -(code * scale) of its 16-element sub-block, in [-128, 124]
+// (the code in [-4, 3], the scale in [-32, 31]), by a byte lookup (v_perm) in
+// the sub-block's table (4 - v) * scale over v = code + 4; the block's matrix-
+// core sum is then minus its integer sum, exact, and the rows' scale operand
+// is -d (a sign flip of the binary16 d).
 template <bool SWIGLU, bool TAP, int FMT>
 __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
     constexpr bool Q5 = FMT == MOE_FMT_Q5_1;
+    constexpr bool K3 = FMT == MOE_FMT_Q3_K;
     constexpr int QB = 16;                                // code bytes per Q4_0 / Q5_1 block
     constexpr int WBYTES = MF_NT * MS_ROWB, XBYTES = MF_MT * MS_ROWB;
     constexpr int SCB = MF_KB * MS_SWR * 2 + MF_KB * MS_SAR * 2;
@@ -462,11 +471,13 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
     }
     __syncthreads();
 
-    const int K = A.K, nb = K / QK;
-    const size_t rowb = (size_t)nb * QB;
+    const int K = A.K, nb = K / QK, nsb = nb / 8;
+    const size_t rowb = K3 ? (size_t)nsb * 108 : (size_t)nb * QB;
     const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
     const uint16_t* scl = reinterpret_cast<const uint16_t*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
     const uint2* side = reinterpret_cast<const uint2*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
+    // Q3_K: one binary16 d per row and super-block
+    const uint16_t* sbd = reinterpret_cast<const uint16_t*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nsb;
 
     // ---- global -> registers -> LDS staging of one stage (blocks kb0 .. kb0+MF_KB)
     constexpr int WCH = 2;                     // 16-byte chunks (= blocks) per thread
@@ -477,12 +488,24 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
     uint2 rdw;
     v4i rsd[2];                                // Q5_1: the row's side data, 4 blocks
     v4i rda;
+    v4i rs3[WCH];                              // Q3_K: each chunk's super-block scale bytes
+    uint32_t rd3 = 0;                          // Q3_K: the row's d (this stage's super-block)
     auto gload = [&](int kb0) {
 #pragma unroll
         for (int j = 0; j < WCH; ++j) {
             const int ch = tid + j * MF_THREADS;
             const int r = ch / WCPR, p = ch - r * WCPR;
-            rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * QB + p * 16);
+            if constexpr (K3) {
+                // block kb0 + p: 12 code bytes, and the super-block's 12 scale bytes
+                const int blk = kb0 + p;
+                const uint8_t* u = codes + (size_t)r * rowb + (size_t)(blk >> 3) * 108;
+                const uint32_t* cw = reinterpret_cast<const uint32_t*>(u + (blk & 7) * 12);
+                const uint32_t* sw = reinterpret_cast<const uint32_t*>(u + 96);
+                rw[j] = v4i{(int)cw[0], (int)cw[1], (int)cw[2], 0};
+                rs3[j] = v4i{(int)sw[0], (int)sw[1], (int)sw[2], 0};
+            } else {
+                rw[j] = ld16(codes + (size_t)r * rowb + (size_t)kb0 * QB + p * 16);
+            }
             if constexpr (Q5) rq[j] = side[(size_t)r * nb + kb0 + p].y;
         }
 #pragma unroll
@@ -492,7 +515,9 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             rx[j] = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)kb0 * QK + p * 16);
         }
         if (tid < MF_NT) {
-            if constexpr (Q5) {
+            if constexpr (K3) {
+                rd3 = sbd[(size_t)tid * nsb + (kb0 >> 3)];
+            } else if constexpr (Q5) {
                 rsd[0] = ld16(side + (size_t)tid * nb + kb0);
                 rsd[1] = ld16(side + (size_t)tid * nb + kb0 + 2);
             } else {
@@ -503,7 +528,7 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             rda = *reinterpret_cast<const v4i*>(A.ain.ds + (size_t)s_row[c] * nb + kb0);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int kb0w) {
         char* st = smem + buf * STAGE;
         int8_t* sw = reinterpret_cast<int8_t*>(st);
         int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
@@ -515,6 +540,33 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             const int r = ch / WCPR, p = ch - r * WCPR;
             // one block (16 bytes) -> 32 int8: elements 0..15, then 16..31
             v4i lo, hi;
+            if constexpr (K3) {
+                int sc0, sc1;
+                k3_scales(rs3[j], (kb0w + p) & 7, sc0, sc1);
+                // byte tables (4 - v) * scale, v = 0..7: low word v < 4, high word v >= 4
+                auto table = [](int sc, uint32_t& tlo, uint32_t& thi) {
+                    tlo = (uint32_t)(4 * sc & 0xFF) | (uint32_t)(3 * sc & 0xFF) << 8 |
+                          (uint32_t)(2 * sc & 0xFF) << 16 | (uint32_t)(sc & 0xFF) << 24;
+                    thi = (uint32_t)(-sc & 0xFF) << 8 | (uint32_t)(-2 * sc & 0xFF) << 16 |
+                          (uint32_t)(-3 * sc & 0xFF) << 24;
+                };
+                uint32_t t0lo, t0hi, t1lo, t1hi;
+                table(sc0, t0lo, t0hi);
+                table(sc1, t1lo, t1hi);
+                const uint32_t H = (uint32_t)rw[j].z;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t v0 = (((uint32_t)rw[j].x >> (2 * m)) & 0x03030303u) |
+                                        (((H >> m) & 0x01010101u) << 2);
+                    const uint32_t v1 = (((uint32_t)rw[j].y >> (2 * m)) & 0x03030303u) |
+                                        (((H >> (4 + m)) & 0x01010101u) << 2);
+                    lo[m] = (int)__builtin_amdgcn_perm(t0hi, t0lo, v0);
+                    hi[m] = (int)__builtin_amdgcn_perm(t1hi, t1lo, v1);
+                }
+                *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32) = lo;
+                *reinterpret_cast<v4i*>(sw + r * MS_ROWB + p * 32 + 16) = hi;
+                continue;
+            }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t x = (uint32_t)rw[j][d];
@@ -536,7 +588,11 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             *reinterpret_cast<v4i*>(sx + c * MS_ROWB + p * 16) = rx[j];
         }
         if (tid < MF_NT) {
-            if constexpr (Q5) {
+            if constexpr (K3) {
+                const uint16_t nd = (uint16_t)(rd3 ^ 0x8000u);     // -d
+#pragma unroll
+                for (int q = 0; q < MF_KB; ++q) sdw[q * MS_SWR + tid] = nd;
+            } else if constexpr (Q5) {
                 // side words: {d | m << 16, qh} per block; blocks 0,1 in rsd[0], 2,3 in rsd[1]
                 const uint32_t dm[4] = {(uint32_t)rsd[0].x, (uint32_t)rsd[0].z, (uint32_t)rsd[1].x,
                                         (uint32_t)rsd[1].z};
@@ -593,7 +649,7 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
             d1 = scale_op(sdw[kb * MS_SWR + o_w1]);
             dc = scale_op(sda[kb * MS_SAR + o_a]);
         };
-        mf_stage<SWIGLU, TAP>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+        mf_stage<SWIGLU, TAP, h4, K3>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
         if constexpr (Q5) {
             // min terms of the stage's four blocks (k slots 0..3; lanes 32..63 zero)
             const uint16_t* smw = sda + MF_KB * MS_SAR;
@@ -614,13 +670,13 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
         }
     };
     gload(0);
-    lstore(0);
+    lstore(0, 0);
     __syncthreads();
 #pragma unroll 1
     for (int s = 0; s + 1 < stages; ++s) {
         gload((s + 1) * MF_KB);
         compute(s & 1, s);
-        lstore((s + 1) & 1);
+        lstore((s + 1) & 1, (s + 1) * MF_KB);
         __syncthreads();
     }
     compute((stages - 1) & 1, stages - 1);
@@ -830,6 +886,11 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
             launch_k(k_mfma_q4<SWIGLU, true, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
         else
             launch_k(k_mfma_q4<SWIGLU, false, MOE_FMT_Q5_1>, grid, block, 0, st, ev, a);
+    } else if (fmt == MOE_FMT_Q3_K) {
+        if (tap)
+            launch_k(k_mfma_q4<SWIGLU, true, MOE_FMT_Q3_K>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_q4<SWIGLU, false, MOE_FMT_Q3_K>, grid, block, 0, st, ev, a);
     } else if (fmt == MOE_FMT_Q4_K) {
         if (tap)
             launch_k(k_mfma_kq<SWIGLU, true, MOE_FMT_Q4_K>, grid, block, 0, st, ev, a);

@@ -42,10 +42,6 @@ inline int unit_side_bytes(int fmt) {
     return fmt == MOE_FMT_Q5_1 ? 8 : fmt == MOE_FMT_Q4_K ? 16 : fmt == MOE_FMT_Q5_K ? 48 : 2;
 }
 inline int unit_bytes(int fmt) { return unit_code_bytes(fmt) + unit_side_bytes(fmt); }
-// matrix-core prefill kernels exist for these formats (the rest run every T on
-// the matrix-vector kernels)
-inline bool has_mfma_path(int fmt) { return fmt != MOE_FMT_Q3_K; }
-
 struct MatLayout {                  // one packed block matrix
     int rows = 0, nblk = 0, fmt = MOE_FMT_Q8_0;
     size_t codes_off = 0;           // from the matrix base

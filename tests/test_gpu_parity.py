@@ -116,6 +116,9 @@ def test_variants(kw):
     (dict(expert_fmt=synth.Q4_K, tokens=100), None, 4),
     (dict(expert_fmt=synth.Q5_K, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300),
      [0, 5, 150, 299], 2),
+    (dict(expert_fmt=synth.Q3_K, tokens=100), None, 4),
+    (dict(expert_fmt=synth.Q3_K, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300,
+          bias=True), [0, 5, 150, 299], 2),
 ])
 def test_gemm_variants(kw, sample, taps):
     w = _variant(**kw)
@@ -204,8 +207,7 @@ def test_q5_k_experts(kw):
 
 # Q3_K experts (super-blocks of 256, 3-bit codes, signed 6-bit scales per 16
 # elements): decode, a verify window, the 9..32-token path, more than 32 tokens
-# (which stay on the matrix-vector kernels), latent with group labels and the
-# latent-prefill D/U on the matrix cores, decode-sized rows
+# (the matrix cores), latent with group labels, latent prefill, decode-sized rows
 @pytest.mark.parametrize("kw", [
     dict(expert_fmt=synth.Q3_K, tokens=1),
     dict(expert_fmt=synth.Q3_K, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
