@@ -46,7 +46,7 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
                              const SelectArgs* route, const RouteOut* rout) {
     int lpr, cpl;
     if (!pick_gu(nchunks(m.kin, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
-    if (64 % (gu_waves(lpr) * (64 / lpr))) return hipErrorInvalidConfiguration;
+    if (64 % (gu_waves(lpr, m.fmt) * (64 / lpr))) return hipErrorInvalidConfiguration;
     GUArgs a;
     a.experts = experts;
     a.eb = m.expert_bytes;

@@ -704,7 +704,7 @@ template <int FMT, bool TAP>
 hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a,
                               hipStream_t st, const KEvents& ev) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
-        constexpr int NW = L == 8 ? 8 : 4;
+        constexpr int NW = gu_waves_c(L, FMT);
         launch_k(k_gate_up_mv<FMT, L, C, NW, TAP>, grid, dim3(NW * 64), lds, st, ev, a);
     }));
     return hipGetLastError();
