@@ -34,9 +34,16 @@ static bool pick_gu(int nch, int& lpr, int& cpl) {
 // staged tokens per chunk: about 32 KB of codes
 static int pick_tch(int K) { return std::max(4, std::min(16, 32768 / K)); }
 
+// rows kernels: K-quant chunks carry their super-block's side data in
+// registers, so they take the gate/up choice of at most four chunks per lane
+// (eight 8-lane chunks spill at F = 1536)
+static bool pick_rows(int nch, int fmt, int& lpr, int& cpl) {
+    return kquant(fmt) ? pick_gu(nch, lpr, cpl) : pick(nch, lpr, cpl);
+}
+
 bool mv_config_ok(int K, int fmt, bool gate_up) {
     int l, c;
-    if (gate_up ? !pick_gu(nchunks(K, fmt), l, c) : !pick(nchunks(K, fmt), l, c)) return false;
+    if (gate_up ? !pick_gu(nchunks(K, fmt), l, c) : !pick_rows(nchunks(K, fmt), fmt, l, c)) return false;
     return c >= 1 && c <= 8 && (l == 8 || l == 16 || l == 32 || l == 64);
 }
 
@@ -100,7 +107,7 @@ static int pick_rt(int rows, int groups, int rpp) {
 
 static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st) {
     int lpr, cpl;
-    if (!pick(nchunks(a.K, fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
+    if (!pick_rows(nchunks(a.K, fmt), fmt, lpr, cpl)) return hipErrorInvalidConfiguration;
     const int rpp = ROWS_NW * (64 / lpr);
     if (a.rows % rpp) return hipErrorInvalidConfiguration;
     a.rt = pick_rt(a.rows, groups, rpp);
