@@ -71,14 +71,13 @@ constexpr int DT_KMAX = 32;  // largest top_k
 constexpr int ROWS_NW = 4;   // waves per rows workgroup (8 spill the K-quant down rows)
 
 // waves per gate/up workgroup: 8 lanes per row cover the 64-row slab in one
-// pass with 8 waves; wider rows use 4 waves and several passes, except the
-// K-quants on 32-lane rows, whose unpack needs the extra waves to hide its
-// latency (measured: Q5_K decode gate/up 44.6 -> 31.2 us, Q4_K 28.3 -> 26.1)
+// pass with 8 waves; Q8_0's wider rows use 4 waves and several passes.  The
+// other formats use 8 waves on every row width: their unpack needs the extra
+// waves to hide its latency, and the 8-wave bound (two waves per SIMD) leaves
+// 256 registers where the 4-wave bound (three) leaves 170 and Q4_0 / Q5_1
+// spilled (measured: Q5_K decode gate/up 44.6 -> 30.9 us, Q4_K 28.3 -> 26.0)
 __host__ __device__ constexpr int gu_waves_c(int lpr, int fmt) {
-    return lpr == 8 || (lpr == 32 && (fmt == MOE_FMT_Q4_K || fmt == MOE_FMT_Q5_K ||
-                                      fmt == MOE_FMT_Q3_K))
-               ? 8
-               : 4;
+    return lpr == 8 || fmt != MOE_FMT_Q8_0 ? 8 : 4;
 }
 inline int gu_waves(int lpr, int fmt) { return gu_waves_c(lpr, fmt); }
 

@@ -34,11 +34,12 @@ static bool pick_gu(int nch, int& lpr, int& cpl) {
 // staged tokens per chunk: about 32 KB of codes
 static int pick_tch(int K) { return std::max(4, std::min(16, 32768 / K)); }
 
-// rows kernels: K-quant chunks carry their super-block's side data in
-// registers, so they take the gate/up choice of at most four chunks per lane
-// (eight 8-lane chunks spill at F = 1536)
+// rows kernels: chunks of the nibble formats carry more registers (unpacked
+// codes, side data), so they take the gate/up choice of at most four chunks
+// per lane (seven or eight spilled: K-quant down at F = 1536, Q4_0 D at
+// H = 4096)
 static bool pick_rows(int nch, int fmt, int& lpr, int& cpl) {
-    return kquant(fmt) ? pick_gu(nch, lpr, cpl) : pick(nch, lpr, cpl);
+    return fmt != MOE_FMT_Q8_0 ? pick_gu(nch, lpr, cpl) : pick(nch, lpr, cpl);
 }
 
 bool mv_config_ok(int K, int fmt, bool gate_up) {
