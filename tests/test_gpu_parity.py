@@ -225,7 +225,8 @@ def test_q3_k_experts(kw):
     _report("q3_k " + str(kw), w.tokens, rep)
 
 
-# path boundaries (decode router up to 8 tokens, matrix-vector experts up to 32)
+# path boundaries (single-token routing at T = 1, the per-token selection kernel with
+# bucketing up to 32 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
 @pytest.mark.parametrize("kw", [
     dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=8),
