@@ -16,7 +16,7 @@ import gpu_helpers as gh  # noqa: E402
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 64), ("decode", 1), ("latent_q8", 6),
-                                    ("latent_q4", 32)])
+                                    ("latent_q4", 32), ("latent_q3_k", 1), ("decode_q5_k", 1)])
 def test_graph_replay_matches_eager(name, T):
     import torch
     w = synth.Workload(**{**synth.WORKLOADS[name].__dict__, "tokens": T})
