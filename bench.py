@@ -337,7 +337,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the layer is a "
-                          "single-GPU kernel path; see DESIGN.md for how it would shard",
+                          "single-GPU kernel path (several GPUs would split the experts and "
+                          "exchange Q8_1 rows and weighted outputs by all-to-all; not built)",
                           "n_gpus": a.gpus}))
         sys.exit(2)
 
