@@ -34,17 +34,16 @@ static bool pick_gu(int nch, int& lpr, int& cpl) {
 // staged tokens per chunk: about 32 KB of codes
 static int pick_tch(int K) { return std::max(4, std::min(16, 32768 / K)); }
 
-// rows kernels: chunks of the nibble formats carry more registers (unpacked
-// codes, side data), so they take the gate/up choice of at most four chunks
-// per lane (seven or eight spilled: K-quant down at F = 1536, Q4_0 D at
-// H = 4096)
-static bool pick_rows(int nch, int fmt, int& lpr, int& cpl) {
-    return fmt != MOE_FMT_Q8_0 ? pick_gu(nch, lpr, cpl) : pick(nch, lpr, cpl);
-}
+// rows kernels: the gate/up choice of at most four chunks per lane.  More
+// chunks per lane spilled for the nibble formats (unpacked codes and side data
+// in registers: K-quant down at F = 1536, Q4_0 D at H = 4096), and for Q8_0
+// fewer rows per workgroup give the short latent D more workgroups (1280 rows
+// at K = 4096: 320 workgroups instead of 160; latent_q8 T = 1 41.1 -> 40.6 us)
+static bool pick_rows(int nch, int& lpr, int& cpl) { return pick_gu(nch, lpr, cpl); }
 
 bool mv_config_ok(int K, int fmt, bool gate_up) {
     int l, c;
-    if (gate_up ? !pick_gu(nchunks(K, fmt), l, c) : !pick_rows(nchunks(K, fmt), fmt, l, c)) return false;
+    if (gate_up ? !pick_gu(nchunks(K, fmt), l, c) : !pick_rows(nchunks(K, fmt), l, c)) return false;
     return c >= 1 && c <= 8 && (l == 8 || l == 16 || l == 32 || l == 64);
 }
 
@@ -108,7 +107,7 @@ static int pick_rt(int rows, int groups, int rpp) {
 
 static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st) {
     int lpr, cpl;
-    if (!pick_rows(nchunks(a.K, fmt), fmt, lpr, cpl)) return hipErrorInvalidConfiguration;
+    if (!pick_rows(nchunks(a.K, fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     const int rpp = ROWS_NW * (64 / lpr);
     if (a.rows % rpp) return hipErrorInvalidConfiguration;
     a.rt = pick_rt(a.rows, groups, rpp);
