@@ -219,6 +219,59 @@ moe_status moe_layer_forward_events(const moe_layer* layer, const float* x, int 
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events);
 
+/*
+ * Experts held apart (edge0-strata README, "Changes from upstream Strata": the
+ * CPU/PCIe share of expert work for experts that are not resident on the GPU;
+ * Strata PR 24 commit log: an expert cache whose slot holds one whole expert
+ * blob).
+ *
+ * moe_layer_forward_table is moe_layer_forward with expert e's pack (the
+ * moe_pack_bytes(EXPERTS) / n_experts bytes of one expert, in the packed
+ * layout) at expert_table[e] instead of at expert_packs + e * that size.
+ * expert_table is a device array of n_experts addresses; each address is
+ * 256-byte aligned and lies either in device memory of the layer's device or
+ * in pinned host memory mapped for it (hipHostMalloc), which the kernels then
+ * read over the bus.  The library cannot check the entries: a wrong address
+ * faults the device.  The kernels and out are those of moe_layer_forward, so
+ * the same packs give bitwise the same out.
+ */
+moe_status moe_layer_forward_table(const moe_layer* layer, const float* x, int T,
+                                   const float* router_w, const float* router_b,
+                                   const int32_t* group_of_expert,
+                                   const void* const* expert_table, const void* D,
+                                   const void* U, int k, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * A cache of resident experts that keeps such a table.  host_packs: all
+ * n_experts packs (moe_pack_host's output) in pinned host memory mapped for
+ * the device, 256-byte aligned; slots: device memory for n_slots packs
+ * (0 <= n_slots <= n_experts), 256-byte aligned; table: device memory for
+ * n_experts addresses, passed to moe_layer_forward_table.  The caller owns all
+ * three and keeps them alive while the cache lives.  create points every entry
+ * at the host copy (on `stream`); it refuses host memory that is not pinned and
+ * mapped, and slots or a table that is not device memory of the layer's device
+ * or is smaller than stated.
+ *
+ * admit makes the n experts listed (host int32 ids; at most n_slots distinct)
+ * resident: each one not yet in a slot takes an empty slot, else the slot whose
+ * expert was named least recently by an earlier admit (ties: lower slot); the
+ * evicted expert's entry points at the host copy again before its slot is
+ * overwritten.  The copies and entry updates are queued on `stream` in that
+ * order, so calls that read the table on the same stream afterwards see whole
+ * packs; calls on other streams must be ordered by the caller.  *n_copied
+ * (may be NULL) receives the number of packs copied.  slot gives an expert's
+ * slot, or -1 when it is read from host memory.
+ */
+typedef struct moe_expert_cache moe_expert_cache;
+moe_status moe_expert_cache_create(const moe_layer* layer, const void* host_packs, void* slots,
+                                   int n_slots, void* table, void* stream,
+                                   moe_expert_cache** out);
+moe_status moe_expert_cache_admit(moe_expert_cache* cache, const int32_t* experts, int n,
+                                  void* stream, int* n_copied);
+moe_status moe_expert_cache_slot(const moe_expert_cache* cache, int expert, int* slot);
+void moe_expert_cache_destroy(moe_expert_cache* cache);
+
 /* Text of the last error on this thread ("" when none). */
 const char* moe_last_error(void);
 

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["mv_q8_0.hip", "mv_q4_0.hip", "mv_q5_1.hip", "mv_q4_k.hip", "mv_q5_k.hip", "mv_q3_k.hip",
            "mfma.hip",
-           "route.hip", "matvec.hip", "capi.cpp"]
+           "route.hip", "matvec.hip", "table.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 

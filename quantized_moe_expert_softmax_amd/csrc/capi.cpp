@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -335,7 +336,7 @@ extern "C" moe_status moe_workspace_bytes(const moe_layer* L, int T, size_t* byt
 static const int DOWN_TOK_MAX_T = 8;
 
 static moe_status forward_impl(const moe_layer* L, const float* x, int T, const float* router_w,
-                               const float* router_b, const int32_t* groups, const void* experts,
+                               const float* router_b, const int32_t* groups, ExpertSrc ex,
                                const void* Dp, const void* Up, int k, float* out, void* workspace,
                                size_t ws_bytes, void* stream, const moe_taps* taps,
                                void* const* events) {
@@ -345,8 +346,8 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     if (T < 0 || T > m.max_tokens)
         return fail(MOE_EINVAL, "T %d out of range 0..max_tokens=%d", T, m.max_tokens);
     if (T == 0) return MOE_OK;
-    if (!x || !router_w || !experts || !out || !workspace)
-        return fail(MOE_EINVAL, "NULL x, router_w, expert_packs, out or workspace");
+    if (!x || !router_w || !(ex.base || ex.table) || !out || !workspace)
+        return fail(MOE_EINVAL, "NULL x, router_w, expert packs (or table), out or workspace");
     if (m.L && (!Dp || !Up)) return fail(MOE_EINVAL, "latent layer needs D and U");
     if (m.G && !groups) return fail(MOE_EINVAL, "n_groups %d needs group_of_expert", m.G);
     const WsLayout w = ws_layout(m, T);
@@ -357,7 +358,6 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    const uint8_t* ex = (const uint8_t*)experts;
     const int A = T * m.k;
     ActPtr xq{(int8_t*)(ws + w.xq_q), (uint32_t*)(ws + w.xq_ds), (int32_t*)(ws + w.xq_sq)};
     ActPtr zq{(int8_t*)(ws + w.zq_q), (uint32_t*)(ws + w.zq_ds), (int32_t*)(ws + w.zq_sq)};
@@ -499,8 +499,8 @@ extern "C" moe_status moe_layer_forward(const moe_layer* L, const float* x, int 
                                         const int32_t* groups, const void* experts, const void* D,
                                         const void* U, int k, float* out, void* workspace,
                                         size_t workspace_bytes, void* stream) {
-    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
-                        workspace_bytes, stream, nullptr, nullptr);
+    return forward_impl(L, x, T, router_w, router_b, groups, ExpertSrc((const uint8_t*)experts), D,
+                        U, k, out, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 extern "C" moe_status moe_layer_forward_events(const moe_layer* L, const float* x, int T,
@@ -509,8 +509,8 @@ extern "C" moe_status moe_layer_forward_events(const moe_layer* L, const float* 
                                                const void* D, const void* U, int k, float* out,
                                                void* workspace, size_t workspace_bytes,
                                                void* stream, void* const* events) {
-    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
-                        workspace_bytes, stream, nullptr, events);
+    return forward_impl(L, x, T, router_w, router_b, groups, ExpertSrc((const uint8_t*)experts), D,
+                        U, k, out, workspace, workspace_bytes, stream, nullptr, events);
 }
 
 extern "C" moe_status moe_layer_forward_taps(const moe_layer* L, const float* x, int T,
@@ -520,6 +520,192 @@ extern "C" moe_status moe_layer_forward_taps(const moe_layer* L, const float* x,
                                              void* workspace, size_t workspace_bytes, void* stream,
                                              const moe_taps* taps) {
     if (!taps) return fail(MOE_EINVAL, "taps is NULL");
-    return forward_impl(L, x, T, router_w, router_b, groups, experts, D, U, k, out, workspace,
-                        workspace_bytes, stream, taps, nullptr);
+    return forward_impl(L, x, T, router_w, router_b, groups, ExpertSrc((const uint8_t*)experts), D,
+                        U, k, out, workspace, workspace_bytes, stream, taps, nullptr);
 }
+
+// ---------------------------------------------------------------------------
+// Experts held apart from one array: a table of pack addresses, and a cache of
+// resident packs in device slots in front of a pinned host copy (edge0-strata
+// README, "Changes from upstream Strata": the CPU/PCIe share of expert work for
+// experts not resident on the GPU; Strata PR 24 commit log: an expert cache
+// whose slot holds one whole expert blob, and a cache once filled from a
+// staging ring that had already been overwritten).  Here a non-resident
+// expert is read by the same kernels straight from mapped host memory, over
+// the bus; a resident one from its slot.
+
+extern "C" moe_status moe_layer_forward_table(const moe_layer* L, const float* x, int T,
+                                              const float* router_w, const float* router_b,
+                                              const int32_t* groups,
+                                              const void* const* expert_table, const void* D,
+                                              const void* U, int k, float* out, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    if (!expert_table) return fail(MOE_EINVAL, "expert_table is NULL");
+    return forward_impl(L, x, T, router_w, router_b, groups,
+                        ExpertSrc(nullptr, (const uint8_t* const*)expert_table), D, U, k, out,
+                        workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+struct moe_expert_cache {
+    int device = 0, E = 0, n_slots = 0;
+    size_t eb = 0;
+    const uint8_t* host = nullptr;      // the caller's pinned copy (copy source)
+    const uint8_t* host_dev = nullptr;  // the same memory as the device addresses it
+    uint8_t* slots = nullptr;
+    const uint8_t** table = nullptr;
+    std::vector<int> slot_of;           // expert -> slot, -1 = read from host memory
+    std::vector<int> expert_in;         // slot -> expert, -1 = empty
+    std::vector<uint64_t> last_use;     // slot -> admit call that last named its expert
+    uint64_t tick = 0;
+};
+
+// the allocation that holds [p, p + bytes) must be device memory of `device`
+static moe_status check_device_range(const void* p, size_t bytes, int device, const char* what) {
+    hipPointerAttribute_t a;
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess || a.type != hipMemoryTypeDevice || a.device != device) {
+        (void)hipGetLastError();
+        return fail(MOE_EINVAL, "%s is not device memory of device %d", what, device);
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_EINVAL, "%s: no allocation range (%s)", what, hipGetErrorString(e));
+    }
+    if ((const char*)p + bytes > (const char*)base + size)
+        return fail(MOE_EINVAL, "%s: %zu bytes needed past the pointer, the allocation holds %zu", what,
+                    bytes, (size_t)((const char*)base + size - (const char*)p));
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_cache_create(const moe_layer* L, const void* host_packs,
+                                              void* slots, int n_slots, void* table, void* stream,
+                                              moe_expert_cache** out) {
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    const Dims& m = L->dims;
+    if (!host_packs || !table || (n_slots > 0 && !slots))
+        return fail(MOE_EINVAL, "NULL host_packs, table or slots");
+    if (n_slots < 0 || n_slots > m.E)
+        return fail(MOE_EINVAL, "n_slots %d out of range 0..n_experts=%d", n_slots, m.E);
+    if ((uintptr_t)host_packs % 256 || (uintptr_t)slots % 256 || (uintptr_t)table % 8)
+        return fail(MOE_EINVAL, "host_packs and slots must be 256-byte aligned, table 8-byte");
+    DeviceGuard g(L->device);
+    if (!g.ok) return fail(MOE_EDEVICE, "cannot select device %d", L->device);
+    // the host copy must be pinned and mapped: the kernels read it over the bus
+    hipPointerAttribute_t a;
+    hipError_t e = hipPointerGetAttributes(&a, host_packs);
+    if (e != hipSuccess || a.type != hipMemoryTypeHost || !a.devicePointer) {
+        (void)hipGetLastError();
+        return fail(MOE_EINVAL, "host_packs is not pinned host memory mapped for the device");
+    }
+    moe_status s = check_device_range(table, sizeof(void*) * m.E, L->device, "table");
+    if (s != MOE_OK) return s;
+    if (n_slots > 0) {
+        s = check_device_range(slots, m.expert_bytes * n_slots, L->device, "slots");
+        if (s != MOE_OK) return s;
+    }
+    moe_expert_cache* c = new (std::nothrow) moe_expert_cache;
+    if (!c) return fail(MOE_ENOMEM, "cache object");
+    c->device = L->device;
+    c->E = m.E;
+    c->n_slots = n_slots;
+    c->eb = m.expert_bytes;
+    c->host = (const uint8_t*)host_packs;
+    c->host_dev = (const uint8_t*)a.devicePointer;
+    c->slots = (uint8_t*)slots;
+    c->table = (const uint8_t**)table;
+    c->slot_of.assign(m.E, -1);
+    c->expert_in.assign(n_slots, -1);
+    c->last_use.assign(n_slots, 0);
+    e = launch_table_fill(c->table, m.E, c->host_dev, c->eb, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "table fill");
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_cache_admit(moe_expert_cache* c, const int32_t* experts, int n,
+                                             void* stream, int* n_copied) {
+    if (n_copied) *n_copied = 0;
+    if (!c) return fail(MOE_EINVAL, "cache is NULL");
+    if (n < 0 || (n > 0 && !experts)) return fail(MOE_EINVAL, "bad expert list (n = %d)", n);
+    std::vector<char> named(c->E, 0);
+    int distinct = 0;
+    for (int i = 0; i < n; ++i) {
+        const int e = experts[i];
+        if (e < 0 || e >= c->E) return fail(MOE_EINVAL, "expert %d out of range 0..%d", e, c->E - 1);
+        if (!named[e]) ++distinct;
+        named[e] = 1;
+    }
+    if (distinct > c->n_slots)
+        return fail(MOE_EINVAL, "%d distinct experts named, the cache has %d slots", distinct,
+                    c->n_slots);
+    DeviceGuard g(c->device);
+    if (!g.ok) return fail(MOE_EDEVICE, "cannot select device %d", c->device);
+    hipStream_t st = (hipStream_t)stream;
+    const uint64_t now = ++c->tick;
+    // experts already resident are kept: they are not eviction candidates now
+    for (int e = 0; e < c->E; ++e)
+        if (named[e] && c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = now;
+    TableUpdate u;
+    u.n = 0;
+    hipError_t err;
+    auto flush = [&]() -> hipError_t {
+        hipError_t r = launch_table_set(c->table, u, st);
+        u.n = 0;
+        return r;
+    };
+    auto set = [&](int e, const uint8_t* p) -> hipError_t {
+        u.expert[u.n] = e;
+        u.addr[u.n] = p;
+        return ++u.n == TABLE_UPDATE_MAX ? flush() : hipSuccess;
+    };
+    int copied = 0;
+    for (int e = 0; e < c->E; ++e) {
+        if (!named[e] || c->slot_of[e] >= 0) continue;
+        // an empty slot first, else the least recently named one not named now
+        int v = -1;
+        for (int s = 0; s < c->n_slots && v < 0; ++s)
+            if (c->expert_in[s] < 0) v = s;
+        if (v < 0)
+            for (int s = 0; s < c->n_slots; ++s)
+                if (c->last_use[s] < now && (v < 0 || c->last_use[s] < c->last_use[v])) v = s;
+        if (v < 0) return fail(MOE_EINVAL, "no slot to evict");   // unreachable: distinct <= n_slots
+        const int old = c->expert_in[v];
+        uint8_t* slot = c->slots + (size_t)v * c->eb;
+        if (old >= 0) {
+            // the evicted expert is read from host memory again; its entry
+            // changes before the slot is overwritten (stream order)
+            c->slot_of[old] = -1;
+            if ((err = set(old, c->host_dev + (size_t)old * c->eb)) != hipSuccess ||
+                (err = flush()) != hipSuccess)
+                return hip_fail(err, "table update");
+        }
+        err = hipMemcpyAsync(slot, c->host + (size_t)e * c->eb, c->eb, hipMemcpyHostToDevice, st);
+        if (err != hipSuccess) return hip_fail(err, "expert copy into a slot");
+        c->expert_in[v] = e;
+        c->slot_of[e] = v;
+        c->last_use[v] = now;
+        if ((err = set(e, slot)) != hipSuccess) return hip_fail(err, "table update");
+        ++copied;
+    }
+    if ((err = flush()) != hipSuccess) return hip_fail(err, "table update");
+    if (n_copied) *n_copied = copied;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_cache_slot(const moe_expert_cache* c, int expert, int* slot) {
+    if (!c || !slot) return fail(MOE_EINVAL, "NULL argument");
+    if (expert < 0 || expert >= c->E)
+        return fail(MOE_EINVAL, "expert %d out of range 0..%d", expert, c->E - 1);
+    *slot = c->slot_of[expert];
+    return MOE_OK;
+}
+
+extern "C" void moe_expert_cache_destroy(moe_expert_cache* c) { delete c; }

@@ -19,6 +19,23 @@ struct Buckets {
     const float* wts;         // [T][k]
 };
 
+// Where the expert FFN kernels find expert e's pack: at base + e * stride (one
+// array of E packs), or at table[e] when a table is given.  A table entry may
+// point into device memory or into pinned host memory that is mapped into the
+// device's address space (the kernels then read that expert over the bus).
+struct ExpertSrc {
+    const uint8_t* base = nullptr;
+    const uint8_t* const* table = nullptr;
+    ExpertSrc() = default;
+    ExpertSrc(const uint8_t* b, const uint8_t* const* t = nullptr) : base(b), table(t) {}
+};
+
+__device__ __forceinline__ const uint8_t* expert_pack(const uint8_t* base,
+                                                      const uint8_t* const* table, int e,
+                                                      size_t stride) {
+    return table ? table[e] : base + (size_t)e * stride;
+}
+
 // Events recorded by one kernel's own dispatch (its start and end), for timing
 // that kernel alone; both null = a plain launch.
 struct KEvents {
@@ -94,13 +111,13 @@ bool mv_config_ok(int K, int fmt, bool gate_up);
 // route != null (T == 1 only): every workgroup selects the token's experts
 // from the router logits in its prologue and workgroup 0 publishes ids,
 // weights and buckets to *rout; b is then not read.
-hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
                              const SelectArgs* route = nullptr, const RouteOut* rout = nullptr);
-hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st);
-hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st);
 hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
                            const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
@@ -109,13 +126,25 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 // Many-token path: grouped int8 matrix-core GEMM over the token tiles that the
 // bucketing kernel numbered in tile_map (tiles of GEMM_TILE_M assignments).
 bool mfma_config_ok(int rows, int K);
-hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+hipError_t launch_gate_up_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                                const Buckets& b, const int32_t* tile_map, ActPtr hq,
                                const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{});
-hipError_t launch_down_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                             const Buckets& b, const int32_t* tile_map, float* y, const Taps& taps,
                             hipStream_t st);
 hipError_t launch_dense_mfma(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
                              int32_t* isum_tap, int tap_tokens, hipStream_t st);
+
+// Expert-address table: fill entries 0..E-1 with base + e * stride, or set
+// u.n (at most TABLE_UPDATE_MAX) entries, stream-ordered.
+constexpr int TABLE_UPDATE_MAX = 64;
+struct TableUpdate {
+    int n;
+    int expert[TABLE_UPDATE_MAX];
+    const uint8_t* addr[TABLE_UPDATE_MAX];
+};
+hipError_t launch_table_fill(const uint8_t** table, int E, const uint8_t* base, size_t stride,
+                             hipStream_t st);
+hipError_t launch_table_set(const uint8_t** table, const TableUpdate& u, hipStream_t st);
 
 }  // namespace moe

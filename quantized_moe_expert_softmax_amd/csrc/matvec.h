@@ -18,6 +18,7 @@ __host__ __device__ constexpr size_t stage_bytes(int n, int K) {
 // to it.  Output: hq rows a = t*k + j, block fb.
 struct GUArgs {
     const uint8_t* experts;
+    const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
     size_t eb, gu_scales_off;
     int K, F, k, T, tch;
     ActPtr ain;           // quantised expert input rows [T][K], or
@@ -39,6 +40,7 @@ struct GUArgs {
 struct RowsArgs {
     const uint8_t* base;
     size_t group_stride, codes_off, scales_off;
+    const uint8_t* const* etab;   // expert mode: pack addresses, or null (base + e * stride)
     int rows, K, T, rt, tch;
     Buckets b;                 // b.ctrl == nullptr: dense mode
     ActPtr ain;                // quantised act rows, or
@@ -56,6 +58,7 @@ struct RowsArgs {
 // rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).
 struct DownTokArgs {
     const uint8_t* experts;
+    const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
     size_t eb, dn_off, dn_scales_off;
     int F, Kout, k;
     ActPtr hq;

@@ -47,7 +47,7 @@ bool mv_config_ok(int K, int fmt, bool gate_up) {
     return c >= 1 && c <= 8 && (l == 8 || l == 16 || l == 32 || l == 64);
 }
 
-hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev,
                              const SelectArgs* route, const RouteOut* rout) {
@@ -55,7 +55,8 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, const uint8_t* experts, ActPt
     if (!pick_gu(nchunks(m.kin, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (64 % (gu_waves(lpr, m.fmt) * (64 / lpr))) return hipErrorInvalidConfiguration;
     GUArgs a;
-    a.experts = experts;
+    a.experts = experts.base;
+    a.etab = experts.table;
     a.eb = m.expert_bytes;
     a.gu_scales_off = m.gu.scales_off;
     a.K = m.kin; a.F = m.F; a.k = m.k; a.T = T;
@@ -134,10 +135,11 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
 
-hipError_t launch_down_slot_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st) {
     RowsArgs a{};
-    a.base = experts;
+    a.base = experts.base;
+    a.etab = experts.table;
     a.group_stride = m.expert_bytes;
     a.codes_off = m.dn_off + m.dn.codes_off;
     a.scales_off = m.dn_off + m.dn.scales_off;
@@ -162,14 +164,15 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
     return rows_dispatch(W.fmt, 1, a, st);
 }
 
-hipError_t launch_down_tok_mv(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
     if (kquant(m.fmt)) return hipErrorInvalidConfiguration;   // (down per slot instead)
     int lpr, cpl;
     if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;
     DownTokArgs a;
-    a.experts = experts;
+    a.experts = experts.base;
+    a.etab = experts.table;
     a.eb = m.expert_bytes;
     a.dn_off = m.dn_off + m.dn.codes_off;
     a.dn_scales_off = m.dn.scales_off - m.dn.codes_off;

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         lst = A.b.lists + (size_t)e * A.T;
     }
     const size_t rowb = Fmt<FMT>::row_bytes(nb);
-    const uint8_t* ebase = A.experts + (size_t)e * A.eb;
+    const uint8_t* ebase = expert_pack(A.experts, A.etab, e, A.eb);
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
     using SM = typename Fmt<FMT>::SideMem;
     const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * (nb / Fmt<FMT>::SBLK);
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     if (A.b.ctrl) {
         if (g >= (int)A.b.ctrl[CW_N_ACTIVE]) return;
         const int e = A.b.active[g];
-        mat = A.base + (size_t)e * A.group_stride;
+        mat = expert_pack(A.base, A.etab, e, A.group_stride);
         cnt = A.b.counts[e];
         lst = A.b.lists + (size_t)e * A.T;
     } else {
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     for (int j = wave; j < A.k; j += DT_NW) {
         const int a = t * A.k + j;
         const int e = A.b.ids[a];
-        const uint8_t* mat = A.experts + (size_t)e * A.eb + A.dn_off;
+        const uint8_t* mat = expert_pack(A.experts, A.etab, e, A.eb) + A.dn_off;
         const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
         using SM = typename F::SideMem;
         const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);

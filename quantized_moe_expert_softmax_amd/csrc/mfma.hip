@@ -45,6 +45,7 @@ constexpr int MF_THREADS = 256;
 struct MfArgs {
     const uint8_t* base;          // expert packs (group mode) or the dense matrix
     size_t group_stride;          // bytes per expert
+    const uint8_t* const* etab;   // group mode: expert pack addresses, or null (base + e * stride)
     size_t codes_off, scales_off; // of the matrix inside an expert pack
     int rows, K, T;               // weight rows, elements per row, tokens
     int max_tiles;                // token tiles covered by the grid
@@ -99,7 +100,7 @@ __device__ __forceinline__ bool mf_tile(const MfArgs& A, MfTile& t, int* s_row, 
         t.m0 = (tm >> 16) * MF_MT;
         cnt = A.b.counts[e];
         lst = A.b.lists + (size_t)e * A.T;
-        t.mat = A.base + (size_t)e * A.group_stride;
+        t.mat = expert_pack(A.base, A.etab, e, A.group_stride);
     } else {
         t.m0 = g * MF_MT;
         if (t.m0 >= A.T) return false;
@@ -912,11 +913,12 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
     return hipGetLastError();
 }
 
-hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr ain,
+hipError_t launch_gate_up_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                                const Buckets& b, const int32_t* tile_map, ActPtr hq,
                                const Taps& taps, hipStream_t st, const KEvents& ev) {
     MfArgs a{};
-    a.base = experts;
+    a.base = experts.base;
+    a.etab = experts.table;
     a.group_stride = m.expert_bytes;
     a.codes_off = m.gu.codes_off;
     a.scales_off = m.gu.scales_off;
@@ -930,11 +932,12 @@ hipError_t launch_gate_up_mfma(const Dims& m, int T, const uint8_t* experts, Act
     return mfma_fmt<true>(m.fmt, a, taps.h || taps.isum_gu, st, ev);
 }
 
-hipError_t launch_down_mfma(const Dims& m, int T, const uint8_t* experts, ActPtr hq,
+hipError_t launch_down_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                             const Buckets& b, const int32_t* tile_map, float* y, const Taps& taps,
                             hipStream_t st) {
     MfArgs a{};
-    a.base = experts;
+    a.base = experts.base;
+    a.etab = experts.table;
     a.group_stride = m.expert_bytes;
     a.codes_off = m.dn_off + m.dn.codes_off;
     a.scales_off = m.dn_off + m.dn.scales_off;

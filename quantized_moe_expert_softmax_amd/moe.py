@@ -24,7 +24,8 @@ MOE_PACK_EXPERTS, MOE_PACK_D, MOE_PACK_U = 0, 1, 2
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_bytes",
            "moe_pack_host", "moe_unpack_host", "moe_pack", "moe_workspace_bytes",
            "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
-           "moe_last_error", "moe_version"]
+           "moe_layer_forward_table", "moe_expert_cache_create", "moe_expert_cache_admit",
+           "moe_expert_cache_slot", "moe_expert_cache_destroy", "moe_last_error", "moe_version"]
 (MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END,
  MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND) = range(8)
 MOE_EV_COUNT = 8
@@ -75,9 +76,16 @@ def lib():
         L.moe_layer_forward.argtypes = fwd
         L.moe_layer_forward_taps.argtypes = fwd + [P(moe_taps)]
         L.moe_layer_forward_events.argtypes = fwd + [P(vp)]
+        L.moe_layer_forward_table.argtypes = fwd
+        L.moe_expert_cache_create.argtypes = [vp, vp, vp, i32, vp, vp, P(vp)]
+        L.moe_expert_cache_admit.argtypes = [vp, P(ctypes.c_int32), i32, vp, P(i32)]
+        L.moe_expert_cache_slot.argtypes = [vp, i32, P(i32)]
+        L.moe_expert_cache_destroy.argtypes = [vp]
+        L.moe_expert_cache_destroy.restype = None
         for f in ("moe_desc_check", "moe_layer_create", "moe_pack_bytes", "moe_pack_host",
                   "moe_unpack_host", "moe_pack", "moe_workspace_bytes", "moe_layer_forward",
-                  "moe_layer_forward_taps", "moe_layer_forward_events"):
+                  "moe_layer_forward_taps", "moe_layer_forward_events", "moe_layer_forward_table",
+                  "moe_expert_cache_create", "moe_expert_cache_admit", "moe_expert_cache_slot"):
             getattr(L, f).restype = ctypes.c_int
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -172,6 +180,39 @@ def moe_layer_forward_events(handle, x, T, router_w, router_b, groups, experts, 
                                           k, out, workspace, workspace_bytes, stream, arr))
 
 
+def moe_layer_forward_table(handle, x, T, router_w, router_b, groups, expert_table, D, U, k, out,
+                            workspace, workspace_bytes, stream=0) -> None:
+    """expert_table: device address of n_experts pack addresses."""
+    _check(lib().moe_layer_forward_table(handle, x, T, router_w, router_b, groups, expert_table, D,
+                                         U, k, out, workspace, workspace_bytes, stream))
+
+
+def moe_expert_cache_create(handle, host_packs, slots, n_slots, table, stream=0) -> int:
+    c = ctypes.c_void_p()
+    _check(lib().moe_expert_cache_create(handle, host_packs, slots, n_slots, table, stream,
+                                         ctypes.byref(c)))
+    return c.value
+
+
+def moe_expert_cache_admit(cache, experts, stream=0) -> int:
+    """experts: iterable of expert ids; returns the number of packs copied."""
+    ids = list(experts)
+    arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+    n = ctypes.c_int()
+    _check(lib().moe_expert_cache_admit(cache, arr, len(ids), stream, ctypes.byref(n)))
+    return n.value
+
+
+def moe_expert_cache_slot(cache, expert: int) -> int:
+    s = ctypes.c_int()
+    _check(lib().moe_expert_cache_slot(cache, expert, ctypes.byref(s)))
+    return s.value
+
+
+def moe_expert_cache_destroy(cache) -> None:
+    lib().moe_expert_cache_destroy(cache)
+
+
 # ---------------------------------------------------------------------------
 class MoeLayer:
     """A layer with its packed weights resident in device memory (torch tensors).
@@ -237,6 +278,60 @@ class MoeLayer:
     def close(self):
         if self.handle:
             moe_layer_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class ExpertCache:
+    """A layer's experts in pinned host memory with ``n_slots`` of them resident
+    in device slots (the library's expert cache); ``forward`` runs the layer
+    through the cache's address table.  ``layer`` supplies the router, D/U and
+    the layer handle."""
+
+    def __init__(self, layer: "MoeLayer", canonical_experts, n_slots: int):
+        torch = layer.torch
+        self.layer = layer
+        self.torch = torch
+        n = moe_pack_bytes(layer.desc, MOE_PACK_EXPERTS)
+        assert canonical_experts.nbytes == n, (canonical_experts.nbytes, n)
+        self.eb = n // layer.desc.n_experts
+        self.host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        moe_pack_host(layer.desc, MOE_PACK_EXPERTS, canonical_experts.ctypes.data,
+                      self.host.data_ptr())
+        self.slots = torch.empty(max(n_slots, 1) * self.eb, dtype=torch.uint8, device=layer.dev)
+        self.table = torch.zeros(layer.desc.n_experts, dtype=torch.int64, device=layer.dev)
+        st = torch.cuda.current_stream(layer.dev).cuda_stream
+        self.handle = moe_expert_cache_create(layer.handle, self.host.data_ptr(),
+                                              self.slots.data_ptr(), n_slots,
+                                              self.table.data_ptr(), st)
+
+    def admit(self, experts, stream=None) -> int:
+        st = (self.torch.cuda.current_stream(self.layer.dev) if stream is None else stream).cuda_stream
+        return moe_expert_cache_admit(self.handle, [int(e) for e in experts], st)
+
+    def slot(self, expert: int) -> int:
+        return moe_expert_cache_slot(self.handle, expert)
+
+    def forward(self, x, out=None, stream=None):
+        L, torch = self.layer, self.torch
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, L.desc.hidden), dtype=torch.float32, device=L.dev)
+        ws = L.workspace(T)
+        st = (torch.cuda.current_stream(L.dev) if stream is None else stream).cuda_stream
+        moe_layer_forward_table(L.handle, x.data_ptr(), T, L.router_w.data_ptr(), L._ptr(L.router_b),
+                                L._ptr(L.groups), self.table.data_ptr(), L._ptr(L.D), L._ptr(L.U),
+                                L.k, out.data_ptr(), ws.data_ptr(), ws.numel(), st)
+        return out
+
+    def close(self):
+        if self.handle:
+            moe_expert_cache_destroy(self.handle)
             self.handle = 0
 
     def __del__(self):
