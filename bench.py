@@ -62,6 +62,9 @@ def parse():
                    help="also print per-stage milliseconds to stderr")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--expert-cache", action="store_true",
+                   help="also time the expert-table path: every expert read from pinned host "
+                        "memory over the bus, then with the routed experts admitted to slots")
     p.add_argument("--calibration-copy", action="store_true",
                    help="end with three copy kernels of 256 MiB each way (x * 1.0 in fp32), "
                         "the calibration of the HBM byte counters")
@@ -253,6 +256,65 @@ def measure(w, T, steps, warmup, pool, copies, profile=False, graphs=True):
                 mean_active=mean_active, copies=copies, pool=pool, t_gen=t_gen, inp=inp, xs=xs)
 
 
+def measure_cache(w, T, steps, warmup, pool=8):
+    """The table form of the layer call through the expert cache: steps with
+    every expert read from the pinned host copy (over the bus), then with the
+    experts that the token pool routes to admitted into device slots; and the
+    host-to-device rate of admitting packs."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_expert_softmax_amd import moe, synth
+
+    dev = torch.device("cuda", 0)
+    inp = synth.gen_layer(w)
+    layer = moe.MoeLayer(moe.desc_of(w, max_tokens=T), inp, device=0)
+    xd = [torch.from_numpy(synth.gen_x(w, batch=b)).to(dev) for b in range(pool)]
+    routed = set()
+    for x in xd:
+        ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
+        taps = moe.moe_taps()
+        taps.ids = ids.data_ptr()
+        layer.forward(x, taps=taps)
+        torch.cuda.synchronize()
+        routed |= set(int(e) for e in ids.cpu().numpy().ravel())
+    S = len(routed)
+    cache = moe.ExpertCache(layer, inp["experts"], n_slots=S)
+    out = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
+
+    def run(n):
+        for i in range(n):
+            cache.forward(xd[i % pool], out=out)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / steps
+    t0 = time.perf_counter()
+    copied = cache.admit(sorted(routed))
+    torch.cuda.synchronize()
+    admit_ms = (time.perf_counter() - t0) * 1e3
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    slot_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the bytes one step reads from the experts: k packs per token (distinct per
+    # batch at T = 1)
+    step_bytes = min(T * w.top_k, w.n_experts) * w.expert_bytes
+    cache.close()
+    layer.close()
+    return {"workload": w.name, "tokens_per_step": T, "slots": S,
+            "host": {"tokens_per_s": T / (host_ms * 1e-3), "ms_per_step": host_ms,
+                     "expert_read_gbs": step_bytes / (host_ms * 1e-3) / 1e9},
+            "slots_resident": {"tokens_per_s": T / (slot_ms * 1e-3), "ms_per_step": slot_ms},
+            "admit": {"packs": copied, "ms": admit_ms,
+                      "h2d_gbs": copied * w.expert_bytes / (admit_ms * 1e-3) / 1e9}}
+
+
 def hbm_probe(reps=10):
     """The same box's plain streaming rates, as context for the kernel figures:
     torch's copy (read + write) and sum (read) over 1 GiB of fp32, timed with
@@ -406,6 +468,10 @@ def main():
                    "stage_ms": mp["st_ms"], "layer_ms_pct": mp["layer_ms_pct"],
                    "graph": graph_rate(wp.tokens, mp["graph_ms_step"])}
 
+    cache = None
+    if a.expert_cache:
+        cache = measure_cache(w, T, min(a.steps, 40), 3)
+
     probe = hbm_probe()
 
     if a.calibration_copy:
@@ -448,6 +514,7 @@ def main():
         "graph": graph_rate(T, m["graph_ms_step"]),
         "hbm_probe": probe,
         "prefill": prefill,
+        "expert_cache": cache,
         "cpu_baseline": cpu,
         "input_generation_s": m["t_gen"],
     }
