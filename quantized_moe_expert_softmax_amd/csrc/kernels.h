@@ -30,10 +30,15 @@ struct ExpertSrc {
     ExpertSrc(const uint8_t* b, const uint8_t* const* t = nullptr) : base(b), table(t) {}
 };
 
+// The entries are read as global-address-space pointers: a pointer loaded from
+// memory is otherwise generic, and the loads through it (and through the other
+// arm of the select) would become flat loads.
 __device__ __forceinline__ const uint8_t* expert_pack(const uint8_t* base,
                                                       const uint8_t* const* table, int e,
                                                       size_t stride) {
-    return table ? table[e] : base + (size_t)e * stride;
+    typedef __attribute__((address_space(1))) const uint8_t* gptr;
+    if (!table) return base + (size_t)e * stride;
+    return (const uint8_t*)static_cast<const gptr*>(static_cast<const void*>(table))[e];
 }
 
 // Events recorded by one kernel's own dispatch (its start and end), for timing

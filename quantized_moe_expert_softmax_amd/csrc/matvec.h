@@ -58,13 +58,13 @@ struct RowsArgs {
 // rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).
 struct DownTokArgs {
     const uint8_t* experts;
-    const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
     size_t eb, dn_off, dn_scales_off;
     int F, Kout, k;
     ActPtr hq;
     Buckets b;
     float* out;              // [T][Kout]: the layer output, or y_lat for a latent layer
     Taps taps;
+    const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
 };
 
 constexpr int DT_RT = 16;    // output rows per workgroup
@@ -85,7 +85,8 @@ __host__ __device__ constexpr int gu_waves_c(int lpr, int fmt) {
 inline int gu_waves(int lpr, int fmt) { return gu_waves_c(lpr, fmt); }
 
 // Launch one instance by (lanes per row, 16-byte chunks per lane); defined and
-// instantiated for every format in mv_*.hip (down_tok_fmt for Q8_0, Q4_0, Q5_1).
+// instantiated for every format in mv_*.hip (down_tok_fmt for Q8_0, Q4_0, Q5_1,
+// down_tok_kq_fmt for the K-quants).
 template <int FMT, bool TAP>
 hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a, hipStream_t st,
                        const KEvents& ev);
@@ -93,5 +94,7 @@ template <int FMT, bool TAP>
 hipError_t rows_fmt(int lpr, int cpl, dim3 grid, size_t lds, const RowsArgs& a, hipStream_t st);
 template <int FMT, bool TAP>
 hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream_t st);
+template <int FMT, bool TAP>
+hipError_t down_tok_kq_fmt(int lpr, int cpl, int T, size_t lds, const DownTokArgs& a, hipStream_t st);
 
 }  // namespace moe

@@ -166,9 +166,12 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
-    if (kquant(m.fmt)) return hipErrorInvalidConfiguration;   // (down per slot instead)
+    const bool kq = kquant(m.fmt);
     int lpr, cpl;
-    if (!pick(nchunks(m.F, m.fmt), lpr, cpl)) return hipErrorInvalidConfiguration;
+    // (the K-quant dots keep a whole super-block's side data per chunk: at most
+    // four chunks per lane, as in the rows kernel)
+    if (!(kq ? pick_rows(nchunks(m.F, m.fmt), lpr, cpl) : pick(nchunks(m.F, m.fmt), lpr, cpl)))
+        return hipErrorInvalidConfiguration;
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;
     DownTokArgs a;
     a.experts = experts.base;
@@ -179,6 +182,17 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     a.F = m.F; a.Kout = m.kout; a.k = m.k;
     a.hq = hq; a.b = b; a.out = out; a.taps = taps;
     bool tap = taps.isum_dn || taps.y;
+    if (kq) {
+        const size_t lds = (size_t)m.k * (m.F + 8 * (m.F / QK));
+        if (m.fmt == MOE_FMT_Q4_K)
+            return tap ? down_tok_kq_fmt<MOE_FMT_Q4_K, true>(lpr, cpl, T, lds, a, st)
+                       : down_tok_kq_fmt<MOE_FMT_Q4_K, false>(lpr, cpl, T, lds, a, st);
+        if (m.fmt == MOE_FMT_Q5_K)
+            return tap ? down_tok_kq_fmt<MOE_FMT_Q5_K, true>(lpr, cpl, T, lds, a, st)
+                       : down_tok_kq_fmt<MOE_FMT_Q5_K, false>(lpr, cpl, T, lds, a, st);
+        return tap ? down_tok_kq_fmt<MOE_FMT_Q3_K, true>(lpr, cpl, T, lds, a, st)
+                   : down_tok_kq_fmt<MOE_FMT_Q3_K, false>(lpr, cpl, T, lds, a, st);
+    }
     if (m.fmt == MOE_FMT_Q4_0)
         return tap ? down_tok_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, T, a, st)
                    : down_tok_fmt<MOE_FMT_Q4_0, false>(lpr, cpl, T, a, st);

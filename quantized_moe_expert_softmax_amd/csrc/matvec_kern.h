@@ -564,7 +564,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
 }
 
 
-template <int FMT, int LPR, int CPL, bool TAP>
+// (TABLE: the packs are found through A.etab; a separate instance, so that the
+// array form's rank loop carries no table load and no wait for it)
+template <int FMT, int LPR, int CPL, bool TAP, bool TABLE = false>
 __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     using F = Fmt<FMT>;
     constexpr int RPW = 64 / LPR;
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     for (int j = wave; j < A.k; j += DT_NW) {
         const int a = t * A.k + j;
         const int e = A.b.ids[a];
-        const uint8_t* mat = expert_pack(A.experts, A.etab, e, A.eb) + A.dn_off;
+        const uint8_t* mat = (TABLE ? expert_pack(nullptr, A.etab, e, 0) : A.experts + (size_t)e * A.eb) + A.dn_off;
         const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
         using SM = typename F::SideMem;
         const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);
@@ -636,6 +638,89 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
             }
             const float y = group_sum_fast<LPR>(acc);
             if (sl == 0) s_y[j][r] = y;
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) {
+                wq[jj] = wn[jj];
+                wsc[jj] = wsn[jj];
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < DT_RT) {
+        const int r = threadIdx.x;
+        float o = 0.0f;
+        for (int j = 0; j < A.k; ++j) {
+            const int a = t * A.k + j;
+            o = fmaf(A.b.wts[a], s_y[j][r], o);
+            if constexpr (TAP) {
+                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * DT_RT + r] = s_y[j][r];
+            }
+        }
+        A.out[(size_t)t * A.Kout + rt * DT_RT + r] = o;
+    }
+}
+
+// The same for K-quant experts (Q4_K, Q5_K, Q3_K), whose chunk dots read the
+// activations from LDS: the token's k rows of Q8_1(h) are staged once for every
+// wave (after each wave has requested its first pass of weights), then wave j
+// runs rank j's rows through the row-tile dot and the tile is combined in rank
+// order as above.  Dynamic LDS: k * (F + 8 * F/32) bytes.
+template <int FMT, int LPR, int CPL, bool TAP>
+__global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
+    using F = Fmt<FMT>;
+    using SM = typename F::SideMem;
+    constexpr int RPW = 64 / LPR;
+    constexpr int PASSES = DT_RT / RPW;
+    extern __shared__ __align__(16) char smem[];
+    __shared__ float s_y[DT_KMAX][DT_RT];
+    __shared__ int32_t s_src[DT_KMAX];
+    const int NRT = A.Kout / DT_RT;
+    const int t = blockIdx.x / NRT, rt = blockIdx.x - t * NRT;
+    const int K = A.F, nb = K / QK, NCH = nb * F::CPB;
+    const size_t rowb = F::row_bytes(nb);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sl = lane % LPR, rg = lane / LPR;
+    const bool tap = TAP && t < A.taps.tap_tokens && A.taps.isum_dn;
+    int8_t* s_q = reinterpret_cast<int8_t*>(smem);
+    float* s_d = reinterpret_cast<float*>(smem + (size_t)A.k * K);
+    int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)A.k * K + (size_t)A.k * nb * 4);
+
+    const uint8_t* codes = nullptr;
+    const SM* scl = nullptr;
+    auto locate = [&](int j) {
+        const int e = A.b.ids[t * A.k + j];
+        const uint8_t* mat = expert_pack(A.experts, A.etab, e, A.eb) + A.dn_off;
+        codes = mat + (size_t)rt * DT_RT * rowb;
+        scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);
+    };
+    v4i wq[CPL], wn[CPL];
+    typename F::Side wsc[CPL], wsn[CPL];
+    if (wave < A.k) {
+        locate(wave);
+        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
+    }
+    if ((int)threadIdx.x < A.k) s_src[threadIdx.x] = t * A.k + threadIdx.x;
+    __syncthreads();
+    stage_q<F::Q5>(A.hq, K, s_src, A.k, s_q, s_d, s_sq);
+    __syncthreads();
+    for (int j = wave; j < A.k; j += DT_NW) {
+        const int a = t * A.k + j;
+        if (j != wave) {
+            locate(j);
+            load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
+        }
+        auto emit = [&](int, int r, float v) { s_y[j][r] = v; };
+        auto emit_isum = [&](int, int r, int blk, int v) {
+            A.taps.isum_dn[((size_t)a * A.Kout + rt * DT_RT + r) * nb + blk] = v;
+        };
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int r = p * RPW + rg;
+            if (p + 1 < PASSES)
+                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
+                                        NCH, wn, wsn);
+            pass_dot<FMT, LPR, CPL, TAP>(wq, wsc, r, sl, NCH, nb, 1, K, s_q + (size_t)j * K, s_d + j * nb,
+                                         s_sq + j * nb, emit, emit_isum, tap);
 #pragma unroll
             for (int jj = 0; jj < CPL; ++jj) {
                 wq[jj] = wn[jj];
@@ -724,7 +809,23 @@ hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         if constexpr (DT_RT % (64 / L) == 0) {
             dim3 grid(T * (a.Kout / DT_RT));
-            hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), 0, st, a);
+            if (a.etab)
+                hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, false, true>), grid, dim3(DT_NW * 64), 0, st, a);
+            else
+                hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), 0, st, a);
+        } else {
+            return hipErrorInvalidConfiguration;
+        }
+    }));
+    return hipGetLastError();
+}
+
+template <int FMT, bool TAP>
+hipError_t down_tok_kq_fmt(int lpr, int cpl, int T, size_t lds, const DownTokArgs& a, hipStream_t st) {
+    MOE_LPR_CPL_SWITCH(lpr, cpl, ({
+        if constexpr (DT_RT % (64 / L) == 0) {
+            dim3 grid(T * (a.Kout / DT_RT));
+            hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), lds, st, a);
         } else {
             return hipErrorInvalidConfiguration;
         }
@@ -743,5 +844,8 @@ hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream
 #define MOE_MV_DOWN_TOK_INSTANCES(F)                                                           \
     template hipError_t down_tok_fmt<F, false>(int, int, int, const DownTokArgs&, hipStream_t); \
     template hipError_t down_tok_fmt<F, true>(int, int, int, const DownTokArgs&, hipStream_t);
+#define MOE_MV_DOWN_TOK_KQ_INSTANCES(F)                                                              \
+    template hipError_t down_tok_kq_fmt<F, false>(int, int, int, size_t, const DownTokArgs&, hipStream_t); \
+    template hipError_t down_tok_kq_fmt<F, true>(int, int, int, size_t, const DownTokArgs&, hipStream_t);
 
 }  // namespace moe

@@ -3,4 +3,5 @@
 
 namespace moe {
 MOE_MV_INSTANCES(MOE_FMT_Q3_K)
+MOE_MV_DOWN_TOK_KQ_INSTANCES(MOE_FMT_Q3_K)
 }  // namespace moe
