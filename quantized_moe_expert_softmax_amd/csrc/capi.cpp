@@ -332,13 +332,14 @@ extern "C" moe_status moe_workspace_bytes(const moe_layer* L, int T, size_t* byt
 // forward
 
 // Decode sizes run the down projection per token with the combine fused;
-// larger T runs it per expert bucket and combines afterwards.  K-quant experts
-// take the fused form for one token (its kernel stages the token's rows in LDS;
-// measured on one box, Q3_K experts: 42.1 -> 37.9 us per layer); from two tokens
-// on they keep the per-bucket kernel, which reads each expert once for all its
-// tokens (at T = 6 the two forms measured within 3% of each other).
+// larger T runs it per expert bucket and combines afterwards.  For K-quant
+// experts (whose per-token kernel stages the token's rows in LDS) the fused
+// form stops at 6 tokens; measured on one box against the per-bucket kernel,
+// us per layer: Q3_K T = 1 42.1 -> 37.9, T = 2 63.7 -> 57.9; Q4_K T = 2
+// 67.5 -> 61.4, T = 4 108.0 -> 104.5; T = 6 Q5_K 174.2 -> 171.4, latent Q3_K
+// 132.7 -> 127.6, Q3_K 132.5 -> 133.6; Q4_K T = 8 171.9 -> 177.3.
 static const int DOWN_TOK_MAX_T = 8;
-static const int DOWN_TOK_KQ_MAX_T = 1;
+static const int DOWN_TOK_KQ_MAX_T = 6;
 
 static moe_status forward_impl(const moe_layer* L, const float* x, int T, const float* router_w,
                                const float* router_b, const int32_t* groups, ExpertSrc ex,
