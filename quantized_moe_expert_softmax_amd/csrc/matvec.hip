@@ -188,9 +188,19 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     const bool kq = kquant(m.fmt);
     int lpr, cpl;
     // (the K-quant dots keep a whole super-block's side data per chunk: at most
-    // four chunks per lane, as in the rows kernel)
-    if (!(kq ? pick_rows(nchunks(m.F, m.fmt), lpr, cpl) : pick(nchunks(m.F, m.fmt), lpr, cpl)))
+    // four chunks per lane, as in the rows kernel).  The others take three
+    // chunks per lane where that splits the row exactly (measured, us per
+    // layer: Q8_0 at F = 1536, 32 x 3 against 16 x 6: T = 6 163.0 -> 159.4, T = 1
+    // unchanged; Q5_1, 16 x 3 against 8 x 6: T = 1 32.9 -> 32.2)
+    const int nch = nchunks(m.F, m.fmt);
+    if (kq) {
+        if (!pick_rows(nch, lpr, cpl)) return hipErrorInvalidConfiguration;
+    } else if (nch % 3 == 0 && (nch / 3 == 8 || nch / 3 == 16 || nch / 3 == 32 || nch / 3 == 64)) {
+        lpr = nch / 3;
+        cpl = 3;
+    } else if (!pick(nch, lpr, cpl)) {
         return hipErrorInvalidConfiguration;
+    }
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;
     DownTokArgs a;
     a.experts = experts.base;
