@@ -219,3 +219,20 @@ def test_forward_argument_checks_without_gpu(L):
     assert st == moe.MOE_EINVAL
     ws = ctypes.c_size_t()
     assert L.moe_workspace_bytes(None, 1, ctypes.byref(ws)) == moe.MOE_EINVAL
+
+
+def test_expert_cache_refusals_without_a_device(L):
+    """The expert-cache calls refuse NULL handles by name before touching a device."""
+    n = ctypes.c_int(-5)
+    arr = (ctypes.c_int32 * 1)(0)
+    assert L.moe_expert_cache_admit(None, arr, 1, None, ctypes.byref(n)) == moe.MOE_EINVAL
+    assert "cache is NULL" in moe.moe_last_error()
+    assert n.value == 0
+    s = ctypes.c_int()
+    assert L.moe_expert_cache_slot(None, 0, ctypes.byref(s)) == moe.MOE_EINVAL
+    out = ctypes.c_void_p(1)
+    assert L.moe_expert_cache_create(None, None, None, 0, None, None, ctypes.byref(out)) == moe.MOE_EINVAL
+    assert out.value is None
+    L.moe_expert_cache_destroy(None)
+    assert L.moe_layer_forward_table(None, None, 1, None, None, None, None, None, None, 1, None,
+                                     None, 0, None) == moe.MOE_EINVAL
