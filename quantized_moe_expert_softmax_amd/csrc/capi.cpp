@@ -454,8 +454,12 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
            "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs
+    // one token of a latent layer (array form, non-K-quant experts): the down
+    // kernel also writes Q8_1(y_lat), in 32-row tiles, for the U projection
+    const bool ylq_in_down = m.L && lat_fused_q && down_tok && !kquant(m.fmt) && !ex.table;
     if (down_tok) {
-        CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st), "down+combine");
+        CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st, ylq_in_down ? ylq : none),
+           "down+combine");
     } else {
         if (gemm)
             CK(launch_down_mfma(m, T, ex, hq, b, tile_map, y, tp, st), "down");
@@ -469,6 +473,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (gemm) {
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
+        } else if (ylq_in_down) {
+            CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, nullptr, none, out, tp.isum_u,
+                               tp.tap_tokens, st), "U");
         } else if (lat_fused_q) {
             // the U kernel quantises y_lat on the way in
             CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, none, ylat, taps ? ylq : none, out,

@@ -55,7 +55,9 @@ struct RowsArgs {
 // ---------------------------------------------------------------------------
 // Down projection with the combine fused, one workgroup per (token, 16-row
 // tile); wave j computes rank j's expert rows, then the tile is combined in
-// rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).
+// rank order: out[t][r] = sum_j w[t][j] * (W_down[e_j][r] . hq[t*k+j]).  With
+// outq, 32-row tiles, and each tile's Q8_1 block of out is written as well (the
+// latent layer's y_lat, quantised once for the U projection).
 struct DownTokArgs {
     const uint8_t* experts;
     size_t eb, dn_off, dn_scales_off;
@@ -65,6 +67,7 @@ struct DownTokArgs {
     float* out;              // [T][Kout]: the layer output, or y_lat for a latent layer
     Taps taps;
     const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
+    ActPtr outq;                  // q != null: also Q8_1 of out (32-row tiles; not with etab)
 };
 
 constexpr int DT_RT = 16;    // output rows per workgroup

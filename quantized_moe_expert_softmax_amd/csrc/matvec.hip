@@ -184,8 +184,10 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 }
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
-                              const Buckets& b, float* out, const Taps& taps, hipStream_t st) {
+                              const Buckets& b, float* out, const Taps& taps, hipStream_t st,
+                              ActPtr outq) {
     const bool kq = kquant(m.fmt);
+    if (outq.q && (kq || experts.table || m.kout % QK)) return hipErrorInvalidValue;
     int lpr, cpl;
     // (the K-quant dots keep a whole super-block's side data per chunk: at most
     // four chunks per lane, as in the rows kernel).  The others take three
@@ -210,6 +212,7 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     a.dn_scales_off = m.dn.scales_off - m.dn.codes_off;
     a.F = m.F; a.Kout = m.kout; a.k = m.k;
     a.hq = hq; a.b = b; a.out = out; a.taps = taps;
+    a.outq = outq;
     bool tap = taps.isum_dn || taps.y;
     if (kq) {
         const size_t lds = (size_t)m.k * (m.F + 8 * (m.F / QK));

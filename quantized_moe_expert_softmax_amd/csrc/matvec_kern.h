@@ -565,14 +565,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
 
 
 // (TABLE: the packs are found through A.etab; a separate instance, so that the
-// array form's rank loop carries no table load and no wait for it)
-template <int FMT, int LPR, int CPL, bool TAP, bool TABLE = false>
+// array form's rank loop carries no table load and no wait for it.  RT: output
+// rows per workgroup; 32-row tiles also write Q8_1 of the combined rows)
+template <int FMT, int LPR, int CPL, bool TAP, bool TABLE = false, int RT = DT_RT>
 __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     using F = Fmt<FMT>;
     constexpr int RPW = 64 / LPR;
     constexpr int NA = F::CPB == 1 ? 2 : 1;     // 16-byte activation pieces per chunk
-    __shared__ float s_y[DT_KMAX][DT_RT];
-    const int NRT = A.Kout / DT_RT;
+    __shared__ float s_y[DT_KMAX][RT];
+    const int NRT = A.Kout / RT;
     const int t = blockIdx.x / NRT, rt = blockIdx.x - t * NRT;
     const int nb = A.F / QK;
     const int NCH = nb * F::CPB;
@@ -580,14 +581,14 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sl = lane % LPR, rg = lane / LPR;
     const bool tap = TAP && t < A.taps.tap_tokens && A.taps.isum_dn;
-    constexpr int PASSES = DT_RT / RPW;
+    constexpr int PASSES = RT / RPW;
     for (int j = wave; j < A.k; j += DT_NW) {
         const int a = t * A.k + j;
         const int e = A.b.ids[a];
         const uint8_t* mat = (TABLE ? expert_pack(nullptr, A.etab, e, 0) : A.experts + (size_t)e * A.eb) + A.dn_off;
-        const uint8_t* codes = mat + (size_t)rt * DT_RT * rowb;
+        const uint8_t* codes = mat + (size_t)rt * RT * rowb;
         using SM = typename F::SideMem;
-        const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);
+        const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * RT * (nb / F::SBLK);
         v4i wq[CPL], wn[CPL];
         typename F::Side wsc[CPL], wsn[CPL];
         load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
                         int full = is;
                         if constexpr (F::CPB == 2) full += __shfl_xor(is, 1, 64);
                         if (valid && (F::CPB == 1 || (sl & 1) == 0))
-                            A.taps.isum_dn[((size_t)a * A.Kout + rt * DT_RT + r) * nb + c / F::CPB] = full;
+                            A.taps.isum_dn[((size_t)a * A.Kout + rt * RT + r) * nb + c / F::CPB] = full;
                     }
                 }
             }
@@ -646,17 +647,28 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < DT_RT) {
+    if (threadIdx.x < RT) {
         const int r = threadIdx.x;
         float o = 0.0f;
         for (int j = 0; j < A.k; ++j) {
             const int a = t * A.k + j;
             o = fmaf(A.b.wts[a], s_y[j][r], o);
             if constexpr (TAP) {
-                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * DT_RT + r] = s_y[j][r];
+                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * RT + r] = s_y[j][r];
             }
         }
-        A.out[(size_t)t * A.Kout + rt * DT_RT + r] = o;
+        A.out[(size_t)t * A.Kout + rt * RT + r] = o;
+        if constexpr (RT == QK) {
+            // a 32-row tile is one Q8_1 block of the combined row: quantised
+            // here once for the kernel that reads it (lanes 0..31 of wave 0)
+            const Q81 q = q8_1_lane(o);
+            const int nbk = A.Kout / QK;
+            A.outq.q[(size_t)t * A.Kout + rt * RT + r] = (int8_t)q.q;
+            if (r == 0) {
+                A.outq.ds[(size_t)t * nbk + rt] = q.ds;
+                A.outq.sq[(size_t)t * nbk + rt] = q.sum;
+            }
+        }
     }
 }
 
@@ -809,7 +821,10 @@ hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         if constexpr (DT_RT % (64 / L) == 0) {
             dim3 grid(T * (a.Kout / DT_RT));
-            if (a.etab)
+            if (a.outq.q)
+                hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP, false, QK>), dim3(T * (a.Kout / QK)),
+                                   dim3(DT_NW * 64), 0, st, a);
+            else if (a.etab)
                 hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, false, true>), grid, dim3(DT_NW * 64), 0, st, a);
             else
                 hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), 0, st, a);
