@@ -120,7 +120,7 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
                              const SelectArgs* route = nullptr, const RouteOut* rout = nullptr);
-// outq.q != null (array form, non-K-quant experts): Q8_1 of out is written too
+// outq.q != null (array form): Q8_1 of out is written too
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st,
                               ActPtr outq = ActPtr{nullptr, nullptr, nullptr});

@@ -187,7 +187,7 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st,
                               ActPtr outq) {
     const bool kq = kquant(m.fmt);
-    if (outq.q && (kq || experts.table || m.kout % QK)) return hipErrorInvalidValue;
+    if (outq.q && (experts.table || m.kout % QK)) return hipErrorInvalidValue;
     int lpr, cpl;
     // (the K-quant dots keep a whole super-block's side data per chunk: at most
     // four chunks per lane, as in the rows kernel).  The others take three

@@ -677,16 +677,16 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
 // wave (after each wave has requested its first pass of weights), then wave j
 // runs rank j's rows through the row-tile dot and the tile is combined in rank
 // order as above.  Dynamic LDS: k * (F + 8 * F/32) bytes.
-template <int FMT, int LPR, int CPL, bool TAP>
+template <int FMT, int LPR, int CPL, bool TAP, int RT = DT_RT>
 __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
     using F = Fmt<FMT>;
     using SM = typename F::SideMem;
     constexpr int RPW = 64 / LPR;
-    constexpr int PASSES = DT_RT / RPW;
+    constexpr int PASSES = RT / RPW;
     extern __shared__ __align__(16) char smem[];
-    __shared__ float s_y[DT_KMAX][DT_RT];
+    __shared__ float s_y[DT_KMAX][RT];
     __shared__ int32_t s_src[DT_KMAX];
-    const int NRT = A.Kout / DT_RT;
+    const int NRT = A.Kout / RT;
     const int t = blockIdx.x / NRT, rt = blockIdx.x - t * NRT;
     const int K = A.F, nb = K / QK, NCH = nb * F::CPB;
     const size_t rowb = F::row_bytes(nb);
@@ -702,8 +702,8 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
     auto locate = [&](int j) {
         const int e = A.b.ids[t * A.k + j];
         const uint8_t* mat = expert_pack(A.experts, A.etab, e, A.eb) + A.dn_off;
-        codes = mat + (size_t)rt * DT_RT * rowb;
-        scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * DT_RT * (nb / F::SBLK);
+        codes = mat + (size_t)rt * RT * rowb;
+        scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * RT * (nb / F::SBLK);
     };
     v4i wq[CPL], wn[CPL];
     typename F::Side wsc[CPL], wsn[CPL];
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
         }
         auto emit = [&](int, int r, float v) { s_y[j][r] = v; };
         auto emit_isum = [&](int, int r, int blk, int v) {
-            A.taps.isum_dn[((size_t)a * A.Kout + rt * DT_RT + r) * nb + blk] = v;
+            A.taps.isum_dn[((size_t)a * A.Kout + rt * RT + r) * nb + blk] = v;
         };
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
@@ -741,17 +741,27 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < DT_RT) {
+    if (threadIdx.x < RT) {
         const int r = threadIdx.x;
         float o = 0.0f;
         for (int j = 0; j < A.k; ++j) {
             const int a = t * A.k + j;
             o = fmaf(A.b.wts[a], s_y[j][r], o);
             if constexpr (TAP) {
-                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * DT_RT + r] = s_y[j][r];
+                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * RT + r] = s_y[j][r];
             }
         }
-        A.out[(size_t)t * A.Kout + rt * DT_RT + r] = o;
+        A.out[(size_t)t * A.Kout + rt * RT + r] = o;
+        if constexpr (RT == QK) {
+            // one Q8_1 block of the combined row per 32-row tile (as above)
+            const Q81 q = q8_1_lane(o);
+            const int nbk = A.Kout / QK;
+            A.outq.q[(size_t)t * A.Kout + rt * RT + r] = (int8_t)q.q;
+            if (r == 0) {
+                A.outq.ds[(size_t)t * nbk + rt] = q.ds;
+                A.outq.sq[(size_t)t * nbk + rt] = q.sum;
+            }
+        }
     }
 }
 
@@ -840,7 +850,11 @@ hipError_t down_tok_kq_fmt(int lpr, int cpl, int T, size_t lds, const DownTokArg
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         if constexpr (DT_RT % (64 / L) == 0) {
             dim3 grid(T * (a.Kout / DT_RT));
-            hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), lds, st, a);
+            if (a.outq.q)
+                hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP, QK>), dim3(T * (a.Kout / QK)),
+                                   dim3(DT_NW * 64), lds, st, a);
+            else
+                hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), lds, st, a);
         } else {
             return hipErrorInvalidConfiguration;
         }
