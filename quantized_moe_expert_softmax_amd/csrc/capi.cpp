@@ -454,9 +454,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
            "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs
-    // one token of a latent layer (array form): the down kernel also writes
-    // Q8_1(y_lat), in 32-row tiles, for the U projection
-    const bool ylq_in_down = m.L && lat_fused_q && down_tok && !ex.table;
+    // a latent layer whose down projection runs per token (array form): that
+    // kernel also writes Q8_1(y_lat), in 32-row tiles, for the U projection
+    const bool ylq_in_down = m.L && down_tok && !ex.table;
     if (down_tok) {
         CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st, ylq_in_down ? ylq : none),
            "down+combine");
