@@ -54,6 +54,12 @@ class Taps(ctypes.Structure):
     _fields_ = _TAP_FIELDS
 
 
+class Given(ctypes.Structure):
+    """Intermediates to evaluate the oracle downstream of (NULL = its own)."""
+    _fields_ = [("ids", ctypes.c_void_p), ("zq", ctypes.c_void_p), ("hq", ctypes.c_void_p),
+                ("ylq", ctypes.c_void_p)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -106,6 +112,10 @@ def lib():
         L.orc_layer_forward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                         vp, ctypes.POINTER(Taps), i32]
         L.orc_layer_forward.restype = ctypes.c_int
+        L.orc_layer_forward_given.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                              i32, vp, ctypes.POINTER(Taps), ctypes.POINTER(Given),
+                                              i32]
+        L.orc_layer_forward_given.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -249,11 +259,14 @@ TAP_NAMES = [n for n, _ in _TAP_FIELDS]
 
 def layer_forward(w, x, router_w, router_b=None, groups=None, experts=None, D=None, U=None,
                   tokens: Optional[Sequence[int]] = None, taps: Sequence[str] = (),
-                  nthreads: int = 1):
+                  nthreads: int = 1, given: Optional[dict] = None):
     """The layer for the given tokens (all when None).
 
     Returns (out [n][H] float32, dict of the requested taps), everything indexed
-    by position in the token list.
+    by position in the token list.  ``given`` may hold any of ids [n][k],
+    zq [n][L/32][36], hq [n][k][F/32][36] and ylq [n][L/32][36]: the oracle
+    then takes these experts / Q8_1 vectors in place of its own selection /
+    quantisation and computes everything else as usual.
     """
     d = desc_of(w)
     T = x.shape[0]
@@ -278,12 +291,22 @@ def layer_forward(w, x, router_w, router_b=None, groups=None, experts=None, D=No
         arrs[name] = np.zeros(shp, dtype=dt)
         setattr(t, name, arrs[name].ctypes.data)
     out = np.empty((n, H), dtype=np.float32)
-    rc = lib().orc_layer_forward(
+    gv = Given()
+    keep = []
+    for name, dt, shp in (("ids", np.int32, (n, k)), ("zq", np.uint8, (n, L // 32, 36)),
+                          ("hq", np.uint8, (n, k, F // 32, 36)), ("ylq", np.uint8, (n, L // 32, 36))):
+        if given is not None and given.get(name) is not None:
+            a = np.ascontiguousarray(given[name], dtype=dt)
+            assert a.size == int(np.prod(shp)), (name, a.shape, shp)
+            keep.append(a)
+            setattr(gv, name, a.ctypes.data)
+    rc = lib().orc_layer_forward_given(
         ctypes.byref(d), _p(np.ascontiguousarray(x, np.float32)),
         _p(np.ascontiguousarray(router_w, np.float32)),
         _p(None if router_b is None else np.ascontiguousarray(router_b, np.float32)),
         _p(None if groups is None else np.ascontiguousarray(groups, np.int32)),
-        _p(experts), _p(D), _p(U), _p(lst), n, _p(out), ctypes.byref(t), int(nthreads))
+        _p(experts), _p(D), _p(U), _p(lst), n, _p(out), ctypes.byref(t), ctypes.byref(gv),
+        int(nthreads))
     if rc != 0:
         raise ValueError("oracle refused the layer arguments")
     return out, arrs

@@ -80,6 +80,22 @@ typedef struct {
     int32_t* isum_u;   /* [n][H][L/32]    latent only */
 } orc_taps;
 
+/*
+ * Optional given intermediates, indexed like the taps (NULL = the oracle's
+ * own).  Where several results are correct (a routing near-tie, a Q8_1 code
+ * that a float computed in another order rounds to the other side of a .5
+ * boundary), a check evaluates the oracle downstream of the result actually
+ * taken: the given experts replace the top-k selection (their weights are
+ * still the softmax over their logits), and a given Q8_1 vector replaces the
+ * quantisation of z, of h or of y_lat.  Everything else is computed as usual.
+ */
+typedef struct {
+    const int32_t* ids;   /* [n][k]                                    */
+    const uint8_t* zq;    /* [n][L/32][36]     expert input (latent)   */
+    const uint8_t* hq;    /* [n][k][F/32][36]  down projection input   */
+    const uint8_t* ylq;   /* [n][L/32][36]     U input (latent)        */
+} orc_given;
+
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16                                                         */
 /* ------------------------------------------------------------------------ */
@@ -406,8 +422,9 @@ void orc_matvec(int fmt, int rows, int nblk, const uint8_t* W, const uint8_t* ac
  * Readings: group score = largest member logit; softmax after top-k equals
  * softmax over all experts renormalised over the chosen ones.
  */
-void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const float* br,
-                     const int32_t* groups, int32_t* ids, float* w, double* logits_out) {
+static void route_token(const orc_desc* d, const float* x, const float* Wr, const float* br,
+                        const int32_t* groups, const int32_t* given_ids, int32_t* ids, float* w,
+                        double* logits_out) {
     int H = d->hidden, E = d->n_experts, k = d->top_k;
     double* l = (double*)malloc(sizeof(double) * E);
     char* allowed = (char*)malloc(E);
@@ -419,35 +436,47 @@ void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const f
         allowed[e] = 1;
         if (logits_out) logits_out[e] = acc;
     }
-    if (d->n_groups > 0 && groups) {
-        int G = d->n_groups;
-        double* gs = (double*)malloc(sizeof(double) * G);
-        char* gsel = (char*)calloc(G, 1);
-        for (int g = 0; g < G; ++g) gs[g] = -INFINITY;
-        for (int e = 0; e < E; ++e)
-            if (l[e] > gs[groups[e]]) gs[groups[e]] = l[e];
-        for (int n = 0; n < d->topk_groups; ++n) {
-            int best = -1;
-            for (int g = 0; g < G; ++g)
-                if (!gsel[g] && (best < 0 || gs[g] > gs[best])) best = g;
-            gsel[best] = 1;
+    if (given_ids) {
+        memcpy(ids, given_ids, sizeof(int32_t) * k);
+    } else {
+        if (d->n_groups > 0 && groups) {
+            int G = d->n_groups;
+            double* gs = (double*)malloc(sizeof(double) * G);
+            char* gsel = (char*)calloc(G, 1);
+            for (int g = 0; g < G; ++g) gs[g] = -INFINITY;
+            for (int e = 0; e < E; ++e)
+                if (l[e] > gs[groups[e]]) gs[groups[e]] = l[e];
+            for (int n = 0; n < d->topk_groups; ++n) {
+                int best = -1;
+                for (int g = 0; g < G; ++g)
+                    if (!gsel[g] && (best < 0 || gs[g] > gs[best])) best = g;
+                gsel[best] = 1;
+            }
+            for (int e = 0; e < E; ++e) allowed[e] = gsel[groups[e]];
+            free(gs);
+            free(gsel);
         }
-        for (int e = 0; e < E; ++e) allowed[e] = gsel[groups[e]];
-        free(gs);
-        free(gsel);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (allowed[e] && (best < 0 || l[e] > l[best])) best = e;
+            ids[j] = best;
+            allowed[best] = 0;
+        }
     }
-    for (int j = 0; j < k; ++j) {
-        int best = -1;
-        for (int e = 0; e < E; ++e)
-            if (allowed[e] && (best < 0 || l[e] > l[best])) best = e;
-        ids[j] = best;
-        allowed[best] = 0;
-    }
+    /* the largest chosen logit: ids[0] for the oracle's own selection */
     double m = l[ids[0]], s = 0.0;
+    for (int j = 1; j < k; ++j)
+        if (l[ids[j]] > m) m = l[ids[j]];
     for (int j = 0; j < k; ++j) s += exp(l[ids[j]] - m);
     for (int j = 0; j < k; ++j) w[j] = (float)(exp(l[ids[j]] - m) / s);
     free(l);
     free(allowed);
+}
+
+void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const float* br,
+                     const int32_t* groups, int32_t* ids, float* w, double* logits_out) {
+    route_token(d, x, Wr, br, groups, NULL, ids, w, logits_out);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -469,8 +498,9 @@ size_t orc_expert_bytes(const orc_desc* d) { return expert_bytes(d); }
  *   (double from the float g and u, rounded to float), hq = Q8_1(h) per 32,
  *   y = W_down hq (float).  SwiGLU with the gate first is the reading taken.
  */
-void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, float* h,
-                    uint8_t* hq, float* y, int32_t* isum_gu, int32_t* isum_dn) {
+static void expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq,
+                       const uint8_t* given_hq, float* h, uint8_t* hq, float* y, int32_t* isum_gu,
+                       int32_t* isum_dn) {
     int fmt = d->expert_fmt, F = d->n_ff;
     int kin = d->latent ? d->latent : d->hidden, kout = kin;
     int nbi = kin / ORC_QK, nbf = F / ORC_QK;
@@ -485,8 +515,16 @@ void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, f
         double gd = (double)g;
         h[r] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
     }
-    orc_quantize_q8_1(h, F, hq);
+    if (given_hq)
+        memcpy(hq, given_hq, (size_t)nbf * ORC_Q8_1_BYTES);
+    else
+        orc_quantize_q8_1(h, F, hq);
     orc_matvec(fmt, kout, nbf, down, hq, y, isum_dn);
+}
+
+void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, float* h,
+                    uint8_t* hq, float* y, int32_t* isum_gu, int32_t* isum_dn) {
+    expert_ffn(d, blob, aq, NULL, h, hq, y, isum_gu, isum_dn);
 }
 
 typedef struct {
@@ -496,6 +534,7 @@ typedef struct {
     const uint8_t *experts, *D, *U;
     float* out;
     const orc_taps* taps;
+    const orc_given* given;
     const int32_t* list;
     int n;
     int next;
@@ -507,14 +546,15 @@ typedef struct {
 static void run_token(job_t* J, int i) {
     const orc_desc* d = J->d;
     const orc_taps* tp = J->taps;
+    const orc_given* gv = J->given;
     int t = J->list ? J->list[i] : i;
     int H = d->hidden, E = d->n_experts, k = d->top_k, F = d->n_ff, L = d->latent;
     int kin = L ? L : H, kout = kin;
     const float* x = J->x + (size_t)t * H;
     int32_t ids[512];
     float w[512];
-    orc_route_token(d, x, J->Wr, J->br, J->groups, ids, w,
-                    tp ? TAP(tp->logits, E) : NULL);
+    route_token(d, x, J->Wr, J->br, J->groups, gv && gv->ids ? gv->ids + (size_t)i * k : NULL,
+                ids, w, tp ? TAP(tp->logits, E) : NULL);
     if (tp && tp->ids) memcpy(tp->ids + (size_t)i * k, ids, sizeof(int32_t) * k);
     if (tp && tp->weights) memcpy(tp->weights + (size_t)i * k, w, sizeof(float) * k);
 
@@ -529,7 +569,10 @@ static void run_token(job_t* J, int i) {
         z = (float*)malloc(sizeof(float) * L);
         zq = (uint8_t*)malloc((size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
         orc_matvec(d->dense_fmt, L, H / ORC_QK, J->D, xq, z, tp ? TAP(tp->isum_d, (size_t)L * (H / ORC_QK)) : NULL);
-        orc_quantize_q8_1(z, L, zq);
+        if (gv && gv->zq)
+            memcpy(zq, gv->zq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        else
+            orc_quantize_q8_1(z, L, zq);
         if (tp && tp->z) memcpy(tp->z + (size_t)i * L, z, sizeof(float) * L);
         if (tp && tp->zq) memcpy(tp->zq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, zq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
         ain = zq;
@@ -541,9 +584,10 @@ static void run_token(job_t* J, int i) {
     float* y = (float*)malloc(sizeof(float) * (size_t)k * kout);
     for (int j = 0; j < k; ++j) {
         size_t a = (size_t)i * k + j;
-        orc_expert_ffn(d, J->experts + (size_t)ids[j] * eb, ain, h, hq, y + (size_t)j * kout,
-                       tp && tp->isum_gu ? tp->isum_gu + a * 2 * F * (kin / ORC_QK) : NULL,
-                       tp && tp->isum_dn ? tp->isum_dn + a * kout * (F / ORC_QK) : NULL);
+        expert_ffn(d, J->experts + (size_t)ids[j] * eb, ain,
+                   gv && gv->hq ? gv->hq + a * (F / ORC_QK) * ORC_Q8_1_BYTES : NULL, h, hq,
+                   y + (size_t)j * kout, tp && tp->isum_gu ? tp->isum_gu + a * 2 * F * (kin / ORC_QK) : NULL,
+                   tp && tp->isum_dn ? tp->isum_dn + a * kout * (F / ORC_QK) : NULL);
         if (tp && tp->h) memcpy(tp->h + a * F, h, sizeof(float) * F);
         if (tp && tp->hq) memcpy(tp->hq + a * (F / ORC_QK) * ORC_Q8_1_BYTES, hq, (size_t)(F / ORC_QK) * ORC_Q8_1_BYTES);
         if (tp && tp->y) memcpy(tp->y + a * kout, y + (size_t)j * kout, sizeof(float) * kout);
@@ -557,7 +601,10 @@ static void run_token(job_t* J, int i) {
     }
     if (L) {                                   /* out = U Q8_1(y_lat) */
         uint8_t* ylq = (uint8_t*)malloc((size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
-        orc_quantize_q8_1(comb, L, ylq);
+        if (gv && gv->ylq)
+            memcpy(ylq, gv->ylq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
+        else
+            orc_quantize_q8_1(comb, L, ylq);
         if (tp && tp->ylat) memcpy(tp->ylat + (size_t)i * L, comb, sizeof(float) * L);
         if (tp && tp->ylq) memcpy(tp->ylq + (size_t)i * (L / ORC_QK) * ORC_Q8_1_BYTES, ylq, (size_t)(L / ORC_QK) * ORC_Q8_1_BYTES);
         orc_matvec(d->dense_fmt, H, L / ORC_QK, J->U, ylq, J->out + (size_t)i * H,
@@ -593,10 +640,11 @@ static void* worker(void* p) {
  * over nthreads threads; each token is computed by one thread alone.
  * Returns 0, or -1 on a bad argument.
  */
-int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const float* br,
-                      const int32_t* groups, const uint8_t* experts, const uint8_t* D,
-                      const uint8_t* U, const int32_t* list, int n, float* out,
-                      const orc_taps* taps, int nthreads) {
+int orc_layer_forward_given(const orc_desc* d, const float* x, const float* Wr,
+                            const float* br, const int32_t* groups, const uint8_t* experts,
+                            const uint8_t* D, const uint8_t* U, const int32_t* list, int n,
+                            float* out, const orc_taps* taps, const orc_given* given,
+                            int nthreads) {
     if (!d || !x || !Wr || !experts || !out || n < 0) return -1;
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
@@ -623,7 +671,17 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     }
     job_t J;
     J.d = d; J.x = x; J.Wr = Wr; J.br = br; J.groups = groups; J.experts = experts;
-    J.D = D; J.U = U; J.out = out; J.taps = taps; J.list = list; J.n = n; J.next = 0;
+    if (given && given->ids) {                 /* given experts: distinct and in range */
+        for (int i = 0; i < n; ++i)
+            for (int j = 0; j < d->top_k; ++j) {
+                int32_t e = given->ids[(size_t)i * d->top_k + j];
+                if (e < 0 || e >= d->n_experts) return -1;
+                for (int m = 0; m < j; ++m)
+                    if (given->ids[(size_t)i * d->top_k + m] == e) return -1;
+            }
+    }
+    J.D = D; J.U = U; J.out = out; J.taps = taps; J.given = given; J.list = list; J.n = n;
+    J.next = 0;
     pthread_mutex_init(&J.mu, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads == 1) {
@@ -636,4 +694,12 @@ int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const 
     }
     pthread_mutex_destroy(&J.mu);
     return 0;
+}
+
+int orc_layer_forward(const orc_desc* d, const float* x, const float* Wr, const float* br,
+                      const int32_t* groups, const uint8_t* experts, const uint8_t* D,
+                      const uint8_t* U, const int32_t* list, int n, float* out,
+                      const orc_taps* taps, int nthreads) {
+    return orc_layer_forward_given(d, x, Wr, br, groups, experts, D, U, list, n, out, taps, NULL,
+                                   nthreads);
 }

@@ -1,8 +1,12 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on the same
-seeded inputs.  Bit-exact: routing ids, Q8_1(x) bytes, every integer block sum
-(gate/up on the GPU's expert input, down on the GPU's own requantised h, D/U),
-and each requantisation of a GPU intermediate.  Within 2e-3 of the output RMS:
-the layer output (fp32 accumulation order and occasional requant flips)."""
+seeded inputs.  Bit-exact: routing ids (near-tie tokens: a valid top-k), Q8_1(x)
+bytes, every integer block sum of the tap tokens (gate/up on the GPU's expert
+input, down on the GPU's own requantised h, D/U), and each requantisation of a
+GPU intermediate.  Q8_1 vectors of z, h and y_lat: equal to the oracle's except
+for flips (a code moved by 1 where the oracle's value lies within 2e-3 of a .5
+boundary), at most 1e-4 of the codes.  Layer output: within 2e-3 of the oracle's
+output RMS on every token without a flip; a token with a flip within 1e-5 of the
+oracle evaluated on the GPU's ids and Q8_1 vectors."""
 import dataclasses
 import sys
 
@@ -15,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 sys.path.insert(0, __file__.rsplit("/", 1)[0])
 import gpu_helpers as gh  # noqa: E402
+import parity_cases  # noqa: E402
 
 _cache = {}
 
@@ -31,6 +36,7 @@ def _layer(name, max_tokens):
 
 
 def _report(name, T, rep):
+    rep = {k: v for k, v in rep.items() if not k.startswith("_")}
     print(f"\n[parity] {name} T={T}: {rep}", flush=True)
 
 
@@ -58,25 +64,29 @@ def test_latent_q8(T):
 @pytest.mark.parametrize("T", [1, 32])
 def test_latent_q4(T):
     layer, inp = _layer("latent_q4", 32)
-    rep = gh.check_case(synth.WORKLOADS["latent_q4"], T, tap_tokens=2, layer=layer, inp=inp,
-                        tokens=None if T == 1 else list(range(12)) + [31])
+    rep = gh.check_case(synth.WORKLOADS["latent_q4"], T, tap_tokens=2, layer=layer, inp=inp)
     _report("latent_q4", T, rep)
 
 
-def test_prefill_sampled():
+def test_prefill_every_token():
+    """The prefill layer at its measured size: ids, weights, Q8_1 vectors and the
+    output of all 2048 tokens against the oracle (run on the host's cores)."""
     layer, inp = _layer("prefill", 2048)
-    rng = np.random.default_rng(5)
-    sample = sorted(set([0, 1, 2, 2047] + list(rng.choice(2048, 20, replace=False))))
-    rep = gh.check_case(synth.WORKLOADS["prefill"], 2048, tokens=sample, tap_tokens=2,
-                        layer=layer, inp=inp)
+    rep = gh.check_case(synth.WORKLOADS["prefill"], 2048, tap_tokens=2, layer=layer, inp=inp)
     _report("prefill", 2048, rep)
 
 
+@pytest.mark.parametrize("name", ["latent_q8", "latent_q4"])
+def test_latent_prefill_every_token(name):
+    """Latent prefill at the size it is measured (2048 tokens, about 64 per expert, so
+    every expert runs several 64-token tiles): every token against the oracle."""
+    layer, inp = _layer(name, 2048)
+    rep = gh.check_case(synth.WORKLOADS[name], 2048, tap_tokens=2, layer=layer, inp=inp)
+    _report(name, 2048, rep)
+
+
 # --------------------------------------------------------------- small variants
-def _variant(**kw):
-    base = dict(name="v", hidden=512, n_experts=8, top_k=2, n_ff=256, tokens=5, seed=300)
-    base.update(kw)
-    return synth.Workload(**base)
+_variant = parity_cases.variant
 
 
 @pytest.mark.parametrize("kw", [
@@ -109,16 +119,16 @@ def test_variants(kw):
     (dict(latent=256, n_experts=16, top_k=4, n_groups=4, topk_groups=2, tokens=70), None, 3),
     (dict(latent=256, expert_fmt=synth.Q4_0, n_experts=16, top_k=4, tokens=97), None, 3),
     (dict(hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300, bias=True),
-     [0, 1, 77, 150, 298, 299], 2),
+     None, 2),
     (dict(expert_fmt=synth.Q5_1, tokens=100), None, 4),
     (dict(expert_fmt=synth.Q5_1, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300),
-     [0, 5, 150, 299], 2),
+     None, 2),
     (dict(expert_fmt=synth.Q4_K, tokens=100), None, 4),
     (dict(expert_fmt=synth.Q5_K, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300),
-     [0, 5, 150, 299], 2),
+     None, 2),
     (dict(expert_fmt=synth.Q3_K, tokens=100), None, 4),
     (dict(expert_fmt=synth.Q3_K, hidden=1280, n_ff=768, n_experts=32, top_k=4, tokens=300,
-          bias=True), [0, 5, 150, 299], 2),
+          bias=True), None, 2),
 ])
 def test_gemm_variants(kw, sample, taps):
     w = _variant(**kw)
@@ -126,11 +136,20 @@ def test_gemm_variants(kw, sample, taps):
     _report("gemm " + str(kw), w.tokens, rep)
 
 
+# every expert format on the grouped GEMM with buckets of more than 128 tokens
+# (4 experts, top-2, 300 tokens: 150 per expert on average), so each expert runs
+# two full 64-token tiles and a ragged third; integer sums tapped on every token
+@pytest.mark.parametrize("kw", parity_cases.MULTI_TILE)
+def test_multi_tile_gemm_every_format(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=w.tokens)
+    _report("multi-tile " + str(kw), w.tokens, rep)
+
+
 @pytest.mark.parametrize("name,T", [("latent_q8", 48), ("latent_q4", 40)])
-def test_latent_gemm_sampled(name, T):
+def test_latent_gemm(name, T):
     layer, inp = _layer(name, T)
-    rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp,
-                        tokens=[0, 1, 17, T - 1])
+    rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp)
     _report(name, T, rep)
 
 

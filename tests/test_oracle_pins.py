@@ -882,3 +882,73 @@ def test_q8_1_s_is_rounded_twice(orc):
     assert len(blocks) == 6
     for v in blocks:
         _check_exact(orc, v)
+
+
+# ------------------------------------------- the oracle downstream of given intermediates
+@pytest.mark.parametrize("latent", [0, 64])
+def test_given_own_intermediates_reproduce_the_layer(orc, synth, latent):
+    """Given its own ids and Q8_1 vectors, the oracle returns its own output bit for bit."""
+    w = _wl(hidden=128, n_experts=8, top_k=3, n_ff=64, tokens=5, latent=latent,
+            n_groups=4 if latent else 0, topk_groups=2 if latent else 0, seed=12)
+    inp = _layer_inputs(synth, w)
+    names = ("ids", "weights", "hq") + (("zq", "ylq") if latent else ())
+    ref, t = orc.layer_forward(w, inp["x"], inp["router_w"], groups=inp["groups"],
+                               experts=inp["experts"], D=inp["D"], U=inp["U"], taps=names)
+    given = {n: t[n] for n in ("ids", "zq", "hq", "ylq") if n in t}
+    out, t2 = orc.layer_forward(w, inp["x"], inp["router_w"], groups=inp["groups"],
+                                experts=inp["experts"], D=inp["D"], U=inp["U"], taps=names,
+                                given=given)
+    assert np.array_equal(out, ref)
+    for n in names:
+        assert np.array_equal(t2[n], t[n]), n
+
+
+def test_given_ids_take_the_softmax_of_their_own_logits(orc, synth):
+    """Given experts (any order, not the top-k) get weights exp(l_j) / sum exp(l_i) over
+    their own logits, and the output is their weighted sum: here checked against
+    expert_ffn of each and an exact-rational softmax of the fp64 logits."""
+    w = _wl(hidden=128, n_experts=8, top_k=3, n_ff=64, tokens=3, seed=13)
+    inp = _layer_inputs(synth, w)
+    ids = np.array([[7, 0, 4], [1, 2, 3], [5, 6, 0]], dtype=np.int32)
+    out, t = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                               taps=("ids", "weights", "logits", "xq"), given=dict(ids=ids))
+    assert np.array_equal(t["ids"], ids)
+    eb = w.expert_bytes
+    for i in range(3):
+        l = t["logits"][i][ids[i]]
+        ex = np.exp(l - l.max())
+        assert np.allclose(t["weights"][i], ex / ex.sum(), rtol=2e-7, atol=0)
+        ys = np.stack([orc.expert_ffn(w, inp["experts"][e * eb:(e + 1) * eb], t["xq"][i])["y"]
+                       for e in ids[i]]).astype(np.float64)
+        comb = (t["weights"][i].astype(np.float64)[:, None] * ys).sum(0)
+        assert np.allclose(out[i], comb, rtol=0, atol=1e-6 * np.abs(comb).max())
+    with pytest.raises(ValueError):                 # a repeated expert is refused
+        orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                          given=dict(ids=np.array([[1, 1, 2]] * 3, dtype=np.int32)))
+
+
+def test_given_hq_enters_the_down_projection(orc, synth):
+    """One code of a given Q8_1(h) moved by +1 moves that expert's y by exactly
+    d_h * d_w[r] * q_w[r, e] in every down row r (Q8_0), nothing else."""
+    w = _wl(hidden=64, n_experts=4, top_k=1, n_ff=64, tokens=1, seed=14)
+    inp = _layer_inputs(synth, w)
+    _, t = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                             taps=("ids", "hq", "y"))
+    hq = t["hq"].copy()                               # [1][1][F/32][36]
+    b, e = 1, 5
+    q = hq[0, 0, b, 4 + e].view(np.int8)
+    assert abs(int(q)) < 127
+    hq[0, 0, b, 4 + e] = np.array([int(q) + 1], dtype=np.int8).view(np.uint8)[0]
+    _, t2 = orc.layer_forward(w, inp["x"], inp["router_w"], experts=inp["experts"],
+                              taps=("y",), given=dict(hq=hq))
+    eid = int(t["ids"][0, 0])
+    eb = w.expert_bytes
+    down = inp["experts"][eid * eb:(eid + 1) * eb][2 * w.n_ff * (w.hidden // 32) * 34:]
+    D = down.reshape(w.hidden, w.n_ff // 32, 34)
+    dw = D[:, b, :2].copy().view(np.float16).astype(np.float64).reshape(-1)
+    qw = D[:, b, 2 + e].view(np.int8).astype(np.float64)
+    dh = float(hq[0, 0, b, :2].copy().view(np.float16)[0])
+    delta = t2["y"][0, 0].astype(np.float64) - t["y"][0, 0].astype(np.float64)
+    expect = dh * dw * qw
+    assert np.allclose(delta, expect, rtol=0, atol=4 * np.spacing(np.abs(t["y"]).max()))
+    assert np.any(expect != 0)
