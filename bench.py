@@ -17,8 +17,9 @@ the CPU oracle's throughput on a bounded sample of the same workload
 (cpu_baseline), and, unless --no-prefill, the 2048-token prefill layer with the
 int8 matrix-core utilisation of its grouped gate/up GEMM.  Also reported: the
 10th/50th/90th percentiles of the per-step layer time (events), the same steps
-replayed from HIP graphs (graph), and the box's plain torch copy and read rates
-over 1 GiB (hbm_probe) as context for the kernel bandwidths.
+replayed from HIP graphs (graph), and the box's single-launch HBM read rate from
+libmoe's 16-byte-load probe at the gate/up launch's size, the down weights' size,
+the layer's size and 1 GiB (hbm_probe), as the ceiling for the kernel bandwidths.
 
 Traffic (roofline.traffic) comes from two rocprofv3 counter runs of this script
 with --calibration-copy (FETCH_SIZE, then WRITE_SIZE), summarised by
@@ -61,6 +62,7 @@ def parse():
     p.add_argument("--profile-steps", action="store_true",
                    help="also print per-stage milliseconds to stderr")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    p.add_argument("--no-hbm-probe", action="store_true", help="skip the HBM read probe")
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--expert-cache", action="store_true",
                    help="also time the expert-table path: every expert read from pinned host "
@@ -315,31 +317,90 @@ def measure_cache(w, T, steps, warmup, pool=8):
                       "h2d_gbs": copied * w.expert_bytes / (admit_ms * 1e-3) / 1e9}}
 
 
-def hbm_probe(reps=10):
-    """The same box's plain streaming rates, as context for the kernel figures:
-    torch's copy (read + write) and sum (read) over 1 GiB of fp32, timed with
-    events on torch's stream."""
+def hbm_probe(sizes, reps=20):
+    """The box's single-launch HBM read rate, the ceiling the expert kernels are
+    compared with: libmoe's read probe (include/moe_probe.h, 16-byte loads) over
+    each size, one launch timed by its own dispatch events, swept over grid sizes,
+    loads in flight per thread and the load kind; the best median is reported.
+    Launches rotate over disjoint regions of a 2 GiB buffer of random bytes, so no
+    launch is served from the 256 MB MALL by the previous ones."""
+    import numpy as np
     import torch
-    n = 1 << 28
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    res = {}
-    for name, fn, nbytes in (("copy_gbs", lambda: dst.copy_(src), 8 * n),
-                             ("read_gbs", lambda: src.sum(), 4 * n)):
-        for _ in range(2):
-            fn()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+
+    from quantized_moe_expert_softmax_amd import moe
+    dev = torch.device("cuda", 0)
+    total = 2 << 30
+    buf = torch.randint(0, 256, (total,), dtype=torch.uint8, device=dev)
+    blocks_opts, unroll_opts = (512, 1024, 2048, 4096, 8192), (2, 4, 8)
+    sink = torch.empty(max(blocks_opts) * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    he = HipEvents()
+    evs = [(he.create(), he.create()) for _ in range(reps)]
+    res = []
+    for nbytes in sizes:
+        nbytes = nbytes // 4096 * 4096
+        nreg = max(2, total // nbytes)
+        best = None
+        for blocks in blocks_opts:
+            for unroll in unroll_opts:
+                for nt in (0, moe.MOE_PROBE_NONTEMPORAL):
+                    for r in range(reps + 3):
+                        e = evs[r - 3] if r >= 3 else (0, 0)
+                        moe.moe_probe_read(buf.data_ptr() + (r % nreg) * nbytes, nbytes, blocks,
+                                           unroll, nt, sink.data_ptr(), st, *e)
+                    torch.cuda.synchronize()
+                    med = float(np.median([he.elapsed_ms(a, b) for a, b in evs]))
+                    if best is None or med < best[0]:
+                        best = (med, blocks, unroll, nt)
+        med, blocks, unroll, nt = best
+        res.append({"bytes": nbytes, "gbs": nbytes / (med * 1e-3) / 1e9, "us": med * 1e3,
+                    "blocks": blocks, "loads_in_flight": unroll, "nontemporal": bool(nt)})
+    for a, b in evs:
+        he.destroy(a)
+        he.destroy(b)
+    del buf, sink
     torch.cuda.empty_cache()
-    res["bytes"] = 4 * n
-    return res
+    return {"kernel": "moe_probe_read: 16-byte loads, one launch per size, dispatch events",
+            "reps": reps, "sizes": res}
+
+
+def host_cpu():
+    """The host's CPU model and the threads this process may use (at most 16, the
+    GPU machine's CPU share for one GPU)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return model, avail, max(1, min(16, avail))
+
+
+def cpu_oracle_rate(w, inp, xs, seconds, nthreads):
+    """The oracle, untuned, on the host: calls of nthreads tokens each (one per
+    thread; every token is routed and computed on its own), taken in turn from
+    the token batches stacked into one pool, for about `seconds`.  Returns
+    (tokens/s, tokens, calls, elapsed)."""
+    import numpy as np
+
+    import oracle
+    X = np.ascontiguousarray(np.concatenate(xs, axis=0))
+    n = X.shape[0]
+    chunk = max(1, min(nthreads, n))
+    t0 = time.perf_counter()
+    done = calls = 0
+    while time.perf_counter() - t0 < seconds:
+        first = calls * chunk % n
+        oracle.layer_forward(w, X, inp["router_w"], inp["router_b"], inp["groups"],
+                             inp["experts"], inp["D"], inp["U"],
+                             tokens=[(first + t) % n for t in range(chunk)], nthreads=nthreads)
+        done += chunk
+        calls += 1
+    el = time.perf_counter() - t0
+    return done / el, done, calls, el
 
 
 def graph_rate(T, ms):
@@ -429,30 +490,28 @@ def main():
 
     cpu = None
     if not a.no_cpu_baseline:
-        import oracle
-        inp, xs, pool = m["inp"], m["xs"], m["pool"]
-        ncores = 1
-        chunk = min(T, 8)
-        t_c0 = time.perf_counter()
-        done = 0
-        b = 0
-        while time.perf_counter() - t_c0 < a.cpu_seconds:
-            first = (b // pool) * chunk % T
-            oracle.layer_forward(w, xs[b % pool], inp["router_w"], inp["router_b"],
-                                 inp["groups"], inp["experts"], inp["D"], inp["U"],
-                                 tokens=[(first + t) % T for t in range(chunk)], nthreads=ncores)
-            done += chunk
-            b += 1
-        el = time.perf_counter() - t_c0
-        cpu = {"value": done / el, "unit": "tokens/s", "cores": ncores, "kind": "oracle",
-               "sample": f"{done} tokens ({b} calls of {chunk} tokens from the batches of "
-                         f"this workload), {el:.1f} s on one host thread"}
+        model, avail, nth = host_cpu()
+        rate, done, calls, el = cpu_oracle_rate(w, m["inp"], m["xs"], a.cpu_seconds, nth)
+        cpu = {"value": rate, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"{done} tokens of this workload ({calls} oracle calls of {nth} "
+                         f"tokens drawn in turn from its {len(m['xs'])} token batches, one token "
+                         f"per thread), {el:.1f} s on {nth} host threads",
+               "cpu_model": model, "host_cpus_available": avail}
     m.pop("inp"), m.pop("xs")
 
     prefill = None
     if not a.no_prefill and a.workload != "prefill":
         wp = synth.WORKLOADS["prefill"]
         mp = measure(wp, wp.tokens, a.prefill_steps, 3, 4, 1, a.profile_steps)
+        cpu_p = None
+        if not a.no_cpu_baseline:
+            model, avail, nth = host_cpu()
+            rate, done, calls, el = cpu_oracle_rate(wp, mp["inp"], mp["xs"][:1], a.cpu_seconds / 2,
+                                                    nth)
+            cpu_p = {"value": rate, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+                     "sample": f"{done} of the 2048 tokens of one prefill batch ({calls} calls of "
+                               f"{nth} tokens, one per thread), {el:.1f} s on {nth} host threads",
+                     "cpu_model": model}
         mp.pop("inp"), mp.pop("xs")
         ops = gemm_int8_ops(wp, wp.tokens)
         k_ms = mp["st_ms"]["gate_up_kernel"]
@@ -466,13 +525,19 @@ def main():
                                  "unit": "TOP/s", "frac": ops / (k_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS},
                    "gate_up_gbs": gb / (k_ms * 1e-3) / 1e9,
                    "stage_ms": mp["st_ms"], "layer_ms_pct": mp["layer_ms_pct"],
-                   "graph": graph_rate(wp.tokens, mp["graph_ms_step"])}
+                   "graph": graph_rate(wp.tokens, mp["graph_ms_step"]),
+                   "cpu_baseline": cpu_p}
 
     cache = None
     if a.expert_cache:
         cache = measure_cache(w, T, min(a.steps, 40), 3)
 
-    probe = hbm_probe()
+    probe = None
+    if not a.no_hbm_probe:
+        # the gate/up launch's bytes, the down weights', the whole layer's, and 1 GiB
+        dn_bytes = m["mean_active"] * w.matrix_bytes(w.k_out, w.n_ff // 32)
+        probe = hbm_probe([int(gu_bytes), int(dn_bytes), int(layer_bytes), 1 << 30])
+        probe["gate_up_vs_probe"] = gu_gbs / probe["sizes"][0]["gbs"]
 
     if a.calibration_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")

@@ -25,7 +25,9 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_
            "moe_pack_host", "moe_unpack_host", "moe_pack", "moe_workspace_bytes",
            "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
            "moe_layer_forward_table", "moe_expert_cache_create", "moe_expert_cache_admit",
-           "moe_expert_cache_slot", "moe_expert_cache_destroy", "moe_last_error", "moe_version"]
+           "moe_expert_cache_slot", "moe_expert_cache_destroy", "moe_last_error", "moe_version",
+           "moe_probe_read"]
+MOE_PROBE_NONTEMPORAL = 1
 (MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END,
  MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND) = range(8)
 MOE_EV_COUNT = 8
@@ -91,6 +93,8 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_version.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
+        L.moe_probe_read.argtypes = [vp, sz, i32, i32, i32, vp, vp, vp, vp]
+        L.moe_probe_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -211,6 +215,15 @@ def moe_expert_cache_slot(cache, expert: int) -> int:
 
 def moe_expert_cache_destroy(cache) -> None:
     lib().moe_expert_cache_destroy(cache)
+
+
+def moe_probe_read(buf, nbytes, blocks, unroll, flags, sink, stream=0, ev_start=0,
+                   ev_stop=0) -> None:
+    """One read-probe launch (include/moe_probe.h); raises on a refused argument."""
+    rc = lib().moe_probe_read(buf, nbytes, blocks, unroll, flags, sink, stream, ev_start or None,
+                              ev_stop or None)
+    if rc != 0:
+        raise MoeError(rc, "moe_probe_read refused its arguments or failed to launch")
 
 
 # ---------------------------------------------------------------------------

@@ -22,8 +22,9 @@ def L():
 
 
 def test_exports_match_header(L):
-    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
-    declared = set(re.findall(r"\b(moe_[a-z_]+)\s*\(", hdr))
+    import glob
+    hdr = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
+    declared = set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", hdr))
     assert declared == set(moe.EXPORTS), declared ^ set(moe.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
