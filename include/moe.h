@@ -35,7 +35,9 @@
  *   - All shape, format and device checks happen in moe_layer_create / the
  *     pack calls; moe_layer_forward re-checks only T, k and pointers.
  *   - The caller owns every buffer.  The library allocates no device memory;
- *     moe_layer holds host metadata only.
+ *     moe_layer holds host metadata only.  (The one exception is static: the
+ *     workspace array of moe_layer_forward_noalloc, 64 MiB per GPU, which the
+ *     first moe_layer_create on a GPU looks up and zeroes.)
  *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
  *     Forward calls are asynchronous on it and never synchronise the host.
  */
@@ -190,6 +192,29 @@ moe_status moe_layer_forward_taps(const moe_layer* layer, const float* x, int T,
                                   const void* D, const void* U, int k, float* out,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const moe_taps* taps);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward with the library's own workspace instead of one passed in.
+ * That workspace is a static device array of MOE_NOALLOC_WORKSPACE_BYTES
+ * (64 MiB), one copy per GPU, looked up and zeroed by the first
+ * moe_layer_create on that GPU and held until the process ends.  The call
+ * allocates nothing.  A T whose workspace (moe_workspace_bytes) exceeds the
+ * array is refused with MOE_ENOMEM; every decode and verify size fits, the
+ * 2048-token prefill layers do not.  Every call on one GPU, from any layer,
+ * shares that GPU's array: calls that overlap in time on one GPU race and give
+ * undefined results, so the caller orders them (one stream, or events).  Each
+ * call leaves the array's counters at zero for the next one.  Arguments,
+ * results and errors are otherwise those of moe_layer_forward.
+ */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+moe_status moe_layer_forward_noalloc(const moe_layer* layer, const float* x, int T,
+                                     const float* router_w, const float* router_b,
+                                     const int32_t* group_of_expert, const void* expert_packs,
+                                     const void* D, const void* U, int k, float* out,
+                                     void* stream);
 
 /*
  * Stage boundaries for timing (the pages' per-stage profiler idea: milliseconds

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -44,6 +45,20 @@ static moe_status fail(moe_status s, const char* fmt, ...) {
 static moe_status hip_fail(hipError_t e, const char* what) {
     return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// The device made current for the lifetime of the object (the caller's again after).
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
 
 extern "C" const char* moe_last_error(void) { return g_err.c_str(); }
 extern "C" const char* moe_version(void) { return "moe-gfx950 0.1"; }
@@ -109,6 +124,39 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The workspace of moe_layer_forward_noalloc: one file-scope device array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes `scratch` itself to a kernel or a copy (in host
+// code it names a host-side stand-in): its device address on each GPU comes
+// from hipGetSymbolAddress, once per device, at moe_layer_create.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
+static const int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[SCRATCH_MAX_DEVICES] = {};
+
+// With `device` current: look up that GPU's copy of `scratch` and zero it (the
+// workspace contract: zero before first use; every call leaves its counters at
+// zero again).
+static moe_status scratch_init(int device) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (device < 0 || device >= SCRATCH_MAX_DEVICES)
+        return fail(MOE_EDEVICE, "device %d beyond the %d the static workspace supports", device,
+                    SCRATCH_MAX_DEVICES);
+    if (g_scratch[device]) return MOE_OK;
+    DeviceGuard g(device);
+    if (!g.ok) return fail(MOE_EDEVICE, "cannot select device %d", device);
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+    e = hipMemset(p, 0, MOE_NOALLOC_WORKSPACE_BYTES);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "zeroing the static workspace");
+    g_scratch[device] = p;
+    return MOE_OK;
+}
+
 extern "C" moe_status moe_layer_create(const moe_desc* desc, int device, moe_layer** out) {
     if (!out) return fail(MOE_EINVAL, "out is NULL");
     *out = nullptr;
@@ -125,6 +173,8 @@ extern "C" moe_status moe_layer_create(const moe_desc* desc, int device, moe_lay
     if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
         return fail(MOE_EDEVICE, "device %d is %s; the kernels are built for gfx950 only", device,
                     p.gcnArchName);
+    s = scratch_init(device);
+    if (s != MOE_OK) return s;
     moe_layer* L = new moe_layer;
     L->desc = *desc;
     L->dims = make_dims(*desc);
@@ -274,18 +324,6 @@ extern "C" moe_status moe_unpack_host(const moe_desc* d, int which, const void* 
 }
 
 namespace {
-struct DeviceGuard {
-    int prev = -1;
-    bool ok = true;
-    explicit DeviceGuard(int dev) {
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
-    }
-    ~DeviceGuard() {
-        int cur;
-        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-    }
-};
 }  // namespace
 
 extern "C" moe_status moe_pack(const moe_layer* L, int which, const void* host_canonical,
@@ -513,6 +551,31 @@ extern "C" moe_status moe_layer_forward(const moe_layer* L, const float* x, int 
                                         size_t workspace_bytes, void* stream) {
     return forward_impl(L, x, T, router_w, router_b, groups, ExpertSrc((const uint8_t*)experts), D,
                         U, k, out, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" moe_status moe_layer_forward_noalloc(const moe_layer* L, const float* x, int T,
+                                                const float* router_w, const float* router_b,
+                                                const int32_t* groups, const void* experts,
+                                                const void* D, const void* U, int k, float* out,
+                                                void* stream) {
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    if (T < 0 || T > L->dims.max_tokens)
+        return fail(MOE_EINVAL, "T %d out of range 0..max_tokens=%d", T, L->dims.max_tokens);
+    const size_t need = ws_layout(L->dims, std::max(T, 1)).total;
+    if (need > (size_t)MOE_NOALLOC_WORKSPACE_BYTES)
+        return fail(MOE_ENOMEM,
+                    "T=%d needs %zu bytes of workspace; the static workspace holds %zu "
+                    "(call moe_layer_forward with a workspace of the caller's)",
+                    T, need, (size_t)MOE_NOALLOC_WORKSPACE_BYTES);
+    void* ws;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ws = L->device < SCRATCH_MAX_DEVICES ? g_scratch[L->device] : nullptr;
+    }
+    if (!ws) return fail(MOE_EDEVICE, "no static workspace on device %d", L->device);
+    return forward_impl(L, x, T, router_w, router_b, groups, ExpertSrc((const uint8_t*)experts), D,
+                        U, k, out, ws, (size_t)MOE_NOALLOC_WORKSPACE_BYTES, stream, nullptr,
+                        nullptr);
 }
 
 extern "C" moe_status moe_layer_forward_events(const moe_layer* L, const float* x, int T,

@@ -26,7 +26,8 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_
            "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
            "moe_layer_forward_table", "moe_expert_cache_create", "moe_expert_cache_admit",
            "moe_expert_cache_slot", "moe_expert_cache_destroy", "moe_last_error", "moe_version",
-           "moe_probe_read"]
+           "moe_probe_read", "moe_layer_forward_noalloc"]
+MOE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 MOE_PROBE_NONTEMPORAL = 1
 (MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END,
  MOE_EV_GATE_UP_KSTART, MOE_EV_GATE_UP_KEND) = range(8)
@@ -79,6 +80,8 @@ def lib():
         L.moe_layer_forward_taps.argtypes = fwd + [P(moe_taps)]
         L.moe_layer_forward_events.argtypes = fwd + [P(vp)]
         L.moe_layer_forward_table.argtypes = fwd
+        L.moe_layer_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
         L.moe_expert_cache_create.argtypes = [vp, vp, vp, i32, vp, vp, P(vp)]
         L.moe_expert_cache_admit.argtypes = [vp, P(ctypes.c_int32), i32, vp, P(i32)]
         L.moe_expert_cache_slot.argtypes = [vp, i32, P(i32)]
@@ -167,6 +170,13 @@ def moe_layer_forward(handle, x, T, router_w, router_b, groups, experts, D, U, k
                       workspace_bytes, stream=0) -> None:
     _check(lib().moe_layer_forward(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,
                                    workspace, workspace_bytes, stream))
+
+
+def moe_layer_forward_noalloc(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,
+                              stream=0) -> None:
+    """moe_layer_forward on the library's static per-GPU workspace (no allocation)."""
+    _check(lib().moe_layer_forward_noalloc(handle, x, T, router_w, router_b, groups, experts, D, U,
+                                           k, out, stream))
 
 
 def moe_layer_forward_taps(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,
