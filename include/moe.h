@@ -139,6 +139,15 @@ moe_status moe_unpack_host(const moe_desc* desc, int which, const void* packed, 
 moe_status moe_pack(const moe_layer* layer, int which, const void* host_canonical,
                     void* dev_dst, void* stream);
 
+/* Checks host group labels (group_of_expert's content, E int32) against the
+ * contract of a layer with n_groups > 0 (the expert group labels of the
+ * edge0-strata README, section "Changes from upstream Strata", read as equal
+ * groups, step 2 above): every label in [0, n_groups) and exactly
+ * E / n_groups experts per label.  MOE_EINVAL names the first label or
+ * group that breaks it.  With n_groups == 0, labels must be NULL.  Needs no
+ * device. */
+moe_status moe_group_labels_check(const moe_desc* desc, const int32_t* labels);
+
 /* Device workspace a forward call with T tokens needs (T <= max_tokens).
  * The workspace must be zero-filled before its first use; every call leaves
  * its internal counters at zero again, so one zeroing suffices. */
@@ -151,7 +160,10 @@ moe_status moe_workspace_bytes(const moe_layer* layer, int T, size_t* bytes);
  * the packed tensors (D, U NULL when latent == 0); k must equal desc.top_k;
  * out [T][H] fp32.  T == 0 is a no-op.  Inputs must be finite (NaN/Inf:
  * unspecified output).  Deterministic: the same inputs give bitwise the same
- * out.  Calls sharing one workspace must not overlap in time.
+ * out.  Calls sharing one workspace must not overlap in time.  The kernels do
+ * not re-check the group labels: labels outside that contract (out of range,
+ * or groups of unequal size) give an unspecified output; moe_group_labels_check
+ * validates them on the host once per layer.
  */
 moe_status moe_layer_forward(const moe_layer* layer, const float* x, int T,
                              const float* router_w, const float* router_b,

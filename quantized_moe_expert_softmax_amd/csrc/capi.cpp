@@ -358,6 +358,30 @@ extern "C" moe_status moe_pack(const moe_layer* L, int which, const void* host_c
     return MOE_OK;
 }
 
+extern "C" moe_status moe_group_labels_check(const moe_desc* d, const int32_t* labels) {
+    moe_status s = moe_desc_check(d);
+    if (s != MOE_OK) return s;
+    if (d->n_groups == 0) {
+        if (labels) return fail(MOE_EINVAL, "labels given for a layer with n_groups == 0");
+        return MOE_OK;
+    }
+    if (!labels) return fail(MOE_EINVAL, "n_groups %d needs labels", d->n_groups);
+    std::vector<int> count(d->n_groups, 0);
+    for (int e = 0; e < d->n_experts; ++e) {
+        if (labels[e] < 0 || labels[e] >= d->n_groups)
+            return fail(MOE_EINVAL, "label %d of expert %d outside 0..%d", labels[e], e,
+                        d->n_groups - 1);
+        ++count[labels[e]];
+    }
+    const int per = d->n_experts / d->n_groups;
+    for (int g = 0; g < d->n_groups; ++g)
+        if (count[g] != per)
+            return fail(MOE_EINVAL, "group %d holds %d experts, not E / n_groups = %d", g,
+                        count[g], per);
+    g_err.clear();
+    return MOE_OK;
+}
+
 extern "C" moe_status moe_workspace_bytes(const moe_layer* L, int T, size_t* bytes) {
     if (!L || !bytes) return fail(MOE_EINVAL, "NULL argument");
     if (T < 0 || T > L->desc.max_tokens)

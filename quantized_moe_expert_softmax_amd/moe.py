@@ -26,7 +26,7 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_desc_check", "moe_pack_
            "moe_layer_forward", "moe_layer_forward_taps", "moe_layer_forward_events",
            "moe_layer_forward_table", "moe_expert_cache_create", "moe_expert_cache_admit",
            "moe_expert_cache_slot", "moe_expert_cache_destroy", "moe_last_error", "moe_version",
-           "moe_probe_read", "moe_layer_forward_noalloc"]
+           "moe_probe_read", "moe_layer_forward_noalloc", "moe_group_labels_check"]
 MOE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 MOE_PROBE_NONTEMPORAL = 1
 (MOE_EV_BEGIN, MOE_EV_ROUTED, MOE_EV_EXPERT_IN, MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_END,
@@ -82,6 +82,8 @@ def lib():
         L.moe_layer_forward_table.argtypes = fwd
         L.moe_layer_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         L.moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.moe_group_labels_check.argtypes = [P(moe_desc), vp]
+        L.moe_group_labels_check.restype = ctypes.c_int
         L.moe_expert_cache_create.argtypes = [vp, vp, vp, i32, vp, vp, P(vp)]
         L.moe_expert_cache_admit.argtypes = [vp, P(ctypes.c_int32), i32, vp, P(i32)]
         L.moe_expert_cache_slot.argtypes = [vp, i32, P(i32)]
@@ -170,6 +172,17 @@ def moe_layer_forward(handle, x, T, router_w, router_b, groups, experts, D, U, k
                       workspace_bytes, stream=0) -> None:
     _check(lib().moe_layer_forward(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,
                                    workspace, workspace_bytes, stream))
+
+
+def moe_group_labels_check(desc: moe_desc, labels) -> None:
+    """Raise unless the host int32 labels (numpy array, or None) meet the layer's
+    group contract."""
+    import numpy as np
+    ptr = None
+    if labels is not None:
+        labels = np.ascontiguousarray(labels, dtype=np.int32)
+        ptr = labels.ctypes.data
+    _check(lib().moe_group_labels_check(ctypes.byref(desc), ptr))
 
 
 def moe_layer_forward_noalloc(handle, x, T, router_w, router_b, groups, experts, D, U, k, out,

@@ -237,3 +237,45 @@ def test_expert_cache_refusals_without_a_device(L):
     L.moe_expert_cache_destroy(None)
     assert L.moe_layer_forward_table(None, None, 1, None, None, None, None, None, None, 1, None,
                                      None, 0, None) == moe.MOE_EINVAL
+
+
+def test_group_labels_check(L):
+    """The host validator of the group-label contract: every synthetic workload's labels
+    pass; out-of-range labels and unequal groups are refused by name."""
+    import numpy as np
+    for name, w in synth.WORKLOADS.items():
+        moe.moe_group_labels_check(moe.desc_of(w), synth.gen_groups(w))
+    d = moe.make_desc(512, 16, 3, 256, n_groups=4, topk_groups=2, max_tokens=4)
+    good = np.arange(16, dtype=np.int32) // 4
+    moe.moe_group_labels_check(d, good)
+    moe.moe_group_labels_check(d, good[::-1].copy())          # any order of equal groups
+    bad = good.copy()
+    bad[5] = 4
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_group_labels_check(d, bad)
+    assert ei.value.status == moe.MOE_EINVAL and "expert 5" in ei.value.message
+    bad = good.copy()
+    bad[0] = 1                                                  # group 0: 3, group 1: 5
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_group_labels_check(d, bad)
+    assert "group 0 holds 3" in ei.value.message
+    with pytest.raises(moe.MoeError):
+        moe.moe_group_labels_check(d, None)
+    with pytest.raises(moe.MoeError):
+        moe.moe_group_labels_check(moe.make_desc(512, 16, 3, 256, max_tokens=4), good)
+
+
+def test_oracle_refuses_what_the_label_check_refuses(L):
+    """The oracle's own refusal of unequal groups matches the library's validator."""
+    import numpy as np
+    import oracle
+    w = synth.Workload("g", hidden=256, n_experts=8, top_k=2, n_ff=256, tokens=1, n_groups=4,
+                       topk_groups=2, seed=1)
+    inp = synth.gen_layer(w)
+    bad = inp["groups"].copy()
+    bad[0] = 1
+    with pytest.raises(moe.MoeError):
+        moe.moe_group_labels_check(moe.desc_of(w), bad)
+    with pytest.raises(ValueError):
+        oracle.layer_forward(w, inp["x"], inp["router_w"], groups=bad, experts=inp["experts"])
+    oracle.layer_forward(w, inp["x"], inp["router_w"], groups=inp["groups"], experts=inp["experts"])
