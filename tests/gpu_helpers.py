@@ -123,6 +123,16 @@ def requant_flips(gq: np.ndarray, v_ref: np.ndarray, what: str):
     gd = gb[:, 0:2].copy().view("<u2").astype(np.int64).reshape(-1)
     rd = rb[:, 0:2].copy().view("<u2").astype(np.int64).reshape(-1)
     assert np.all(np.abs(gd - rd) <= 1), (what, "binary16 d differs by more than 1 ulp")
+    dd = np.nonzero(gd != rd)[0]
+    if dd.size:
+        # a d that rounds to the other binary16 neighbour: the oracle's fp32
+        # amax / 127 lies within 1e-5 (relative) of the midpoint of the two
+        va = np.abs(np.asarray(v_ref, dtype=np.float32).reshape(-1, 32)[bad[dd]]).max(axis=1)
+        d32 = (va / np.float32(127)).astype(np.float64)
+        mid = 0.5 * (gd[dd].astype(np.uint16).view(np.float16).astype(np.float64) +
+                     rd[dd].astype(np.uint16).view(np.float16).astype(np.float64))
+        assert np.all(np.abs(d32 - mid) <= 1e-5 * d32), (what, "binary16 d differs away from a "
+                                                         "rounding boundary")
     dc = gb[:, 4:].view(np.int8).astype(np.int64) - rb[:, 4:].view(np.int8).astype(np.int64)
     assert np.all(np.abs(dc) <= 1), (what, "a code differs by more than 1")
     v = np.asarray(v_ref, dtype=np.float32).reshape(-1, 32)[bad]
