@@ -206,4 +206,12 @@ __device__ __forceinline__ v4i ld16(const void* p) {
     return *reinterpret_cast<const v4i*>(p);
 }
 
+// A 16-byte load of data read once per call (expert and dense weight codes):
+// marked non-temporal (streaming), which keeps it from displacing reused lines
+// in the caches.  A single-launch read of 107 MB measured 6.1-6.4 TB/s with
+// such loads against 5.5 TB/s with plain ones on MI355X.
+__device__ __forceinline__ v4i ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
 }  // namespace moe

@@ -188,6 +188,9 @@ __device__ __forceinline__ void stage_q(const ActPtr& a, int K, const int32_t* s
 
 // fp32 rows quantised to Q8_1 straight into LDS; one 32-lane group per block.
 // When `keep` has a q pointer the blocks are also written to it (row src_row[i]).
+// (Loading several blocks' values before quantising the first measured no gain
+// at one token and, inlined into every gate/up instance, took the 8-wave Q4_0
+// kernel from 110 to 148 registers: half the occupancy at 32 tokens.)
 template <bool S_VAL>
 __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t* src_row, int n,
                                           int8_t* s_q, float* s_d, int32_t* s_sq, ActPtr keep) {
@@ -218,8 +221,15 @@ __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t
 // emit(i, r, W[r] . act[i]) from lane 0 of each row's lane group.
 // Loads are unconditional (a chunk index past the row is clamped to the last
 // chunk and its contribution masked later), and the scale stays as raw binary16
-// bits until it is used, so no load waits on another.
-template <int FMT, int LPR, int CPL>
+// bits until it is used, so no load waits on another.  STREAM loads the code
+// bytes non-temporal, right for rows that a call reads once (every decode
+// kernel here: one token, or an expert bucket that fits one chunk of staged
+// tokens), as the caches then keep what is reused; the side data always loads
+// plainly.  Measured on MI355X against plain loads: one-token layers 40.2 ->
+// 37.9 us, six-token 158.2 -> 144.6 us; a row that its workgroup re-reads for a
+// later chunk of tokens lost (the 32-token latent D in four-token chunks, 67 ->
+// 75 us) and should load plainly.
+template <int FMT, int LPR, int CPL, bool STREAM>
 __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<FMT>::SideMem* rscl,
                                          int sl, int NCH, v4i (&wq)[CPL],
                                          typename Fmt<FMT>::Side (&wsc)[CPL]) {
@@ -237,7 +247,7 @@ __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<
             wsc[j] = v4i{(int)sw[0], (int)sw[1], (int)sw[2], (int)rscl[c >> 3]};
             continue;
         }
-        wq[j] = ld16(row + (size_t)c * 16);
+        wq[j] = STREAM ? ld16_stream(row + (size_t)c * 16) : ld16(row + (size_t)c * 16);
         if constexpr (F::K5) {
             // the super-block's scales and the qh half of this chunk
             const v4i* u = reinterpret_cast<const v4i*>(rscl + c / F::CPSIDE);
@@ -336,7 +346,8 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
 // no register copy forces a wait.  A load past the last pass re-reads the last
 // pass's rows (it is never used) so that every load is unconditional.  On
 // entry A must hold pass 0 when `a_loaded`.
-template <int FMT, int LPR, int CPL, int NW, bool TAP, int PASSES = 0, class Emit, class EmitIsum>
+template <int FMT, int LPR, int CPL, int NW, bool TAP, bool STREAM, int PASSES = 0, class Emit,
+          class EmitIsum>
 __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fmt<FMT>::SideMem* scl,
                                          size_t rowb,
                                          int nb, int rows, int n, int K, const int8_t* s_q,
@@ -352,7 +363,7 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
     if constexpr (PASSES == 1) {
         // a single pass: one buffer
         const int r = wave * RPW + rg;
-        if (!a_loaded) load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
+        if (!a_loaded) load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, r, sl, NCH, nb, n, K, s_q, s_d, s_sq, emit, emit_isum,
                                      tap);
         return;
@@ -362,18 +373,18 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
     typename F::Side sB[CPL];
     if (!a_loaded) {
         const int r = row_of(0);
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
+        load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
     }
     for (int p = 0; p < passes; p += 2) {
         {
             const int r = row_of(p + 1);
-            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wB, sB);
+            load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wB, sB);
         }
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, row_of(p), sl, NCH, nb, n, K, s_q, s_d, s_sq, emit,
                                      emit_isum, tap);
         {
             const int r = row_of(p + 2);
-            load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
+            load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
         }
         if (p + 1 < passes)
             pass_dot<FMT, LPR, CPL, TAP>(wB, sB, row_of(p + 1), sl, NCH, nb, n, K, s_q, s_d, s_sq,
@@ -411,6 +422,7 @@ __device__ __forceinline__ void publish_route(const GUArgs& A, const RouteLds& S
 // three 4-wave workgroups share a CU)
 template <int FMT, int LPR, int CPL, int NW, bool TAP>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs A) {
+    constexpr bool STREAM = true;   // an expert's tokens fit one chunk at decode sizes
     constexpr int PASSES = 64 / (NW * (64 / LPR));
     extern __shared__ __align__(16) char smem[];
     const int FB = A.F / QK;
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
         const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
+        load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
                                 nb * Fmt<FMT>::CPB, wA, sA);
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
@@ -480,7 +492,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
                 A.taps.isum_gu[((size_t)s_a[i] * 2 * A.F + row) * nb + blk] = v;
             }
         };
-        row_tile<FMT, LPR, CPL, NW, TAP, PASSES>(codes, scl, rowb, nb, 64, n, K, s_q, s_d, s_sq,
+        row_tile<FMT, LPR, CPL, NW, TAP, STREAM, PASSES>(codes, scl, rowb, nb, 64, n, K, s_q, s_d, s_sq,
                                                  emit, emit_isum, tap, wA, sA, i0 == 0);
         __syncthreads();
         // SwiGLU and Q8_1: one 32-lane group per token, lane = output f
@@ -506,6 +518,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
 
 template <int FMT, int LPR, int CPL, int NW, bool TAP>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
+    constexpr bool STREAM = true;   // one token (dense) or one bucket chunk (experts)
     extern __shared__ __align__(16) char smem[];
     const int NRT = A.rows / A.rt;
     const int g = blockIdx.x / NRT, rt = blockIdx.x - g * NRT;
@@ -539,7 +552,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
         constexpr int RPW = 64 / LPR;
         const int lane = threadIdx.x & 63;
         const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
-        load_row<FMT, LPR, CPL>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
+        load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
                                 nb * Fmt<FMT>::CPB, wA, sA);
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
@@ -557,7 +570,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
             if (s_s[i] / A.tap_div < A.tap_tokens)
                 A.isum_tap[((size_t)s_s[i] * A.rows + r0 + r) * nb + blk] = v;
         };
-        row_tile<FMT, LPR, CPL, NW, TAP>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d, s_sq, emit,
+        row_tile<FMT, LPR, CPL, NW, TAP, STREAM>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d, s_sq, emit,
                                          emit_isum, TAP && A.isum_tap, wA, sA, i0 == 0);
         __syncthreads();
     }
@@ -569,6 +582,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
 // rows per workgroup; 32-row tiles also write Q8_1 of the combined rows)
 template <int FMT, int LPR, int CPL, bool TAP, bool TABLE = false, int RT = DT_RT>
 __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
+    constexpr bool STREAM = true;
     using F = Fmt<FMT>;
     constexpr int RPW = 64 / LPR;
     constexpr int NA = F::CPB == 1 ? 2 : 1;     // 16-byte activation pieces per chunk
@@ -591,7 +605,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * RT * (nb / F::SBLK);
         v4i wq[CPL], wn[CPL];
         typename F::Side wsc[CPL], wsn[CPL];
-        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
+        load_row<FMT, LPR, CPL, STREAM>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
         // this rank's activation chunks, the same for every row
         v4i act[CPL][NA];
         int asq[CPL];
@@ -609,7 +623,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         for (int p = 0; p < PASSES; ++p) {
             const int r = p * RPW + rg;
             if (p + 1 < PASSES)
-                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
+                load_row<FMT, LPR, CPL, STREAM>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
                                         NCH, wn, wsn);
             float acc = 0.0f;
 #pragma unroll
@@ -679,6 +693,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
 // order as above.  Dynamic LDS: k * (F + 8 * F/32) bytes.
 template <int FMT, int LPR, int CPL, bool TAP, int RT = DT_RT>
 __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
+    constexpr bool STREAM = true;
     using F = Fmt<FMT>;
     using SM = typename F::SideMem;
     constexpr int RPW = 64 / LPR;
@@ -709,7 +724,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
     typename F::Side wsc[CPL], wsn[CPL];
     if (wave < A.k) {
         locate(wave);
-        load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
+        load_row<FMT, LPR, CPL, STREAM>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
     }
     if ((int)threadIdx.x < A.k) s_src[threadIdx.x] = t * A.k + threadIdx.x;
     __syncthreads();
@@ -719,7 +734,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
         const int a = t * A.k + j;
         if (j != wave) {
             locate(j);
-            load_row<FMT, LPR, CPL>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
+            load_row<FMT, LPR, CPL, STREAM>(codes + rg * rowb, scl + (size_t)rg * (nb / F::SBLK), sl, NCH, wq, wsc);
         }
         auto emit = [&](int, int r, float v) { s_y[j][r] = v; };
         auto emit_isum = [&](int, int r, int blk, int v) {
@@ -729,7 +744,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
         for (int p = 0; p < PASSES; ++p) {
             const int r = p * RPW + rg;
             if (p + 1 < PASSES)
-                load_row<FMT, LPR, CPL>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
+                load_row<FMT, LPR, CPL, STREAM>(codes + (r + RPW) * rowb, scl + (size_t)(r + RPW) * (nb / F::SBLK), sl,
                                         NCH, wn, wsn);
             pass_dot<FMT, LPR, CPL, TAP>(wq, wsc, r, sl, NCH, nb, 1, K, s_q + (size_t)j * K, s_d + j * nb,
                                          s_sq + j * nb, emit, emit_isum, tap);
