@@ -459,6 +459,11 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel
     const bool lat_fused_q = T <= LAT_FUSED_Q_MAX_T;
+    // a few tokens: the latent D and U on the few-token matrix-core kernel
+    // (measured on MI355X against the matrix-vector kernels, us per stage:
+    // latent Q4_0 experts at T = 32, D 75 -> 17 and U 42 -> 15; latent Q8_0
+    // experts at T = 6, D 15 -> 12 and U 10 -> 8)
+    const bool thin = m.L && !gemm && T >= THIN_MIN_T && dense_thin_ok(m.D, T) && dense_thin_ok(m.U, T);
     if (taps && down_tok) tp.y = taps->y;
     const ActPtr none{nullptr, nullptr, nullptr};
 
@@ -490,6 +495,12 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (gemm) {
             CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
             CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
+        } else if (thin) {
+            // K-sliced partial rows, added in slice order by the quantisation
+            const int S = thin_splits(m.L, m.H / QK);
+            float* zp = S > 1 ? (float*)(ws + w.dpart) : z;
+            CK(launch_dense_thin(m.D, (const uint8_t*)Dp, T, xq, zp, S, tp.isum_d, tp.tap_tokens, st), "D");
+            CK(launch_quant_rows_sum(zp, S, S > 1 ? z : nullptr, T, m.L, zq, st), "Q8_1(z)");
         } else {
             CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
                                tp.tap_tokens, st), "D");
@@ -535,6 +546,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         if (gemm) {
             CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
+        } else if (thin) {
+            if (!ylq_in_down) CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
+            CK(launch_dense_thin(m.U, (const uint8_t*)Up, T, ylq, out, 1, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (ylq_in_down) {
             CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, nullptr, none, out, tp.isum_u,
                                tp.tap_tokens, st), "U");

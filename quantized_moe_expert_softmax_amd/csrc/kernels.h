@@ -91,6 +91,10 @@ struct Taps {                 // device pointers, NULL = off
 };
 
 hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStream_t st);
+// the same of x = sum_{s < S} part[s] (added in slice order; part[s] is
+// [rows][K]), also stored to x when x is not null
+hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, int K, ActPtr out,
+                                 hipStream_t st);
 // Q8_1(x) and the router logits; then, from two tokens on, top-k and softmax
 // per token, and up to 32 tokens the bucketing too.  *done tells how far the
 // launched kernels go; *sel receives the selection parameters (for a single
@@ -141,6 +145,12 @@ hipError_t launch_down_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                             hipStream_t st);
 hipError_t launch_dense_mfma(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
                              int32_t* isum_tap, int tap_tokens, hipStream_t st);
+
+// Few-token dense projection (T <= 32, Q8_0 or Q4_0, rows a multiple of 32):
+// out[s][t][r] over S K-slices (S divides the blocks per row; thin_splits).
+bool dense_thin_ok(const MatLayout& W, int T);
+hipError_t launch_dense_thin(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
+                             int S, int32_t* isum_tap, int tap_tokens, hipStream_t st);
 
 // Expert-address table: fill entries 0..E-1 with base + e * stride, or set
 // u.n (at most TABLE_UPDATE_MAX) entries, stream-ordered.

@@ -29,13 +29,9 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "mfma_ops.h"
 
 namespace moe {
-
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int MF_MT = GEMM_TILE_M;        // token columns per workgroup
 constexpr int MF_NT = 128;                // weight rows per workgroup
@@ -60,17 +56,6 @@ struct MfArgs {
     int32_t* tap_isum;            // [output row][canonical row][K/32]
     int tap_tokens, tap_div;      // token of output row o = o / tap_div
 };
-
-__device__ __forceinline__ int mf_row_of(int i, int half) { return (i >> 2) * 8 + half * 4 + (i & 3); }
-
-// Q4_0 bytes (low nibble = element j, high nibble = element j + 16) widened to
-// int8 (c - 8).  For a nibble c in each byte: c ^ 8 is c - 8 when c >= 8 and
-// needs the sign bits 0xF0 when c < 8.
-__device__ __forceinline__ uint32_t q4_widen(uint32_t nib) {
-    const uint32_t v = nib ^ 0x08080808u;
-    const uint32_t neg = (~nib) & 0x08080808u;
-    return v | (neg * 0x1Eu);
-}
 
 // ---------------------------------------------------------------------------
 // Shared pieces of both kernels.
@@ -128,17 +113,6 @@ struct MfWave {
 // (row / column l32's d at k = 0 in lanes 0..31, zero elsewhere; a zero-
 // extended 16-bit load gives the first register, the second is zero).  Block
 // kb+1's products are issued before block kb is rescaled.
-__device__ __forceinline__ h4 scale_op(uint32_t d16) { return __builtin_bit_cast(h4, v2i{(int)d16, 0}); }
-
-// the scale outer product: binary16 operands (exact in fp32), or fp32 operands
-// (one k of v_mfma_f32_32x32x2_f32: lanes 0..31 carry the values, 32..63 zero)
-__device__ __forceinline__ v16f scale_mfma(h4 a, h4 b) {
-    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, v16f{}, 0, 0, 0);
-}
-__device__ __forceinline__ v16f scale_mfma(float a, float b) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, v16f{}, 0, 0, 0);
-}
-
 template <bool SWIGLU, bool TAP, class SOp = h4, bool NEG = false, class Frag, class SFrag>
 __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const MfWave& w, int s,
                                          const int* s_orow, Frag frag, SFrag sfrag,

@@ -115,6 +115,7 @@ struct WsLayout {
     size_t hq_q, hq_ds, hq_sq;
     size_t y;
     size_t ylat, ylq_q, ylq_ds, ylq_sq;
+    size_t dpart;                   // latent D partial rows of the few-token kernel
     size_t total;
     int T, S;                       // tokens, router K-splits
 };
@@ -127,6 +128,17 @@ constexpr int DECODE_T = 8;  // largest T the few-token router logits kernel is 
 constexpr int ROUTE_DEC_MAX_T = 1;
 constexpr int MV_MAX_T = 32; // T up to this runs the matrix-vector expert kernels
 constexpr int LAT_FUSED_Q_MAX_T = 1;  // latent: consumers quantise z / y_lat up to this T
+// latent D and U at THIN_MIN_T..MV_MAX_T tokens: the few-token matrix-core kernel
+constexpr int THIN_MIN_T = 2;
+
+// K slices of the few-token dense kernel for a rows x (nb blocks) matrix:
+// doubled while fewer than 256 workgroups (32-row tiles x slices) would run and
+// a slice keeps at least 16 blocks (two per wave).
+inline int thin_splits(int rows, int nb) {
+    int S = 1;
+    while ((rows / 32) * S < 256 && nb % (2 * S) == 0 && nb / (2 * S) >= 16) S *= 2;
+    return S;
+}
 constexpr int GEMM_TILE_M = 64;  // token tile of the grouped matrix-core GEMM
 
 // Upper bound of the token tiles over all active experts: every expert adds at
@@ -192,6 +204,8 @@ inline WsLayout ws_layout(const Dims& m, int T) {
     w.ylq_q = take((size_t)T * L);
     w.ylq_ds = take(sizeof(uint32_t) * T * (L / QK));
     w.ylq_sq = take(sizeof(int32_t) * T * (L / QK));
+    const bool thin = m.L && T >= THIN_MIN_T && T <= MV_MAX_T;
+    w.dpart = take(thin ? sizeof(float) * thin_splits(m.L, m.H / QK) * (size_t)T * m.L : 0);
     w.total = o;
     return w;
 }

@@ -15,14 +15,19 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Q8_1 quantisation of fp32 rows [rows][K]: one 32-lane group per block.
-__global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x, int rows, int K,
-                                                    ActPtr out) {
+// With S > 1, x holds S partial arrays that are added in slice order first
+// (and the sums stored to xsum when it is not null).
+__global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ x, int S, float* xsum,
+                                                    int rows, int K, ActPtr out) {
     const int nb = K / QK;
     const long blk = (long)blockIdx.x * 8 + threadIdx.x / 32;
     if (blk >= (long)rows * nb) return;               // whole 32-lane groups exit together
     const int l = threadIdx.x % 32;
     const long r = blk / nb, b = blk % nb;
-    float v = x[r * K + b * QK + l];
+    const long i = r * K + b * QK + l;
+    float v = x[i];
+    for (int s = 1; s < S; ++s) v += x[(long)s * rows * K + i];
+    if (xsum) xsum[i] = v;
     quant_q8_1_32(v, l, out.q + r * K + b * QK, out.ds + r * nb + b, out.sq + r * nb + b);
 }
 
@@ -584,8 +589,18 @@ __global__ __launch_bounds__(256) void k_tap_q8_1(ActPtr a, long rows, int K,
 hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStream_t st) {
     long blocks = (long)rows * (K / QK);
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((blocks + 7) / 8)), dim3(256), 0, st, x, rows,
-                       K, out);
+    hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((blocks + 7) / 8)), dim3(256), 0, st, x, 1,
+                       (float*)nullptr, rows, K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, int K, ActPtr out,
+                                 hipStream_t st) {
+    long blocks = (long)rows * (K / QK);
+    if (blocks == 0) return hipSuccess;
+    if (S < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((blocks + 7) / 8)), dim3(256), 0, st, part, S,
+                       x, rows, K, out);
     return hipGetLastError();
 }
 
