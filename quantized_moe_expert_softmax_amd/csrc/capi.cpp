@@ -481,8 +481,11 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     EV(MOE_EV_BEGIN);
     RouteDone routed;
     SelectArgs sel;
+    // 2 to DECODE_T tokens whose down projection runs per token: no buckets;
+    // the gate/up kernel takes its expert and tokens from the routing ids
+    const bool ids_only = T >= 2 && T <= DECODE_T && down_tok;
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
-                     &routed, &sel, st), "router");
+                     ids_only, &routed, &sel, st), "router");
     if (routed == ROUTE_SELECTED) CK(launch_bucket(m, w, ws, T, st), "bucketing");
     // a single token is selected and bucketed by the gate/up kernel's prologue
     const SelectArgs* gu_route = routed == ROUTE_LOGITS ? &sel : nullptr;
@@ -520,10 +523,12 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev, gu_route, &rout),
            "gate/up");
     else if (m.L)
-        CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout),
+        CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout,
+                             routed == ROUTE_IDS),
            "gate/up");
     else
-        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout),
+        CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout,
+                             routed == ROUTE_IDS),
            "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs

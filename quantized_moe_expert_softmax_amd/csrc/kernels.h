@@ -96,13 +96,14 @@ hipError_t launch_quant_rows(const float* x, int rows, int K, ActPtr out, hipStr
 hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, int K, ActPtr out,
                                  hipStream_t st);
 // Q8_1(x) and the router logits; then, from two tokens on, top-k and softmax
-// per token, and up to 32 tokens the bucketing too.  *done tells how far the
-// launched kernels go; *sel receives the selection parameters (for a single
-// token the gate/up kernel selects in its prologue from them).
-enum RouteDone { ROUTE_LOGITS, ROUTE_SELECTED, ROUTE_BUCKETED };
+// per token, and up to 32 tokens the bucketing too, unless `ids_only` (2 to
+// DECODE_T tokens whose consumers read the ids: no buckets).  *done tells how
+// far the launched kernels go; *sel receives the selection parameters (for a
+// single token the gate/up kernel selects in its prologue from them).
+enum RouteDone { ROUTE_LOGITS, ROUTE_SELECTED, ROUTE_BUCKETED, ROUTE_IDS };
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, RouteDone* done, SelectArgs* sel, hipStream_t st);
+                         ActPtr xq, bool ids_only, RouteDone* done, SelectArgs* sel, hipStream_t st);
 // Per-expert assignment lists in token order, the active experts, and the
 // token tiles (GEMM_TILE_M assignments) of each, numbered in tile_map.
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, hipStream_t st);
@@ -123,7 +124,8 @@ bool mv_config_ok(int K, int fmt, bool gate_up);
 hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
-                             const SelectArgs* route = nullptr, const RouteOut* rout = nullptr);
+                             const SelectArgs* route = nullptr, const RouteOut* rout = nullptr,
+                             bool ids_slots = false);
 // outq.q != null (array form): Q8_1 of out is written too
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st,

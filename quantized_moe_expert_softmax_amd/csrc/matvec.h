@@ -29,6 +29,7 @@ struct GUArgs {
     Taps taps;
     SelectArgs route;     // route.part != null: one token, routed in the prologue
     RouteOut rout;
+    int ids_slots;        // 1: the slots come from b.ids (T * k <= DECODE_T * 32), not buckets
 };
 
 

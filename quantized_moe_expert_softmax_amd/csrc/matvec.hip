@@ -69,7 +69,7 @@ bool mv_config_ok(int K, int fmt, bool gate_up) {
 hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev,
-                             const SelectArgs* route, const RouteOut* rout) {
+                             const SelectArgs* route, const RouteOut* rout, bool ids_slots) {
     int lpr, cpl;
     if (!pick_gu_fmt(nchunks(m.kin, m.fmt), m.fmt, lpr, cpl)) return hipErrorInvalidConfiguration;
     if (64 % (gu_waves(lpr, m.fmt) * (64 / lpr))) return hipErrorInvalidConfiguration;
@@ -85,6 +85,14 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
     size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 64 * 4 + (size_t)a.tch * 8;
     a.route = SelectArgs{};
     a.rout = RouteOut{};
+    a.ids_slots = 0;
+    if (ids_slots) {
+        // every assignment id is held by one thread of the (at least 256-thread) workgroup
+        // (and the expert ids fit the prologue's two per thread)
+        if (route || T * m.k > DECODE_T * 32 || !b.ids || m.E > 2 * 64 * gu_waves(lpr, m.fmt))
+            return hipErrorInvalidValue;
+        a.ids_slots = 1;
+    }
     if (route) {
         // the prologue's selection: one token, its whole logits (S = 1), and
         // its LDS after the staging area

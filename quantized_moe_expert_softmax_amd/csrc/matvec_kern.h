@@ -442,6 +442,55 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         if (blockIdx.x == 0) publish_route<NW * 64>(A, S, wt);
         e = __builtin_amdgcn_readfirstlane(S.sel[slot]);
         cnt = 1;
+    } else if (A.ids_slots) {
+        // a few tokens, no buckets: from the T * k routing ids, slot j serves the
+        // j-th smallest distinct expert, whose assignments are listed in order
+        // (the bucketing kernel's active / counts / lists, for this slot only):
+        // counts per expert in LDS, then ballots and per-wave totals
+        constexpr int NT = NW * 64;
+        __shared__ int s_cnt[2 * NT], s_lst[DECODE_T * 32], s_wc[3][NW];
+        __shared__ int s_e;
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, nA = A.T * A.k;
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        const int id = tid < nA ? A.b.ids[tid] : -1;
+        s_cnt[tid] = 0;
+        s_cnt[tid + NT] = 0;
+        if (tid == 0) s_e = -1;
+        __syncthreads();
+        if (id >= 0) atomicAdd(&s_cnt[id], 1);
+        __syncthreads();
+        // expert ids tid (pass 0) and tid + NT (pass 1); rank = active ids below
+        unsigned long long bal[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            bal[m] = __ballot(s_cnt[tid + m * NT] > 0);
+            if (lane == 0) s_wc[m][wave] = __popcll(bal[m]);
+        }
+        __syncthreads();
+        int base = 0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            for (int w = 0; w < NW; ++w) base += w < wave ? s_wc[m][w] : 0;
+            if ((bal[m] >> lane) & 1ull) {
+                if (base + __popcll(bal[m] & lt) == slot) s_e = tid + m * NT;
+            }
+            for (int w = wave; w < NW; ++w) base += s_wc[m][w];
+        }
+        __syncthreads();
+        e = s_e;
+        if (e < 0) return;              // (uniform) no expert for this slot
+        const bool mine = id == e;
+        const unsigned long long bm = __ballot(mine);
+        if (lane == 0) s_wc[2][wave] = __popcll(bm);
+        __syncthreads();
+        if (mine) {
+            int pos = __popcll(bm & lt);
+            for (int w = 0; w < wave; ++w) pos += s_wc[2][w];
+            s_lst[pos] = tid;
+        }
+        cnt = s_cnt[e];
+        __syncthreads();
+        lst = s_lst;
     } else {
         if (slot >= (int)A.b.ctrl[CW_N_ACTIVE]) return;
         e = A.b.active[slot];

@@ -123,6 +123,8 @@ struct WsLayout {
 inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr int DECODE_T = 8;  // largest T the few-token router logits kernel is sized for
+// (and up to which the gate/up kernel can take its expert and tokens straight
+// from the routing ids: T * k <= DECODE_T * 32 assignments)
 // T up to this takes that kernel and leaves top-k, softmax and bucketing to the
 // gate/up kernel's prologue, which routes a single token
 constexpr int ROUTE_DEC_MAX_T = 1;
@@ -163,7 +165,7 @@ inline int router_splits(const Dims& m, int T) {
     // K slices of the router logits: enough workgroups to spread the router
     // matrix (few tokens) or the token x expert tiles (many); the single-token
     // router computes whole logits
-    if (T <= ROUTE_DEC_MAX_T) return 1;
+    if (T <= DECODE_T) return 1;
     const RouterTile rt = router_tile(T);
     const long tiles = (long)((T + rt.bm - 1) / rt.bm) * ((m.E + rt.bn - 1) / rt.bn);
     const int chunks = m.H / 16;

@@ -167,8 +167,9 @@ __global__ __launch_bounds__(256) void k_route_logits_mf(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Router logits of a few tokens (T <= DECODE_T; launched for a single token,
-// whose top-k, softmax and bucketing run in the prologue of the gate/up kernel).
+// Router logits of a few tokens (T <= DECODE_T): whole logits, no K slices.  A
+// single token's top-k, softmax and bucketing then run in the prologue of the
+// gate/up kernel; two to DECODE_T tokens are selected by k_route_select_tok.
 //
 // k_route_logits_dec: workgroups [0, E): expert e = blockIdx.x, 256 threads
 // over the H-wide row of W_r with every load issued at once (indices past the
@@ -203,11 +204,14 @@ __global__ __launch_bounds__(256) void k_route_logits_dec(const float* __restric
         valid[u] = i < h4;
         w[u] = wrow[min(i, h4 - 1)];
     }
-    for (int t = 0; t < T; ++t) {
-        const float4* xr = reinterpret_cast<const float4*>(x + (size_t)t * H);
-        float4 xv[ROUTE_U];
+    // token rows through two register buffers: the next token's row is in
+    // flight while one is multiplied (a load past the last token re-reads it)
+    auto load_x = [&](int t, float4 (&xv)[ROUTE_U]) {
+        const float4* xr = reinterpret_cast<const float4*>(x + (size_t)min(t, T - 1) * H);
 #pragma unroll
         for (int u = 0; u < ROUTE_U; ++u) xv[u] = xr[min((int)threadIdx.x + 256 * u, h4 - 1)];
+    };
+    auto dot = [&](int t, const float4 (&xv)[ROUTE_U]) {
         double acc = 0.0;
 #pragma unroll
         for (int u = 0; u < ROUTE_U; ++u) {
@@ -220,6 +224,14 @@ __global__ __launch_bounds__(256) void k_route_logits_dec(const float* __restric
         }
         acc = wave_sum_d(acc);
         if (lane == 0) s_part[t][wave] = acc;
+    };
+    float4 xa[ROUTE_U], xb[ROUTE_U];
+    load_x(0, xa);
+    for (int t = 0; t < T; t += 2) {
+        load_x(t + 1, xb);
+        dot(t, xa);
+        load_x(t + 2, xa);
+        if (t + 1 < T) dot(t + 1, xb);
     }
     __syncthreads();
     if ((int)threadIdx.x < T) {
@@ -606,7 +618,8 @@ hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, i
 
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, RouteDone* done, SelectArgs* sel, hipStream_t st) {
+                         ActPtr xq, bool ids_only, RouteDone* done, SelectArgs* sel,
+                         hipStream_t st) {
     double* part = (double*)(ws + w.logit_part);
     const int S = w.S;
     const long qblocks = (long)T * (m.H / QK);
@@ -617,10 +630,25 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     a.part = part; a.S = S; a.T = T; a.E = m.E; a.k = m.k;
     a.bias = br; a.groups = groups; a.G = m.G; a.TG = m.TG; a.logits_tap = logits_tap;
     *sel = a;
-    if (T <= ROUTE_DEC_MAX_T) {
+    int32_t* counts = (int32_t*)(ws + w.counts);
+    int32_t* lists = (int32_t*)(ws + w.lists);
+    uint32_t* ctrl = (uint32_t*)(ws + w.ctrl);
+    int32_t* active = (int32_t*)(ws + w.active);
+    if (T <= DECODE_T) {
+        if (S != 1) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_route_logits_dec, dim3(m.E + qwg), dim3(256), 0, st, x, Wr, T, m.H,
                            m.E, part, xq);
-        *done = ROUTE_LOGITS;
+        if (T <= ROUTE_DEC_MAX_T) {
+            *done = ROUTE_LOGITS;
+        } else if (ids_only) {
+            hipLaunchKernelGGL((k_route_select_tok<false, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
+                               wts, counts, lists, ctrl, active);
+            *done = ROUTE_IDS;
+        } else {
+            hipLaunchKernelGGL((k_route_select_tok<true, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
+                               wts, counts, lists, ctrl, active);
+            *done = ROUTE_BUCKETED;
+        }
         return hipGetLastError();
     }
     const RouterTile rt = router_tile(T);
@@ -642,10 +670,6 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int32_t* counts = (int32_t*)(ws + w.counts);
-    int32_t* lists = (int32_t*)(ws + w.lists);
-    uint32_t* ctrl = (uint32_t*)(ws + w.ctrl);
-    int32_t* active = (int32_t*)(ws + w.active);
     if (T <= MV_MAX_T && T * m.k <= 1024 && m.E <= 512) {
         hipLaunchKernelGGL((k_route_select_tok<true, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
                            wts, counts, lists, ctrl, active);
