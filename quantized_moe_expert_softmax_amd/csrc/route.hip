@@ -264,6 +264,7 @@ __global__ __launch_bounds__(TSEL_NT) void k_route_select_tok(SelectArgs A,
     __shared__ unsigned long long s_key[512];
     __shared__ unsigned s_khi[512];
     __shared__ unsigned long long s_gkey[64];
+    __shared__ int s_gcnt[64];
     __shared__ unsigned char s_gsel[64];
     __shared__ int s_nallow;
     __shared__ int s_sel[32];
@@ -271,53 +272,74 @@ __global__ __launch_bounds__(TSEL_NT) void k_route_select_tok(SelectArgs A,
     __shared__ int s_last;
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = A.T, E = A.E, k = A.k, G = A.G;
-    for (int e = tid; e < E; e += TSEL_NT) {
-        double ps[ROUTE_SMAX];
+    // each thread's experts tid + m * TSEL_NT: partial logits, bias and group
+    // label, every load issued before the first is used
+    constexpr int EPT = (512 + TSEL_NT - 1) / TSEL_NT;
+    unsigned gl[EPT];
+    unsigned long long key[EPT];
+    if (G > 0 && tid < 64) {
+        s_gkey[tid] = 0ull;
+        s_gcnt[tid] = 0;
+    }
 #pragma unroll
-        for (int sl = 0; sl < ROUTE_SMAX; ++sl)
-            ps[sl] = sl < A.S ? A.part[((size_t)sl * T + t) * E + e] : 0.0;
-        double v = 0.0;
+    for (int m = 0; m < EPT; ++m) {
+        const int e = tid + m * TSEL_NT;
+        gl[m] = ~0u;
+        key[m] = 0ull;
+        if (e < E) {
+            double ps[ROUTE_SMAX];
 #pragma unroll
-        for (int sl = 0; sl < ROUTE_SMAX; ++sl)
-            if (sl < A.S) v += ps[sl];
-        if (A.bias) v += (double)A.bias[e];
-        if (A.logits_tap) A.logits_tap[(size_t)t * E + e] = v;
-        s_key[e] = dkey(v + 0.0);
+            for (int sl = 0; sl < ROUTE_SMAX; ++sl)
+                ps[sl] = sl < A.S ? A.part[((size_t)sl * T + t) * E + e] : 0.0;
+            const float b = A.bias ? A.bias[e] : 0.0f;
+            if (G > 0) gl[m] = (unsigned)A.groups[e];
+            double v = 0.0;
+#pragma unroll
+            for (int sl = 0; sl < ROUTE_SMAX; ++sl)
+                if (sl < A.S) v += ps[sl];
+            if (A.bias) v += (double)b;
+            if (A.logits_tap) A.logits_tap[(size_t)t * E + e] = v;
+            key[m] = dkey(v + 0.0);
+        }
     }
     if (G > 0) {
-        if (tid < 64) s_gkey[tid] = 0ull;
-        if (tid == 0) s_nallow = 0;
+        // groups ranked by their largest member key (ties to the lower group);
+        // the experts outside the TG best get key 0, unless fewer than k would
+        // stay (labels that break the equal-size-groups contract)
         __syncthreads();
-        for (int e = tid; e < E; e += TSEL_NT) {
-            const unsigned gl = (unsigned)A.groups[e];
-            if (gl < (unsigned)G) atomicMax(&s_gkey[gl], s_key[e]);
-        }
+#pragma unroll
+        for (int m = 0; m < EPT; ++m)
+            if (gl[m] < (unsigned)G) {
+                atomicMax(&s_gkey[gl[m]], key[m]);
+                atomicAdd(&s_gcnt[gl[m]], 1);
+            }
         __syncthreads();
-        if (tid < G) {
-            const unsigned long long kg = s_gkey[tid];
+        if (tid < 64) {
+            const unsigned long long kg = tid < G ? s_gkey[tid] : 0ull;
             int r = 0;
             for (int h = 0; h < G; ++h) {
                 const unsigned long long kh = s_gkey[h];
                 r += (int)(kh > kg) | ((int)(kh == kg) & (int)(h < tid));
             }
-            s_gsel[tid] = r < A.TG;
+            const bool kept = tid < G && r < A.TG;
+            if (tid < G) s_gsel[tid] = kept;
+            int n = kept ? s_gcnt[tid] : 0;
+            for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+            if (tid == 0) s_nallow = n;
         }
         __syncthreads();
-        int nal = 0;
-        for (int e = tid; e < E; e += TSEL_NT) {
-            const unsigned gl = (unsigned)A.groups[e];
-            nal += (int)(gl < (unsigned)G && s_gsel[gl]);
-        }
-        for (int o = 32; o > 0; o >>= 1) nal += __shfl_xor(nal, o, 64);
-        if (lane == 0 && nal) atomicAdd(&s_nallow, nal);
-        __syncthreads();
-        // fewer than k allowed (labels that break the equal-size-groups
-        // contract): every expert stays a candidate
         if (s_nallow >= k) {
-            for (int e = tid; e < E; e += TSEL_NT) {
-                const unsigned gl = (unsigned)A.groups[e];
-                if (!(gl < (unsigned)G && s_gsel[gl])) s_key[e] = 0ull;
-            }
+#pragma unroll
+            for (int m = 0; m < EPT; ++m)
+                if (!(gl[m] < (unsigned)G && s_gsel[gl[m]])) key[m] = 0ull;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+        const int e = tid + m * TSEL_NT;
+        if (e < E) {
+            s_key[e] = key[m];
+            s_khi[e] = (unsigned)(key[m] >> 32);
         }
     }
     __syncthreads();
@@ -325,8 +347,6 @@ __global__ __launch_bounds__(TSEL_NT) void k_route_select_tok(SelectArgs A,
     // on the top 32 bits of the keys (one compare each); an expert that could
     // be chosen and shares those bits with a rival is ranked again on the
     // whole keys
-    for (int e = tid; e < E; e += TSEL_NT) s_khi[e] = (unsigned)(s_key[e] >> 32);
-    __syncthreads();
     int P = 1;
     while (P < 64 && E * P * 2 <= TSEL_NT) P *= 2;
     const int lp = 31 - __clz(P);
