@@ -543,16 +543,23 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
             CK(launch_down_mfma(m, T, ex, hq, b, tile_map, y, tp, st), "down");
         else
             CK(launch_down_slot_mv(m, T, ex, hq, b, y, tp, st), "down");
-        CK(launch_combine(y, b.wts, T, m.k, m.kout, comb, st), "combine");
+        // a latent layer's combine also quantises y_lat for the U projection
+        if (m.L)
+            CK(launch_combine_q(y, b.wts, T, m.k, m.kout, comb, ylq, st), "combine+Q8_1");
+        else
+            CK(launch_combine(y, b.wts, T, m.k, m.kout, comb, st), "combine");
     }
     EV(MOE_EV_DOWN);
     if (m.L) {
         // out = U . Q8_1(y_lat)
+        // Q8_1(y_lat) comes from the down kernel (per-token form, array of
+        // packs) or from the combine (per-bucket form), else is made here
+        const bool ylq_ready = ylq_in_down || !down_tok;
         if (gemm) {
-            CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
+            if (!ylq_ready) CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (thin) {
-            if (!ylq_in_down) CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
+            if (!ylq_ready) CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_thin(m.U, (const uint8_t*)Up, T, ylq, out, 1, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (ylq_in_down) {
             CK(launch_dense_mv(m.U, (const uint8_t*)Up, T, ylq, nullptr, none, out, tp.isum_u,

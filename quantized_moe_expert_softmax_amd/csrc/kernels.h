@@ -109,6 +109,9 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, hipStream_t st);
 hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R, float* out,
                           hipStream_t st);
+// the same, and Q8_1 of out into outq (R a multiple of 32)
+hipError_t launch_combine_q(const float* y, const float* wts, int T, int k, int R, float* out,
+                            ActPtr outq, hipStream_t st);
 hipError_t launch_tap_q8_1(ActPtr a, long rows, int K, uint8_t* out, hipStream_t st);
 
 // True when the matrix-vector kernels have a configuration for rows of K

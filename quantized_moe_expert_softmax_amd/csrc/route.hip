@@ -602,6 +602,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
     reinterpret_cast<float4*>(out)[i] = acc;
 }
 
+// The same sums, one 32-lane group per Q8_1 block of out, which also writes
+// Q8_1(out) (a latent layer's y_lat, for the U projection): each element is
+// added in the same order as above, so out is the same.
+__global__ __launch_bounds__(256) void k_combine_q(const float* __restrict__ y,
+                                                   const float* __restrict__ wts, int T, int k,
+                                                   int R, float* __restrict__ out, ActPtr outq) {
+    const int nb = R / QK;
+    const long blk = (long)blockIdx.x * 8 + threadIdx.x / 32;
+    if (blk >= (long)T * nb) return;                  // whole 32-lane groups exit together
+    const int l = threadIdx.x % 32;
+    const long t = blk / nb, b = blk % nb;
+    const long r = b * QK + l;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) acc = fmaf(wts[t * k + j], y[(t * k + j) * R + r], acc);
+    out[t * R + r] = acc;
+    quant_q8_1_32(acc, l, outq.q + t * R + b * QK, outq.ds + t * nb + b, outq.sq + t * nb + b);
+}
+
 // Canonical 36-byte Q8_1 blocks from the split activation layout.
 __global__ __launch_bounds__(256) void k_tap_q8_1(ActPtr a, long rows, int K,
                                                   uint8_t* __restrict__ out) {
@@ -718,6 +736,15 @@ hipError_t launch_combine(const float* y, const float* wts, int T, int k, int R,
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, y, wts, T, k,
                        R, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_q(const float* y, const float* wts, int T, int k, int R, float* out,
+                            ActPtr outq, hipStream_t st) {
+    long blocks = (long)T * (R / QK);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_combine_q, dim3((unsigned)((blocks + 7) / 8)), dim3(256), 0, st, y, wts, T,
+                       k, R, out, outq);
     return hipGetLastError();
 }
 
