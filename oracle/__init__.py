@@ -24,6 +24,7 @@ Q5_1 = 7
 Q4_K = 12
 Q5_K = 13
 Q3_K = 11
+NVFP4 = 40
 Q8_1_BYTES = 36
 
 
@@ -97,6 +98,16 @@ def lib():
         L.orc_q3_k_scale.restype = ctypes.c_int
         L.orc_isum_q3_k.argtypes = [vp, i32, vp]
         L.orc_isum_q3_k.restype = ctypes.c_int32
+        L.orc_e2m1_decode.argtypes = [i32]
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [i32]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_nvfp4_code.argtypes = [vp, i32]
+        L.orc_nvfp4_code.restype = ctypes.c_int
+        L.orc_isum_nvfp4_half.argtypes = [vp, vp, i32]
+        L.orc_isum_nvfp4_half.restype = ctypes.c_int32
+        L.orc_row_dot_nvfp4.argtypes = [vp, vp, i32, ctypes.c_double, vp]
+        L.orc_row_dot_nvfp4.restype = ctypes.c_float
         L.orc_dequant_weight.argtypes = [i32, vp, i32]
         L.orc_dequant_weight.restype = ctypes.c_double
         L.orc_row_dot.argtypes = [i32, vp, vp, i32, vp]
@@ -201,6 +212,34 @@ def isum_q3_k(sblk: np.ndarray, b: int, ablk: np.ndarray) -> int:
     sblk = np.ascontiguousarray(sblk, dtype=np.uint8)
     ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
     return int(lib().orc_isum_q3_k(_p(sblk), b, _p(ablk)))
+
+
+def e2m1(code: int) -> float:
+    return float(lib().orc_e2m1_decode(code))
+
+
+def e4m3(byte: int) -> float:
+    return float(lib().orc_e4m3_decode(byte))
+
+
+def nvfp4_code(wblk: np.ndarray, j: int) -> int:
+    wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
+    return int(lib().orc_nvfp4_code(_p(wblk), j))
+
+
+def isum_nvfp4_half(wblk: np.ndarray, ablk: np.ndarray, h: int) -> int:
+    wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
+    ablk = np.ascontiguousarray(ablk, dtype=np.uint8)
+    return int(lib().orc_isum_nvfp4_half(_p(wblk), _p(ablk), h))
+
+
+def row_dot_nvfp4(row: np.ndarray, act: np.ndarray, nblk: int, tensor_scale: float,
+                  with_isum: bool = False):
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    act = np.ascontiguousarray(act, dtype=np.uint8)
+    tap = np.empty(nblk, dtype=np.int32) if with_isum else None
+    y = float(lib().orc_row_dot_nvfp4(_p(row), _p(act), nblk, tensor_scale, _p(tap)))
+    return (y, tap) if with_isum else y
 
 
 def q5_1_code(wblk: np.ndarray, j: int) -> int:

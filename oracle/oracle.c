@@ -28,6 +28,12 @@
  *        llama.cpp's Q3_K (the ggml that the same README builds against), and
  *        its dot against Q8_1 as the block's two 16-element halves, each with
  *        its signed sub-block scale, times d * d_a (no min term).
+ *   [NV] edge0-strata README, section "Changes from upstream Strata": NVFP4
+ *        latent experts.  The pages name the format only; it is read as its
+ *        published definition (FP4 E2M1 elements, one FP8 E4M3 scale per 16
+ *        consecutive elements, one fp32 scale per tensor), and its dot against
+ *        Q8_1 as each 16-element half's integer sum of 2 * e2m1(code) * q_a
+ *        times that half's scale / 2, times d_a, times the tensor scale.
  *   [E0] edge0-strata README, section "Changes from upstream Strata":
  *        latent-MoE with dense D/U projections in Q8 or Q4 into a 1280/1792-
  *        wide latent space, expert group labels, Q4_0 x Q8_1 rows (the Q4 of
@@ -51,12 +57,13 @@
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
 #define ORC_Q3_K 11
+#define ORC_NVFP4 40
 #define ORC_QK 32
 #define ORC_Q8_1_BYTES 36
 
 typedef struct {
     int hidden, n_experts, top_k, n_ff, latent;
-    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1, ORC_Q4_K, ORC_Q5_K or ORC_Q3_K */
+    int expert_fmt;           /* ORC_Q8_0, ORC_Q4_0, ORC_Q5_1, ORC_Q4_K, ORC_Q5_K, ORC_Q3_K or ORC_NVFP4 */
     int n_groups, topk_groups;/* 0 = no group limit */
     int dense_fmt;            /* D/U: ORC_Q8_0 or ORC_Q4_0 */
 } orc_desc;
@@ -316,15 +323,58 @@ int32_t orc_isum_q3_k(const uint8_t* sb, int b, const uint8_t* a) {
     return s;
 }
 
+/*
+ * NVFP4 [NV].  A code c (4 bits) is FP4 E2M1: bit 3 the sign, bits 2..1 the
+ * exponent e (bias 1), bit 0 the mantissa m; e = 0 is subnormal, m * 0.5, else
+ * (1 + m / 2) * 2^(e - 1).  A scale s (8 bits) is FP8 E4M3: bit 7 the sign,
+ * bits 6..3 the exponent e (bias 7), bits 2..0 the mantissa m; e = 0 is
+ * subnormal, m / 8 * 2^-6, else (1 + m / 8) * 2^(e - 7); 0x7F and 0xFF are NaN.
+ * Canonical block of 32 elements (18 bytes): byte 0 the scale of elements
+ * 0..15, byte 1 that of 16..31, then 16 code bytes, element 2i in the low
+ * nibble and 2i + 1 in the high nibble of byte 2 + i.
+ */
+double orc_e2m1_decode(int c) {
+    int e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    return (c & 8) ? -v : v;
+}
+
+double orc_e4m3_decode(int s) {
+    int e = (s >> 3) & 15, m = s & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? (m / 8.0) * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return (s & 0x80) ? -v : v;
+}
+
+int orc_nvfp4_code(const uint8_t* w, int j) {
+    uint8_t b = w[2 + j / 2];
+    return (j & 1) ? b >> 4 : b & 0x0F;
+}
+
+/* half h (elements 16h .. 16h + 15) of a block against a Q8_1 block: the sum of
+ * 2 * e2m1(code) * q_a, an integer (2 * e2m1 is one of 0, 1, 2, 3, 4, 6, 8, 12,
+ * signed) */
+int32_t orc_isum_nvfp4_half(const uint8_t* w, const uint8_t* a, int h) {
+    int32_t s = 0;
+    for (int i = 0; i < 16; ++i) {
+        int j = 16 * h + i;
+        int v2 = (int)(2.0 * orc_e2m1_decode(orc_nvfp4_code(w, j)));
+        s += v2 * (int32_t)(int8_t)a[4 + j];
+    }
+    return s;
+}
+
 static inline int kq_bytes(int fmt) { return fmt == ORC_Q5_K ? 176 : fmt == ORC_Q3_K ? 110 : 144; }
 static inline int is_kq(int fmt) { return fmt == ORC_Q4_K || fmt == ORC_Q5_K || fmt == ORC_Q3_K; }
 
-static inline int fmt_bytes(int fmt) {
-    return fmt == ORC_Q4_0 ? 18 : fmt == ORC_Q5_1 ? 24 : 34;   /* per 32; Q4_K: 144 per 256 */
+static inline int fmt_bytes(int fmt) {   /* per 32; Q4_K: 144 per 256 */
+    return fmt == ORC_Q4_0 || fmt == ORC_NVFP4 ? 18 : fmt == ORC_Q5_1 ? 24 : 34;
 }
 
 /* Dequantised value of element j of a weight block, for the cross-check tests. */
 double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
+    if (fmt == ORC_NVFP4)                          /* without the tensor scale */
+        return orc_e4m3_decode(w[j / 16]) * orc_e2m1_decode(orc_nvfp4_code(w, j));
     double d = orc_f16_decode(rd16(w));
     if (fmt == ORC_Q8_0) return d * (double)(int8_t)w[2 + j];
     if (fmt == ORC_Q5_1) return d * (double)orc_q5_1_code(w, j) + orc_f16_decode(rd16(w + 2));
@@ -348,8 +398,35 @@ double orc_dequant_weight(int fmt, const uint8_t* w, int j) {
  * in double and the sum rounded to float.  The Q5_1 min term takes s, the
  * Q8_1 block's stored d * sum(q) [Q5], [KQ].
  */
+static double row_dot_d(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap);
+
 float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
+    return (float)row_dot_d(fmt, row, act, nblk, isum_tap);
+}
+
+/*
+ * NVFP4 [NV]: tensor_scale * sum_b d_a,b * sum_h e4m3(s_b,h) / 2 * isum_b,h,
+ * each term exact in double, the blocks added in order, rounded to float once.
+ * The tap of block b holds its two half sums as 16-bit halves (half 0 low).
+ */
+float orc_row_dot_nvfp4(const uint8_t* row, const uint8_t* act, int nblk, double tensor_scale,
+                        int32_t* isum_tap) {
+    return (float)(row_dot_d(ORC_NVFP4, row, act, nblk, isum_tap) * tensor_scale);
+}
+
+static double row_dot_d(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int32_t* isum_tap) {
     double acc = 0.0;
+    if (fmt == ORC_NVFP4) {
+        for (int b = 0; b < nblk; ++b) {
+            const uint8_t* w = row + (size_t)b * 18;
+            const uint8_t* a = act + (size_t)b * ORC_Q8_1_BYTES;
+            int32_t i0 = orc_isum_nvfp4_half(w, a, 0), i1 = orc_isum_nvfp4_half(w, a, 1);
+            if (isum_tap) isum_tap[b] = (int32_t)(((uint32_t)i0 & 0xFFFFu) | ((uint32_t)i1 << 16));
+            double da = orc_f16_decode(rd16(a));
+            acc += da * (orc_e4m3_decode(w[0]) * 0.5 * (double)i0 + orc_e4m3_decode(w[1]) * 0.5 * (double)i1);
+        }
+        return acc;
+    }
     if (fmt == ORC_Q3_K) {
         /* block b against Q8_1 block b: d * d_a * isum_b, exact in double [Q3] */
         for (int b = 0; b < nblk; ++b) {
@@ -359,7 +436,7 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
             if (isum_tap) isum_tap[b] = is;
             acc += orc_f16_decode(rd16(sb + 108)) * orc_f16_decode(rd16(a)) * (double)is;
         }
-        return (float)acc;
+        return acc;
     }
     if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {
         /*
@@ -381,7 +458,7 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
             c -= orc_f16_decode(rd16(sb + 2)) * mn * da * (double)qs;
             acc += c;
         }
-        return (float)acc;
+        return acc;
     }
     int bb = fmt_bytes(fmt);
     for (int b = 0; b < nblk; ++b) {
@@ -394,7 +471,7 @@ float orc_row_dot(int fmt, const uint8_t* row, const uint8_t* act, int nblk, int
         if (fmt == ORC_Q5_1) c += orc_f16_decode(rd16(w + 2)) * orc_f16_decode(rd16(a + 2));
         acc += c;
     }
-    return (float)acc;
+    return acc;
 }
 
 /* rows outputs of a [rows][nblk] block matrix times a Q8_1 vector */
@@ -483,11 +560,21 @@ void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const f
 /* Expert FFN and the layer [Q8], [E0]                                       */
 /* ------------------------------------------------------------------------ */
 
+/* An NVFP4 expert's blob ends with its tensor scales: gate, up, down (fp32,
+ * little-endian) and four zero bytes [NV]. */
 static size_t expert_bytes(const orc_desc* d) {
     int kin = d->latent ? d->latent : d->hidden;
     int kout = kin;
     return 2 * d->n_ff * row_bytes(d->expert_fmt, kin / ORC_QK) +
-           (size_t)kout * row_bytes(d->expert_fmt, d->n_ff / ORC_QK);
+           (size_t)kout * row_bytes(d->expert_fmt, d->n_ff / ORC_QK) +
+           (d->expert_fmt == ORC_NVFP4 ? 16 : 0);
+}
+
+static double rdf32(const uint8_t* p) {
+    uint32_t u = (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
 }
 
 size_t orc_expert_bytes(const orc_desc* d) { return expert_bytes(d); }
@@ -508,10 +595,16 @@ static void expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq
     const uint8_t* gate = blob;
     const uint8_t* up = gate + (size_t)F * rbi;
     const uint8_t* down = up + (size_t)F * rbi;
+    const int nv = fmt == ORC_NVFP4;
+    size_t rbf = row_bytes(fmt, nbf);
+    const uint8_t* ts = down + (size_t)kout * rbf;    /* NVFP4 tensor scales */
     for (int r = 0; r < F; ++r) {
-        float g = orc_row_dot(fmt, gate + r * rbi, aq, nbi, isum_gu ? isum_gu + (size_t)r * nbi : NULL);
-        float u = orc_row_dot(fmt, up + r * rbi, aq, nbi,
-                              isum_gu ? isum_gu + (size_t)(F + r) * nbi : NULL);
+        int32_t* tg = isum_gu ? isum_gu + (size_t)r * nbi : NULL;
+        int32_t* tu = isum_gu ? isum_gu + (size_t)(F + r) * nbi : NULL;
+        float g = nv ? orc_row_dot_nvfp4(gate + r * rbi, aq, nbi, rdf32(ts), tg)
+                     : orc_row_dot(fmt, gate + r * rbi, aq, nbi, tg);
+        float u = nv ? orc_row_dot_nvfp4(up + r * rbi, aq, nbi, rdf32(ts + 4), tu)
+                     : orc_row_dot(fmt, up + r * rbi, aq, nbi, tu);
         double gd = (double)g;
         h[r] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
     }
@@ -519,7 +612,13 @@ static void expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq
         memcpy(hq, given_hq, (size_t)nbf * ORC_Q8_1_BYTES);
     else
         orc_quantize_q8_1(h, F, hq);
-    orc_matvec(fmt, kout, nbf, down, hq, y, isum_dn);
+    if (nv) {
+        for (int r = 0; r < kout; ++r)
+            y[r] = orc_row_dot_nvfp4(down + r * rbf, hq, nbf, rdf32(ts + 8),
+                                     isum_dn ? isum_dn + (size_t)r * nbf : NULL);
+    } else {
+        orc_matvec(fmt, kout, nbf, down, hq, y, isum_dn);
+    }
 }
 
 void orc_expert_ffn(const orc_desc* d, const uint8_t* blob, const uint8_t* aq, float* h,
@@ -649,7 +748,8 @@ int orc_layer_forward_given(const orc_desc* d, const float* x, const float* Wr,
     if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 512) return -1;
     if (d->latent && (!D || !U)) return -1;
     if (d->expert_fmt != ORC_Q8_0 && d->expert_fmt != ORC_Q4_0 && d->expert_fmt != ORC_Q5_1 &&
-        d->expert_fmt != ORC_Q4_K && d->expert_fmt != ORC_Q5_K && d->expert_fmt != ORC_Q3_K)
+        d->expert_fmt != ORC_Q4_K && d->expert_fmt != ORC_Q5_K && d->expert_fmt != ORC_Q3_K &&
+        d->expert_fmt != ORC_NVFP4)
         return -1;
     if (is_kq(d->expert_fmt) &&
         ((d->latent ? d->latent : d->hidden) % 256 || d->n_ff % 256))

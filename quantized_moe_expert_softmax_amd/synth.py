@@ -14,12 +14,22 @@ page, section "GPU expert kernels", and the edge0-strata README, section
 * Q8_0 weight blocks: 32 int8 codes uniform in [-127, 127] and a binary16 scale
   ``d = |N(0, 0.02)| / 127``;
 * Q4_0 weight blocks: 32 nibbles uniform in [0, 15] and ``d = |N(0, 0.02)| / 8``;
+* NVFP4 weight blocks (the edge0-strata README names NVFP4 latent experts;
+  the format is read as FP4 E2M1 codes with an FP8 E4M3 scale per 16 elements
+  and an fp32 scale per tensor): 32 codes uniform in [0, 15], each 16-element
+  half's E4M3 scale with exponent field uniform in 5..9 and mantissa field
+  uniform in 0..7 (0.25 to 7.5), and per expert matrix (gate, up, down) a
+  tensor scale ``0.002 + |N(0, 0.002)|`` rounded to fp32;
 * expert group labels ``group[e] = e // (E // n_groups)``.
 
 Canonical block layouts (little-endian): Q8_0 = binary16 d, 32 x int8 (34 B);
 Q4_0 = binary16 d, 16 bytes whose low nibble is element j and high nibble
-element j + 16 (18 B).  A canonical expert blob holds gate [F][Kin/32],
-up [F][Kin/32] and down [Kout][F/32] blocks, in that order, rows row-major.
+element j + 16 (18 B); NVFP4 = the E4M3 scales of elements 0..15 and
+16..31, then 16 bytes whose byte i holds element 2i in its low nibble and
+element 2i + 1 in its high nibble (18 B).  A canonical expert blob holds gate
+[F][Kin/32], up [F][Kin/32] and down [Kout][F/32] blocks, in that order, rows
+row-major; an NVFP4 blob ends with the three tensor scales (fp32) and four
+zero bytes.
 """
 from __future__ import annotations
 
@@ -41,8 +51,11 @@ Q5_1 = 7
 Q4_K = 12
 Q5_K = 13
 Q3_K = 11
+NVFP4 = 40
 # bytes per 32 elements (Q4_K / Q5_K: 144 / 176-byte super-blocks of 256)
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18, Q5_K: 22}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18, Q5_K: 22, NVFP4: 18}
+# bytes after an expert's three matrices (NVFP4: the tensor scales)
+EXPERT_TAIL = {NVFP4: 16}
 # bytes per super-block of 256 elements
 SUPER_BYTES = {Q4_K: 144, Q5_K: 176, Q3_K: 110}
 
@@ -154,6 +167,21 @@ def blocks(fmt: int, seed: int, q_stream: int, d_stream: int, nblk: int,
         assert out.nbytes == nsb * sbb
         lib.synth_interleave_blocks(nsb, _ptr(d16), _ptr(payload), sbb - 2, _ptr(out))
         return out
+    elif fmt == NVFP4:
+        # two E4M3 scale bytes (exponent field 5..9, mantissa field 0..7), then
+        # 16 code bytes with every bit uniform
+        if out is None:
+            out = np.empty(nblk * 18, dtype=np.uint8)
+        assert out.nbytes == nblk * 18
+        o = out.reshape(nblk, 18)
+        codes = np.empty(nblk * 16, dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, q_stream, 0, nblk * 16, _ptr(codes))
+        sraw = np.empty(nblk * 2, dtype=np.uint8)
+        lib.synth_nibble_bytes(seed, d_stream, 0, nblk * 2, _ptr(sraw))
+        e = 5 + (sraw >> 3) % 5
+        o[:, :2] = ((e << 3) | (sraw & 7)).astype(np.uint8).reshape(nblk, 2)
+        o[:, 2:] = codes.reshape(nblk, 16)
+        return out
     elif fmt == Q3_K:
         # super-blocks: 32 hmask bytes, 64 qs bytes, 12 scale bytes (all bits
         # uniform), then binary16 d
@@ -215,7 +243,8 @@ class Workload:
 
     @property
     def expert_bytes(self) -> int:
-        return sum(matrix_bytes(self.expert_fmt, r, b) for r, b in self.role_rows())
+        return (sum(matrix_bytes(self.expert_fmt, r, b) for r, b in self.role_rows()) +
+                EXPERT_TAIL.get(self.expert_fmt, 0))
 
     def matrix_bytes(self, rows: int, nblk: int) -> int:
         """Canonical bytes of an expert matrix of `rows` rows of `nblk` blocks."""
@@ -254,6 +283,13 @@ WORKLOADS = {
     "latent_q3_k": Workload("latent_q3_k", hidden=7168, n_experts=256, top_k=8, n_ff=1024,
                             tokens=1, latent=1792, expert_fmt=Q3_K, n_groups=16, topk_groups=4,
                             seed=1009),
+    # NVFP4 experts: the decode shapes, and the latent_q4 shapes (decode path
+    # only, up to 32 tokens)
+    "decode_nvfp4": Workload("decode_nvfp4", hidden=4096, n_experts=128, top_k=8, n_ff=1536,
+                             tokens=1, expert_fmt=NVFP4, seed=1010),
+    "latent_nvfp4": Workload("latent_nvfp4", hidden=7168, n_experts=256, top_k=8, n_ff=1024,
+                             tokens=1, latent=1792, expert_fmt=NVFP4, n_groups=16, topk_groups=4,
+                             seed=1011),
 }
 
 
@@ -290,6 +326,10 @@ def gen_expert(w: Workload, e: int, out: Optional[np.ndarray] = None) -> np.ndar
         blocks(w.expert_fmt, w.seed, S_EXP_Q + 4 * e + role, S_EXP_D + 4 * e + role, rows * nb,
                out=out[off:off + n])
         off += n
+    if w.expert_fmt == NVFP4:
+        ts = (0.002 + absnormal_f64(w.seed, S_EXP_D + 4 * e + 3, 3, 0.002)).astype(np.float32)
+        out[off:off + 12] = ts.view(np.uint8)
+        out[off + 12:off + 16] = 0
     return out
 
 

@@ -571,6 +571,89 @@ def test_q3_k_bruteforce_and_dequantised_dot(orc):
         assert y[r] == np.float32(acc)
 
 
+# -------------------------------------------------------------------- NVFP4
+def _nvfp4_gold():
+    return json.load(open(os.path.join(GOLD, "nvfp4.json")))
+
+
+def test_nvfp4_e2m1_value_table(orc):
+    """Every FP4 E2M1 code decodes to the published value table (sign bit 3)."""
+    g = _nvfp4_gold()
+    for c in range(16):
+        v = orc.e2m1(c)
+        assert v == g["e2m1"][c] and math.copysign(1.0, v) == math.copysign(1.0, g["e2m1"][c]), c
+
+
+def test_nvfp4_e4m3_values(orc):
+    """E4M3 scale bytes: zero, subnormals, the smallest normal, a mantissa, the largest finite,
+    a negative, and NaN at 0x7F / 0xFF."""
+    for e in _nvfp4_gold()["e4m3"]:
+        assert orc.e4m3(int(e["byte"], 16)) == e["value"], e
+    assert math.isnan(orc.e4m3(0x7F)) and math.isnan(orc.e4m3(0xFF))
+
+
+def _nvfp4_act(orc, case):
+    """The Q8_1 activation block of a golden case (d, the codes, and s = d * sum(q) in binary16)."""
+    j = np.arange(32)
+    q = (j - 16) if case["act_q"].startswith("q_j = j - 16") else np.where(j < 16, j + 1, 1)
+    a = np.zeros(36, dtype=np.uint8)
+    d16 = int(case["act_d"], 16)
+    a[0], a[1] = d16 & 0xFF, d16 >> 8
+    s16 = orc.f16_encode(orc.f16_decode(d16) * float(q.sum()))
+    a[2], a[3] = s16 & 0xFF, s16 >> 8
+    a[4:] = q.astype(np.int8).view(np.uint8)
+    return a
+
+
+def test_nvfp4_golden_blocks(orc):
+    """Hand-derived blocks pin the nibble order (2i low, 2i + 1 high), the per-half scales,
+    the sign bit, a subnormal scale, the half sums of 2 * e2m1 * q_a, the tap packing (half 0
+    in the low 16 bits) and the tensor scale."""
+    for case in _nvfp4_gold()["blocks"]:
+        w = np.array([int(b, 16) for b in case["block"].split()], dtype=np.uint8)
+        a = _nvfp4_act(orc, case)
+        h0, h1 = case["isum_half"]
+        assert orc.isum_nvfp4_half(w, a, 0) == h0, case["name"]
+        assert orc.isum_nvfp4_half(w, a, 1) == h1, case["name"]
+        y, tap = orc.row_dot_nvfp4(w, a, 1, case["tensor_scale"], with_isum=True)
+        assert y == np.float32(case["dot"]), (case["name"], y)
+        assert int(tap[0]) == np.int32(np.uint32((h0 & 0xFFFF) | ((h1 & 0xFFFF) << 16))), case["name"]
+        for j, v in case["dequant"].items():
+            assert orc.dequant_weight(40, w, int(j)) == v, (case["name"], j)
+
+
+def test_nvfp4_bruteforce_and_dequantised_dot(orc):
+    """Random rows: the half sums equal brute force over the golden E2M1 table and the
+    canonical nibble order; per block the fp64 dot of the dequantised weights (E2M1 x E4M3)
+    and activations is exact and equals the integer path; the row is their sum in block
+    order times the tensor scale, rounded once."""
+    table = np.array(_nvfp4_gold()["e2m1"])
+    rng = np.random.default_rng(41)
+    nblk, rows = 9, 4
+    W = rng.integers(0, 256, size=(rows * nblk, 18), dtype=np.uint8)
+    W[:, :2] = ((5 + rng.integers(0, 5, size=(rows * nblk, 2))) << 3 | rng.integers(0, 8, size=(rows * nblk, 2))).astype(np.uint8)
+    A = _rand_q8_1(orc, rng, nblk)
+    ts = 0.0037
+    for r in range(rows):
+        row = W[r * nblk:(r + 1) * nblk]
+        y, tap = orc.row_dot_nvfp4(row.reshape(-1), A.reshape(-1), nblk, ts, with_isum=True)
+        acc = 0.0
+        for b in range(nblk):
+            wb, a = row[b], A[b]
+            codes = np.stack([wb[2:] & 0x0F, wb[2:] >> 4], axis=1).reshape(-1)   # element order
+            qa = a[4:].view(np.int8).astype(np.int64)
+            halves = [int(np.dot((2 * table[codes[16 * h:16 * h + 16]]).astype(np.int64),
+                                 qa[16 * h:16 * h + 16])) for h in (0, 1)]
+            assert orc.isum_nvfp4_half(wb, a, 0) == halves[0]
+            assert orc.isum_nvfp4_half(wb, a, 1) == halves[1]
+            assert int(tap[b]) == np.int32(np.uint32((halves[0] & 0xFFFF) | ((halves[1] & 0xFFFF) << 16)))
+            da = orc.f16_decode(int(a[0]) | int(a[1]) << 8)
+            part = math.fsum(orc.dequant_weight(40, wb, j) * da * int(qa[j]) for j in range(32))
+            assert part == da * (orc.e4m3(int(wb[0])) * halves[0] + orc.e4m3(int(wb[1])) * halves[1]) / 2
+            acc += part
+        assert y == np.float32(acc * ts)
+
+
 @pytest.mark.parametrize("fmt", [8, 2])
 def test_dequantised_fp64_dot_equals_int_path_per_block(orc, fmt):
     """Per block, the fp64 dot of the dequantised weights and activations is exact and equals
@@ -764,9 +847,14 @@ def test_token_list_matches_full_run(orc, synth):
     assert np.array_equal(part, full[[6, 2]])
 
 
-def _dequant_rows(orc, fmt, blocks, rows, nblk):
+def _dequant_rows(orc, fmt, blocks, rows, nblk, tensor_scale=1.0):
     bb = 34 if fmt == 8 else 18
     B = blocks.reshape(rows * nblk, bb)
+    if fmt == 40:
+        table = np.array(_nvfp4_gold()["e2m1"])
+        codes = np.stack([B[:, 2:] & 0x0F, B[:, 2:] >> 4], axis=2).reshape(rows * nblk, 32)
+        sc = np.array([[orc.e4m3(int(b)) for b in blk[:2]] for blk in B])
+        return (tensor_scale * np.repeat(sc, 16, axis=1) * table[codes]).reshape(rows, nblk * 32)
     d = B[:, :2].copy().view(np.float16).astype(np.float64).reshape(-1)
     if fmt == 8:
         q = B[:, 2:].view(np.int8).astype(np.float64)
@@ -775,7 +863,7 @@ def _dequant_rows(orc, fmt, blocks, rows, nblk):
     return (d[:, None] * q).reshape(rows, nblk * 32)
 
 
-@pytest.mark.parametrize("latent,fmt", [(0, 8), (0, 2), (64, 8), (64, 2)])
+@pytest.mark.parametrize("latent,fmt", [(0, 8), (0, 2), (64, 8), (64, 2), (0, 40), (64, 40)])
 def test_layer_close_to_unquantised_float_layer(orc, synth, latent, fmt):
     """Sanity band: the quantised layer is within activation-quantisation error (about 1e-2
     relative) of the same layer in float64 with unquantised activations.  Catches transposed
@@ -805,9 +893,12 @@ def test_layer_close_to_unquantised_float_layer(orc, synth, latent, fmt):
             blob = inp["experts"][e * eb:(e + 1) * eb]
             bb = w.block_bytes
             n_gu = F * (kin // 32) * bb
-            G = _dequant_rows(orc, fmt, blob[:n_gu], F, kin // 32)
-            Uu = _dequant_rows(orc, fmt, blob[n_gu:2 * n_gu], F, kin // 32)
-            Dn = _dequant_rows(orc, fmt, blob[2 * n_gu:], kin, F // 32)
+            n_dn = kin * (F // 32) * bb
+            ts = blob[2 * n_gu + n_dn:2 * n_gu + n_dn + 12].view("<f4").astype(np.float64) \
+                if fmt == 40 else np.ones(3)
+            G = _dequant_rows(orc, fmt, blob[:n_gu], F, kin // 32, ts[0])
+            Uu = _dequant_rows(orc, fmt, blob[n_gu:2 * n_gu], F, kin // 32, ts[1])
+            Dn = _dequant_rows(orc, fmt, blob[2 * n_gu:2 * n_gu + n_dn], kin, F // 32, ts[2])
             g, u = G @ a, Uu @ a
             acc += float(taps["weights"][t, j]) * (Dn @ (g / (1 + np.exp(-g)) * u))
         ref[t] = Um @ acc if latent else acc
