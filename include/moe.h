@@ -83,7 +83,7 @@ typedef enum {
  * of scale * sum(code * q_a).
  * Q5_1, Q4_K, Q5_K and Q3_K are expert formats only. */
 enum { MOE_FMT_Q8_0 = 8, MOE_FMT_Q4_0 = 2, MOE_FMT_Q5_1 = 7, MOE_FMT_Q4_K = 12, MOE_FMT_Q5_K = 13,
-       MOE_FMT_Q3_K = 11 };
+       MOE_FMT_Q3_K = 11, MOE_FMT_NVFP4 = 40 };
 
 /* Which packed tensor a pack call is about. */
 enum { MOE_PACK_EXPERTS = 0, MOE_PACK_D = 1, MOE_PACK_U = 2 };
@@ -94,7 +94,7 @@ typedef struct {
     int32_t top_k;        /* k: 1..min(E, 32)                                             */
     int32_t n_ff;         /* F: expert intermediate width, multiple of 256                */
     int32_t latent;       /* L: 0 = plain MoE; else the latent width, multiple of 256     */
-    int32_t expert_fmt;   /* MOE_FMT_Q8_0, _Q4_0, _Q5_1, _Q4_K, _Q5_K or _Q3_K           */
+    int32_t expert_fmt;   /* MOE_FMT_Q8_0, _Q4_0, _Q5_1, _Q4_K, _Q5_K, _Q3_K or _NVFP4   */
     int32_t dense_fmt;    /* D/U format: MOE_FMT_Q8_0 or MOE_FMT_Q4_0 (latent == 0: unused)*/
     int32_t n_groups;     /* 0 = no group limit; else divides E                           */
     int32_t topk_groups;  /* groups kept per token: 1..n_groups, topk_groups*E/n_groups>=k*/
@@ -108,8 +108,16 @@ typedef struct moe_layer moe_layer;
  *   Q8_0 block = binary16 d (little-endian) + 32 int8 q              (34 bytes)
  *   Q4_0 block = binary16 d + 16 bytes; byte j: element j in the low nibble,
  *                element j+16 in the high nibble; value d*(c-8)       (18 bytes)
+ *   NVFP4 block of 32 (edge0-strata README, section "Changes from upstream
+ *          Strata", names NVFP4 latent experts; read as FP4 E2M1 codes, an
+ *          FP8 E4M3 scale per 16 elements and an fp32 scale per tensor) =
+ *          E4M3 scale of elements 0..15, E4M3 scale of 16..31, 16 bytes; byte
+ *          i: element 2i in the low nibble, 2i+1 in the high nibble     (18 bytes)
  *   EXPERTS: for e in 0..E-1: gate [F][Kin/32], up [F][Kin/32], down [Kout][F/32]
- *            blocks, rows row-major; Kin = Kout = latent ? L : H.
+ *            blocks, rows row-major; Kin = Kout = latent ? L : H.  An NVFP4
+ *            expert then holds a 256-byte tail: its tensor scales gate, up,
+ *            down (fp32), then zero bytes.  NVFP4 experts run the matrix-vector kernels only:
+ *            max_tokens <= 32.
  *   D: [L][H/32] Q8_0 blocks.  U: [H][L/32] Q8_0 blocks.
  * The packed (device) layout has the same byte count; it splits codes from
  * scales and orders gate/up rows in 32-row pairs.  It is private to the library.

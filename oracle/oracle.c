@@ -560,14 +560,14 @@ void orc_route_token(const orc_desc* d, const float* x, const float* Wr, const f
 /* Expert FFN and the layer [Q8], [E0]                                       */
 /* ------------------------------------------------------------------------ */
 
-/* An NVFP4 expert's blob ends with its tensor scales: gate, up, down (fp32,
- * little-endian) and four zero bytes [NV]. */
+/* An NVFP4 expert's blob ends with a 256-byte tail: its tensor scales gate, up,
+ * down (fp32, little-endian), then zero bytes [NV]. */
 static size_t expert_bytes(const orc_desc* d) {
     int kin = d->latent ? d->latent : d->hidden;
     int kout = kin;
     return 2 * d->n_ff * row_bytes(d->expert_fmt, kin / ORC_QK) +
            (size_t)kout * row_bytes(d->expert_fmt, d->n_ff / ORC_QK) +
-           (d->expert_fmt == ORC_NVFP4 ? 16 : 0);
+           (d->expert_fmt == ORC_NVFP4 ? 256 : 0);
 }
 
 static double rdf32(const uint8_t* p) {

@@ -19,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["mv_q8_0.hip", "mv_q4_0.hip", "mv_q5_1.hip", "mv_q4_k.hip", "mv_q5_k.hip", "mv_q3_k.hip",
+           "mv_nvfp4.hip",
            "mfma.hip", "thin.hip",
            "route.hip", "matvec.hip", "table.hip", "probe.hip", "capi.cpp"]
 ARCH = "gfx950"

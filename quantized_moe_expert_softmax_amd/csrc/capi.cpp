@@ -68,10 +68,10 @@ static bool mult(int v, int m) { return v > 0 && v % m == 0; }
 extern "C" moe_status moe_desc_check(const moe_desc* d) {
     if (!d) return fail(MOE_EINVAL, "desc is NULL");
     if (d->expert_fmt != MOE_FMT_Q8_0 && d->expert_fmt != MOE_FMT_Q4_0 &&
-        d->expert_fmt != MOE_FMT_Q5_1 && !kquant(d->expert_fmt))
+        d->expert_fmt != MOE_FMT_Q5_1 && !kquant(d->expert_fmt) && d->expert_fmt != MOE_FMT_NVFP4)
         return fail(MOE_EUNSUPPORTED,
                     "expert_fmt %d is none of Q8_0 (8), Q4_0 (2), Q5_1 (7), Q4_K (12), Q5_K (13), "
-                    "Q3_K (11)",
+                    "Q3_K (11), NVFP4 (40)",
                     d->expert_fmt);
     // edge0-strata README, changes from upstream Strata: the latent D/U
     // projections come in Q8 or Q4 (the Q4 rows kernel there is Q4_0 x Q8_1)
@@ -105,6 +105,10 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     }
     if (d->max_tokens < 1 || d->max_tokens > 65536)
         return fail(MOE_EINVAL, "max_tokens %d out of range 1..65536", d->max_tokens);
+    // (no matrix-core kernel reads NVFP4 blocks: its layers stay on the decode path)
+    if (d->expert_fmt == MOE_FMT_NVFP4 && d->max_tokens > MV_MAX_T)
+        return fail(MOE_EUNSUPPORTED, "NVFP4 experts run the matrix-vector kernels only: "
+                    "max_tokens %d must be at most %d", d->max_tokens, MV_MAX_T);
     const int kin = d->latent ? d->latent : d->hidden;
     if (!mv_config_ok(kin, d->expert_fmt, true))
         return fail(MOE_EUNSUPPORTED, "no gate/up kernel for %d-wide %s rows", kin,
@@ -113,6 +117,7 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
                     : d->expert_fmt == MOE_FMT_Q4_K ? "Q4_K"
                     : d->expert_fmt == MOE_FMT_Q5_K ? "Q5_K"
                     : d->expert_fmt == MOE_FMT_Q3_K ? "Q3_K"
+                    : d->expert_fmt == MOE_FMT_NVFP4 ? "NVFP4"
                                                     : "Q8_0");
     if (!mv_config_ok(d->n_ff, d->expert_fmt, false))
         return fail(MOE_EUNSUPPORTED, "no down kernel for %d-wide rows", d->n_ff);
@@ -279,6 +284,26 @@ static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t*
                     q3_k_to_packed(c, codes + ppos * cb, scales + sb * ppos);
                 else
                     q3_k_to_canonical(codes + ppos * cb, scales + sb * ppos, c);
+            } else if (M.fmt == MOE_FMT_NVFP4) {
+                // canonical byte 2 + i: elements 2i (low nibble), 2i + 1 (high);
+                // packed byte j: elements j (low), j + 16 (high), as Q4_0
+                uint8_t* pc = codes + ppos * cb;
+                if (to_packed) {
+                    memcpy(scales + sb * ppos, c, 2);
+                    for (int j = 0; j < 16; ++j) {
+                        const int lo = (c[2 + j / 2] >> (4 * (j & 1))) & 15;
+                        const int hi = (c[2 + (j + 16) / 2] >> (4 * (j & 1))) & 15;
+                        pc[j] = (uint8_t)(lo | hi << 4);
+                    }
+                } else {
+                    memcpy(c, scales + sb * ppos, 2);
+                    for (int i = 0; i < 16; ++i) {
+                        const int e0 = 2 * i, e1 = 2 * i + 1;
+                        const int c0 = e0 < 16 ? pc[e0] & 15 : pc[e0 - 16] >> 4;
+                        const int c1 = e1 < 16 ? pc[e1] & 15 : pc[e1 - 16] >> 4;
+                        c[2 + i] = (uint8_t)(c0 | c1 << 4);
+                    }
+                }
             } else if (to_packed) {
                 memcpy(scales + sb * ppos, c, sb);
                 memcpy(codes + ppos * cb, c + sb, cb);
@@ -293,6 +318,13 @@ static void convert_matrix(const MatLayout& M, RowMap map, int F, const uint8_t*
 static void convert_expert(const Dims& m, const uint8_t* canon, uint8_t* packed, bool to_packed) {
     convert_matrix(m.gu, gate_up_row, m.F, canon, packed, to_packed);
     convert_matrix(m.dn, identity_row, m.F, canon + m.gu.bytes(), packed + m.dn_off, to_packed);
+    if (m.ts_off) {
+        // NVFP4 tensor scales: the same 256-byte tail in both forms
+        if (to_packed)
+            memcpy(packed + m.ts_off, canon + m.ts_off, 256);
+        else
+            memcpy(const_cast<uint8_t*>(canon) + m.ts_off, packed + m.ts_off, 256);
+    }
 }
 
 static moe_status convert(const moe_desc* d, int which, const void* src, void* dst, bool to_packed) {

@@ -98,6 +98,44 @@ __device__ __forceinline__ int dot_q4(const v4i& w, const v4i& a_lo, const v4i& 
     return dot4((w.w >> 4) & m, a_hi.w, s);
 }
 
+// NVFP4 (edge0-strata README, section "Changes from upstream Strata", NVFP4
+// latent experts; the format read as FP4 E2M1 codes with an FP8 E4M3 scale per
+// 16 elements and an fp32 scale per tensor).  Four codes, one per byte (0..15),
+// become four int8 values 2 * e2m1(code): 0, 1, 2, 3, 4, 6, 8, 12 for the low
+// three bits, negated when bit 3 is set.  v_perm looks the magnitude up in an
+// 8-byte table (selector bytes 0..3 pick the low word, 4..7 the high word), a
+// second lookup in the negated table gives the negative, and bit 3 selects.
+__device__ __forceinline__ int e2m1x2_widen(uint32_t nib) {
+    const uint32_t sel = nib & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sel);
+    const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sel);
+    const uint32_t m = ((nib >> 3) & 0x01010101u) * 0xFFu;
+    return (int)((pos & ~m) | (neg & m));
+}
+
+// The two 16-element half sums of an NVFP4 chunk (byte j: element j in the low
+// nibble, j + 16 in the high) against its Q8_1 codes: sum 2 * e2m1(c) * q_a.
+__device__ __forceinline__ void dot_nv4(const v4i& w, const v4i& a_lo, const v4i& a_hi, int& s0, int& s1) {
+    const uint32_t m = 0x0F0F0F0Fu;
+    s0 = dot4(e2m1x2_widen((uint32_t)w.x & m), a_lo.x, 0);
+    s0 = dot4(e2m1x2_widen((uint32_t)w.y & m), a_lo.y, s0);
+    s0 = dot4(e2m1x2_widen((uint32_t)w.z & m), a_lo.z, s0);
+    s0 = dot4(e2m1x2_widen((uint32_t)w.w & m), a_lo.w, s0);
+    s1 = dot4(e2m1x2_widen(((uint32_t)w.x >> 4) & m), a_hi.x, 0);
+    s1 = dot4(e2m1x2_widen(((uint32_t)w.y >> 4) & m), a_hi.y, s1);
+    s1 = dot4(e2m1x2_widen(((uint32_t)w.z >> 4) & m), a_hi.z, s1);
+    s1 = dot4(e2m1x2_widen(((uint32_t)w.w >> 4) & m), a_hi.w, s1);
+}
+
+// An FP8 E4M3 byte as float, exactly: bit 7 the sign, bits 6..3 the exponent
+// (bias 7; 0 is subnormal, m * 2^-9), bits 2..0 the mantissa.  (0x7F / 0xFF,
+// NaN in E4M3, decode as 480: non-finite input gives unspecified output.)
+__device__ __forceinline__ float e4m3f(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -v : v;
+}
+
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll

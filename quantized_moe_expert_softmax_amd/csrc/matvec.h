@@ -30,6 +30,7 @@ struct GUArgs {
     SelectArgs route;     // route.part != null: one token, routed in the prologue
     RouteOut rout;
     int ids_slots;        // 1: the slots come from b.ids (T * k <= DECODE_T * 32), not buckets
+    size_t ts_off;        // NVFP4: the tensor scales (gate, up fp32) in an expert pack; else 0
 };
 
 
@@ -51,6 +52,7 @@ struct RowsArgs {
     int tap_div;               // token of act row s = s / tap_div
     int32_t* isum_tap;         // [act row][rows][K/32]
     int tap_tokens;
+    size_t ts_off;             // expert mode, NVFP4: the down tensor scale in a pack; else 0
 };
 
 // ---------------------------------------------------------------------------
@@ -69,6 +71,7 @@ struct DownTokArgs {
     Taps taps;
     const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
     ActPtr outq;                  // q != null: also Q8_1 of out (32-row tiles; not with etab)
+    size_t ts_off;                // NVFP4: the down tensor scale in an expert pack; else 0
 };
 
 constexpr int DT_RT = 16;    // output rows per workgroup

@@ -82,6 +82,7 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
     a.tch = pick_tch(m.kin);
     a.ain = ain; a.ain_f32 = ain_f32; a.keep = keep;
     a.b = b; a.hq = hq; a.taps = taps;
+    a.ts_off = m.ts_off;
     size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 64 * 4 + (size_t)a.tch * 8;
     a.route = SelectArgs{};
     a.rout = RouteOut{};
@@ -121,6 +122,9 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
     if (m.fmt == MOE_FMT_Q3_K)
         return tap ? gate_up_fmt<MOE_FMT_Q3_K, true>(lpr, cpl, grid, lds, a, st, ev)
                    : gate_up_fmt<MOE_FMT_Q3_K, false>(lpr, cpl, grid, lds, a, st, ev);
+    if (m.fmt == MOE_FMT_NVFP4)
+        return tap ? gate_up_fmt<MOE_FMT_NVFP4, true>(lpr, cpl, grid, lds, a, st, ev)
+                   : gate_up_fmt<MOE_FMT_NVFP4, false>(lpr, cpl, grid, lds, a, st, ev);
     return tap ? gate_up_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st, ev)
                : gate_up_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st, ev);
 }
@@ -158,6 +162,9 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (fmt == MOE_FMT_Q3_K)
         return tap ? rows_fmt<MOE_FMT_Q3_K, true>(lpr, cpl, grid, lds, a, st)
                    : rows_fmt<MOE_FMT_Q3_K, false>(lpr, cpl, grid, lds, a, st);
+    if (fmt == MOE_FMT_NVFP4)
+        return tap ? rows_fmt<MOE_FMT_NVFP4, true>(lpr, cpl, grid, lds, a, st)
+                   : rows_fmt<MOE_FMT_NVFP4, false>(lpr, cpl, grid, lds, a, st);
     return tap ? rows_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, grid, lds, a, st)
                : rows_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, grid, lds, a, st);
 }
@@ -173,6 +180,7 @@ hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr h
     a.rows = m.kout; a.K = m.F; a.T = T;
     a.b = b; a.ain = hq; a.ain_f32 = nullptr; a.keep = ActPtr{}; a.out = y;
     a.tap_div = m.k; a.isum_tap = taps.isum_dn; a.tap_tokens = taps.tap_tokens;
+    a.ts_off = m.ts_off ? m.ts_off + 8 : 0;     // NVFP4: the down tensor scale
     return rows_dispatch(m.fmt, std::min(m.E, T * m.k), a, st);
 }
 
@@ -221,6 +229,7 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     a.F = m.F; a.Kout = m.kout; a.k = m.k;
     a.hq = hq; a.b = b; a.out = out; a.taps = taps;
     a.outq = outq;
+    a.ts_off = m.ts_off ? m.ts_off + 8 : 0;     // NVFP4: the down tensor scale
     bool tap = taps.isum_dn || taps.y;
     if (kq) {
         const size_t lds = (size_t)m.k * (m.F + 8 * (m.F / QK));
@@ -239,6 +248,9 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     if (m.fmt == MOE_FMT_Q5_1)
         return tap ? down_tok_fmt<MOE_FMT_Q5_1, true>(lpr, cpl, T, a, st)
                    : down_tok_fmt<MOE_FMT_Q5_1, false>(lpr, cpl, T, a, st);
+    if (m.fmt == MOE_FMT_NVFP4)
+        return tap ? down_tok_fmt<MOE_FMT_NVFP4, true>(lpr, cpl, T, a, st)
+                   : down_tok_fmt<MOE_FMT_NVFP4, false>(lpr, cpl, T, a, st);
     return tap ? down_tok_fmt<MOE_FMT_Q8_0, true>(lpr, cpl, T, a, st)
                : down_tok_fmt<MOE_FMT_Q8_0, false>(lpr, cpl, T, a, st);
 }

@@ -40,6 +40,7 @@ struct Fmt {
     static constexpr bool K5 = FMT == MOE_FMT_Q5_K;
     static constexpr bool K4 = FMT == MOE_FMT_Q4_K || K5;      // super-blocks of 256
     static constexpr bool K3 = FMT == MOE_FMT_Q3_K;            // super-blocks of 256
+    static constexpr bool NV4 = FMT == MOE_FMT_NVFP4;          // two E4M3 scales per block
     static constexpr int QB = NIB ? 16 : 32;                  // code bytes per block of 32
     static constexpr int CPB = NIB ? 1 : 2;                   // chunks per block of 32
     static constexpr int SBLK = K4 || K3 ? 8 : 1;             // blocks of 32 per side-data unit
@@ -319,6 +320,18 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
                         }
                     }
                 }
+            } else if constexpr (F::NV4) {
+                // the two halves' sums times their E4M3 scales, times d_a / 2
+                const v4i lo = *reinterpret_cast<const v4i*>(arow + c * 32);
+                const v4i hi = *reinterpret_cast<const v4i*>(arow + c * 32 + 16);
+                int i0, i1;
+                dot_nv4(wq[j], lo, hi, i0, i1);
+                const float dh = valid ? 0.5f * ad[c] : 0.0f;
+                acc = fmaf((float)i0, e4m3f(wsc[j] & 0xFFu) * dh, acc);
+                acc = fmaf((float)i1, e4m3f((wsc[j] >> 8) & 0xFFu) * dh, acc);
+                if constexpr (TAP) {
+                    if (tap && valid) emit_isum(i, r, c, (int)(((uint32_t)i0 & 0xFFFFu) | ((uint32_t)i1 << 16)));
+                }
             } else {
                 const int blk = c / F::CPB;
                 const int is = chunk_isum_lds<FMT>(wq[j], wsc[j], arow, asq, c);
@@ -500,6 +513,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     const size_t rowb = Fmt<FMT>::row_bytes(nb);
     const uint8_t* ebase = expert_pack(A.experts, A.etab, e, A.eb);
     const uint8_t* codes = ebase + (size_t)fb * 64 * rowb;
+    float tsg = 1.0f, tsu = 1.0f;
+    if constexpr (Fmt<FMT>::NV4) {
+        tsg = reinterpret_cast<const float*>(ebase + A.ts_off)[0];
+        tsu = reinterpret_cast<const float*>(ebase + A.ts_off)[1];
+    }
     using SM = typename Fmt<FMT>::SideMem;
     const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * (nb / Fmt<FMT>::SBLK);
 
@@ -534,7 +552,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
             stage_q<Fmt<FMT>::Q5>(A.ain, K, s_t, n, s_q, s_d, s_sq);
         __syncthreads();
         const bool tap = TAP && A.taps.isum_gu;
-        auto emit = [&](int i, int r, float v) { s_gu[i * 64 + r] = v; };
+        auto emit = [&](int i, int r, float v) {
+            // NVFP4: the gate (rows 0..31 of the slab) or up tensor scale
+            s_gu[i * 64 + r] = Fmt<FMT>::NV4 ? v * (r < 32 ? tsg : tsu) : v;
+        };
         auto emit_isum = [&](int i, int r, int blk, int v) {
             if (s_t[i] < A.taps.tap_tokens) {
                 const int row = r < 32 ? fb * 32 + r : A.F + fb * 32 + (r - 32);
@@ -587,6 +608,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     const int K = A.K, nb = K / QK, TCH = A.tch;
     const size_t rowb = Fmt<FMT>::row_bytes(nb);
     const uint8_t* codes = mat + A.codes_off + (size_t)rt * A.rt * rowb;
+    // NVFP4 expert mode: the matrix's tensor scale
+    const float tsr = Fmt<FMT>::NV4 && A.ts_off ? *reinterpret_cast<const float*>(mat + A.ts_off) : 1.0f;
     using SM = typename Fmt<FMT>::SideMem;
     const SM* scl = reinterpret_cast<const SM*>(mat + A.scales_off) + (size_t)rt * A.rt * (nb / Fmt<FMT>::SBLK);
     int8_t* s_q = reinterpret_cast<int8_t*>(smem);
@@ -614,7 +637,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
             stage_q<Fmt<FMT>::Q5>(A.ain, K, s_s, n, s_q, s_d, s_sq);
         __syncthreads();
         const int r0 = rt * A.rt;
-        auto emit = [&](int i, int r, float v) { A.out[(size_t)s_s[i] * A.rows + r0 + r] = v; };
+        auto emit = [&](int i, int r, float v) { A.out[(size_t)s_s[i] * A.rows + r0 + r] = v * tsr; };
         auto emit_isum = [&](int i, int r, int blk, int v) {
             if (s_s[i] / A.tap_div < A.tap_tokens)
                 A.isum_tap[((size_t)s_s[i] * A.rows + r0 + r) * nb + blk] = v;
@@ -648,8 +671,11 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
     for (int j = wave; j < A.k; j += DT_NW) {
         const int a = t * A.k + j;
         const int e = A.b.ids[a];
-        const uint8_t* mat = (TABLE ? expert_pack(nullptr, A.etab, e, 0) : A.experts + (size_t)e * A.eb) + A.dn_off;
+        const uint8_t* ebase = TABLE ? expert_pack(nullptr, A.etab, e, 0) : A.experts + (size_t)e * A.eb;
+        const uint8_t* mat = ebase + A.dn_off;
         const uint8_t* codes = mat + (size_t)rt * RT * rowb;
+        // NVFP4: the down matrix's tensor scale
+        const float tsd = F::NV4 ? *reinterpret_cast<const float*>(ebase + A.ts_off) : 1.0f;
         using SM = typename F::SideMem;
         const SM* scl = reinterpret_cast<const SM*>(mat + A.dn_scales_off) + (size_t)rt * RT * (nb / F::SBLK);
         v4i wq[CPL], wn[CPL];
@@ -680,13 +706,24 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
                 const int c = jj * LPR + sl;
                 const bool valid = c < NCH;
                 int is;
-                if constexpr (F::Q5)
-                    is = dot_q5(wq[jj], wsc[jj].y, act[jj][0], act[jj][NA - 1]);
-                else if constexpr (F::CPB == 1)
-                    is = dot_q4(wq[jj], act[jj][0], act[jj][NA - 1]) - 8 * asq[jj];
-                else
-                    is = dot16(wq[jj], act[jj][0]);
-                acc = fmaf((float)is, valid ? h2f(side_d(wsc[jj])) * h2f(ads[jj]) : 0.0f, acc);
+                if constexpr (F::NV4) {
+                    // two halves, each with its E4M3 scale, times d_a / 2; the
+                    // tap holds both sums (half 0 in the low 16 bits)
+                    int i0, i1;
+                    dot_nv4(wq[jj], act[jj][0], act[jj][NA - 1], i0, i1);
+                    const float dh = valid ? 0.5f * h2f(ads[jj]) : 0.0f;
+                    acc = fmaf((float)i0, e4m3f(wsc[jj] & 0xFFu) * dh, acc);
+                    acc = fmaf((float)i1, e4m3f((wsc[jj] >> 8) & 0xFFu) * dh, acc);
+                    is = (int)(((uint32_t)i0 & 0xFFFFu) | ((uint32_t)i1 << 16));
+                } else {
+                    if constexpr (F::Q5)
+                        is = dot_q5(wq[jj], wsc[jj].y, act[jj][0], act[jj][NA - 1]);
+                    else if constexpr (F::CPB == 1)
+                        is = dot_q4(wq[jj], act[jj][0], act[jj][NA - 1]) - 8 * asq[jj];
+                    else
+                        is = dot16(wq[jj], act[jj][0]);
+                    acc = fmaf((float)is, valid ? h2f(side_d(wsc[jj])) * h2f(ads[jj]) : 0.0f, acc);
+                }
                 if constexpr (F::Q5) {
                     // min term: m_w times the block's stored s
                     acc = fmaf(valid ? h2f(wsc[jj].x >> 16) : 0.0f, h2f(ads[jj] >> 16), acc);
@@ -701,7 +738,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
                 }
             }
             const float y = group_sum_fast<LPR>(acc);
-            if (sl == 0) s_y[j][r] = y;
+            if (sl == 0) s_y[j][r] = F::NV4 ? y * tsd : y;
 #pragma unroll
             for (int jj = 0; jj < CPL; ++jj) {
                 wq[jj] = wn[jj];

@@ -65,6 +65,8 @@ struct Dims {
     int H, E, k, F, L, kin, kout, fmt, dfmt, G, TG, max_tokens;
     MatLayout gu, dn;               // offsets within one expert
     size_t dn_off;                  // byte offset of the down matrix in an expert
+    size_t ts_off;                  // NVFP4: of the tensor scales (gate, up, down fp32), the
+                                    // start of a 256-byte tail (packs stay 256-byte multiples); else 0
     size_t expert_bytes;
     MatLayout D, U;                 // latent dense projections
 };
@@ -80,6 +82,11 @@ inline Dims make_dims(const moe_desc& d) {
     m.dn = mat_layout(m.kout, m.F / QK, m.fmt);
     m.dn_off = m.gu.bytes();
     m.expert_bytes = m.gu.bytes() + m.dn.bytes();
+    m.ts_off = 0;
+    if (m.fmt == MOE_FMT_NVFP4) {
+        m.ts_off = m.expert_bytes;
+        m.expert_bytes += 256;
+    }
     if (m.L) {
         m.D = mat_layout(m.L, m.H / QK, m.dfmt);
         m.U = mat_layout(m.H, m.L / QK, m.dfmt);

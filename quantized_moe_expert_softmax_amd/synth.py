@@ -28,8 +28,8 @@ element j + 16 (18 B); NVFP4 = the E4M3 scales of elements 0..15 and
 16..31, then 16 bytes whose byte i holds element 2i in its low nibble and
 element 2i + 1 in its high nibble (18 B).  A canonical expert blob holds gate
 [F][Kin/32], up [F][Kin/32] and down [Kout][F/32] blocks, in that order, rows
-row-major; an NVFP4 blob ends with the three tensor scales (fp32) and four
-zero bytes.
+row-major; an NVFP4 blob ends with a 256-byte tail: the three tensor scales
+(fp32), then zero bytes.
 """
 from __future__ import annotations
 
@@ -55,7 +55,7 @@ NVFP4 = 40
 # bytes per 32 elements (Q4_K / Q5_K: 144 / 176-byte super-blocks of 256)
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q5_1: 24, Q4_K: 18, Q5_K: 22, NVFP4: 18}
 # bytes after an expert's three matrices (NVFP4: the tensor scales)
-EXPERT_TAIL = {NVFP4: 16}
+EXPERT_TAIL = {NVFP4: 256}
 # bytes per super-block of 256 elements
 SUPER_BYTES = {Q4_K: 144, Q5_K: 176, Q3_K: 110}
 
@@ -329,7 +329,7 @@ def gen_expert(w: Workload, e: int, out: Optional[np.ndarray] = None) -> np.ndar
     if w.expert_fmt == NVFP4:
         ts = (0.002 + absnormal_f64(w.seed, S_EXP_D + 4 * e + 3, 3, 0.002)).astype(np.float32)
         out[off:off + 12] = ts.view(np.uint8)
-        out[off + 12:off + 16] = 0
+        out[off + 12:off + 256] = 0
     return out
 
 

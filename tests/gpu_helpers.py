@@ -289,6 +289,10 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
             y_gu, is_gu = oracle.matvec(w.expert_fmt, blob[:ngu], 2 * F, nbi, ain[t].reshape(-1),
                                         with_isum=True)
             assert np.array_equal(g["isum_gu"][a], is_gu), (t, j)
+            # NVFP4: the tensor scales (gate, up, down) at the start of the expert's tail
+            ts = (blob[eb - 256:eb - 244].view("<f4").astype(np.float64)
+                  if w.expert_fmt == synth.NVFP4 else np.ones(3))
+            y_gu = np.concatenate([y_gu[:F] * ts[0], y_gu[F:] * ts[1]]).astype(np.float32)
             # h from the oracle's g and u on the GPU's own input: fp32 order only
             gg, uu = y_gu[:F].astype(np.float64), y_gu[F:].astype(np.float64)
             h_own = (gg / (1.0 + np.exp(-gg)) * uu).astype(np.float32)
@@ -296,7 +300,7 @@ def check_case(w: synth.Workload, T: int, tokens=None, tap_tokens: int = 4, batc
             y_dn, is_dn = oracle.matvec(w.expert_fmt, blob[ngu:], kout, nbf,
                                         g["hq"][a].reshape(-1), with_isum=True)
             assert np.array_equal(g["isum_dn"][a], is_dn), (t, j)
-            assert rel_max(g["y"][a], y_dn) < 1e-5
+            assert rel_max(g["y"][a], (y_dn * ts[2]).astype(np.float32)) < 1e-5
     if w.latent and tt:
         H, L = w.hidden, w.latent
         z_ref, iss = dense_isums(w.dense_fmt, inp["D"], L, H // 32, g["xq"][:tt])

@@ -34,7 +34,12 @@ def test_exports_match_header(L):
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_descs_valid(L, name):
     w = synth.WORKLOADS[name]
-    moe.moe_desc_check(moe.desc_of(w, max_tokens=2048))
+    if w.expert_fmt == synth.NVFP4:
+        # NVFP4 experts run the matrix-vector kernels only: up to 32 tokens
+        moe.moe_desc_check(moe.desc_of(w, max_tokens=32))
+        _refused(moe.desc_of(w, max_tokens=33), moe.MOE_EUNSUPPORTED, "max_tokens")
+    else:
+        moe.moe_desc_check(moe.desc_of(w, max_tokens=2048))
 
 
 def _refused(desc, status, word):
@@ -96,8 +101,9 @@ def _small(fmt=8, latent=0):
                           latent=latent, expert_fmt=fmt, seed=77)
 
 
-@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (13, 0), (11, 0), (8, 256),
-                                        (2, 256), (7, 256), (12, 256), (13, 256), (11, 256)])
+@pytest.mark.parametrize("fmt,latent", [(8, 0), (2, 0), (7, 0), (12, 0), (13, 0), (11, 0), (40, 0),
+                                        (8, 256), (2, 256), (7, 256), (12, 256), (13, 256), (11, 256),
+                                        (40, 256)])
 def test_pack_roundtrip(L, fmt, latent):
     w = _small(fmt, latent)
     d = moe.desc_of(w)
@@ -116,6 +122,36 @@ def test_pack_roundtrip(L, fmt, latent):
             b = np.zeros_like(t)
             moe.moe_unpack_host(d, which, p.ctypes.data, b.ctypes.data)
             assert np.array_equal(b, t)
+
+
+def test_pack_layout_nvfp4(L):
+    """The packed NVFP4 layout: each row's 16-byte code chunks hold element j in the low
+    nibble and j + 16 in the high nibble (canonical: 2i low, 2i + 1 high), the two E4M3 scale
+    bytes of each block follow all the codes, gate/up rows interleave in 32-row tiles, and the
+    expert's 256-byte tail (tensor scales, then zeros) is copied unchanged."""
+    w = _small(40)
+    d = moe.desc_of(w)
+    ex = synth.gen_experts(w)
+    packed = np.empty_like(ex)
+    moe.moe_pack_host(d, moe.MOE_PACK_EXPERTS, ex.ctypes.data, packed.ctypes.data)
+    eb, F, nb = w.expert_bytes, w.n_ff, w.k_in // 32
+    rows = 2 * F
+    for e in (0, 2):
+        c = ex[e * eb:(e + 1) * eb]
+        p = packed[e * eb:(e + 1) * eb]
+        for prow in (0, 31, 32, 63, 64, 130, rows - 1):
+            fb, r = divmod(prow, 64)
+            crow = fb * 32 + r if r < 32 else F + fb * 32 + (r - 32)
+            for b in (0, nb - 1):
+                blk = c[(crow * nb + b) * 18:(crow * nb + b + 1) * 18]
+                el = [(blk[2 + i // 2] >> (4 * (i % 2))) & 15 for i in range(32)]
+                want = np.array([el[j] | el[j + 16] << 4 for j in range(16)], dtype=np.uint8)
+                assert np.array_equal(p[(prow * nb + b) * 16:(prow * nb + b + 1) * 16], want)
+                so = rows * nb * 16 + (prow * nb + b) * 2
+                assert np.array_equal(p[so:so + 2], blk[:2])
+        assert np.array_equal(p[eb - 256:], c[eb - 256:])
+        assert np.all(c[eb - 244:] == 0) and np.all(c[eb - 256:eb - 244].view("<f4") > 0)
+        assert eb % 256 == 0
 
 
 @pytest.mark.parametrize("fmt", [8, 2, 7])

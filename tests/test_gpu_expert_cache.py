@@ -20,10 +20,11 @@ sys.path.insert(0, __file__.rsplit("/", 1)[0])
 import gpu_helpers as gh  # noqa: E402
 
 # decode (selection in the gate/up prologue), the per-token down kernel, the
-# per-slot rows kernels (K-quants), the grouped matrix-core path (T > 32) and
-# the latent path
+# per-slot rows kernels (K-quants), the grouped matrix-core path (T > 32), the
+# latent path, and NVFP4 experts (per-token and per-slot down)
 CASES = [("tiny", 4), ("tiny", 64), ("decode", 1), ("decode", 6), ("latent_q4", 1),
-         ("latent_q8", 40), ("decode_q4_k", 1), ("decode_q3_k", 40)]
+         ("latent_q8", 40), ("decode_q4_k", 1), ("decode_q3_k", 40), ("latent_nvfp4", 6),
+         ("decode_nvfp4", 20)]
 
 
 def _setup(name, T):

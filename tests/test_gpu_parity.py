@@ -244,6 +244,37 @@ def test_q3_k_experts(kw):
     _report("q3_k " + str(kw), w.tokens, rep)
 
 
+# NVFP4 experts (E2M1 codes, an E4M3 scale per 16 elements, an fp32 scale per
+# tensor; matrix-vector kernels only, up to 32 tokens): decode, a verify window
+# with groups (slots from the routing ids), the 9..32-token path (per-bucket
+# down), 32 tokens, latent layers, decode-sized rows
+@pytest.mark.parametrize("kw", [
+    dict(expert_fmt=synth.NVFP4, tokens=1),
+    dict(expert_fmt=synth.NVFP4, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
+    dict(expert_fmt=synth.NVFP4, tokens=20, bias=True),
+    dict(expert_fmt=synth.NVFP4, tokens=32),
+    dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, n_groups=4, topk_groups=2,
+         tokens=1),
+    dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, tokens=6),
+    dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, tokens=24),
+    dict(expert_fmt=synth.NVFP4, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
+    dict(expert_fmt=synth.NVFP4, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=6),
+])
+def test_nvfp4_experts(kw):
+    w = _variant(**kw)
+    rep = gh.check_case(w, w.tokens, tap_tokens=min(w.tokens, 3))
+    _report("nvfp4 " + str(kw), w.tokens, rep)
+
+
+# the full-size NVFP4 layers: decode shapes and the latent_q4 shapes
+@pytest.mark.parametrize("name,T", [("decode_nvfp4", 1), ("decode_nvfp4", 6), ("latent_nvfp4", 1),
+                                    ("latent_nvfp4", 32)])
+def test_nvfp4_layers(name, T):
+    layer, inp = _layer(name, 32)
+    rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp)
+    _report(name, T, rep)
+
+
 # path boundaries (single-token routing at T = 1, the per-token selection kernel with
 # bucketing up to 32 tokens, matrix-vector experts up to 32)
 # and the largest routing sizes the ABI accepts
