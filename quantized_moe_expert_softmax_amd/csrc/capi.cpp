@@ -105,10 +105,6 @@ extern "C" moe_status moe_desc_check(const moe_desc* d) {
     }
     if (d->max_tokens < 1 || d->max_tokens > 65536)
         return fail(MOE_EINVAL, "max_tokens %d out of range 1..65536", d->max_tokens);
-    // (no matrix-core kernel reads NVFP4 blocks: its layers stay on the decode path)
-    if (d->expert_fmt == MOE_FMT_NVFP4 && d->max_tokens > MV_MAX_T)
-        return fail(MOE_EUNSUPPORTED, "NVFP4 experts run the matrix-vector kernels only: "
-                    "max_tokens %d must be at most %d", d->max_tokens, MV_MAX_T);
     const int kin = d->latent ? d->latent : d->hidden;
     if (!mv_config_ok(kin, d->expert_fmt, true))
         return fail(MOE_EUNSUPPORTED, "no gate/up kernel for %d-wide %s rows", kin,
@@ -486,7 +482,10 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     const bool down_tok = T <= (kquant(m.fmt) ? DOWN_TOK_KQ_MAX_T : DOWN_TOK_MAX_T);
     // many tokens: grouped matrix-core GEMMs over token tiles
-    const bool gemm = T > MV_MAX_T;
+    const bool dense_gemm = T > MV_MAX_T;
+    // (NVFP4 experts have no matrix-core kernel: they stay on the matrix-vector
+    // kernels, per bucket, at every T; their D/U still take the matrix cores)
+    const bool gemm = dense_gemm && m.fmt != MOE_FMT_NVFP4;
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel
@@ -495,7 +494,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     // (measured on MI355X against the matrix-vector kernels, us per stage:
     // latent Q4_0 experts at T = 32, D 75 -> 17 and U 42 -> 15; latent Q8_0
     // experts at T = 6, D 15 -> 12 and U 10 -> 8)
-    const bool thin = m.L && !gemm && T >= THIN_MIN_T && dense_thin_ok(m.D, T) && dense_thin_ok(m.U, T);
+    const bool thin = m.L && !dense_gemm && T >= THIN_MIN_T && dense_thin_ok(m.D, T) && dense_thin_ok(m.U, T);
     if (taps && down_tok) tp.y = taps->y;
     const ActPtr none{nullptr, nullptr, nullptr};
 
@@ -527,7 +526,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
         // z = D . Q8_1(x), fp32
-        if (gemm) {
+        if (dense_gemm) {
             CK(launch_dense_mfma(m.D, (const uint8_t*)Dp, T, xq, z, tp.isum_d, tp.tap_tokens, st), "D");
             CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         } else if (thin) {
@@ -587,7 +586,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
         // Q8_1(y_lat) comes from the down kernel (per-token form, array of
         // packs) or from the combine (per-bucket form), else is made here
         const bool ylq_ready = ylq_in_down || !down_tok;
-        if (gemm) {
+        if (dense_gemm) {
             if (!ylq_ready) CK(launch_quant_rows(ylat, T, m.L, ylq, st), "Q8_1(y_lat)");
             CK(launch_dense_mfma(m.U, (const uint8_t*)Up, T, ylq, out, tp.isum_u, tp.tap_tokens, st), "U");
         } else if (thin) {

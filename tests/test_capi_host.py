@@ -34,12 +34,7 @@ def test_exports_match_header(L):
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_descs_valid(L, name):
     w = synth.WORKLOADS[name]
-    if w.expert_fmt == synth.NVFP4:
-        # NVFP4 experts run the matrix-vector kernels only: up to 32 tokens
-        moe.moe_desc_check(moe.desc_of(w, max_tokens=32))
-        _refused(moe.desc_of(w, max_tokens=33), moe.MOE_EUNSUPPORTED, "max_tokens")
-    else:
-        moe.moe_desc_check(moe.desc_of(w, max_tokens=2048))
+    moe.moe_desc_check(moe.desc_of(w, max_tokens=2048))
 
 
 def _refused(desc, status, word):

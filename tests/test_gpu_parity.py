@@ -245,9 +245,10 @@ def test_q3_k_experts(kw):
 
 
 # NVFP4 experts (E2M1 codes, an E4M3 scale per 16 elements, an fp32 scale per
-# tensor; matrix-vector kernels only, up to 32 tokens): decode, a verify window
-# with groups (slots from the routing ids), the 9..32-token path (per-bucket
-# down), 32 tokens, latent layers, decode-sized rows
+# tensor; matrix-vector kernels at every T): decode, a verify window with groups
+# (slots from the routing ids), the 9..32-token path (per-bucket down), 32
+# tokens, more than 32 (bucketed by the many-token router), latent layers,
+# decode-sized rows
 @pytest.mark.parametrize("kw", [
     dict(expert_fmt=synth.NVFP4, tokens=1),
     dict(expert_fmt=synth.NVFP4, tokens=6, n_experts=16, top_k=3, n_groups=4, topk_groups=2),
@@ -257,6 +258,9 @@ def test_q3_k_experts(kw):
          tokens=1),
     dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, tokens=6),
     dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, tokens=24),
+    dict(expert_fmt=synth.NVFP4, tokens=100, bias=True),
+    dict(expert_fmt=synth.NVFP4, latent=256, n_experts=16, top_k=4, n_groups=4, topk_groups=2,
+         tokens=70),
     dict(expert_fmt=synth.NVFP4, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=1),
     dict(expert_fmt=synth.NVFP4, hidden=4096, n_ff=1536, n_experts=8, top_k=2, tokens=6),
 ])
@@ -271,6 +275,14 @@ def test_nvfp4_experts(kw):
                                     ("latent_nvfp4", 32)])
 def test_nvfp4_layers(name, T):
     layer, inp = _layer(name, 32)
+    rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp)
+    _report(name, T, rep)
+
+
+def test_nvfp4_latent_prefill():
+    """latent_nvfp4 at 2048 tokens (matrix-vector experts per bucket, matrix-core D/U)."""
+    name, T = "latent_nvfp4", 2048
+    layer, inp = _layer(name, T)
     rep = gh.check_case(synth.WORKLOADS[name], T, tap_tokens=2, layer=layer, inp=inp)
     _report(name, T, rep)
 
