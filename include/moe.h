@@ -116,9 +116,7 @@ typedef struct moe_layer moe_layer;
  *   EXPERTS: for e in 0..E-1: gate [F][Kin/32], up [F][Kin/32], down [Kout][F/32]
  *            blocks, rows row-major; Kin = Kout = latent ? L : H.  An NVFP4
  *            expert then holds a 256-byte tail: its tensor scales gate, up,
- *            down (fp32), then zero bytes.  NVFP4 experts run the
- *            matrix-vector kernels at every T (per token up to 8, per
- *            expert bucket above).
+ *            down (fp32), then zero bytes.
  *   D: [L][H/32] Q8_0 blocks.  U: [H][L/32] Q8_0 blocks.
  * The packed (device) layout has the same byte count; it splits codes from
  * scales and orders gate/up rows in 32-row pairs.  It is private to the library.

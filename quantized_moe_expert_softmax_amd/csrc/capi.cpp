@@ -482,10 +482,8 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     }
     const bool down_tok = T <= (kquant(m.fmt) ? DOWN_TOK_KQ_MAX_T : DOWN_TOK_MAX_T);
     // many tokens: grouped matrix-core GEMMs over token tiles
-    const bool dense_gemm = T > MV_MAX_T;
-    // (NVFP4 experts have no matrix-core kernel: they stay on the matrix-vector
-    // kernels, per bucket, at every T; their D/U still take the matrix cores)
-    const bool gemm = dense_gemm && m.fmt != MOE_FMT_NVFP4;
+    const bool dense_gemm = T > MV_MAX_T;     // the latent D/U
+    const bool gemm = dense_gemm;             // the experts
     // latent rows of a single token are quantised by each consumer workgroup as
     // it stages them (no extra launch); with more tokens every workgroup would
     // repeat that work, so z and y_lat are quantised once by their own kernel

@@ -55,6 +55,7 @@ struct MfArgs {
     float* tap_h;                 // [A][F]
     int32_t* tap_isum;            // [output row][canonical row][K/32]
     int tap_tokens, tap_div;      // token of output row o = o / tap_div
+    size_t ts_off;                // NVFP4 group mode: tensor scales (gate, up, down fp32) in a pack
 };
 
 // ---------------------------------------------------------------------------
@@ -113,7 +114,8 @@ struct MfWave {
 // (row / column l32's d at k = 0 in lanes 0..31, zero elsewhere; a zero-
 // extended 16-bit load gives the first register, the second is zero).  Block
 // kb+1's products are issued before block kb is rescaled.
-template <bool SWIGLU, bool TAP, class SOp = h4, bool NEG = false, class Frag, class SFrag>
+template <bool SWIGLU, bool TAP, class SOp = h4, bool NEG = false, bool NV4 = false, class Frag,
+          class SFrag>
 __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const MfWave& w, int s,
                                          const int* s_orow, Frag frag, SFrag sfrag,
                                          float (&acc0)[16], float (&acc1)[16]) {
@@ -157,7 +159,14 @@ __device__ __forceinline__ void mf_stage(const MfArgs& A, const MfTile& t, const
                                               : pr;
                         // (NEG: the staged codes were negated, so the sum is too)
                         const int v = q ? i1[i] : i0[i];
-                        A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = NEG ? -v : v;
+                        if constexpr (NV4) {
+                            // staged block blk is half blk & 1 of block blk / 2: the
+                            // tap holds the two half sums as 16-bit halves
+                            reinterpret_cast<int16_t*>(A.tap_isum + ((size_t)o * A.rows + cr) * nb +
+                                                       (blk >> 1))[blk & 1] = (int16_t)v;
+                        } else {
+                            A.tap_isum[((size_t)o * A.rows + cr) * nb + blk] = NEG ? -v : v;
+                        }
                     }
                 }
             }
@@ -659,6 +668,158 @@ __global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_q4(MfArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4 (edge0-strata README, section "Changes from upstream Strata", NVFP4
+// latent experts; read as FP4 E2M1 codes, an FP8 E4M3 scale per 16 elements and
+// an fp32 scale per tensor).  Each 16-element half of a block is staged as a
+// block of its own: the half's codes widened to int8 2 * e2m1 (v_perm table
+// lookups, as in the matrix-vector kernels) and then 16 zero bytes, the matching
+// activation half beside them; so one int8 MFMA gives the half's exact sum, and
+// its scale operand is e4m3(s) / 2 in binary16 (exact) against d_a.  A stage of
+// MF_KB staged blocks covers two blocks.  The tensor scales multiply the fp32
+// accumulators before the epilogue.
+template <bool SWIGLU, bool TAP>
+__global__ __launch_bounds__(MF_THREADS, 2) void k_mfma_nv4(MfArgs A) {
+    constexpr int WBYTES = MF_NT * MS_ROWB, XBYTES = MF_MT * MS_ROWB;
+    constexpr int SCB = MF_KB * MS_SWR * 2 + MF_KB * MS_SAR * 2;
+    constexpr int STAGE = WBYTES + XBYTES + SCB;
+    __shared__ __align__(16) char smem[2 * STAGE];
+    __shared__ int s_row[MF_MT], s_orow[MF_MT];
+
+    MfTile t;
+    if (!mf_tile(A, t, s_row, s_orow)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    {
+        // zero tails of the scale rows, both stage buffers
+        const int buf = tid >> 7, kb = (tid >> 5) & 3, z = tid & 31;
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(smem + buf * STAGE + WBYTES + XBYTES);
+        sdw[kb * MS_SWR + MF_NT + z] = 0;
+        sdw[MF_KB * MS_SWR + kb * MS_SAR + MF_MT + z] = 0;
+        // the upper 16 bytes of every staged weight block stay zero (both buffers):
+        // 2 x 128 rows x 4 blocks
+        for (int i = tid; i < 2 * MF_NT * MF_KB; i += MF_THREADS) {
+            const int b = i / (MF_NT * MF_KB), r = (i / MF_KB) % MF_NT, q = i % MF_KB;
+            *reinterpret_cast<v4i*>(smem + b * STAGE + r * MS_ROWB + q * QK + 16) = v4i{0, 0, 0, 0};
+        }
+    }
+    __syncthreads();
+
+    const int K = A.K, nb = K / QK;
+    const size_t rowb = (size_t)nb * 16;
+    const uint8_t* codes = t.mat + A.codes_off + (size_t)t.nt * MF_NT * rowb;
+    // two E4M3 bytes per block (half 0 low)
+    const uint16_t* scl = reinterpret_cast<const uint16_t*>(t.mat + A.scales_off) + (size_t)t.nt * MF_NT * nb;
+
+    // stage s holds blocks 2s and 2s + 1 (staged blocks 4s .. 4s + 3)
+    v4i rw, rx;
+    uint32_t rdw = 0;
+    uint2 rda = uint2{0u, 0u};
+    auto gload = [&](int s) {
+        const int b0 = 2 * s;
+        {
+            const int r = tid >> 1, p = tid & 1;               // 128 rows x 2 blocks
+            rw = ld16(codes + (size_t)r * rowb + (size_t)(b0 + p) * 16);
+        }
+        {
+            const int c = tid >> 2, p = tid & 3;               // 64 tokens x 4 halves
+            rx = ld16(A.ain.q + (size_t)s_row[c] * K + (size_t)b0 * QK + p * 16);
+        }
+        if (tid < MF_NT) {
+            rdw = *reinterpret_cast<const uint32_t*>(scl + (size_t)tid * nb + b0);
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+            rda = *reinterpret_cast<const uint2*>(A.ain.ds + (size_t)s_row[c] * nb + b0);
+        }
+    };
+    auto lstore = [&](int buf) {
+        char* st = smem + buf * STAGE;
+        int8_t* sw = reinterpret_cast<int8_t*>(st);
+        int8_t* sx = reinterpret_cast<int8_t*>(st + WBYTES);
+        uint16_t* sdw = reinterpret_cast<uint16_t*>(st + WBYTES + XBYTES);
+        uint16_t* sda = sdw + MF_KB * MS_SWR;
+        {
+            // block p of the row: low nibbles = half 0 -> staged block 2p, high -> 2p + 1
+            const int r = tid >> 1, p = tid & 1;
+            v4i lo, hi;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t x = (uint32_t)rw[d];
+                lo[d] = e2m1x2_widen(x & 0x0F0F0F0Fu);
+                hi[d] = e2m1x2_widen((x >> 4) & 0x0F0F0F0Fu);
+            }
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + (2 * p) * QK) = lo;
+            *reinterpret_cast<v4i*>(sw + r * MS_ROWB + (2 * p + 1) * QK) = hi;
+        }
+        {
+            // half p & 1 of block p / 2 of the token = staged block p
+            const int c = tid >> 2, p = tid & 3;
+            *reinterpret_cast<v4i*>(sx + c * MS_ROWB + p * QK) = rx;
+        }
+        if (tid < MF_NT) {
+#pragma unroll
+            for (int q = 0; q < MF_KB; ++q)
+                sdw[q * MS_SWR + tid] = (uint16_t)f2h_bits(0.5f * e4m3f((rdw >> (8 * q)) & 0xFFu));
+        } else if (tid < MF_NT + MF_MT) {
+            const int c = tid - MF_NT;
+#pragma unroll
+            for (int q = 0; q < MF_KB; ++q)
+                sda[q * MS_SAR + c] = (uint16_t)(((q >> 1) ? rda.y : rda.x) & 0xffffu);
+        }
+    };
+
+    MfWave w{wave & 1, wave >> 1, lane >> 5, lane & 31};
+    const int o_w0 = w.half ? MF_NT + w.l32 : w.wr * 64 + w.l32;
+    const int o_w1 = w.half ? MF_NT + w.l32 : w.wr * 64 + 32 + w.l32;
+    const int o_a = w.half ? MF_MT + w.l32 : w.wc * 32 + w.l32;
+    const bool busy = w.wc * 32 < t.ncol;   // a wave past the tile's tokens only stages
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+
+    const int stages = nb / 2;
+    auto compute = [&](int buf, int s) {
+        if (!busy) return;
+        const char* st = smem + buf * STAGE;
+        const int8_t* sw = reinterpret_cast<const int8_t*>(st);
+        const int8_t* sx = reinterpret_cast<const int8_t*>(st + WBYTES);
+        const uint16_t* sdw = reinterpret_cast<const uint16_t*>(st + WBYTES + XBYTES);
+        const uint16_t* sda = sdw + MF_KB * MS_SWR;
+        auto frag = [&](int kb, v4i& a0, v4i& a1, v4i& bx) {
+            a0 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            a1 = *reinterpret_cast<const v4i*>(sw + (w.wr * 64 + 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+            bx = *reinterpret_cast<const v4i*>(sx + (w.wc * 32 + w.l32) * MS_ROWB + kb * QK + w.half * 16);
+        };
+        auto sfrag = [&](int kb, h4& d0, h4& d1, h4& dc) {
+            d0 = scale_op(sdw[kb * MS_SWR + o_w0]);
+            d1 = scale_op(sdw[kb * MS_SWR + o_w1]);
+            dc = scale_op(sda[kb * MS_SAR + o_a]);
+        };
+        mf_stage<SWIGLU, TAP, h4, false, true>(A, t, w, s, s_orow, frag, sfrag, acc0, acc1);
+    };
+    gload(0);
+    lstore(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s + 1 < stages; ++s) {
+        gload(s + 1);
+        compute(s & 1, s);
+        lstore((s + 1) & 1);
+        __syncthreads();
+    }
+    compute((stages - 1) & 1, stages - 1);
+    if (A.ts_off) {
+        // gate rows (acc0) and up rows (acc1) of the slab, or the down rows
+        const float* ts = reinterpret_cast<const float*>(t.mat + A.ts_off);
+        const float s0 = SWIGLU ? ts[0] : ts[2], s1 = SWIGLU ? ts[1] : ts[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc0[i] *= s0;
+            acc1[i] *= s1;
+        }
+    }
+    mf_epilogue<SWIGLU, TAP>(A, t, w, s_orow, acc0, acc1);
+}
+
+// ---------------------------------------------------------------------------
 // Q4_K / Q5_K (FMT): a stage of four blocks is half a super-block.  Its 64
 // nibble bytes widen to int8 (plus Q5_K's fifth bits from qh): nibble byte
 // 32g' + i of the stage gives element i of stage block 2g' (low nibble) and of
@@ -876,6 +1037,11 @@ static hipError_t mfma_fmt(int fmt, const MfArgs& a, bool tap, hipStream_t st,
             launch_k(k_mfma_kq<SWIGLU, true, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
         else
             launch_k(k_mfma_kq<SWIGLU, false, MOE_FMT_Q5_K>, grid, block, 0, st, ev, a);
+    } else if (fmt == MOE_FMT_NVFP4) {
+        if (tap)
+            launch_k(k_mfma_nv4<SWIGLU, true>, grid, block, 0, st, ev, a);
+        else
+            launch_k(k_mfma_nv4<SWIGLU, false>, grid, block, 0, st, ev, a);
     } else if (fmt != MOE_FMT_Q8_0) {
         return hipErrorInvalidValue;   // (no matrix-core path for this format)
     } else {
@@ -903,6 +1069,7 @@ hipError_t launch_gate_up_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr a
     a.ain = ain;
     a.F = m.F; a.hq = hq;
     a.tap_h = taps.h; a.tap_isum = taps.isum_gu; a.tap_tokens = taps.tap_tokens; a.tap_div = m.k;
+    a.ts_off = m.ts_off;
     return mfma_fmt<true>(m.fmt, a, taps.h || taps.isum_gu, st, ev);
 }
 
@@ -922,6 +1089,7 @@ hipError_t launch_down_mfma(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
     a.ain = hq;
     a.out = y;
     a.tap_isum = taps.isum_dn; a.tap_tokens = taps.tap_tokens; a.tap_div = m.k;
+    a.ts_off = m.ts_off;
     return mfma_fmt<false>(m.fmt, a, taps.isum_dn != nullptr, st);
 }
 

@@ -7,7 +7,7 @@ from quantized_moe_expert_softmax_amd import synth
 # and a latent one whose D/U are Q4_0.
 MULTI_TILE = [
     dict(n_experts=4, top_k=2, tokens=300, expert_fmt=fmt) for fmt in
-    (synth.Q8_0, synth.Q4_0, synth.Q5_1, synth.Q4_K, synth.Q5_K, synth.Q3_K)
+    (synth.Q8_0, synth.Q4_0, synth.Q5_1, synth.Q4_K, synth.Q5_K, synth.Q3_K, synth.NVFP4)
 ] + [
     dict(n_experts=4, top_k=2, tokens=300, latent=256, expert_fmt=synth.Q4_0,
          dense_fmt=synth.Q4_0),
