@@ -430,6 +430,8 @@ extern "C" moe_status moe_workspace_bytes(const moe_layer* L, int T, size_t* byt
 // 132.7 -> 127.6, Q3_K 132.5 -> 133.6; Q4_K T = 8 171.9 -> 177.3.
 static const int DOWN_TOK_MAX_T = 8;
 static const int DOWN_TOK_KQ_MAX_T = 6;
+// (the Q8_1(y_lat) arrival counters of the per-token down kernel cover DECODE_T tokens)
+static_assert(DOWN_TOK_MAX_T <= DECODE_T && DOWN_TOK_KQ_MAX_T <= DECODE_T, "arrival counters");
 
 static moe_status forward_impl(const moe_layer* L, const float* x, int T, const float* router_w,
                                const float* router_b, const int32_t* groups, ExpertSrc ex,
@@ -565,7 +567,13 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     // kernel also writes Q8_1(y_lat), in 32-row tiles, for the U projection
     const bool ylq_in_down = m.L && down_tok && !ex.table;
     if (down_tok) {
-        CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st, ylq_in_down ? ylq : none),
+        // (one token: 16-row tiles that hand each Q8_1(y_lat) block to its second
+        // finisher, twice the workgroups of 32-row tiles; measured on one box, us
+        // per layer: latent_q8 40.6 -> 38.9, latent_q3_k 48.2 -> 46.9, latent_q4
+        // 43.3 -> 43.1.  At six tokens 32-row tiles already fill the chip and the
+        // hand-off cost 3-3.5 us, so from two tokens on the tiles are 32 rows.)
+        CK(launch_down_tok_mv(m, T, ex, hq, b, comb, tp, st, ylq_in_down ? ylq : none,
+                              ylq_in_down && T == 1 ? (uint32_t*)(ws + w.yarrive) : nullptr),
            "down+combine");
     } else {
         if (gemm)

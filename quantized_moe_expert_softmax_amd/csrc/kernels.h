@@ -129,10 +129,13 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
                              const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
                              const SelectArgs* route = nullptr, const RouteOut* rout = nullptr,
                              bool ids_slots = false);
-// outq.q != null (array form): Q8_1 of out is written too
+// outq.q != null (array form): Q8_1 of out is written too, by 16-row tiles that
+// hand each block to its second finisher through the counters `arrive` ([T][Kout/32],
+// zero on entry and left zero), or by 32-row tiles when arrive is null
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st,
-                              ActPtr outq = ActPtr{nullptr, nullptr, nullptr});
+                              ActPtr outq = ActPtr{nullptr, nullptr, nullptr},
+                              uint32_t* arrive = nullptr);
 hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st);
 hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,

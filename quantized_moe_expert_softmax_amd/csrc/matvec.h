@@ -70,7 +70,9 @@ struct DownTokArgs {
     float* out;              // [T][Kout]: the layer output, or y_lat for a latent layer
     Taps taps;
     const uint8_t* const* etab;   // expert pack addresses, or null (experts + e * eb)
-    ActPtr outq;                  // q != null: also Q8_1 of out (32-row tiles; not with etab)
+    ActPtr outq;                  // q != null: also Q8_1 of out (not with etab)
+    uint32_t* arrive;             // with outq: [T][Kout/32] block arrival counters (16-row
+                                  // tiles, zero on entry and on exit); null: 32-row tiles
     size_t ts_off;                // NVFP4: the down tensor scale in an expert pack; else 0
 };
 

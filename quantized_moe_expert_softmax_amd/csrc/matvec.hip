@@ -201,7 +201,7 @@ hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPt
 
 hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                               const Buckets& b, float* out, const Taps& taps, hipStream_t st,
-                              ActPtr outq) {
+                              ActPtr outq, uint32_t* arrive) {
     const bool kq = kquant(m.fmt);
     if (outq.q && (experts.table || m.kout % QK)) return hipErrorInvalidValue;
     int lpr, cpl;
@@ -229,6 +229,7 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     a.F = m.F; a.Kout = m.kout; a.k = m.k;
     a.hq = hq; a.b = b; a.out = out; a.taps = taps;
     a.outq = outq;
+    a.arrive = outq.q ? arrive : nullptr;
     a.ts_off = m.ts_off ? m.ts_off + 8 : 0;     // NVFP4: the down tensor scale
     bool tap = taps.isum_dn || taps.y;
     if (kq) {

@@ -649,6 +649,69 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
 }
 
 
+// The down kernels' epilogue: rows rt * RT .. + RT of token t combined in rank
+// order from s_y.  With outq (a latent layer's y_lat, quantised once for the U
+// projection): a 32-row tile is one Q8_1 block, quantised here; a 16-row tile is
+// half of one, and the second of the block's two tiles to finish quantises it.
+// That hand-off has no wait: each tile stores its rows with agent-scope stores
+// (written through to the device-coherent level), waits for their completion,
+// then counts itself in on the block's arrival counter (A.arrive, zero on
+// entry); the tile that finds the other one there reads the 32 rows with
+// agent-scope loads, writes the block and clears the counter for the next call.
+template <bool TAP, int RT, int KMAX>
+__device__ __forceinline__ void down_combine(const DownTokArgs& A, int t, int rt,
+                                             const float (&s_y)[KMAX][RT]) {
+    const int nbk = A.Kout / QK;
+    const bool half = RT < QK && A.outq.q != nullptr;
+    if (threadIdx.x < RT) {
+        const int r = threadIdx.x;
+        float o = 0.0f;
+        for (int j = 0; j < A.k; ++j) {
+            const int a = t * A.k + j;
+            o = fmaf(A.b.wts[a], s_y[j][r], o);
+            if constexpr (TAP) {
+                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * RT + r] = s_y[j][r];
+            }
+        }
+        float* dst = A.out + (size_t)t * A.Kout + rt * RT + r;
+        if (half)
+            __hip_atomic_store(dst, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *dst = o;
+        if constexpr (RT == QK) {
+            // lanes 0..31 of wave 0: the tile's block
+            const Q81 q = q8_1_lane(o);
+            A.outq.q[(size_t)t * A.Kout + rt * RT + r] = (int8_t)q.q;
+            if (r == 0) {
+                A.outq.ds[(size_t)t * nbk + rt] = q.ds;
+                A.outq.sq[(size_t)t * nbk + rt] = q.sum;
+            }
+        }
+    }
+    if constexpr (RT < QK) {
+        if (!half) return;                  // (uniform)
+        __shared__ int s_last;
+        const int blk = rt * RT / QK;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(A.arrive + (size_t)t * nbk + blk, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(QK / RT - 1);
+        __syncthreads();
+        if (s_last && threadIdx.x < QK) {
+            const size_t i = (size_t)t * A.Kout + (size_t)blk * QK + threadIdx.x;
+            const float v = __hip_atomic_load(A.out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const Q81 q = q8_1_lane(v);
+            A.outq.q[i] = (int8_t)q.q;
+            if (threadIdx.x == 0) {
+                A.outq.ds[(size_t)t * nbk + blk] = q.ds;
+                A.outq.sq[(size_t)t * nbk + blk] = q.sum;
+                A.arrive[(size_t)t * nbk + blk] = 0u;
+            }
+        }
+    }
+}
+
 // (TABLE: the packs are found through A.etab; a separate instance, so that the
 // array form's rank loop carries no table load and no wait for it.  RT: output
 // rows per workgroup; 32-row tiles also write Q8_1 of the combined rows)
@@ -747,29 +810,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_mv(DownTokArgs A) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < RT) {
-        const int r = threadIdx.x;
-        float o = 0.0f;
-        for (int j = 0; j < A.k; ++j) {
-            const int a = t * A.k + j;
-            o = fmaf(A.b.wts[a], s_y[j][r], o);
-            if constexpr (TAP) {
-                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * RT + r] = s_y[j][r];
-            }
-        }
-        A.out[(size_t)t * A.Kout + rt * RT + r] = o;
-        if constexpr (RT == QK) {
-            // a 32-row tile is one Q8_1 block of the combined row: quantised
-            // here once for the kernel that reads it (lanes 0..31 of wave 0)
-            const Q81 q = q8_1_lane(o);
-            const int nbk = A.Kout / QK;
-            A.outq.q[(size_t)t * A.Kout + rt * RT + r] = (int8_t)q.q;
-            if (r == 0) {
-                A.outq.ds[(size_t)t * nbk + rt] = q.ds;
-                A.outq.sq[(size_t)t * nbk + rt] = q.sum;
-            }
-        }
-    }
+    down_combine<TAP, RT>(A, t, rt, s_y);
 }
 
 // The same for K-quant experts (Q4_K, Q5_K, Q3_K), whose chunk dots read the
@@ -842,28 +883,7 @@ __global__ __launch_bounds__(DT_NW * 64, 2) void k_down_tok_kq(DownTokArgs A) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < RT) {
-        const int r = threadIdx.x;
-        float o = 0.0f;
-        for (int j = 0; j < A.k; ++j) {
-            const int a = t * A.k + j;
-            o = fmaf(A.b.wts[a], s_y[j][r], o);
-            if constexpr (TAP) {
-                if (A.taps.y) A.taps.y[(size_t)a * A.Kout + rt * RT + r] = s_y[j][r];
-            }
-        }
-        A.out[(size_t)t * A.Kout + rt * RT + r] = o;
-        if constexpr (RT == QK) {
-            // one Q8_1 block of the combined row per 32-row tile (as above)
-            const Q81 q = q8_1_lane(o);
-            const int nbk = A.Kout / QK;
-            A.outq.q[(size_t)t * A.Kout + rt * RT + r] = (int8_t)q.q;
-            if (r == 0) {
-                A.outq.ds[(size_t)t * nbk + rt] = q.ds;
-                A.outq.sq[(size_t)t * nbk + rt] = q.sum;
-            }
-        }
-    }
+    down_combine<TAP, RT>(A, t, rt, s_y);
 }
 
 // ---------------------------------------------------------------------------
@@ -932,7 +952,7 @@ hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         if constexpr (DT_RT % (64 / L) == 0) {
             dim3 grid(T * (a.Kout / DT_RT));
-            if (a.outq.q)
+            if (a.outq.q && !a.arrive)
                 hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP, false, QK>), dim3(T * (a.Kout / QK)),
                                    dim3(DT_NW * 64), 0, st, a);
             else if (a.etab)
@@ -951,7 +971,7 @@ hipError_t down_tok_kq_fmt(int lpr, int cpl, int T, size_t lds, const DownTokArg
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         if constexpr (DT_RT % (64 / L) == 0) {
             dim3 grid(T * (a.Kout / DT_RT));
-            if (a.outq.q)
+            if (a.outq.q && !a.arrive)
                 hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP, QK>), dim3(T * (a.Kout / QK)),
                                    dim3(DT_NW * 64), lds, st, a);
             else

@@ -123,6 +123,8 @@ struct WsLayout {
     size_t y;
     size_t ylat, ylq_q, ylq_ds, ylq_sq;
     size_t dpart;                   // latent D partial rows of the few-token kernel
+    size_t yarrive;                 // latent, per-token down: Q8_1(y_lat) block arrival
+                                    // counters [T][L/32] (T <= DECODE_T), fixed offset and size
     size_t total;
     int T, S;                       // tokens, router K-splits
 };
@@ -189,6 +191,12 @@ inline WsLayout ws_layout(const Dims& m, int T) {
     auto take = [&](size_t bytes) { size_t r = o; o = al256(o + bytes); return r; };
     size_t A = (size_t)T * m.k;
     w.ctrl = take(sizeof(uint32_t) * CW_COUNT);
+    // counters that must read zero at every call sit at the same offsets, with
+    // the same sizes, for every layer and every T (a call with another layer or
+    // T sharing the workspace may leave data anywhere else): the control words,
+    // then the per-token down kernel's Q8_1(y_lat) block arrivals for DECODE_T
+    // tokens of the widest latent row (8192)
+    w.yarrive = take(sizeof(uint32_t) * DECODE_T * (8192 / QK));
     w.logit_part = take(sizeof(double) * w.S * T * m.E);
     w.ids = take(sizeof(int32_t) * A);
     w.wts = take(sizeof(float) * A);
