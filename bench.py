@@ -451,6 +451,11 @@ def write_traffic(fetch_dir, write_dir):
     return res
 
 
+def _progress(msg: str):
+    """One line per finished phase, on stderr (the result line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     a = parse()
     if a.write_traffic:
@@ -477,6 +482,7 @@ def main():
     w = synth.Workload(**{**w0.__dict__, **over})
     m = measure(w, T, a.steps, a.warmup, a.pool, a.copies, a.profile_steps)
     st_ms = m["st_ms"]
+    _progress(f"{w.name} T={T}: {m['ms_step'] * 1e3:.1f} us/step")
 
     gu_bytes, layer_bytes, expert_bytes = algorithmic_bytes(w, T, m["mean_active"])
     gu_gbs = gu_bytes / (st_ms["gate_up_kernel"] * 1e-3) / 1e9
@@ -492,6 +498,7 @@ def main():
     if not a.no_cpu_baseline:
         model, avail, nth = host_cpu()
         rate, done, calls, el = cpu_oracle_rate(w, m["inp"], m["xs"], a.cpu_seconds, nth)
+        _progress(f"CPU oracle: {rate:.1f} tokens/s on {nth} threads")
         cpu = {"value": rate, "unit": "tokens/s", "cores": nth, "kind": "oracle",
                "sample": f"{done} tokens of this workload ({calls} oracle calls of {nth} "
                          f"tokens drawn in turn from its {len(m['xs'])} token batches, one token "
@@ -503,6 +510,7 @@ def main():
     if not a.no_prefill and a.workload != "prefill":
         wp = synth.WORKLOADS["prefill"]
         mp = measure(wp, wp.tokens, a.prefill_steps, 3, 4, 1, a.profile_steps)
+        _progress(f"prefill T={wp.tokens}: {mp['ms_step'] * 1e3:.1f} us/step")
         cpu_p = None
         if not a.no_cpu_baseline:
             model, avail, nth = host_cpu()
@@ -537,6 +545,7 @@ def main():
         # the gate/up launch's bytes, the down weights', the whole layer's, and 1 GiB
         dn_bytes = m["mean_active"] * w.matrix_bytes(w.k_out, w.n_ff // 32)
         probe = hbm_probe([int(gu_bytes), int(dn_bytes), int(layer_bytes), 1 << 30])
+        _progress("HBM read probe done")
         probe["gate_up_vs_probe"] = gu_gbs / probe["sizes"][0]["gbs"]
 
     if a.calibration_copy:
