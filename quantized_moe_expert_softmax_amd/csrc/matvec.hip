@@ -79,7 +79,8 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
     a.eb = m.expert_bytes;
     a.gu_scales_off = m.gu.scales_off;
     a.K = m.kin; a.F = m.F; a.k = m.k; a.T = T;
-    a.tch = pick_tch(m.kin);
+    // (no expert holds more than T tokens: staging room for min(T, chunk))
+    a.tch = std::min(pick_tch(m.kin), std::max(T, 1));
     a.ain = ain; a.ain_f32 = ain_f32; a.keep = keep;
     a.b = b; a.hq = hq; a.taps = taps;
     a.ts_off = m.ts_off;
@@ -102,7 +103,7 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
             return hipErrorInvalidValue;
         a.route = *route;
         a.rout = *rout;
-        lds += sizeof(RouteLds);
+        lds = ((lds + 15) & ~(size_t)15) + sizeof(RouteLds);
     }
     int slots = std::min(m.E, T * m.k);
     dim3 grid(slots * (m.F / QK));
@@ -143,7 +144,7 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     const int rpp = ROWS_NW * (64 / lpr);
     if (a.rows % rpp) return hipErrorInvalidConfiguration;
     a.rt = pick_rt(a.rows, groups, rpp);
-    a.tch = pick_tch(a.K);
+    a.tch = std::min(pick_tch(a.K), std::max(a.T, 1));
     const size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 4;
     dim3 grid(groups * (a.rows / a.rt));
     bool tap = a.isum_tap != nullptr;

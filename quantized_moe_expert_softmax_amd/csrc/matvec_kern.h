@@ -447,7 +447,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         // one token: the workgroup selects the experts (workgroup 0 also the
         // weights, and publishes the routing); slot j serves the rank-j expert,
         // whose one assignment is a = j
-        RouteLds& S = *reinterpret_cast<RouteLds*>(smem + stage_bytes(TCH, K) + (size_t)TCH * (64 * 4 + 8));
+        const size_t route_off = (stage_bytes(TCH, K) + (size_t)TCH * (64 * 4 + 8) + 15) & ~(size_t)15;
+        RouteLds& S = *reinterpret_cast<RouteLds*>(smem + route_off);
         SelectArgs sa = A.route;
         if (blockIdx.x != 0) sa.logits_tap = nullptr;
         float wt = 0.0f;
