@@ -518,10 +518,13 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
                      ids_only, &routed, &sel, st), "router");
     if (routed == ROUTE_SELECTED) CK(launch_bucket(m, w, ws, T, st), "bucketing");
-    // a single token is selected and bucketed by the gate/up kernel's prologue
-    const SelectArgs* gu_route = routed == ROUTE_LOGITS ? &sel : nullptr;
     RouteOut rout{(int32_t*)(ws + w.ids), (float*)(ws + w.wts), (int32_t*)(ws + w.counts),
                   (int32_t*)(ws + w.lists), (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active)};
+    // a single token is selected and bucketed by one more workgroup of the
+    // latent D launch, which does not depend on the routing and runs between
+    // the router and the experts; without D, by the gate/up kernel's prologue
+    const bool sel_in_d = routed == ROUTE_LOGITS && m.L && !dense_gemm && !thin;
+    const SelectArgs* gu_route = routed == ROUTE_LOGITS && !sel_in_d ? &sel : nullptr;
     EV(MOE_EV_ROUTED);
     const int32_t* tile_map = (const int32_t*)(ws + w.tile_map);
     if (m.L) {
@@ -537,7 +540,7 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
             CK(launch_quant_rows_sum(zp, S, S > 1 ? z : nullptr, T, m.L, zq, st), "Q8_1(z)");
         } else {
             CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
-                               tp.tap_tokens, st), "D");
+                               tp.tap_tokens, st, sel_in_d ? &sel : nullptr, &rout, m.k), "D");
             // one token: the gate/up kernel quantises z on the way in; more: once, here
             if (!lat_fused_q) CK(launch_quant_rows(z, T, m.L, zq, st), "Q8_1(z)");
         }
@@ -551,7 +554,8 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     if (gemm)
         CK(launch_gate_up_mfma(m, T, ex, m.L ? zq : xq, b, tile_map, hq, tp, st, gev), "gate/up");
     else if (m.L && lat_fused_q)
-        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev, gu_route, &rout),
+        CK(launch_gate_up_mv(m, T, ex, none, z, taps ? zq : none, b, hq, tp, st, gev, gu_route, &rout,
+                             false, sel_in_d),
            "gate/up");
     else if (m.L)
         CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout,

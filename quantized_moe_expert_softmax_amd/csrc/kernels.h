@@ -123,12 +123,13 @@ bool mv_config_ok(int K, int fmt, bool gate_up);
 // the kernel (ain_f32, with `keep` receiving the Q8_1 blocks when non-null).
 // route != null (T == 1 only): every workgroup selects the token's experts
 // from the router logits in its prologue and workgroup 0 publishes ids,
-// weights and buckets to *rout; b is then not read.
+// weights and buckets to *rout; b is then not read.  ids_direct (T == 1): an
+// earlier launch routed the token, and slot j serves expert b.ids[j].
 hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev = KEvents{},
                              const SelectArgs* route = nullptr, const RouteOut* rout = nullptr,
-                             bool ids_slots = false);
+                             bool ids_slots = false, bool ids_direct = false);
 // outq.q != null (array form): Q8_1 of out is written too, by 16-row tiles that
 // hand each block to its second finisher through the counters `arrive` ([T][Kout/32],
 // zero on entry and left zero), or by 32-row tiles when arrive is null
@@ -138,9 +139,13 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
                               uint32_t* arrive = nullptr);
 hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq,
                                const Buckets& b, float* y, const Taps& taps, hipStream_t st);
+// route != null (T == 1, dense): one more workgroup selects the token's k
+// experts from the router logits and publishes ids, weights and buckets to
+// *rout, in parallel with the row tiles.
 hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
                            const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
-                           int tap_tokens, hipStream_t st);
+                           int tap_tokens, hipStream_t st, const SelectArgs* route = nullptr,
+                           const RouteOut* rout = nullptr, int k = 0);
 
 // Many-token path: grouped int8 matrix-core GEMM over the token tiles that the
 // bucketing kernel numbered in tile_map (tiles of GEMM_TILE_M assignments).

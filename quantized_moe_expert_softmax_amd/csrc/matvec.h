@@ -30,6 +30,7 @@ struct GUArgs {
     SelectArgs route;     // route.part != null: one token, routed in the prologue
     RouteOut rout;
     int ids_slots;        // 1: the slots come from b.ids (T * k <= DECODE_T * 32), not buckets
+    int ids_direct;       // 1: one token routed by an earlier launch: slot j serves b.ids[j]
     size_t ts_off;        // NVFP4: the tensor scales (gate, up fp32) in an expert pack; else 0
 };
 
@@ -53,6 +54,12 @@ struct RowsArgs {
     int32_t* isum_tap;         // [act row][rows][K/32]
     int tap_tokens;
     size_t ts_off;             // expert mode, NVFP4: the down tensor scale in a pack; else 0
+    // dense mode, one token, route.part != null: workgroup 0 selects the token's
+    // k experts from the router logits and publishes the routing to rout (as
+    // the gate/up prologue does); the row tiles are workgroups 1..
+    SelectArgs route;
+    RouteOut rout;
+    int k;
 };
 
 // ---------------------------------------------------------------------------
@@ -77,6 +84,10 @@ struct DownTokArgs {
 };
 
 constexpr int DT_RT = 16;    // output rows per workgroup
+// output rows per workgroup of a latent layer's one-token down projection (the
+// Q8_1(y_lat) blocks handed over by arrival counters): 1280 or 1792 latent rows
+// give 320 or 448 workgroups instead of 80 or 112 with 16-row tiles
+constexpr int DT_RT_ONE = 4;
 constexpr int DT_NW = 8;     // waves per workgroup (ranks in parallel)
 constexpr int DT_KMAX = 32;  // largest top_k
 

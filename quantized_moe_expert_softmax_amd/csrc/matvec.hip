@@ -69,7 +69,8 @@ bool mv_config_ok(int K, int fmt, bool gate_up) {
 hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain,
                              const float* ain_f32, ActPtr keep, const Buckets& b, ActPtr hq,
                              const Taps& taps, hipStream_t st, const KEvents& ev,
-                             const SelectArgs* route, const RouteOut* rout, bool ids_slots) {
+                             const SelectArgs* route, const RouteOut* rout, bool ids_slots,
+                             bool ids_direct) {
     int lpr, cpl;
     if (!pick_gu_fmt(nchunks(m.kin, m.fmt), m.fmt, lpr, cpl)) return hipErrorInvalidConfiguration;
     if (64 % (gu_waves(lpr, m.fmt) * (64 / lpr))) return hipErrorInvalidConfiguration;
@@ -88,6 +89,12 @@ hipError_t launch_gate_up_mv(const Dims& m, int T, ExpertSrc experts, ActPtr ain
     a.route = SelectArgs{};
     a.rout = RouteOut{};
     a.ids_slots = 0;
+    a.ids_direct = 0;
+    if (ids_direct) {
+        // one token whose k ids an earlier launch wrote to b.ids
+        if (route || ids_slots || T != 1 || !b.ids) return hipErrorInvalidValue;
+        a.ids_direct = 1;
+    }
     if (ids_slots) {
         // every assignment id is held by one thread of the (at least 256-thread) workgroup
         // (and the expert ids fit the prologue's two per thread)
@@ -145,8 +152,13 @@ static hipError_t rows_dispatch(int fmt, int groups, RowsArgs& a, hipStream_t st
     if (a.rows % rpp) return hipErrorInvalidConfiguration;
     a.rt = pick_rt(a.rows, groups, rpp);
     a.tch = std::min(pick_tch(a.K), std::max(a.T, 1));
-    const size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 4;
+    size_t lds = stage_bytes(a.tch, a.K) + (size_t)a.tch * 4;
     dim3 grid(groups * (a.rows / a.rt));
+    if (a.route.part) {
+        // one more workgroup, the selection (its LDS is the selection's only)
+        grid.x += 1;
+        lds = std::max(lds, sizeof(RouteLds));
+    }
     bool tap = a.isum_tap != nullptr;
     if (fmt == MOE_FMT_Q4_0)
         return tap ? rows_fmt<MOE_FMT_Q4_0, true>(lpr, cpl, grid, lds, a, st)
@@ -187,8 +199,18 @@ hipError_t launch_down_slot_mv(const Dims& m, int T, ExpertSrc experts, ActPtr h
 
 hipError_t launch_dense_mv(const MatLayout& W, const uint8_t* base, int T, ActPtr ain,
                            const float* ain_f32, ActPtr keep, float* out, int32_t* isum_tap,
-                           int tap_tokens, hipStream_t st) {
+                           int tap_tokens, hipStream_t st, const SelectArgs* route,
+                           const RouteOut* rout, int k) {
     RowsArgs a{};
+    if (route) {
+        // one token, its whole logits (S = 1), within the selection's limits
+        if (T != 1 || !rout || route->S != 1 || route->T != 1 || route->E > 512 || route->k > 32 ||
+            route->G > 64 || route->k != k)
+            return hipErrorInvalidValue;
+        a.route = *route;
+        a.rout = *rout;
+        a.k = k;
+    }
     a.base = base;
     a.group_stride = 0;
     a.codes_off = W.codes_off;
@@ -212,13 +234,22 @@ hipError_t launch_down_tok_mv(const Dims& m, int T, ExpertSrc experts, ActPtr hq
     // layer: Q8_0 at F = 1536, 32 x 3 against 16 x 6: T = 6 163.0 -> 159.4, T = 1
     // unchanged; Q5_1, 16 x 3 against 8 x 6: T = 1 32.9 -> 32.2)
     const int nch = nchunks(m.F, m.fmt);
-    if (kq) {
-        if (!pick_rows(nch, lpr, cpl)) return hipErrorInvalidConfiguration;
-    } else if (nch % 3 == 0 && (nch / 3 == 8 || nch / 3 == 16 || nch / 3 == 32 || nch / 3 == 64)) {
-        lpr = nch / 3;
-        cpl = 3;
-    } else if (!pick(nch, lpr, cpl)) {
-        return hipErrorInvalidConfiguration;
+    // one token of a latent layer (Q8_1(y_lat) through arrival counters): rows of
+    // at least 16 lanes, so that DT_RT_ONE-row tiles hold whole passes
+    bool one = false;
+    if (outq.q && arrive) {
+        for (int l = 16; l <= 64 && !one; l *= 2)
+            if (nch % l == 0 && nch / l <= (kq ? 4 : 8)) { lpr = l; cpl = nch / l; one = true; }
+    }
+    if (!one) {
+        if (kq) {
+            if (!pick_rows(nch, lpr, cpl)) return hipErrorInvalidConfiguration;
+        } else if (nch % 3 == 0 && (nch / 3 == 8 || nch / 3 == 16 || nch / 3 == 32 || nch / 3 == 64)) {
+            lpr = nch / 3;
+            cpl = 3;
+        } else if (!pick(nch, lpr, cpl)) {
+            return hipErrorInvalidConfiguration;
+        }
     }
     if (m.k > DT_KMAX || m.kout % DT_RT) return hipErrorInvalidConfiguration;
     DownTokArgs a;

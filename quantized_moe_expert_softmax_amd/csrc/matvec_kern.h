@@ -407,33 +407,44 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
 
 
 
-// One token's routing result, published by workgroup 0 (NT threads) from its
-// selection: ids and weights (threads j < k hold w_j) in rank order, and the
+// One token's routing result, published by the workgroup that selected it (NT
+// threads): ids and weights (threads j < k hold w_j) in rank order, and the
 // buckets: every expert's count (0 or 1), the one assignment a = j at the head
 // of its expert's list, the active experts in id order.
 template <int NT>
-__device__ __forceinline__ void publish_route(const GUArgs& A, const RouteLds& S, float w) {
-    const int tid = threadIdx.x, k = A.k, E = A.route.E;
+__device__ __forceinline__ void publish_route(const RouteOut& R, int k, int E, const RouteLds& S,
+                                              float w) {
+    const int tid = threadIdx.x;
     if (tid < k) {
         const int id = S.sel[tid];
         int below = 0;
         for (int j = 0; j < k; ++j) below += (int)(S.sel[j] < id);
-        A.rout.ids[tid] = id;
-        A.rout.wts[tid] = w;
-        A.rout.lists[id] = tid;
-        A.rout.active[below] = id;
+        R.ids[tid] = id;
+        R.wts[tid] = w;
+        R.lists[id] = tid;
+        R.active[below] = id;
     }
     for (int e = tid; e < E; e += NT) {
         int c = 0;
         for (int j = 0; j < k; ++j) c |= (int)(S.sel[j] == e);
-        A.rout.counts[e] = c;
+        R.counts[e] = c;
     }
-    if (tid == 0) A.rout.ctrl[CW_N_ACTIVE] = (uint32_t)k;
+    if (tid == 0) R.ctrl[CW_N_ACTIVE] = (uint32_t)k;
 }
 
 // (the second launch bound is the minimum number of waves per SIMD: 3 lets
 // three 4-wave workgroups share a CU)
-template <int FMT, int LPR, int CPL, int NW, bool TAP>
+// (ALL: a slab of at most four passes has all of them in registers at once, see
+// below; an instance of its own because the registers cost the occupancy that
+// the windows of several tokens need)
+template <int FMT, int LPR, int CPL, int NW>
+constexpr bool gu_all_passes_ok() {
+    constexpr int PASSES = 64 / (NW * (64 / LPR));
+    constexpr int SIDE_DW = (int)(sizeof(typename Fmt<FMT>::Side) / 4);
+    return PASSES > 1 && PASSES <= 4 && PASSES * CPL * (4 + SIDE_DW) <= (NW == 4 ? 100 : 128);
+}
+
+template <int FMT, int LPR, int CPL, int NW, bool TAP, bool ALL = false>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs A) {
     constexpr bool STREAM = true;   // an expert's tokens fit one chunk at decode sizes
     constexpr int PASSES = 64 / (NW * (64 / LPR));
@@ -441,6 +452,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     const int FB = A.F / QK;
     const int slot = blockIdx.x / FB, fb = blockIdx.x - slot * FB;
     const int K = A.K, nb = K / QK, TCH = A.tch;
+    // With ALL (one token, a slab of a few passes: the short latent rows) every
+    // pass of weights is requested at once and kept in registers, so the
+    // workgroup waits for memory once instead of once per pass (latent_q8
+    // one-token gate/up 15.9 -> 12.5 us; with several tokens the lost occupancy
+    // made latent_q4 at 32 tokens 166 -> 225 us per layer, hence an instance of
+    // its own).  In the 8-wave instances an fp32 input row (latent z) is then
+    // requested first, before the routing ids and the weights: the loads
+    // complete in order, so its quantisation waits for it alone (one token,
+    // gate/up: latent_q4 11.1 -> 9.8 us, latent_q3_k 11.3 -> 10.3 us; the
+    // 4-wave latent_q8 instance went from 13.6 to 15.7 us with it and does not).
+    constexpr bool ALLP = ALL && gu_all_passes_ok<FMT, LPR, CPL, NW>();
+    constexpr int ZPT = 4;      // fp32 input values per thread (K <= 2048)
+    constexpr bool ZPRE = ALLP && NW == 8;
+    float zv[ZPRE ? ZPT : 1];
+    const bool zpre = ZPRE && A.ain_f32 && K <= ZPT * NW * 64;
+    if constexpr (ZPRE) {
+        if (zpre) {
+#pragma unroll
+            for (int i = 0; i < ZPT; ++i) {
+                const int idx = threadIdx.x + i * NW * 64;
+                zv[i] = idx < K ? A.ain_f32[idx] : 0.0f;     // token 0
+            }
+        }
+    }
     int e, cnt;
     const int32_t* lst = nullptr;
     if (A.route.part) {
@@ -453,8 +488,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         if (blockIdx.x != 0) sa.logits_tap = nullptr;
         float wt = 0.0f;
         select_wg<NW * 64>(sa, S, blockIdx.x == 0, &wt);
-        if (blockIdx.x == 0) publish_route<NW * 64>(A, S, wt);
+        if (blockIdx.x == 0) publish_route<NW * 64>(A.rout, A.k, A.route.E, S, wt);
         e = __builtin_amdgcn_readfirstlane(S.sel[slot]);
+        cnt = 1;
+    } else if (A.ids_direct) {
+        // one token routed by the launch before: slot j serves the rank-j
+        // expert, whose one assignment is a = j
+        e = __builtin_amdgcn_readfirstlane(A.b.ids[slot]);
         cnt = 1;
     } else if (A.ids_slots) {
         // a few tokens, no buckets: from the T * k routing ids, slot j serves the
@@ -529,15 +569,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     int32_t* s_a = reinterpret_cast<int32_t*>(s_gu + TCH * 64);
     int32_t* s_t = s_a + TCH;
 
-    // the first pass of weights is requested before the activations are staged
-    v4i wA[CPL];
-    typename Fmt<FMT>::Side sA[CPL];
-    {
-        constexpr int RPW = 64 / LPR;
-        const int lane = threadIdx.x & 63;
-        const int r = (threadIdx.x >> 6) * RPW + lane / LPR;
-        load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), lane % LPR,
-                                nb * Fmt<FMT>::CPB, wA, sA);
+    // the first pass of weights (with ALL: every pass) is requested before the
+    // activations are staged
+    constexpr int RPW = 64 / LPR;
+    constexpr int NBUF = ALLP ? PASSES : 1;
+    const int sl = (threadIdx.x & 63) % LPR;
+    auto row_of = [&](int p) { return (p * NW + (int)(threadIdx.x >> 6)) * RPW + (int)(threadIdx.x & 63) / LPR; };
+    v4i wP[NBUF][CPL];
+    typename Fmt<FMT>::Side sP[NBUF][CPL];
+#pragma unroll
+    for (int p = 0; p < NBUF; ++p) {
+        const int r = row_of(p);
+        load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / Fmt<FMT>::SBLK), sl,
+                                        nb * Fmt<FMT>::CPB, wP[p], sP[p]);
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
         const int n = min(TCH, cnt - i0);
@@ -547,7 +591,29 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
             s_t[threadIdx.x] = a / A.k;
         }
         __syncthreads();
-        if (A.ain_f32)
+        if (ZPRE && zpre) {
+            // the prefetched row: 32-lane groups hold whole blocks
+            const ActPtr keep = fb == 0 ? A.keep : ActPtr{};
+#pragma unroll
+            for (int i = 0; i < ZPT; ++i) {
+                const int idx = threadIdx.x + i * NW * 64, blk = idx / QK;
+                if (idx < K) {
+                    const Q81 r = q8_1_lane(zv[i]);
+                    s_q[idx] = (int8_t)r.q;
+                    if ((threadIdx.x & 31) == 0) {
+                        s_d[blk] = h2f(r.ds);
+                        s_sq[blk] = Fmt<FMT>::Q5 ? __float_as_int(h2f(r.ds >> 16)) : r.sum;
+                    }
+                    if (keep.q) {
+                        keep.q[idx] = (int8_t)r.q;
+                        if ((threadIdx.x & 31) == 0) {
+                            keep.ds[blk] = r.ds;
+                            keep.sq[blk] = r.sum;
+                        }
+                    }
+                }
+            }
+        } else if (A.ain_f32)
             stage_f32<Fmt<FMT>::Q5>(A.ain_f32, K, s_t, n, s_q, s_d, s_sq, fb == 0 ? A.keep : ActPtr{});
         else
             stage_q<Fmt<FMT>::Q5>(A.ain, K, s_t, n, s_q, s_d, s_sq);
@@ -563,8 +629,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
                 A.taps.isum_gu[((size_t)s_a[i] * 2 * A.F + row) * nb + blk] = v;
             }
         };
-        row_tile<FMT, LPR, CPL, NW, TAP, STREAM, PASSES>(codes, scl, rowb, nb, 64, n, K, s_q, s_d, s_sq,
-                                                 emit, emit_isum, tap, wA, sA, i0 == 0);
+        if constexpr (ALLP) {
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                pass_dot<FMT, LPR, CPL, TAP>(wP[p], sP[p], row_of(p), sl, nb * Fmt<FMT>::CPB, nb, n, K, s_q,
+                                             s_d, s_sq, emit, emit_isum, tap);
+        } else {
+            row_tile<FMT, LPR, CPL, NW, TAP, STREAM, PASSES>(codes, scl, rowb, nb, 64, n, K, s_q, s_d, s_sq,
+                                                             emit, emit_isum, tap, wP[0], sP[0], i0 == 0);
+        }
         __syncthreads();
         // SwiGLU and Q8_1: one 32-lane group per token, lane = output f
         for (int ii = threadIdx.x / 32; ii < n; ii += NW * 2) {
@@ -587,12 +660,27 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
 }
 
 
-template <int FMT, int LPR, int CPL, int NW, bool TAP>
+// (SEL: the dense one-token form with the selection workgroup; an instance of
+// its own, as the selection's registers cost the expert rows kernels occupancy)
+template <int FMT, int LPR, int CPL, int NW, bool TAP, bool SEL = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     constexpr bool STREAM = true;   // one token (dense) or one bucket chunk (experts)
     extern __shared__ __align__(16) char smem[];
+    int bid = blockIdx.x;
+    if constexpr (SEL) {
+        // dense mode, one token: workgroup 0 selects the token's experts (its
+        // LDS holds only the selection), the others are the row tiles
+        if (bid == 0) {
+            RouteLds& S = *reinterpret_cast<RouteLds*>(smem);
+            float wt = 0.0f;
+            select_wg<NW * 64>(A.route, S, true, &wt);
+            publish_route<NW * 64>(A.rout, A.k, A.route.E, S, wt);
+            return;
+        }
+        --bid;
+    }
     const int NRT = A.rows / A.rt;
-    const int g = blockIdx.x / NRT, rt = blockIdx.x - g * NRT;
+    const int g = bid / NRT, rt = bid - g * NRT;
     const uint8_t* mat;
     const int32_t* lst = nullptr;
     int cnt;
@@ -934,6 +1022,12 @@ hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a,
                               hipStream_t st, const KEvents& ev) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         constexpr int NW = gu_waves_c(L, FMT);
+        if constexpr (gu_all_passes_ok<FMT, L, C, NW>()) {
+            if (a.T == 1) {
+                launch_k(k_gate_up_mv<FMT, L, C, NW, TAP, true>, grid, dim3(NW * 64), lds, st, ev, a);
+                break;
+            }
+        }
         launch_k(k_gate_up_mv<FMT, L, C, NW, TAP>, grid, dim3(NW * 64), lds, st, ev, a);
     }));
     return hipGetLastError();
@@ -943,7 +1037,14 @@ template <int FMT, bool TAP>
 hipError_t rows_fmt(int lpr, int cpl, dim3 grid, size_t lds, const RowsArgs& a,
                            hipStream_t st) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
-        hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), lds, st, a);
+        if (a.route.part) {
+            if constexpr (FMT == MOE_FMT_Q8_0 || FMT == MOE_FMT_Q4_0)
+                hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP, true>), grid, dim3(ROWS_NW * 64), lds, st, a);
+            else
+                return hipErrorInvalidValue;      // (the dense formats only)
+        } else {
+            hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), lds, st, a);
+        }
     }));
     return hipGetLastError();
 }
@@ -956,6 +1057,9 @@ hipError_t down_tok_fmt(int lpr, int cpl, int T, const DownTokArgs& a, hipStream
             if (a.outq.q && !a.arrive)
                 hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP, false, QK>), dim3(T * (a.Kout / QK)),
                                    dim3(DT_NW * 64), 0, st, a);
+            else if (a.outq.q && DT_RT_ONE % (64 / L) == 0)
+                hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, TAP, false, DT_RT_ONE % (64 / L) == 0 ? DT_RT_ONE : DT_RT>),
+                                   dim3(T * (a.Kout / DT_RT_ONE)), dim3(DT_NW * 64), 0, st, a);
             else if (a.etab)
                 hipLaunchKernelGGL((k_down_tok_mv<FMT, L, C, false, true>), grid, dim3(DT_NW * 64), 0, st, a);
             else
@@ -975,6 +1079,9 @@ hipError_t down_tok_kq_fmt(int lpr, int cpl, int T, size_t lds, const DownTokArg
             if (a.outq.q && !a.arrive)
                 hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP, QK>), dim3(T * (a.Kout / QK)),
                                    dim3(DT_NW * 64), lds, st, a);
+            else if (a.outq.q && DT_RT_ONE % (64 / L) == 0)
+                hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP, DT_RT_ONE % (64 / L) == 0 ? DT_RT_ONE : DT_RT>),
+                                   dim3(T * (a.Kout / DT_RT_ONE)), dim3(DT_NW * 64), lds, st, a);
             else
                 hipLaunchKernelGGL((k_down_tok_kq<FMT, L, C, TAP>), grid, dim3(DT_NW * 64), lds, st, a);
         } else {
