@@ -434,6 +434,23 @@ __device__ __forceinline__ void publish_route(const RouteOut& R, int k, int E, c
 
 // (the second launch bound is the minimum number of waves per SIMD: 3 lets
 // three 4-wave workgroups share a CU)
+// An empty asm that the compiler must assume rewrites a weight row's side data
+// in place: a value computed from it cannot move above this point.
+__device__ __forceinline__ void opaque_side(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque_side(uint2& v) {
+    asm volatile("" : "+v"(v.x));
+    asm volatile("" : "+v"(v.y));
+}
+__device__ __forceinline__ void opaque_side(v4i& v) {
+    int x = v.x, y = v.y, z = v.z, w = v.w;
+    asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+    v = v4i{x, y, z, w};
+}
+__device__ __forceinline__ void opaque_side(K5Side& v) {
+    opaque_side(v.s);
+    opaque_side(v.qh);
+}
+
 // (ALL: a slab of at most four passes has all of them in registers at once, see
 // below; an instance of its own because the registers cost the occupancy that
 // the windows of several tokens need)
@@ -630,6 +647,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
             }
         };
         if constexpr (ALLP) {
+            // (the scale conversions would otherwise be hoisted above the
+            // staging, which then waits for half of the weights first)
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) opaque_side(sP[p][j]);
 #pragma unroll
             for (int p = 0; p < PASSES; ++p)
                 pass_dot<FMT, LPR, CPL, TAP>(wP[p], sP[p], row_of(p), sl, nb * Fmt<FMT>::CPB, nb, n, K, s_q,
@@ -1022,9 +1045,10 @@ hipError_t gate_up_fmt(int lpr, int cpl, dim3 grid, size_t lds, const GUArgs& a,
                               hipStream_t st, const KEvents& ev) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
         constexpr int NW = gu_waves_c(L, FMT);
-        if constexpr (gu_all_passes_ok<FMT, L, C, NW>()) {
+        // (one token: 8 waves, whose registers hold every pass at once)
+        if constexpr (64 % (8 * (64 / L)) == 0 && gu_all_passes_ok<FMT, L, C, 8>()) {
             if (a.T == 1) {
-                launch_k(k_gate_up_mv<FMT, L, C, NW, TAP, true>, grid, dim3(NW * 64), lds, st, ev, a);
+                launch_k(k_gate_up_mv<FMT, L, C, 8, TAP, true>, grid, dim3(8 * 64), lds, st, ev, a);
                 break;
             }
         }
