@@ -230,6 +230,23 @@ __device__ __forceinline__ void stage_f32(const float* src, int K, const int32_t
 // 37.9 us, six-token 158.2 -> 144.6 us; a row that its workgroup re-reads for a
 // later chunk of tokens lost (the 32-token latent D in four-token chunks, 67 ->
 // 75 us) and should load plainly.
+// An empty asm that the compiler must assume rewrites a weight row's side data
+// in place: a value computed from it cannot move above this point.
+__device__ __forceinline__ void opaque_side(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque_side(uint2& v) {
+    asm volatile("" : "+v"(v.x));
+    asm volatile("" : "+v"(v.y));
+}
+__device__ __forceinline__ void opaque_side(v4i& v) {
+    int x = v.x, y = v.y, z = v.z, w = v.w;
+    asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
+    v = v4i{x, y, z, w};
+}
+__device__ __forceinline__ void opaque_side(K5Side& v) {
+    opaque_side(v.s);
+    opaque_side(v.qh);
+}
+
 template <int FMT, int LPR, int CPL, bool STREAM>
 __device__ __forceinline__ void load_row(const uint8_t* row, const typename Fmt<FMT>::SideMem* rscl,
                                          int sl, int NCH, v4i (&wq)[CPL],
@@ -359,8 +376,8 @@ __device__ __forceinline__ void pass_dot(const v4i (&wq)[CPL], const typename Fm
 // no register copy forces a wait.  A load past the last pass re-reads the last
 // pass's rows (it is never used) so that every load is unconditional.  On
 // entry A must hold pass 0 when `a_loaded`.
-template <int FMT, int LPR, int CPL, int NW, bool TAP, bool STREAM, int PASSES = 0, class Emit,
-          class EmitIsum>
+template <int FMT, int LPR, int CPL, int NW, bool TAP, bool STREAM, int PASSES = 0, bool FENCE = true,
+          class Emit, class EmitIsum>
 __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fmt<FMT>::SideMem* scl,
                                          size_t rowb,
                                          int nb, int rows, int n, int K, const int8_t* s_q,
@@ -373,10 +390,18 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sl = lane % LPR, rg = lane / LPR;
     const int passes = PASSES ? PASSES : rows / (NW * RPW);
+    // (opaque_side before each dot of buffer A keeps the scale conversions of
+    // rows loaded before the staging from being hoisted above it, where the
+    // staging would wait for them; placed after the next pass's loads are out.
+    // Measured on several passes: the gate/up slabs gain (latent_q4 at 32
+    // tokens 80.1 -> 76.5 us), the per-bucket rows lose (48.7 -> 58.3 us) and
+    // take FENCE = false)
     if constexpr (PASSES == 1) {
         // a single pass: one buffer
         const int r = wave * RPW + rg;
         if (!a_loaded) load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wA, sA);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) opaque_side(sA[j]);
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, r, sl, NCH, nb, n, K, s_q, s_d, s_sq, emit, emit_isum,
                                      tap);
         return;
@@ -392,6 +417,10 @@ __device__ __forceinline__ void row_tile(const uint8_t* codes, const typename Fm
         {
             const int r = row_of(p + 1);
             load_row<FMT, LPR, CPL, STREAM>(codes + r * rowb, scl + (size_t)r * (nb / F::SBLK), sl, NCH, wB, sB);
+        }
+        if constexpr (FENCE) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) opaque_side(sA[j]);
         }
         pass_dot<FMT, LPR, CPL, TAP>(wA, sA, row_of(p), sl, NCH, nb, n, K, s_q, s_d, s_sq, emit,
                                      emit_isum, tap);
@@ -434,23 +463,6 @@ __device__ __forceinline__ void publish_route(const RouteOut& R, int k, int E, c
 
 // (the second launch bound is the minimum number of waves per SIMD: 3 lets
 // three 4-wave workgroups share a CU)
-// An empty asm that the compiler must assume rewrites a weight row's side data
-// in place: a value computed from it cannot move above this point.
-__device__ __forceinline__ void opaque_side(uint32_t& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void opaque_side(uint2& v) {
-    asm volatile("" : "+v"(v.x));
-    asm volatile("" : "+v"(v.y));
-}
-__device__ __forceinline__ void opaque_side(v4i& v) {
-    int x = v.x, y = v.y, z = v.z, w = v.w;
-    asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
-    v = v4i{x, y, z, w};
-}
-__device__ __forceinline__ void opaque_side(K5Side& v) {
-    opaque_side(v.s);
-    opaque_side(v.qh);
-}
-
 // (ALL: a slab of at most four passes has all of them in registers at once, see
 // below; an instance of its own because the registers cost the occupancy that
 // the windows of several tokens need)
@@ -493,8 +505,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
             }
         }
     }
+    int8_t* s_q = reinterpret_cast<int8_t*>(smem);
+    float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
+    int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
+    float* s_gu = reinterpret_cast<float*>(smem + stage_bytes(TCH, K));
+    int32_t* s_a = reinterpret_cast<int32_t*>(s_gu + TCH * 64);
+    int32_t* s_t = s_a + TCH;
     int e, cnt;
     const int32_t* lst = nullptr;
+    // one token whose activations are already quantised (the plain layer's
+    // Q8_1(x)): its row is loaded before the routing, so that its loads overlap
+    // the logits' instead of following the first weights
+    const bool prestaged = A.route.part && !A.ain_f32 && K / 16 <= NW * 64;
+    v4i xq = v4i{0, 0, 0, 0};
+    uint32_t xds = 0u;
+    int32_t xsq = 0;
+    if (prestaged) {
+        // (registers now, LDS once the selection is done: the loads are then
+        // in flight together with the logits')
+        if ((int)threadIdx.x < K / 16) xq = ld16(A.ain.q + threadIdx.x * 16);
+        if ((int)threadIdx.x < nb) {
+            xds = A.ain.ds[threadIdx.x];
+            xsq = A.ain.sq[threadIdx.x];
+        }
+    }
     if (A.route.part) {
         // one token: the workgroup selects the experts (workgroup 0 also the
         // weights, and publishes the routing); slot j serves the rank-j expert,
@@ -508,6 +542,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         if (blockIdx.x == 0) publish_route<NW * 64>(A.rout, A.k, A.route.E, S, wt);
         e = __builtin_amdgcn_readfirstlane(S.sel[slot]);
         cnt = 1;
+        if (prestaged) {
+            if (threadIdx.x == 0) {
+                s_a[0] = slot;
+                s_t[0] = 0;
+            }
+            if ((int)threadIdx.x < K / 16) *reinterpret_cast<v4i*>(s_q + threadIdx.x * 16) = xq;
+            if ((int)threadIdx.x < nb) {
+                asm volatile("" : "+v"(xds));   // (no conversion above the selection)
+                s_d[threadIdx.x] = h2f(xds);
+                s_sq[threadIdx.x] = Fmt<FMT>::Q5 ? __float_as_int(h2f(xds >> 16)) : xsq;
+            }
+        }
     } else if (A.ids_direct) {
         // one token routed by the launch before: slot j serves the rank-j
         // expert, whose one assignment is a = j
@@ -579,15 +625,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     using SM = typename Fmt<FMT>::SideMem;
     const SM* scl = reinterpret_cast<const SM*>(ebase + A.gu_scales_off) + (size_t)fb * 64 * (nb / Fmt<FMT>::SBLK);
 
-    int8_t* s_q = reinterpret_cast<int8_t*>(smem);
-    float* s_d = reinterpret_cast<float*>(smem + (size_t)TCH * K);
-    int32_t* s_sq = reinterpret_cast<int32_t*>(smem + (size_t)TCH * K + (size_t)TCH * nb * 4);
-    float* s_gu = reinterpret_cast<float*>(smem + stage_bytes(TCH, K));
-    int32_t* s_a = reinterpret_cast<int32_t*>(s_gu + TCH * 64);
-    int32_t* s_t = s_a + TCH;
-
     // the first pass of weights (with ALL: every pass) is requested before the
-    // activations are staged
+    // activations are staged (a one-token row of quantised activations: staged
+    // in the prologue already)
     constexpr int RPW = 64 / LPR;
     constexpr int NBUF = ALLP ? PASSES : 1;
     const int sl = (threadIdx.x & 63) % LPR;
@@ -602,6 +642,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
     }
     for (int i0 = 0; i0 < cnt; i0 += TCH) {
         const int n = min(TCH, cnt - i0);
+        if (prestaged) {
+            __syncthreads();        // (the row staged after the selection)
+        } else {
         if (threadIdx.x < n) {
             const int a = lst ? lst[i0 + threadIdx.x] : slot;
             s_a[threadIdx.x] = a;
@@ -635,6 +678,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
         else
             stage_q<Fmt<FMT>::Q5>(A.ain, K, s_t, n, s_q, s_d, s_sq);
         __syncthreads();
+        }
         const bool tap = TAP && A.taps.isum_gu;
         auto emit = [&](int i, int r, float v) {
             // NVFP4: the gate (rows 0..31 of the slab) or up tensor scale
@@ -684,8 +728,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void k_gate_up_mv(GUArgs 
 
 
 // (SEL: the dense one-token form with the selection workgroup; an instance of
-// its own, as the selection's registers cost the expert rows kernels occupancy)
-template <int FMT, int LPR, int CPL, int NW, bool TAP, bool SEL = false>
+// its own, as the selection's registers cost the expert rows kernels occupancy.
+// ONE: a tile of one pass, known when compiled (the dense one-token D and U),
+// so that no second buffer re-requests the same rows; as a runtime case in
+// the general instance it cost the per-bucket rows at 20 and 32 tokens 10-20%)
+template <int FMT, int LPR, int CPL, int NW, bool TAP, bool SEL = false, bool ONE = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
     constexpr bool STREAM = true;   // one token (dense) or one bucket chunk (experts)
     extern __shared__ __align__(16) char smem[];
@@ -754,8 +801,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_rows_mv(RowsArgs A) {
             if (s_s[i] / A.tap_div < A.tap_tokens)
                 A.isum_tap[((size_t)s_s[i] * A.rows + r0 + r) * nb + blk] = v;
         };
-        row_tile<FMT, LPR, CPL, NW, TAP, STREAM>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d, s_sq, emit,
-                                         emit_isum, TAP && A.isum_tap, wA, sA, i0 == 0);
+        row_tile<FMT, LPR, CPL, NW, TAP, STREAM, ONE ? 1 : 0, false>(codes, scl, rowb, nb, A.rt, n, K, s_q, s_d,
+                                                                     s_sq, emit, emit_isum, TAP && A.isum_tap, wA,
+                                                                     sA, i0 == 0);
         __syncthreads();
     }
 }
@@ -1061,11 +1109,25 @@ template <int FMT, bool TAP>
 hipError_t rows_fmt(int lpr, int cpl, dim3 grid, size_t lds, const RowsArgs& a,
                            hipStream_t st) {
     MOE_LPR_CPL_SWITCH(lpr, cpl, ({
+        // one pass of rows per tile in the dense one-token form
+        const bool one = !a.b.ctrl && a.T == 1 && a.rt == ROWS_NW * (64 / L);
         if (a.route.part) {
-            if constexpr (FMT == MOE_FMT_Q8_0 || FMT == MOE_FMT_Q4_0)
-                hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP, true>), grid, dim3(ROWS_NW * 64), lds, st, a);
-            else
+            if constexpr (FMT == MOE_FMT_Q8_0 || FMT == MOE_FMT_Q4_0) {
+                if (one)
+                    hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP, true, true>), grid, dim3(ROWS_NW * 64),
+                                       lds, st, a);
+                else
+                    hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP, true>), grid, dim3(ROWS_NW * 64), lds,
+                                       st, a);
+            } else {
                 return hipErrorInvalidValue;      // (the dense formats only)
+            }
+        } else if (one) {
+            if constexpr (FMT == MOE_FMT_Q8_0 || FMT == MOE_FMT_Q4_0)
+                hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP, false, true>), grid, dim3(ROWS_NW * 64),
+                                   lds, st, a);
+            else
+                hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), lds, st, a);
         } else {
             hipLaunchKernelGGL((k_rows_mv<FMT, L, C, ROWS_NW, TAP>), grid, dim3(ROWS_NW * 64), lds, st, a);
         }
