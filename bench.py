@@ -113,12 +113,19 @@ class HipEvents:
         self.lib.hipEventDestroy(e)
 
 
+# The sources that the decode gate/up kernel (the roofline kernel of the
+# default workload) is compiled and launched from: its translation unit, the
+# headers it includes, its launcher and the forward call that picks it.
+GATE_UP_SOURCES = ("mv_q8_0.hip", "matvec_kern.h", "matvec.h", "select.h", "kernels.h", "device.h",
+                   "moe_internal.h", "matvec.hip", "capi.cpp")
+
+
 def src_hash() -> str:
+    """Hash of GATE_UP_SOURCES: a traffic record counts only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in GATE_UP_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
