@@ -515,8 +515,11 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
     // 2 to DECODE_T tokens whose down projection runs per token: no buckets;
     // the gate/up kernel takes its expert and tokens from the routing ids
     const bool ids_only = T >= 2 && T <= DECODE_T && down_tok;
+    // ... and in a latent layer those tokens are selected by T more workgroups
+    // of the few-token D launch, which does not depend on the routing
+    const bool sel_in_thin = ids_only && thin;
     CK(launch_router(m, w, ws, x, T, router_w, router_b, groups, taps ? taps->logits : nullptr, xq,
-                     ids_only, &routed, &sel, st), "router");
+                     ids_only, sel_in_thin, &routed, &sel, st), "router");
     if (routed == ROUTE_SELECTED) CK(launch_bucket(m, w, ws, T, st), "bucketing");
     RouteOut rout{(int32_t*)(ws + w.ids), (float*)(ws + w.wts), (int32_t*)(ws + w.counts),
                   (int32_t*)(ws + w.lists), (uint32_t*)(ws + w.ctrl), (int32_t*)(ws + w.active)};
@@ -536,7 +539,9 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
             // K-sliced partial rows, added in slice order by the quantisation
             const int S = thin_splits(m.L, m.H / QK);
             float* zp = S > 1 ? (float*)(ws + w.dpart) : z;
-            CK(launch_dense_thin(m.D, (const uint8_t*)Dp, T, xq, zp, S, tp.isum_d, tp.tap_tokens, st), "D");
+            CK(launch_dense_thin(m.D, (const uint8_t*)Dp, T, xq, zp, S, tp.isum_d, tp.tap_tokens, st,
+                                 routed == ROUTE_DEFERRED ? &sel : nullptr, (int32_t*)(ws + w.ids),
+                                 (float*)(ws + w.wts)), "D");
             CK(launch_quant_rows_sum(zp, S, S > 1 ? z : nullptr, T, m.L, zq, st), "Q8_1(z)");
         } else {
             CK(launch_dense_mv(m.D, (const uint8_t*)Dp, T, xq, nullptr, none, z, tp.isum_d,
@@ -559,11 +564,11 @@ static moe_status forward_impl(const moe_layer* L, const float* x, int T, const 
            "gate/up");
     else if (m.L)
         CK(launch_gate_up_mv(m, T, ex, zq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout,
-                             routed == ROUTE_IDS),
+                             routed == ROUTE_IDS || routed == ROUTE_DEFERRED),
            "gate/up");
     else
         CK(launch_gate_up_mv(m, T, ex, xq, nullptr, none, b, hq, tp, st, gev, gu_route, &rout,
-                             routed == ROUTE_IDS),
+                             routed == ROUTE_IDS || routed == ROUTE_DEFERRED),
            "gate/up");
     EV(MOE_EV_GATE_UP);
     float* comb = m.L ? ylat : out;     // the combined expert outputs

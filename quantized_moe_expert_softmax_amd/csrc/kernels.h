@@ -100,10 +100,13 @@ hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, i
 // DECODE_T tokens whose consumers read the ids: no buckets).  *done tells how
 // far the launched kernels go; *sel receives the selection parameters (for a
 // single token the gate/up kernel selects in its prologue from them).
-enum RouteDone { ROUTE_LOGITS, ROUTE_SELECTED, ROUTE_BUCKETED, ROUTE_IDS };
+// (ROUTE_DEFERRED: 2..DECODE_T tokens with defer_select, the logits only; the
+// launch after the router selects, writing the ids as ROUTE_IDS does)
+enum RouteDone { ROUTE_LOGITS, ROUTE_SELECTED, ROUTE_BUCKETED, ROUTE_IDS, ROUTE_DEFERRED };
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, bool ids_only, RouteDone* done, SelectArgs* sel, hipStream_t st);
+                         ActPtr xq, bool ids_only, bool defer_select, RouteDone* done, SelectArgs* sel,
+                         hipStream_t st);
 // Per-expert assignment lists in token order, the active experts, and the
 // token tiles (GEMM_TILE_M assignments) of each, numbered in tile_map.
 hipError_t launch_bucket(const Dims& m, const WsLayout& w, char* ws, int T, hipStream_t st);
@@ -162,8 +165,12 @@ hipError_t launch_dense_mfma(const MatLayout& W, const uint8_t* base, int T, Act
 // Few-token dense projection (T <= 32, Q8_0 or Q4_0, rows a multiple of 32):
 // out[s][t][r] over S K-slices (S divides the blocks per row; thin_splits).
 bool dense_thin_ok(const MatLayout& W, int T);
+// route != null: T more workgroups select each token's k experts from its
+// router logits (S = 1) and write ids / wts [T][k], in parallel with the tiles.
 hipError_t launch_dense_thin(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
-                             int S, int32_t* isum_tap, int tap_tokens, hipStream_t st);
+                             int S, int32_t* isum_tap, int tap_tokens, hipStream_t st,
+                             const SelectArgs* route = nullptr, int32_t* ids = nullptr,
+                             float* wts = nullptr);
 
 // Expert-address table: fill entries 0..E-1 with base + e * stride, or set
 // u.n (at most TABLE_UPDATE_MAX) entries, stream-ordered.

@@ -656,8 +656,8 @@ hipError_t launch_quant_rows_sum(const float* part, int S, float* x, int rows, i
 
 hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float* x, int T,
                          const float* Wr, const float* br, const int32_t* groups, double* logits_tap,
-                         ActPtr xq, bool ids_only, RouteDone* done, SelectArgs* sel,
-                         hipStream_t st) {
+                         ActPtr xq, bool ids_only, bool defer_select, RouteDone* done,
+                         SelectArgs* sel, hipStream_t st) {
     double* part = (double*)(ws + w.logit_part);
     const int S = w.S;
     const long qblocks = (long)T * (m.H / QK);
@@ -678,6 +678,8 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
                            m.E, part, xq);
         if (T <= ROUTE_DEC_MAX_T) {
             *done = ROUTE_LOGITS;
+        } else if (ids_only && defer_select) {
+            *done = ROUTE_DEFERRED;
         } else if (ids_only) {
             hipLaunchKernelGGL((k_route_select_tok<false, 1024>), dim3(T), dim3(1024), 0, st, a, ids,
                                wts, counts, lists, ctrl, active);

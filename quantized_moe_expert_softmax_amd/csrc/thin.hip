@@ -24,6 +24,7 @@
 // shared between workgroups.
 #include "kernels.h"
 #include "mfma_ops.h"
+#include "select.h"
 
 namespace moe {
 
@@ -38,18 +39,47 @@ struct ThinArgs {
     float* out;                 // [S][T][rows]
     int32_t* tap_isum;          // [T][rows][nb] block sums of tokens < tap_tokens, or null
     int tap_tokens;
+    // SEL: workgroups 0..T-1 select token t's experts from its whole router
+    // logits (route.part + t * E) and write ids / wts [T][k] in rank order; the
+    // tiles are the workgroups after them
+    SelectArgs route;
+    int32_t* ids;
+    float* wts;
 };
 
-template <int FMT, bool TAP>
+// (SEL: an instance of its own, so that the tiles of the plain instance keep
+// their registers)
+template <int FMT, bool TAP, bool SEL = false>
 __global__ __launch_bounds__(TH_NW * 64) void k_dense_thin(ThinArgs A) {
     constexpr bool Q4 = FMT == MOE_FMT_Q4_0;
     constexpr int CB = Q4 ? 16 : 32;        // code bytes per block
     // [wave][lane][result i], padded so that both the writes (lane-major) and
     // the reads (32 rows of one token) spread over the banks
-    __shared__ float red[TH_NW][64][17];
+    __shared__ __align__(16) float red[TH_NW][64][17];
+    static_assert(sizeof(red) >= sizeof(RouteLds), "the selection's LDS lives in red");
+
+    int bid = blockIdx.x;
+    if constexpr (SEL) {
+        if (bid < A.T) {
+            // one token's selection, in parallel with the tiles
+            const int t = bid;
+            SelectArgs sa = A.route;
+            sa.part += (size_t)t * sa.E;
+            if (sa.logits_tap) sa.logits_tap += (size_t)t * sa.E;
+            RouteLds& S = *reinterpret_cast<RouteLds*>(&red[0][0][0]);
+            float w = 0.0f;
+            select_wg<TH_NW * 64>(sa, S, true, &w);
+            if ((int)threadIdx.x < sa.k) {
+                A.ids[t * sa.k + threadIdx.x] = S.sel[threadIdx.x];
+                A.wts[t * sa.k + threadIdx.x] = w;
+            }
+            return;
+        }
+        bid -= A.T;
+    }
 
     const int ntile = A.rows / 32;
-    const int tile = blockIdx.x % ntile, s = blockIdx.x / ntile;
+    const int tile = bid % ntile, s = bid / ntile;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, half = lane >> 5;
     const int nb = A.nb, bps = nb / A.S;
@@ -128,9 +158,19 @@ bool dense_thin_ok(const MatLayout& W, int T) {
 }
 
 hipError_t launch_dense_thin(const MatLayout& W, const uint8_t* base, int T, ActPtr ain, float* out,
-                             int S, int32_t* isum_tap, int tap_tokens, hipStream_t st) {
+                             int S, int32_t* isum_tap, int tap_tokens, hipStream_t st,
+                             const SelectArgs* route, int32_t* ids, float* wts) {
     if (!dense_thin_ok(W, T) || S < 1 || W.nblk % S) return hipErrorInvalidValue;
-    ThinArgs a;
+    ThinArgs a{};
+    if (route) {
+        // whole logits of T tokens, within the selection's limits
+        if (!ids || !wts || route->S != 1 || route->T != T || route->E > 512 || route->k > 32 ||
+            route->G > 64)
+            return hipErrorInvalidValue;
+        a.route = *route;
+        a.ids = ids;
+        a.wts = wts;
+    }
     a.codes = base + W.codes_off;
     a.scl = reinterpret_cast<const uint16_t*>(base + W.scales_off);
     a.rows = W.rows; a.nb = W.nblk; a.T = T; a.S = S;
@@ -138,8 +178,22 @@ hipError_t launch_dense_thin(const MatLayout& W, const uint8_t* base, int T, Act
     a.out = out;
     a.tap_isum = isum_tap;
     a.tap_tokens = tap_tokens;
-    const dim3 grid((unsigned)((W.rows / 32) * S)), block(TH_NW * 64);
+    const dim3 grid((unsigned)((W.rows / 32) * S + (route ? T : 0))), block(TH_NW * 64);
     const bool tap = isum_tap != nullptr;
+    if (route) {
+        if (W.fmt == MOE_FMT_Q4_0) {
+            if (tap)
+                hipLaunchKernelGGL((k_dense_thin<MOE_FMT_Q4_0, true, true>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((k_dense_thin<MOE_FMT_Q4_0, false, true>), grid, block, 0, st, a);
+        } else {
+            if (tap)
+                hipLaunchKernelGGL((k_dense_thin<MOE_FMT_Q8_0, true, true>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((k_dense_thin<MOE_FMT_Q8_0, false, true>), grid, block, 0, st, a);
+        }
+        return hipGetLastError();
+    }
     if (W.fmt == MOE_FMT_Q4_0) {
         if (tap)
             hipLaunchKernelGGL((k_dense_thin<MOE_FMT_Q4_0, true>), grid, block, 0, st, a);
