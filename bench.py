@@ -324,19 +324,32 @@ def measure_cache(w, T, steps, warmup, pool=8):
                       "h2d_gbs": copied * w.expert_bytes / (admit_ms * 1e-3) / 1e9}}
 
 
+def probe_regions(sizes, min_total=2 << 30):
+    """Buffer size and regions of the HBM read probe: each size rounded down to
+    4 KiB, and a buffer of at least min_total bytes that holds at least two
+    disjoint regions of the largest size.  Returns (total, [(nbytes, nreg)]):
+    launch r of a size reads [(r % nreg) * nbytes, + nbytes), inside the buffer."""
+    sizes = [s // 4096 * 4096 for s in sizes]
+    if not sizes or min(sizes) <= 0:
+        raise ValueError(f"probe sizes must be at least 4 KiB: {sizes}")
+    total = max(min_total, 2 * max(sizes))
+    return total, [(s, total // s) for s in sizes]
+
+
 def hbm_probe(sizes, reps=20):
     """The box's single-launch HBM read rate, the ceiling the expert kernels are
     compared with: libmoe's read probe (include/moe_probe.h, 16-byte loads) over
     each size, one launch timed by its own dispatch events, swept over grid sizes,
     loads in flight per thread and the load kind; the best median is reported.
-    Launches rotate over disjoint regions of a 2 GiB buffer of random bytes, so no
-    launch is served from the 256 MB MALL by the previous ones."""
+    Launches rotate over disjoint regions of a buffer of random bytes (2 GiB, or
+    two of the largest size), so no launch is served from the 256 MB MALL by the
+    previous ones."""
     import numpy as np
     import torch
 
     from quantized_moe_expert_softmax_amd import moe
     dev = torch.device("cuda", 0)
-    total = 2 << 30
+    total, regions = probe_regions(sizes)
     buf = torch.randint(0, 256, (total,), dtype=torch.uint8, device=dev)
     blocks_opts, unroll_opts = (512, 1024, 2048, 4096, 8192), (2, 4, 8)
     sink = torch.empty(max(blocks_opts) * 256, dtype=torch.int32, device=dev)
@@ -344,16 +357,16 @@ def hbm_probe(sizes, reps=20):
     he = HipEvents()
     evs = [(he.create(), he.create()) for _ in range(reps)]
     res = []
-    for nbytes in sizes:
-        nbytes = nbytes // 4096 * 4096
-        nreg = max(2, total // nbytes)
+    for nbytes, nreg in regions:
         best = None
         for blocks in blocks_opts:
             for unroll in unroll_opts:
                 for nt in (0, moe.MOE_PROBE_NONTEMPORAL):
                     for r in range(reps + 3):
                         e = evs[r - 3] if r >= 3 else (0, 0)
-                        moe.moe_probe_read(buf.data_ptr() + (r % nreg) * nbytes, nbytes, blocks,
+                        off = (r % nreg) * nbytes
+                        assert off + nbytes <= buf.numel(), (off, nbytes, buf.numel())
+                        moe.moe_probe_read(buf.data_ptr() + off, nbytes, blocks,
                                            unroll, nt, sink.data_ptr(), st, *e)
                     torch.cuda.synchronize()
                     med = float(np.median([he.elapsed_ms(a, b) for a, b in evs]))
