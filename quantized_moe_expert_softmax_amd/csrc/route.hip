@@ -172,11 +172,13 @@ __global__ __launch_bounds__(256) void k_route_logits_mf(const float* __restrict
 // gate/up kernel; two to DECODE_T tokens are selected by k_route_select_tok.
 //
 // k_route_logits_dec: workgroups [0, E): expert e = blockIdx.x, 256 threads
-// over the H-wide row of W_r with every load issued at once (indices past the
-// row are clamped and masked), logits l[t][e] in fp64 for every token;
-// workgroups [E, E + nq): Q8_1(x).
-constexpr int ROUTE_U = 8;   // float4 per thread: H <= 8192
+// over the H-wide row of W_r with every load issued at once (ROUTE_U float4 per
+// thread, the fewest that cover the row; indices past the row are clamped and
+// masked), logits l[t][e] in fp64 for every token; workgroups [E, E + nq):
+// Q8_1(x).
+constexpr int ROUTE_U_MAX = 8;   // float4 per thread: H <= 8192
 
+template <int ROUTE_U>
 __global__ __launch_bounds__(256) void k_route_logits_dec(const float* __restrict__ x,
                                                           const float* __restrict__ W, int T,
                                                           int H, int E, double* __restrict__ logits,
@@ -674,8 +676,18 @@ hipError_t launch_router(const Dims& m, const WsLayout& w, char* ws, const float
     int32_t* active = (int32_t*)(ws + w.active);
     if (T <= DECODE_T) {
         if (S != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_route_logits_dec, dim3(m.E + qwg), dim3(256), 0, st, x, Wr, T, m.H,
-                           m.E, part, xq);
+        const int h4 = m.H / 4;
+        const dim3 grid(m.E + qwg), block(256);
+        if (h4 <= 256)
+            hipLaunchKernelGGL(k_route_logits_dec<1>, grid, block, 0, st, x, Wr, T, m.H, m.E, part, xq);
+        else if (h4 <= 512)
+            hipLaunchKernelGGL(k_route_logits_dec<2>, grid, block, 0, st, x, Wr, T, m.H, m.E, part, xq);
+        else if (h4 <= 1024)
+            hipLaunchKernelGGL(k_route_logits_dec<4>, grid, block, 0, st, x, Wr, T, m.H, m.E, part, xq);
+        else if (h4 <= 256 * ROUTE_U_MAX)
+            hipLaunchKernelGGL(k_route_logits_dec<8>, grid, block, 0, st, x, Wr, T, m.H, m.E, part, xq);
+        else
+            return hipErrorInvalidValue;
         if (T <= ROUTE_DEC_MAX_T) {
             *done = ROUTE_LOGITS;
         } else if (ids_only && defer_select) {
