@@ -288,9 +288,13 @@ def test_nvfp4_latent_prefill():
 
 
 # path boundaries (single-token routing at T = 1, the per-token selection kernel with
-# bucketing up to 32 tokens, matrix-vector experts up to 32)
-# and the largest routing sizes the ABI accepts
+# bucketing up to 32 tokens, matrix-vector experts up to 32), the few-token router's
+# float4-per-thread sizes (H = 256 and 512: one, partly masked; 1280: two, the second
+# partly masked; 4096: four; 7168 and 8192: eight), and the largest routing sizes the
+# ABI accepts
 @pytest.mark.parametrize("kw", [
+    dict(hidden=1280, n_ff=768, tokens=1),
+    dict(hidden=1280, n_ff=768, n_groups=4, topk_groups=2, tokens=4),
     dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=8),
     dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=9),
     dict(n_experts=16, top_k=3, n_groups=4, topk_groups=2, tokens=32),
